@@ -1,0 +1,67 @@
+"""Plants plausible mistakes in the oracle (on the CPU) and checks that the
+pins in test_oracle_pins.py catch each one."""
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+import tests.test_oracle_pins as P
+
+
+def _swapped_gate_up(xrows, w13, w2, act):
+    I = w13.shape[0] // 2
+    return O.__dict__["_orig_gated_ffn"](xrows, np.concatenate([w13[I:], w13[:I]]), w2, act)
+
+
+def _fails(fn, *a, **k):
+    with pytest.raises(AssertionError):
+        fn(*a, **k)
+
+
+def test_swapped_gate_and_up_is_caught(monkeypatch):
+    monkeypatch.setitem(O.__dict__, "_orig_gated_ffn", O.gated_ffn)
+    monkeypatch.setattr(O, "gated_ffn", _swapped_gate_up)
+    _fails(P.test_brute_force_all_experts_then_mask, 17, 32, 5, 3, 16, "silu")
+
+
+def test_highest_index_tie_break_is_caught(monkeypatch):
+    def bad_topk(z, k):
+        z = np.asarray(z, dtype=np.float64)
+        E = z.shape[-1]
+        return (E - 1 - np.argsort(-z[..., ::-1], axis=-1, kind="stable"))[..., :k]
+    monkeypatch.setattr(O, "select_topk", bad_topk)
+    _fails(P.test_topk_brute_force_with_ties_and_signed_zero)
+
+
+def test_missing_renorm_is_caught(monkeypatch):
+    orig = O.route
+    monkeypatch.setattr(O, "route", lambda z, k, renormalize=True, per_expert_scale=None:
+                        orig(z, k, False, per_expert_scale))
+    _fails(P.test_closed_form_softmax_over_selected, 8, 2)
+    _fails(P.test_worked_example_from_page)
+
+
+def test_scale_indexed_by_slot_is_caught(monkeypatch):
+    orig = O.route
+
+    def bad(z, k, renormalize=True, per_expert_scale=None):
+        w, ids = orig(z, k, renormalize, None)
+        if per_expert_scale is not None:
+            w = w * np.asarray(per_expert_scale)[:k][None, :]
+        return w, ids
+    monkeypatch.setattr(O, "route", bad)
+    _fails(P.test_scale_fold_identity)
+
+
+def test_softmax_over_selected_only_is_caught_without_renorm(monkeypatch):
+    def bad_softmax(z):
+        z = np.asarray(z, dtype=np.float64)
+        e = np.exp(z - z.max(axis=-1, keepdims=True))
+        return e / e.max(axis=-1, keepdims=True)
+    monkeypatch.setattr(O, "softmax_all", bad_softmax)
+    _fails(P.test_no_renorm_is_full_softmax_gathered, 8, 2)
+
+
+def test_dropped_cubic_term_in_gelu_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "gelu_tanh", lambda a: 0.5 * a * (1 + np.tanh(np.sqrt(2 / np.pi) * a)))
+    monkeypatch.setitem(O.ACTIVATIONS, "gelu_tanh", O.gelu_tanh)
+    _fails(P.test_activations_match_torch)
