@@ -1,0 +1,216 @@
+/*
+ * moe.h - C ABI of libmoe_mi355x.so, the MoE FFN layer forward for one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Conventions for every entry point:
+ *   - All tensors are dense, row-major, contiguous device pointers (HIP device
+ *     memory the caller owns).  The library allocates no device memory and keeps
+ *     no state between calls; calls on different streams are independent.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work
+ *     is enqueued asynchronously on it; the call returns once it is enqueued.
+ *   - Arguments are validated on the host before anything is launched.  A bad
+ *     argument returns an error status and launches nothing; nothing is ever
+ *     skipped silently and no call aborts the process.  moe_last_error() gives
+ *     a description of the last failure on the calling thread.
+ *   - T = 0 is a valid no-op.
+ *   - bf16 is stored as uint16_t (the upper half of an IEEE fp32); fp8 weights are
+ *     OCP E4M3 ("fn": finite, max 448) codes stored as uint8_t.
+ *
+ * Citations name the web pages that describe each operation:
+ *   [G4] "Gemma 4 26B-A4B MoE walkthrough" (yeyulingfeng.com/587419)
+ *   [VD] vLLM API docs, vllm.model_executor.models.gemma4 (Gemma4MoE, Gemma4Router)
+ *   [MI] "MOE Inference" (gaohongy.github.io), gated FFN
+ *   [LC] llama.cpp visual guide, lesson 35 (MoE)
+ *   [SG] sglang PR #24696 summary (per-expert FP8 weights with weight_scale)
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_INVALID_ARG = 1,          /* null pointer, bad size, bad enum value */
+  MOE_UNSUPPORTED = 2,          /* valid request the kernels do not cover (e.g. H % 64 != 0) */
+  MOE_WORKSPACE_TOO_SMALL = 3,  /* workspace smaller than moe_forward_workspace_size() */
+  MOE_HIP_ERROR = 4             /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum { MOE_ACT_SILU = 0, MOE_ACT_GELU_TANH = 1 } moe_act;
+typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1, MOE_DT_FP8_E4M3 = 2 } moe_dtype;
+typedef enum { MOE_ROUTER_PLAIN = 0, MOE_ROUTER_GEMMA = 1 } moe_router_mode;
+
+/* Human-readable name of a status code (static storage). */
+const char* moe_status_string(moe_status s);
+/* Description of the last error on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/*
+ * moe_route - softmax over all experts, top-k, renormalisation and the
+ * per-expert scale fold, one token per wavefront.
+ *
+ * Defined by [G4] section 4 (routing maths) and section 5 (per-expert scale),
+ * and the routing function of Gemma4MoE in [VD]; [LC] routing (softmax ->
+ * argsort_top_k -> get_rows -> normalise) is the same with unit scales.
+ * For each token t:
+ *   ids[t, 0..K-1] = the K largest logits, largest first; ties go to the lower
+ *                    expert index and -0.0 equals +0.0;
+ *   renorm != 0:     w[t, j] = exp(z_ids_j) / sum_{i<K} exp(z_ids_i)
+ *                    (= softmax over all E, masked to the top-K, renormalised);
+ *   renorm == 0:     w[t, j] = softmax over all E at ids_j;
+ *   then             w[t, j] *= per_expert_scale[ids_j]   (1 when NULL).
+ *
+ *   logits            [T, E] fp32, finite (non-finite logits give undefined ids).
+ *   per_expert_scale  [E] fp32 or NULL.
+ *   topk_w            [T, K] fp32 out.   topk_ids [T, K] int32 out.
+ * Limits: 1 <= K <= E <= 512, K <= 64.  T >= 0.
+ */
+moe_status moe_route(const float* logits, int64_t T, int32_t E, int32_t K, int32_t renorm,
+                     const float* per_expert_scale, float* topk_w, int32_t* topk_ids,
+                     void* stream);
+
+/*
+ * Capacity (number of int32 entries) sorted_slots must hold for moe_permute:
+ * floor((T*K + E*(block_m-1)) / block_m) * block_m.  Returns -1 on bad arguments.
+ */
+int64_t moe_permute_capacity(int64_t T, int32_t K, int32_t E, int32_t block_m);
+
+/*
+ * moe_permute - the dispatch permutation map: (token, slot) pairs regrouped
+ * expert-major without copying any token data ([G4] sections 6-7: dispatch
+ * builds a permutation map that the grouped GEMM reads indirectly).
+ *
+ * Flat slot f = t*K + j refers to topk_ids[t, j].  Expert e's segment is
+ * sorted_slots[offsets[e] .. offsets[e] + counts[e]) and lists its flat slots
+ * in ascending order (a stable sort by expert); the segment is then padded with
+ * -1 up to a multiple of block_m, so offsets[e+1] - offsets[e] =
+ * ceil(counts[e] / block_m) * block_m and offsets[E] is the padded total.
+ * block_expert[b] = expert owning rows [b*block_m, (b+1)*block_m) for
+ * b < offsets[E] / block_m.  Entries past offsets[E] are left untouched.
+ *
+ *   topk_ids      [T, K] int32, each in [0, E).
+ *   counts        [E] int32 out.          offsets [E+1] int32 out.
+ *   sorted_slots  [moe_permute_capacity(T,K,E,block_m)] int32 out.
+ *   block_expert  [capacity / block_m] int32 out.
+ * Limits: block_m a power of two in [16, 256]; 1 <= K <= 64; 1 <= E <= 1024;
+ * T*K < 2^31.  Expert ids outside [0, E) are a precondition violation: those
+ * slots are dropped from every segment (the counts then sum to less than T*K).
+ */
+moe_status moe_permute(const int32_t* topk_ids, int64_t T, int32_t K, int32_t E, int32_t block_m,
+                       int32_t* counts, int32_t* offsets, int32_t* sorted_slots,
+                       int32_t* block_expert, void* stream);
+
+/* Layer description (host memory, read during the call only). */
+typedef struct {
+  int32_t hidden;        /* H, multiple of 64 */
+  int32_t num_experts;   /* E routed experts, 1..512 */
+  int32_t top_k;         /* K, 1..min(E, 64) */
+  int32_t inter;         /* I of every routed expert, multiple of 64 */
+  int32_t act;           /* moe_act of the routed / shared experts */
+  int32_t act_dtype;     /* MOE_DT_F32 or MOE_DT_BF16: x, out, router / shared / dense weights */
+  int32_t weight_dtype;  /* routed expert weights: F32 (needs act F32), BF16, or FP8_E4M3 (needs BF16) */
+  int32_t renormalize;   /* non-zero: renormalise the top-k weights (see moe_route) */
+  int32_t router_mode;   /* moe_router_mode, used when logits are computed */
+  int32_t n_shared;      /* always-on shared experts (weight 1, same I), 0..8 */
+  int32_t inter_dense;   /* > 0: parallel dense MLP of this I with Gemma post-norms; 0: none */
+  int32_t dense_act;     /* moe_act of the dense MLP */
+  float eps;             /* RMSNorm epsilon (router preprocessing and Gemma norms) */
+} moe_layer_desc;
+
+/* Tensors of one forward call (device pointers unless noted). */
+typedef struct {
+  const void* x;                  /* [T, H] act_dtype */
+  const float* logits;            /* [T, E] fp32 router logits, or NULL: computed from x */
+  const void* w_router;           /* [E, H] act_dtype (needed when logits == NULL) */
+  const float* router_scale;      /* [H] learned per-dimension router scale, NULL = ones (Gemma mode) */
+  const float* per_expert_scale;  /* [E], NULL = ones */
+  const void* w13;                /* [E, 2I, H]: rows [0,I) gate (w1), rows [I,2I) up (w3) */
+  const void* w2;                 /* [E, H, I] down projection */
+  const float* w13_scale;         /* [E, 2I] per-output-channel fp32 scales (FP8 only) */
+  const float* w2_scale;          /* [E, H] (FP8 only) */
+  const void* shared_w13;         /* [n_shared, 2I, H] act_dtype, or NULL when n_shared == 0 */
+  const void* shared_w2;          /* [n_shared, H, I] */
+  const void* dense_w13;          /* [2*inter_dense, H] act_dtype (gate rows first) */
+  const void* dense_w2;           /* [H, inter_dense] */
+  const float* gamma_pre;         /* [H] pre_feedforward_layernorm weight (dense input), NULL = ones */
+  const float* gamma_pre2;        /* [H] pre_feedforward_layernorm_2 weight (expert input), NULL = ones */
+  const float* gamma_post1;       /* [H] post norm of the dense branch, NULL = ones */
+  const float* gamma_post2;       /* [H] post norm of the MoE branch, NULL = ones */
+  void* out;                      /* [T, H] act_dtype, overwritten */
+  float* logits_out;              /* optional [T, E]: the logits the routing used */
+  float* topk_w_out;              /* optional [T, K] */
+  int32_t* topk_ids_out;          /* optional [T, K] */
+  float* out_f32;                 /* optional [T, H] fp32: the output before its final rounding to act_dtype */
+} moe_tensors;
+
+/*
+ * Bytes of workspace moe_forward needs for T tokens (*bytes set on MOE_OK).
+ */
+moe_status moe_forward_workspace_size(const moe_layer_desc* desc, int64_t T, size_t* bytes);
+
+/*
+ * moe_forward - the MoE FFN layer forward.
+ *
+ *   z      = logits if given, else r . W_router^T in fp32, where r = x (plain
+ *            router) or r = RMSNorm_without_gamma(x) * H^-0.5 * router_scale
+ *            (Gemma router: [G4] section 3, Gemma4Router.forward in [VD]);
+ *   w, ids = moe_route(z)                       ([G4] sections 4-5);
+ *   dispatch by moe_permute, no token copies    ([G4] sections 6-7);
+ *   per expert e and routed row: h = act(x_e W1_e^T) * (x_e W3_e^T), y = h W2_e^T
+ *            (gated FFN, [MI]; activation SiLU [LC] or GELU-tanh [G4] section 6);
+ *            x_e = RMSNorm(x) * gamma_pre2 when the dense branch is present, else x;
+ *            FP8 weights: W = decode_e4m3(q) * scale[e, n] ([SG]);
+ *   moe_t  = sum_j w[t,j] y_{t,j}              (weighted combine, [G4] section 7);
+ *   shared experts: moe_t += sum_s FFN_s(x_t) with weight 1 ([LC] shared expert);
+ *   dense branch (inter_dense > 0, [G4] section 1):
+ *            out = RMSNorm(MLP(RMSNorm(x)*gamma_pre))*gamma_post1 + RMSNorm(moe)*gamma_post2;
+ *   otherwise out = moe.
+ * The decoder layer's final post-norm and residual add are not part of it.
+ *
+ * Precision: bf16 operands with fp32 accumulation (fp32 throughout for
+ * act_dtype F32); the gated intermediate and the per-slot expert outputs are
+ * rounded to bf16 in the bf16 path; logits are fp32.
+ *
+ * workspace: device memory of at least moe_forward_workspace_size() bytes,
+ * 256-byte aligned, owned by the caller; contents on entry do not matter and
+ * are clobbered.  Two calls that share a workspace must be stream-ordered.
+ */
+moe_status moe_forward(const moe_layer_desc* desc, const moe_tensors* tensors, int64_t T,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stages of moe_forward, in launch order (indices into the event array below). */
+typedef enum {
+  MOE_STAGE_PRENORM = 0,        /* 1/rms per token (+ rows with learned norm weights) */
+  MOE_STAGE_ROUTER = 1,         /* router logits GEMM */
+  MOE_STAGE_ROUTE = 2,          /* moe_route */
+  MOE_STAGE_PERMUTE = 3,        /* moe_permute */
+  MOE_STAGE_GATE_UP = 4,        /* grouped gate/up GEMM + gated activation */
+  MOE_STAGE_DOWN = 5,           /* grouped down GEMM + routing-weight scatter */
+  MOE_STAGE_DENSE_GATE_UP = 6,  /* dense MLP gate/up GEMM */
+  MOE_STAGE_DENSE_DOWN = 7,     /* dense MLP down GEMM */
+  MOE_STAGE_FINALIZE = 8,       /* per-token combine, post-norms, output rounding */
+  MOE_STAGE_COUNT = 9
+} moe_stage;
+
+/*
+ * moe_forward_profiled - moe_forward (same operation, arguments and errors)
+ * that also records caller-created HIP events (hipEvent_t passed as void*) on
+ * `stream`: events[i] just before stage i and events[MOE_STAGE_COUNT] after the
+ * last one, so hipEventElapsedTime(events[i], events[i+1]) is the time of stage
+ * i.  A stage that does not run for this layer gets two back-to-back records.
+ * It only records: nothing is synchronised.  For measurement.
+ */
+moe_status moe_forward_profiled(const moe_layer_desc* desc, const moe_tensors* tensors, int64_t T,
+                                void* workspace, size_t workspace_bytes, void* stream,
+                                void* const* events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,434 @@
+// C ABI of the MoE FFN layer forward: host-side validation, workspace
+// planning and the launch sequence.  Every argument is checked before the
+// first launch; errors come back as status codes with a message in
+// moe_last_error(), never as a silent skip or an abort.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cmath>
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+moe_status hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(call, what)                      \
+  do {                                           \
+    hipError_t _e = (call);                      \
+    if (_e != hipSuccess) return hip_fail(_e, what); \
+  } while (0)
+
+constexpr size_t ALIGN = 256;
+size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+
+int log2_exact(int v) {
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return (1 << l) == v ? l : -1;
+}
+
+int64_t permute_capacity(int64_t n_slots, int E, int bm) {
+  return (n_slots + (int64_t)E * (bm - 1)) / bm * bm;
+}
+
+// Row-block height of the grouped GEMMs: 256-row blocks once an expert gets
+// enough rows on average to fill them, 64 otherwise; 64 for the fp32 layer.
+int choose_block_m(const moe_layer_desc& d, int64_t T) {
+  if (d.act_dtype == MOE_DT_F32) return 64;
+  const int64_t avg = T * d.top_k / d.num_experts;
+  return avg >= 256 ? 256 : 64;
+}
+
+struct Plan {
+  bool f32;
+  int Kp, Ep, bm;
+  int64_t cap;
+  bool need_logits, need_prenorm, gemma_router, dense;
+  bool mat_r, mat_xn1, mat_xn2;  // normalised rows that must be materialised (learned weight present)
+  bool y_f32;                    // per-slot expert outputs kept in fp32
+  size_t o_logits, o_w, o_ids, o_counts, o_offsets, o_sorted, o_bexp, o_rms, o_r, o_xn1, o_xn2, o_h, o_y,
+      o_dh, o_dout, total;
+};
+
+moe_status validate_desc(const moe_layer_desc* d) {
+  if (!d) return fail(MOE_INVALID_ARG, "desc is NULL");
+  if (d->hidden <= 0 || d->num_experts <= 0 || d->top_k <= 0 || d->inter <= 0)
+    return fail(MOE_INVALID_ARG, "hidden, num_experts, top_k and inter must be positive");
+  if (d->num_experts > 512) return fail(MOE_UNSUPPORTED, "num_experts %d > 512", d->num_experts);
+  if (d->top_k > d->num_experts) return fail(MOE_INVALID_ARG, "top_k %d > num_experts %d", d->top_k, d->num_experts);
+  if (d->n_shared < 0 || d->n_shared > 8) return fail(MOE_INVALID_ARG, "n_shared %d outside [0, 8]", d->n_shared);
+  if (d->top_k + d->n_shared > 64) return fail(MOE_UNSUPPORTED, "top_k + n_shared > 64");
+  if (d->hidden % 64 || d->inter % 64)
+    return fail(MOE_UNSUPPORTED, "hidden (%d) and inter (%d) must be multiples of 64", d->hidden, d->inter);
+  if (d->hidden > 8192) return fail(MOE_UNSUPPORTED, "hidden %d > 8192", d->hidden);
+  if (d->inter_dense < 0 || d->inter_dense % 64)
+    return fail(d->inter_dense < 0 ? MOE_INVALID_ARG : MOE_UNSUPPORTED, "inter_dense %d must be a multiple of 64", d->inter_dense);
+  if (d->act != MOE_ACT_SILU && d->act != MOE_ACT_GELU_TANH) return fail(MOE_INVALID_ARG, "unknown activation %d", d->act);
+  if (d->inter_dense && d->dense_act != MOE_ACT_SILU && d->dense_act != MOE_ACT_GELU_TANH)
+    return fail(MOE_INVALID_ARG, "unknown dense activation %d", d->dense_act);
+  if (d->act_dtype != MOE_DT_F32 && d->act_dtype != MOE_DT_BF16)
+    return fail(MOE_INVALID_ARG, "act_dtype must be F32 or BF16");
+  if (d->act_dtype == MOE_DT_F32 && d->weight_dtype != MOE_DT_F32)
+    return fail(MOE_UNSUPPORTED, "an fp32 layer needs fp32 expert weights");
+  if (d->act_dtype == MOE_DT_BF16 && d->weight_dtype != MOE_DT_BF16 && d->weight_dtype != MOE_DT_FP8_E4M3)
+    return fail(MOE_UNSUPPORTED, "a bf16 layer needs bf16 or fp8 expert weights");
+  if (d->weight_dtype == MOE_DT_FP8_E4M3 && d->n_shared)
+    return fail(MOE_UNSUPPORTED, "shared experts with fp8 routed experts");
+  if (d->router_mode != MOE_ROUTER_PLAIN && d->router_mode != MOE_ROUTER_GEMMA)
+    return fail(MOE_INVALID_ARG, "unknown router mode %d", d->router_mode);
+  if (!(d->eps >= 0.f)) return fail(MOE_INVALID_ARG, "eps must be >= 0");
+  return MOE_OK;
+}
+
+moe_status make_plan(const moe_layer_desc& d, const moe_tensors* t, int64_t T, Plan& p) {
+  p.f32 = d.act_dtype == MOE_DT_F32;
+  p.Kp = d.top_k + d.n_shared;
+  p.Ep = d.num_experts + d.n_shared;
+  p.bm = choose_block_m(d, T);
+  const int64_t slots = T * p.Kp;
+  if (slots >= (int64_t)1 << 31) return fail(MOE_UNSUPPORTED, "T * (top_k + n_shared) >= 2^31");
+  p.cap = permute_capacity(slots, p.Ep, p.bm);
+  // Every GEMM operand is addressed through a buffer resource with 32-bit offsets.
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t wb = d.weight_dtype == MOE_DT_FP8_E4M3 ? 1 : (d.weight_dtype == MOE_DT_F32 ? 4 : 2);
+  if (T * d.hidden * 4 >= lim || p.cap * d.inter * 4 >= lim || T * (int64_t)d.inter_dense * 4 >= lim)
+    return fail(MOE_UNSUPPORTED, "T = %lld too large: an activation buffer would exceed 2 GiB", (long long)T);
+  if ((int64_t)2 * d.inter * d.hidden * wb >= lim || (int64_t)2 * d.inter_dense * d.hidden * 4 >= lim ||
+      (int64_t)d.num_experts * d.hidden * 4 >= lim)
+    return fail(MOE_UNSUPPORTED, "one expert's weights exceed 2 GiB");
+  p.need_logits = !(t && t->logits);
+  p.gemma_router = p.need_logits && d.router_mode == MOE_ROUTER_GEMMA;
+  p.dense = d.inter_dense > 0;
+  p.need_prenorm = p.gemma_router || p.dense;
+  // Without a tensor set (workspace query) size for the case that materialises every row.
+  p.mat_r = p.gemma_router && (!t || t->router_scale);
+  p.mat_xn1 = p.dense && (!t || t->gamma_pre);
+  p.mat_xn2 = p.dense && (!t || t->gamma_pre2);
+  const size_t ae = p.f32 ? 4 : 2;  // activation element bytes
+  // With the dense branch the MoE sum is RMS-normalised afterwards, which turns
+  // its relative error into error at output scale: keep the per-slot rows fp32.
+  p.y_f32 = p.f32 || p.dense;
+  const size_t H = d.hidden;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t r = o;
+    o = align_up(o + bytes);
+    return r;
+  };
+  p.o_logits = take(p.need_logits ? (size_t)T * d.num_experts * 4 : 0);
+  p.o_w = take((size_t)slots * 4);
+  p.o_ids = take((size_t)slots * 4);
+  p.o_counts = take((size_t)p.Ep * 4);
+  p.o_offsets = take((size_t)(p.Ep + 1) * 4);
+  p.o_sorted = take((size_t)p.cap * 4);
+  p.o_bexp = take((size_t)(p.cap / p.bm) * 4);
+  p.o_rms = take(p.need_prenorm ? (size_t)T * 4 : 0);
+  p.o_r = take(p.mat_r ? (size_t)T * H * ae : 0);
+  p.o_xn1 = take(p.mat_xn1 ? (size_t)T * H * ae : 0);
+  p.o_xn2 = take(p.mat_xn2 ? (size_t)T * H * ae : 0);
+  p.o_h = take((size_t)p.cap * d.inter * ae);
+  p.o_y = take((size_t)slots * H * (p.y_f32 ? 4 : ae));
+  p.o_dh = take(p.dense ? (size_t)T * d.inter_dense * ae : 0);
+  p.o_dout = take(p.dense ? (size_t)T * H * 4 : 0);
+  p.total = o;
+  return MOE_OK;
+}
+
+moe_status validate_tensors(const moe_layer_desc& d, const moe_tensors* t) {
+  if (!t) return fail(MOE_INVALID_ARG, "tensors is NULL");
+  if (!t->x || !t->w13 || !t->w2 || !t->out) return fail(MOE_INVALID_ARG, "x, w13, w2 and out are required");
+  if (!t->logits && !t->w_router) return fail(MOE_INVALID_ARG, "either logits or w_router is required");
+  if (d.weight_dtype == MOE_DT_FP8_E4M3 && (!t->w13_scale || !t->w2_scale))
+    return fail(MOE_INVALID_ARG, "fp8 weights need w13_scale and w2_scale");
+  if (d.n_shared && (!t->shared_w13 || !t->shared_w2))
+    return fail(MOE_INVALID_ARG, "n_shared > 0 needs shared_w13 and shared_w2");
+  if (d.inter_dense && (!t->dense_w13 || !t->dense_w2))
+    return fail(MOE_INVALID_ARG, "inter_dense > 0 needs dense_w13 and dense_w2");
+  return MOE_OK;
+}
+
+}  // namespace
+
+MOE_API const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_INVALID_ARG: return "MOE_INVALID_ARG";
+    case MOE_UNSUPPORTED: return "MOE_UNSUPPORTED";
+    case MOE_WORKSPACE_TOO_SMALL: return "MOE_WORKSPACE_TOO_SMALL";
+    case MOE_HIP_ERROR: return "MOE_HIP_ERROR";
+  }
+  return "MOE_UNKNOWN_STATUS";
+}
+
+MOE_API const char* moe_last_error(void) { return g_err; }
+
+MOE_API moe_status moe_route(const float* logits, int64_t T, int32_t E, int32_t K, int32_t renorm,
+                             const float* per_expert_scale, float* topk_w, int32_t* topk_ids, void* stream) {
+  g_err[0] = 0;
+  if (T < 0) return fail(MOE_INVALID_ARG, "T < 0");
+  if (E < 1 || K < 1 || K > E) return fail(MOE_INVALID_ARG, "need 1 <= K <= E (K=%d, E=%d)", K, E);
+  if (E > 512 || K > 64) return fail(MOE_UNSUPPORTED, "E <= 512 and K <= 64 are supported");
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_w || !topk_ids) return fail(MOE_INVALID_ARG, "logits, topk_w and topk_ids are required");
+  if (T > ((int64_t)1 << 32)) return fail(MOE_UNSUPPORTED, "T too large");
+  HIP_TRY(moe::launch_route(logits, T, E, K, renorm, per_expert_scale, topk_w, topk_ids, K, 0,
+                            (hipStream_t)stream),
+          "route launch");
+  return MOE_OK;
+}
+
+MOE_API int64_t moe_permute_capacity(int64_t T, int32_t K, int32_t E, int32_t block_m) {
+  if (T < 0 || K < 1 || E < 1 || log2_exact(block_m) < 4 || block_m > 256) return -1;
+  return permute_capacity(T * K, E, block_m);
+}
+
+MOE_API moe_status moe_permute(const int32_t* topk_ids, int64_t T, int32_t K, int32_t E, int32_t block_m,
+                               int32_t* counts, int32_t* offsets, int32_t* sorted_slots, int32_t* block_expert,
+                               void* stream) {
+  g_err[0] = 0;
+  if (T < 0) return fail(MOE_INVALID_ARG, "T < 0");
+  if (K < 1 || K > 64) return fail(MOE_INVALID_ARG, "K %d outside [1, 64]", K);
+  if (E < 1 || E > 1024) return fail(MOE_INVALID_ARG, "E %d outside [1, 1024]", E);
+  const int l2 = log2_exact(block_m);
+  if (l2 < 4 || block_m > 256) return fail(MOE_INVALID_ARG, "block_m %d must be a power of two in [16, 256]", block_m);
+  if (T * K >= ((int64_t)1 << 31)) return fail(MOE_UNSUPPORTED, "T*K >= 2^31");
+  if (!counts || !offsets || !sorted_slots || !block_expert || (T > 0 && !topk_ids))
+    return fail(MOE_INVALID_ARG, "null output pointer");
+  HIP_TRY(moe::launch_permute(topk_ids, T * K, E, l2, counts, offsets, sorted_slots, block_expert,
+                              (hipStream_t)stream),
+          "permute launch");
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_forward_workspace_size(const moe_layer_desc* desc, int64_t T, size_t* bytes) {
+  g_err[0] = 0;
+  moe_status s = validate_desc(desc);
+  if (s != MOE_OK) return s;
+  if (T < 0) return fail(MOE_INVALID_ARG, "T < 0");
+  if (!bytes) return fail(MOE_INVALID_ARG, "bytes is NULL");
+  Plan p;
+  // Size for computed logits (the larger case); supplied logits need less.
+  s = make_plan(*desc, nullptr, T, p);
+  if (s != MOE_OK) return s;
+  *bytes = p.total;
+  return MOE_OK;
+}
+
+static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t, int64_t T, void* workspace,
+                               size_t workspace_bytes, void* stream, void* const* events) {
+  g_err[0] = 0;
+  moe_status s = validate_desc(desc);
+  if (s != MOE_OK) return s;
+  const moe_layer_desc& d = *desc;
+  s = validate_tensors(d, t);
+  if (s != MOE_OK) return s;
+  if (T < 0) return fail(MOE_INVALID_ARG, "T < 0");
+  if (T == 0) return MOE_OK;
+  Plan p;
+  s = make_plan(d, t, T, p);
+  if (s != MOE_OK) return s;
+  if (!workspace || workspace_bytes < p.total)
+    return fail(MOE_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, p.total);
+  if ((uintptr_t)workspace % ALIGN) return fail(MOE_INVALID_ARG, "workspace must be 256-byte aligned");
+
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* ws = (uint8_t*)workspace;
+  const int H = d.hidden, E = d.num_experts, K = d.top_k, I = d.inter;
+  const int act_elem = p.f32 ? moe::ELEM_F32 : moe::ELEM_BF16;
+  const int b_elem = d.weight_dtype == MOE_DT_FP8_E4M3 ? moe::ELEM_FP8 : moe::ELEM_BF16;
+  float* w = (float*)(ws + p.o_w);
+  int32_t* ids = (int32_t*)(ws + p.o_ids);
+  int32_t* counts = (int32_t*)(ws + p.o_counts);
+  int32_t* offsets = (int32_t*)(ws + p.o_offsets);
+  int32_t* sorted = (int32_t*)(ws + p.o_sorted);
+  int32_t* bexp = (int32_t*)(ws + p.o_bexp);
+  float* inv_rms = p.need_prenorm ? (float*)(ws + p.o_rms) : nullptr;
+  void* r_in = p.mat_r ? ws + p.o_r : nullptr;
+  void* xn1 = p.mat_xn1 ? ws + p.o_xn1 : nullptr;
+  void* xn2 = p.mat_xn2 ? ws + p.o_xn2 : nullptr;
+  void* h = ws + p.o_h;
+  void* y = ws + p.o_y;
+  void* dh = p.dense ? ws + p.o_dh : nullptr;
+  float* dout = p.dense ? (float*)(ws + p.o_dout) : nullptr;
+
+  auto gemm = [&](const moe::GemmArgs& a, int epi, int belem, int bm) -> hipError_t {
+    return p.f32 ? moe::launch_gemm_f32(a, epi, st) : moe::launch_gemm_mfma(a, epi, belem, bm, st);
+  };
+  auto mark = [&](int stage) -> hipError_t {
+    return events ? hipEventRecord((hipEvent_t)events[stage], st) : hipSuccess;
+  };
+#define STAGE(i) HIP_TRY(mark(i), "event record")
+
+  STAGE(MOE_STAGE_PRENORM);
+  // 1. input norms (Gemma router preprocessing, pre_feedforward_layernorm / _2):
+  //    1/rms per token; normalised rows only where a learned weight is given.
+  if (p.need_prenorm)
+    HIP_TRY(moe::launch_prenorm(t->x, act_elem, T, H, d.eps, inv_rms, t->router_scale, t->gamma_pre,
+                                t->gamma_pre2, r_in, xn1, xn2, st),
+            "prenorm launch");
+
+  STAGE(MOE_STAGE_ROUTER);
+  // 2. router logits (fp32)
+  const float* z = t->logits;
+  if (p.need_logits) {
+    float* zo = t->logits_out ? t->logits_out : (float*)(ws + p.o_logits);
+    moe::GemmArgs a{};
+    a.A = p.mat_r ? r_in : t->x;
+    a.lda = H;
+    a.M = T;
+    a.a_rows_alloc = T;
+    if (p.gemma_router && !p.mat_r) {  // RMSNorm without gamma and H^-0.5 as epilogue factors
+      a.row_scale = inv_rms;
+      a.c_scale = 1.0f / sqrtf((float)H);
+    }
+    a.B0 = t->w_router;
+    a.n_routed = 1;
+    a.N = E;
+    a.Kdim = H;
+    a.C = zo;
+    a.ldc = E;
+    HIP_TRY(gemm(a, moe::EPI_STORE_F32, moe::ELEM_BF16, 128), "router gemm launch");
+    z = zo;
+  } else if (t->logits_out) {
+    HIP_TRY(hipMemcpyAsync(t->logits_out, t->logits, (size_t)T * E * 4, hipMemcpyDeviceToDevice, st),
+            "logits copy");
+  }
+
+  STAGE(MOE_STAGE_ROUTE);
+  // 3. routing weights and ids (shared experts appended as ids E.., weight 1)
+  HIP_TRY(moe::launch_route(z, T, E, K, d.renormalize, t->per_expert_scale, w, ids, p.Kp, d.n_shared, st),
+          "route launch");
+
+  STAGE(MOE_STAGE_PERMUTE);
+  // 4. permutation map
+  HIP_TRY(moe::launch_permute(ids, T * p.Kp, p.Ep, log2_exact(p.bm), counts, offsets, sorted, bexp, st),
+          "permute launch");
+
+  STAGE(MOE_STAGE_GATE_UP);
+  // 5. grouped gate/up GEMM + gated activation -> h [cap, I]
+  {
+    moe::GemmArgs a{};
+    a.A = p.mat_xn2 ? xn2 : t->x;
+    if (p.dense && !p.mat_xn2) a.row_scale = inv_rms;
+    a.lda = H;
+    a.a_rows = sorted;
+    a.row_div = p.Kp;
+    a.M = p.cap;
+    a.a_rows_alloc = T;
+    a.m_dev = offsets + p.Ep;
+    a.block_expert = bexp;
+    a.B0 = t->w13;
+    a.B1 = t->shared_w13;
+    a.bstride = (int64_t)2 * I * H;
+    a.n_routed = E;
+    a.bscale0 = t->w13_scale;
+    a.sstride = 2 * I;
+    a.N = I;
+    a.Kdim = H;
+    a.C = h;
+    a.ldc = I;
+    a.act = d.act;
+    HIP_TRY(gemm(a, moe::EPI_GATED, b_elem, p.bm), "gate/up gemm launch");
+  }
+  STAGE(MOE_STAGE_DOWN);
+  // 6. grouped down GEMM, scaled by the routing weight, scattered to per-slot rows
+  {
+    moe::GemmArgs a{};
+    a.A = h;
+    a.lda = I;
+    a.M = p.cap;
+    a.a_rows_alloc = p.cap;
+    a.m_dev = offsets + p.Ep;
+    a.block_expert = bexp;
+    a.B0 = t->w2;
+    a.B1 = t->shared_w2;
+    a.bstride = (int64_t)H * I;
+    a.n_routed = E;
+    a.bscale0 = t->w2_scale;
+    a.sstride = H;
+    a.N = H;
+    a.Kdim = I;
+    a.C = y;
+    a.ldc = H;
+    a.c_rows = sorted;
+    a.row_weight = w;
+    HIP_TRY(gemm(a, (p.y_f32 && !p.f32) ? moe::EPI_SCATTER_F32 : moe::EPI_SCATTER, b_elem, p.bm),
+            "down gemm launch");
+  }
+  STAGE(MOE_STAGE_DENSE_GATE_UP);
+  // 7. parallel dense MLP (Gemma): dense_out = MLP(xn1) in fp32
+  if (!p.dense) STAGE(MOE_STAGE_DENSE_DOWN);
+  if (p.dense) {
+    const int dbm = T >= 1024 ? 256 : 64;
+    moe::GemmArgs a{};
+    a.A = p.mat_xn1 ? xn1 : t->x;
+    if (!p.mat_xn1) a.row_scale = inv_rms;
+    a.lda = H;
+    a.M = T;
+    a.a_rows_alloc = T;
+    a.B0 = t->dense_w13;
+    a.n_routed = 1;
+    a.N = d.inter_dense;
+    a.Kdim = H;
+    a.C = dh;
+    a.ldc = d.inter_dense;
+    a.act = d.dense_act;
+    HIP_TRY(gemm(a, moe::EPI_GATED, moe::ELEM_BF16, dbm), "dense gate/up gemm launch");
+    STAGE(MOE_STAGE_DENSE_DOWN);
+    moe::GemmArgs b{};
+    b.A = dh;
+    b.lda = d.inter_dense;
+    b.M = T;
+    b.a_rows_alloc = T;
+    b.B0 = t->dense_w2;
+    b.n_routed = 1;
+    b.N = H;
+    b.Kdim = d.inter_dense;
+    b.C = dout;
+    b.ldc = H;
+    HIP_TRY(gemm(b, moe::EPI_STORE_F32, moe::ELEM_BF16, dbm), "dense down gemm launch");
+  }
+  STAGE(MOE_STAGE_FINALIZE);
+  // 8. per-token combine in slot order (+ Gemma post-norms and branch sum)
+  HIP_TRY(moe::launch_finalize(y, p.y_f32 ? moe::ELEM_F32 : act_elem, p.Kp, dout, t->gamma_post1, t->gamma_post2, d.eps, t->out, act_elem,
+                               t->out_f32, T, H, st),
+          "finalize launch");
+  // 9. optional copies of the routing result
+  if (t->topk_w_out || t->topk_ids_out)
+    HIP_TRY(moe::launch_gather_topk(w, ids, p.Kp, K, T, t->topk_w_out, t->topk_ids_out, st), "topk copy");
+  STAGE(MOE_STAGE_COUNT);
+#undef STAGE
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_forward(const moe_layer_desc* desc, const moe_tensors* t, int64_t T, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return forward_impl(desc, t, T, workspace, workspace_bytes, stream, nullptr);
+}
+
+MOE_API moe_status moe_forward_profiled(const moe_layer_desc* desc, const moe_tensors* t, int64_t T,
+                                        void* workspace, size_t workspace_bytes, void* stream,
+                                        void* const* events) {
+  if (!events) return fail(MOE_INVALID_ARG, "events is NULL");
+  for (int i = 0; i <= MOE_STAGE_COUNT; ++i)
+    if (!events[i]) return fail(MOE_INVALID_ARG, "events[%d] is NULL", i);
+  return forward_impl(desc, t, T, workspace, workspace_bytes, stream, events);
+}

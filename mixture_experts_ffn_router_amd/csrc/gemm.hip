@@ -1,0 +1,612 @@
+// Grouped expert GEMMs for gfx950 ("Gemma 4 26B-A4B MoE walkthrough" sections
+// 6-7: grouped GEMM by expert over the permutation map, gated activation,
+// weighted combine; "MOE Inference": gated FFN with the merged w13;
+// llama.cpp lesson 35: mul_mat_id computes only the selected experts).
+//
+// C[r, n] = sum_k A[row(r), k] * B_e[n, k] for every row block of the padded,
+// expert-major row list; e = the block's expert.  Both operands are
+// K-contiguous ("NT"), which is what the MFMA operand layout wants.
+//
+// bf16 MFMA kernel (v_mfma_f32_32x32x16_bf16), 256 threads = 4 waves:
+//   * BM x BN output tile; K tiles of 32 (bf16) in 4 LDS stages, or 64 (fp8
+//     weights) in 3, filled by buffer loads that write LDS directly (no staging
+//     registers).  Tiles kt+1 .. kt+NS-1 are in flight while tile kt computes;
+//     the waits are explicit vmcnt counts, so only the oldest tile is waited for.
+//     Buffer resources bound each operand, so a load past the end returns 0.
+//   * LDS rows of 64 / 128 bytes; the 16-byte chunk index is XORed with a
+//     function of the row so the 16 lanes of each ds_read_b128 phase hit
+//     distinct banks.
+//   * Fragments are double-buffered in registers: the LDS reads of the next
+//     sub-step (including the first of the next tile, right after the barrier)
+//     are in flight while the MFMAs of this one run.
+//   * A rows are gathered straight from x through the row map (no permuted copy
+//     of the activations); B rows come from the block's expert.
+//   * The MFMA is issued as B x A, so each lane's accumulator holds 4
+//     consecutive output columns of one row: epilogue stores are 8 bytes.
+//   * Gated epilogue: the B tile holds BN/2 gate rows (w1) and the matching
+//     BN/2 up rows (w3), so the gate and up accumulators of a lane cover the
+//     same (row, col); h = act(g) * u is formed in registers and stored bf16.
+//     The [rows, 2I] product never reaches memory.
+//   * Scatter epilogue (down projection): y = acc * routing weight of the row's
+//     slot, stored (bf16, or fp32 when the branch is renormalised afterwards)
+//     at the slot's row of the per-slot buffer; pad rows are skipped.  The
+//     per-token sum happens in the finalize kernel in slot order.
+//   * FP8 B (OCP E4M3 codes, W8A16): B rows are 64 bytes in LDS, widened to bf16
+//     in registers (exact), and the per-output-channel scale is applied in the
+//     epilogue: sum_k x_k (q_kn s_n) = s_n sum_k x_k q_kn.
+//   * Per-token row scale: an RMSNorm without a learned weight is a per-row
+//     factor, so x_t / rms_t . W = (x_t . W) / rms_t; the epilogue applies it to
+//     the accumulator and the normalised rows are never rounded or stored.
+//
+// fp32 kernel (the fp32 layer): plain LDS-tiled FMA, 64x64 tile, same epilogues.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float apply_act(int act, float g) {
+  return act == 0 ? act_silu(g) : act_gelu_tanh(g);
+}
+
+template <int BELEM>
+struct BTraits;
+template <>
+struct BTraits<ELEM_BF16> {
+  static constexpr int ROW_BYTES = 128;  // 64 bf16
+  static constexpr int ELEM_BYTES = 2;
+};
+template <>
+struct BTraits<ELEM_FP8> {
+  static constexpr int ROW_BYTES = 64;  // 64 fp8
+  static constexpr int ELEM_BYTES = 1;
+};
+
+// 8 fp8 (E4M3) codes in two dwords -> 8 bf16.  v_cvt_pk_f32_fp8 widens two codes
+// (word 0 or word 1 of a dword) to fp32; every E4M3 value has at most 4
+// significant bits, so the upper 16 bits of its fp32 pattern are exactly its
+// bf16 pattern, and one byte permute packs two of them.
+template <bool HI_WORD>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t src) {
+  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8(src, HI_WORD);
+  return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+}
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  u32x4 r;
+  r[0] = fp8x2_to_bf16x2<false>(lo);
+  r[1] = fp8x2_to_bf16x2<true>(lo);
+  r[2] = fp8x2_to_bf16x2<false>(hi);
+  r[3] = fp8x2_to_bf16x2<true>(hi);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // raw buffer: stride 0, num_records = bytes (loads past it return 0)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane, global -> LDS: lane l's data lands at dst + 16 l (dst wave-uniform).
+__device__ __forceinline__ void dma16(rsrc_t r, void* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, (int)voff, (int)soff, 0, 0);
+}
+
+// Tile order: blocks are dealt to the 8 XCDs round-robin, so block b runs on XCD b % 8.
+// Renumber so each XCD walks a contiguous range of logical tiles, and order logical tiles
+// in groups of GM row blocks x all column tiles (row block fastest): the ~32 tiles an
+// XCD runs at once then share GM row blocks of A and a few column tiles of B in its L2.
+__device__ __forceinline__ void tile_of_block(int64_t b, int64_t nblocks, int64_t mb_cap, int64_t nb_cnt,
+                                              int64_t& mb, int64_t& nb) {
+  constexpr int XCDS = 8, GM = 4;
+  int64_t lid = b;
+  if (nblocks % XCDS == 0) lid = (b % XCDS) * (nblocks / XCDS) + b / XCDS;
+  const int64_t per_group = GM * nb_cnt;
+  const int64_t g = lid / per_group, w = lid % per_group;
+  const int64_t gm = min((int64_t)GM, mb_cap - g * GM);  // rows in this (possibly last) group
+  mb = g * GM + w % gm;
+  nb = w / gm;
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14])
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
+// LDS row layout: a K-tile row is 64 or 128 bytes of 16-byte chunks; chunk c of
+// row r sits at chunk c ^ swz(r).  A fragment read has 16 consecutive lanes on
+// 16 consecutive rows at the same logical chunk, and gfx950 serves a
+// ds_read_b128 16 lanes (256 bytes, all 64 banks) per cycle: the swizzle puts
+// those 16 reads in 16 distinct 16-byte bank groups (it is also conflict-free
+// for 8-lane / 128-byte phases).  With row bits b3..b0:
+//   64-byte rows (4 chunks):  swz = (b2, b1 ^ b3)
+//   128-byte rows (8 chunks): swz = (b2, b1, b0 ^ b3)
+template <int ROW_BYTES>
+__device__ __forceinline__ int lds_swz(int row) {
+  if constexpr (ROW_BYTES == 128) return (row & 6) | ((row ^ (row >> 3)) & 1);
+  else return ((row & 4) >> 1) | (((row >> 1) ^ (row >> 3)) & 1);
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI, int BELEM>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N)
+__attribute__((amdgpu_waves_per_eu(WAVES_M * WAVES_N / 4, WAVES_M * WAVES_N / 4)))
+void gemm_mfma_kernel(GemmArgs p) {
+  constexpr bool FP8 = BELEM == ELEM_FP8;
+  // bf16: 32-deep K tiles in 4 stages; fp8 weights: 64-deep K tiles in 3 stages
+  constexpr int BK = FP8 ? 64 : 32;
+  constexpr int NS = FP8 ? 3 : 4;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr bool GATED = EPI == EPI_GATED;
+  constexpr int EB = BTraits<BELEM>::ELEM_BYTES;
+  constexpr int NW = WAVES_M * WAVES_N;  // 4 waves (1 per SIMD) or 8 (2 per SIMD)
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static_assert(TM >= 1 && TN >= 1, "wave tile");
+  static_assert(!GATED || (TN % 2 == 0), "gated needs gate/up tile pairs");
+  constexpr int A_ROW = BK * 2;
+  constexpr int B_ROW = BK * EB;
+  constexpr int A_BYTES = BM * A_ROW;
+  constexpr int B_BYTES = BN * B_ROW;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int A_DMA = A_BYTES / 1024 / NW;  // 1 KiB DMA instructions per wave per stage
+  constexpr int B_DMA = B_BYTES / 1024 / NW;
+  constexpr int A_CH = A_ROW / 16, B_CH = B_ROW / 16;  // 16-byte chunks per row
+  constexpr int A_ROWS_PER_DMA = 1024 / A_ROW, B_ROWS_PER_DMA = 1024 / B_ROW;
+  constexpr int D_TILE = A_DMA + B_DMA;
+  static_assert(A_DMA >= 1 && B_DMA >= 1 && A_DMA * NW * 1024 == A_BYTES && B_DMA * NW * 1024 == B_BYTES,
+                "stage must split into 1 KiB DMA instructions over the waves");
+  static_assert(!GATED || ((BN / 2) % B_ROWS_PER_DMA == 0), "DMA groups must not straddle gate/up");
+  static_assert(NS * STAGE <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  constexpr int NCOLS = GATED ? BN / 2 : BN;  // output columns per block
+  const int64_t mb_cap = (p.M + BM - 1) / BM;
+  const int64_t nb_cnt = (p.N + NCOLS - 1) / NCOLS;
+  int64_t mb, nbi;
+  tile_of_block(blockIdx.x, gridDim.x, mb_cap, nb_cnt, mb, nbi);
+  const int64_t m_rows = p.m_dev ? (int64_t)(*p.m_dev) : p.M;
+  const int64_t m0 = mb * BM;
+  if (m0 >= m_rows) return;
+  const int n0 = (int)nbi * NCOLS;
+  const int e = p.block_expert ? p.block_expert[mb] : 0;
+  const bool routed = e < p.n_routed;
+  const int64_t eoff = routed ? (int64_t)e : (int64_t)(e - p.n_routed);
+  const uint8_t* Bbase = (const uint8_t*)(routed ? p.B0 : p.B1) + eoff * p.bstride * EB;
+  const float* bscale = nullptr;
+  if constexpr (FP8) bscale = (routed ? p.bscale0 : p.bscale1) + eoff * p.sstride;
+
+  const rsrc_t rsA = make_rsrc(p.A, (uint32_t)(p.a_rows_alloc * p.lda * 2));
+  const rsrc_t rsB = make_rsrc(Bbase, (uint32_t)((int64_t)(GATED ? 2 * p.N : p.N) * p.Kdim * EB));
+
+  // ---- DMA source offsets.  Instruction i of this wave fills ROWS_PER_DMA
+  // consecutive tile rows; lane l writes row base + l / CH, physical chunk l % CH,
+  // which holds logical chunk (l % CH) ^ swz(row).
+  uint32_t a_off[A_DMA];
+#pragma unroll
+  for (int i = 0; i < A_DMA; ++i) {
+    const int r = (wave * A_DMA + i) * A_ROWS_PER_DMA + lane / A_CH;
+    const int64_t grow = m0 + r;
+    int64_t tok;
+    if (p.a_rows) {
+      const int slot = grow < p.M ? p.a_rows[grow] : -1;
+      tok = slot >= 0 ? slot / p.row_div : 0;
+    } else {
+      tok = grow < p.M ? grow : p.M - 1;
+    }
+    a_off[i] = (uint32_t)(tok * p.lda * 2) + (uint32_t)((((lane % A_CH) ^ lds_swz<A_ROW>(r))) << 4);
+  }
+  const int bl_row = lane / B_CH;  // row within a DMA group (B rows are 64 bytes: groups of 16 rows)
+  static_assert(B_ROW == 64, "B DMA groups must start at multiples of 16 rows");
+  const uint32_t b_voff = (uint32_t)(bl_row * p.Kdim * EB) + (uint32_t)(((lane % B_CH) ^ lds_swz<B_ROW>(bl_row)) << 4);
+  uint32_t b_soff[B_DMA];
+#pragma unroll
+  for (int i = 0; i < B_DMA; ++i) {
+    const int q0 = (wave * B_DMA + i) * B_ROWS_PER_DMA;
+    int brow;
+    if constexpr (GATED) brow = q0 < BN / 2 ? n0 + q0 : p.N + n0 + (q0 - BN / 2);
+    else brow = n0 + q0;
+    b_soff[i] = (uint32_t)((int64_t)brow * p.Kdim * EB);
+  }
+  const int nk = p.Kdim / BK;
+  // Tile kt into stage buf; tiles past the end are issued with an out-of-range
+  // offset, which the buffer bound turns into zero fill without a memory access.
+  auto issue_dma = [&](int kt, int buf) {
+    uint8_t* sA = smem + buf * STAGE;
+    uint8_t* sB = sA + A_BYTES;
+    const bool live = kt < nk;
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i)
+      dma16(rsA, sA + (wave * A_DMA + i) * 1024, live ? a_off[i] : 0x80000000u, live ? (uint32_t)kt * A_ROW : 0u);
+#pragma unroll
+    for (int i = 0; i < B_DMA; ++i)
+      dma16(rsB, sB + (wave * B_DMA + i) * 1024, live ? b_voff : 0x80000000u,
+            live ? b_soff[i] + (uint32_t)kt * (uint32_t)B_ROW : 0u);
+  };
+
+  // LDS row of the wave's B tile j (output-column tile)
+  auto b_lds_row = [&](int j) {
+    if constexpr (GATED) {
+      constexpr int TH = TN / 2;
+      return (j < TH) ? (wn * (WN / 2) + 32 * j) : (BN / 2 + wn * (WN / 2) + 32 * (j - TH));
+    } else {
+      return wn * WN + 32 * j;
+    }
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int l32 = lane & 31, hsel = lane >> 5;
+  int a_row_off[TM], b_row_off[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) a_row_off[i] = (wm * WM + 32 * i + l32) * A_ROW;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) b_row_off[j] = (b_lds_row(j) + l32) * B_ROW;
+  // every fragment row of this lane is l32 modulo 32
+  const int swa = lds_swz<A_ROW>(l32), swb = lds_swz<B_ROW>(l32);
+
+  // Two sub-steps per K tile: bf16 16 k each; fp8 32 k each (one 16-byte B read
+  // feeds two MFMAs, see below).
+  constexpr int NA = FP8 ? 2 : 1;
+  struct Frags {
+    bf16x8 a[TM][NA];
+    u32x4 b[TN];
+  };
+  auto load_frags = [&](int buf, int s, Frags& f) {
+    const uint8_t* sa = smem + buf * STAGE;
+    const uint8_t* sb = sa + A_BYTES;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if constexpr (!FP8) {
+        const int c = 2 * s + hsel;
+        f.a[i][0] = *(const bf16x8*)(sa + a_row_off[i] + ((c ^ swa) << 4));
+      } else {
+        // fp8 sub-step s: B bytes [16c, 16c+16), c = 2s + hsel, hold k in
+        // [32s + 16hsel, +16); the first 8 pair with A chunk 4s + 2hsel, the next 8
+        // with 4s + 2hsel + 1.  Both MFMAs together cover k in [32s, 32s + 32) once.
+        const int ca = 4 * s + 2 * hsel;
+        f.a[i][0] = *(const bf16x8*)(sa + a_row_off[i] + ((ca ^ swa) << 4));
+        f.a[i][1] = *(const bf16x8*)(sa + a_row_off[i] + (((ca + 1) ^ swa) << 4));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int c = 2 * s + hsel;
+      f.b[j] = *(const u32x4*)(sb + b_row_off[j] + ((c ^ swb) << 4));
+    }
+  };
+  auto mfmas = [&](const Frags& f) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      if constexpr (!FP8) {
+        const bf16x8 bj = __builtin_bit_cast(bf16x8, f.b[j]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bj, f.a[i][0], acc[i][j], 0, 0, 0);
+      } else {
+        const bf16x8 b1 = fp8x8_to_bf16x8(f.b[j][0], f.b[j][1]);
+        const bf16x8 b2 = fp8x8_to_bf16x8(f.b[j][2], f.b[j][3]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, f.a[i][0], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b2, f.a[i][1], acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // ---- pipeline: tiles kt+1 .. kt+NS-1 are in flight while tile kt computes.
+  constexpr int R_SUB = TM * NA + TN;             // LDS reads per sub-step
+  constexpr int M_SUB = TM * TN * (FP8 ? 2 : 1);  // MFMAs per sub-step
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t) issue_dma(t, t);
+  wait_vmcnt<(NS - 2) * D_TILE>();  // this wave's part of tile 0
+  __builtin_amdgcn_s_barrier();      // everyone's part of tile 0
+  Frags f0, f1;
+  load_frags(0, 0, f0);
+  int buf = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int nbuf = buf + 1 == NS ? 0 : buf + 1;
+    // Refill the stage that held tile kt-1: every wave finished reading it
+    // before the barrier of the previous iteration.
+    // Sub-step 0 fragments were read half a tile ago; waiting for them here
+    // (before new reads) keeps the wait from covering the reads issued next.
+    wait_lgkmcnt0();
+    // Sub-step 1 fragments first: they have all of sub-step 0 to land, so the
+    // lgkmcnt wait before the barrier finds them done.
+    load_frags(buf, 1, f1);
+    issue_dma(kt + NS - 1, buf == 0 ? NS - 1 : buf - 1);
+    mfmas(f0);
+    // Own reads of tile kt done and own DMA of tile kt+1 landed; the barrier
+    // extends both to every wave.  Tiles kt+2 .. kt+NS-1 stay in flight.
+    wait_lgkmcnt0();
+    wait_vmcnt<(NS - 2) * D_TILE>();
+    __builtin_amdgcn_s_barrier();
+    load_frags(nbuf, 0, f0);
+    mfmas(f1);
+    // Issue order: sub-step 1 reads; sub-step 0 MFMAs with the DMAs between the
+    // first of them; [barrier]; next tile's sub-step 0 reads between the first
+    // sub-step 1 MFMAs.
+    __builtin_amdgcn_sched_group_barrier(0x100, R_SUB, 0);   // DS read
+#pragma unroll
+    for (int q = 0; q < D_TILE; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // VMEM (LDS DMA)
+    }
+    if (M_SUB > D_TILE) __builtin_amdgcn_sched_group_barrier(0x008, M_SUB - D_TILE, 0);
+#pragma unroll
+    for (int q = 0; q < R_SUB; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if (M_SUB > R_SUB) __builtin_amdgcn_sched_group_barrier(0x008, M_SUB - R_SUB, 0);
+    buf = nbuf;
+  }
+
+  // ---- epilogue.  acc[i][j][v]: row = m0 + wm*WM + 32i + l32,
+  //      col (tile-local) = 8*(v/4) + 4*hsel + (v%4)
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int64_t grow = m0 + wm * WM + 32 * i + l32;
+    if (grow >= m_rows) continue;
+    float rs = 1.f;
+    if (p.row_scale) {
+      int64_t tok = grow;
+      if (p.a_rows) {
+        const int slot = p.a_rows[grow];
+        tok = slot >= 0 ? slot / p.row_div : 0;
+      }
+      rs = p.row_scale[tok];
+    }
+    if constexpr (GATED) {
+      constexpr int TH = TN / 2;
+      bf16_t* C = (bf16_t*)p.C + grow * p.ldc;
+#pragma unroll
+      for (int j = 0; j < TH; ++j) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int col = n0 + wn * (WN / 2) + 32 * j + 8 * g4 + 4 * hsel;
+          if (col >= p.N) continue;
+          float h[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float g = acc[i][j][4 * g4 + q] * rs, u = acc[i][j + TH][4 * g4 + q] * rs;
+            if constexpr (FP8) {
+              g *= bscale[col + q];
+              u *= bscale[p.N + col + q];
+            }
+            h[q] = apply_act(p.act, g) * u;
+          }
+          uint2 pk;
+          pk.x = pack_bf16x2(h[0], h[1]);
+          pk.y = pack_bf16x2(h[2], h[3]);
+          *(uint2*)(C + col) = pk;
+        }
+      }
+    } else if constexpr (EPI == EPI_SCATTER || EPI == EPI_SCATTER_F32) {
+      const int slot = p.c_rows[grow];
+      if (slot < 0) continue;
+      const float w = p.row_weight ? p.row_weight[slot] : 1.f;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int col = n0 + wn * WN + 32 * j + 8 * g4 + 4 * hsel;
+          if (col >= p.N) continue;
+          float y[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            y[q] = acc[i][j][4 * g4 + q] * w;
+            if constexpr (FP8) y[q] *= bscale[col + q];
+          }
+          if constexpr (EPI == EPI_SCATTER) {
+            uint2 pk;
+            pk.x = pack_bf16x2(y[0], y[1]);
+            pk.y = pack_bf16x2(y[2], y[3]);
+            *(uint2*)((bf16_t*)p.C + (int64_t)slot * p.ldc + col) = pk;
+          } else {
+            *(float4*)((float*)p.C + (int64_t)slot * p.ldc + col) = make_float4(y[0], y[1], y[2], y[3]);
+          }
+        }
+      }
+    } else {
+      float* C = (float*)p.C + grow * p.ldc;
+      const float f = rs * p.c_scale;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int col = n0 + wn * WN + 32 * j + 8 * g4 + 4 * hsel;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (col + q < p.N) C[col + q] = acc[i][j][4 * g4 + q] * f;
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ fp32 path
+// 64x64 output tile (gated: 32 gate + 32 up B rows), BK = 16, 16x16 threads,
+// each owning 4 rows x 4 B columns.  Gated threads own 2 gate and the same 2
+// up columns, so act(g) * u needs no exchange.
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
+  constexpr int BM = 64, BN = 64, BK = 16;
+  constexpr bool GATED = EPI == EPI_GATED;
+  constexpr int NCOLS = GATED ? BN / 2 : BN;
+  __shared__ float As[BK][BM + 4];
+  __shared__ float Bs[BK][BN + 4];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int64_t mb_cap = (p.M + BM - 1) / BM;
+  const int64_t mb = (int64_t)blockIdx.x % mb_cap;
+  const int nb = (int)((int64_t)blockIdx.x / mb_cap);
+  const int64_t m_rows = p.m_dev ? (int64_t)(*p.m_dev) : p.M;
+  const int64_t m0 = mb * BM;
+  if (m0 >= m_rows) return;
+  const int n0 = nb * NCOLS;
+  const int e = p.block_expert ? p.block_expert[mb] : 0;
+  const bool routed = e < p.n_routed;
+  const int64_t eoff = routed ? (int64_t)e : (int64_t)(e - p.n_routed);
+  const float* B = (const float*)(routed ? p.B0 : p.B1) + eoff * p.bstride;
+
+  // loads: thread -> (row = tid/4, k4 = tid%4)
+  const int lr = tid >> 2, lk = (tid & 3) * 4;
+  int64_t tok;
+  {
+    const int64_t grow = m0 + lr;
+    if (p.a_rows) {
+      const int slot = grow < p.M ? p.a_rows[grow] : -1;
+      tok = slot >= 0 ? slot / p.row_div : 0;
+    } else {
+      tok = grow < p.M ? grow : p.M - 1;
+    }
+  }
+  const float* a_src = (const float*)p.A + tok * p.lda + lk;
+  int brow;
+  if (GATED) {
+    const int qq = lr % (BN / 2);
+    const int col = min(n0 + qq, p.N - 1);
+    brow = lr < BN / 2 ? col : p.N + col;
+  } else {
+    brow = min(n0 + lr, p.N - 1);
+  }
+  const float* b_src = B + (int64_t)brow * p.Kdim + lk;
+
+  // B columns owned: gated -> LDS rows {2tx, 2tx+1, 32+2tx, 32+2tx+1}; else 4tx..4tx+3
+  int bc[4];
+  for (int q = 0; q < 4; ++q) bc[q] = GATED ? ((q < 2) ? 2 * tx + q : 32 + 2 * tx + (q - 2)) : 4 * tx + q;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < p.Kdim; k0 += BK) {
+    const float4 av = *(const float4*)(a_src + k0);
+    const float4 bv = *(const float4*)(b_src + k0);
+    As[lk + 0][lr] = av.x; As[lk + 1][lr] = av.y; As[lk + 2][lr] = av.z; As[lk + 3][lr] = av.w;
+    Bs[lk + 0][lr] = bv.x; Bs[lk + 1][lr] = bv.y; Bs[lk + 2][lr] = bv.z; Bs[lk + 3][lr] = bv.w;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < BK; ++k) {
+      float a[4], b[4];
+      for (int r = 0; r < 4; ++r) a[r] = As[k][ty * 4 + r];
+      for (int q = 0; q < 4; ++q) b[q] = Bs[k][bc[q]];
+      for (int r = 0; r < 4; ++r)
+        for (int q = 0; q < 4; ++q) acc[r][q] = fmaf(a[r], b[q], acc[r][q]);
+    }
+    __syncthreads();
+  }
+  for (int r = 0; r < 4; ++r) {
+    const int64_t grow = m0 + ty * 4 + r;
+    if (grow >= m_rows) continue;
+    float rs = 1.f;
+    if (p.row_scale) {
+      int64_t tk = grow;
+      if (p.a_rows) {
+        const int slot = p.a_rows[grow];
+        tk = slot >= 0 ? slot / p.row_div : 0;
+      }
+      rs = p.row_scale[tk];
+    }
+    if (GATED) {
+      float* C = (float*)p.C + grow * p.ldc;
+      for (int q = 0; q < 2; ++q) {
+        const int col = n0 + 2 * tx + q;
+        if (col < p.N) C[col] = apply_act(p.act, acc[r][q] * rs) * (acc[r][q + 2] * rs);
+      }
+    } else if (EPI == EPI_SCATTER) {
+      const int slot = p.c_rows[grow];
+      if (slot < 0) continue;
+      const float w = p.row_weight ? p.row_weight[slot] : 1.f;
+      float* C = (float*)p.C + (int64_t)slot * p.ldc;
+      for (int q = 0; q < 4; ++q) {
+        const int col = n0 + 4 * tx + q;
+        if (col < p.N) C[col] = acc[r][q] * w;
+      }
+    } else {
+      float* C = (float*)p.C + grow * p.ldc;
+      for (int q = 0; q < 4; ++q) {
+        const int col = n0 + 4 * tx + q;
+        if (col < p.N) C[col] = acc[r][q] * rs * p.c_scale;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dispatch
+template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI, int BELEM>
+static hipError_t run_mfma(const GemmArgs& a, hipStream_t s) {
+  constexpr int NCOLS = EPI == EPI_GATED ? BN / 2 : BN;
+  const int64_t mb_cap = (a.M + BM - 1) / BM;
+  const int64_t nb = (a.N + NCOLS - 1) / NCOLS;
+  const int64_t blocks = mb_cap * nb;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  gemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, EPI, BELEM>
+      <<<dim3((unsigned)blocks), dim3(64 * WAVES_M * WAVES_N), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int EPI, int BELEM>
+static hipError_t run_grouped(const GemmArgs& a, int block_m, hipStream_t s) {
+  const int N = a.N;
+  if (block_m == 256) {
+    if (EPI == EPI_GATED) {
+      if (N % 128 == 0) return run_mfma<256, 256, 4, 2, EPI, BELEM>(a, s);
+      return run_mfma<256, 128, 4, 1, EPI, BELEM>(a, s);
+    }
+    if (N % 256 == 0) return run_mfma<256, 256, 4, 2, EPI, BELEM>(a, s);
+    return run_mfma<256, 128, 4, 1, EPI, BELEM>(a, s);
+  }
+  if (block_m == 64) {
+    if (EPI == EPI_GATED) {
+      if (N % 128 == 0) return run_mfma<64, 256, 1, 4, EPI, BELEM>(a, s);
+      return run_mfma<64, 128, 2, 2, EPI, BELEM>(a, s);
+    }
+    if (N % 256 == 0) return run_mfma<64, 256, 1, 4, EPI, BELEM>(a, s);
+    return run_mfma<64, 128, 2, 2, EPI, BELEM>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_mfma(const GemmArgs& a, int epi, int belem, int block_m, hipStream_t s) {
+  if (epi == EPI_STORE_F32) {
+    if (belem != ELEM_BF16) return hipErrorInvalidValue;
+    if (block_m == 128) {
+      if (a.N <= 64) return run_mfma<128, 64, 4, 1, EPI_STORE_F32, ELEM_BF16>(a, s);
+      return run_mfma<128, 128, 2, 2, EPI_STORE_F32, ELEM_BF16>(a, s);
+    }
+    return run_grouped<EPI_STORE_F32, ELEM_BF16>(a, block_m, s);
+  }
+  if (epi == EPI_GATED)
+    return belem == ELEM_FP8 ? run_grouped<EPI_GATED, ELEM_FP8>(a, block_m, s)
+                             : run_grouped<EPI_GATED, ELEM_BF16>(a, block_m, s);
+  if (epi == EPI_SCATTER_F32)
+    return belem == ELEM_FP8 ? run_grouped<EPI_SCATTER_F32, ELEM_FP8>(a, block_m, s)
+                             : run_grouped<EPI_SCATTER_F32, ELEM_BF16>(a, block_m, s);
+  return belem == ELEM_FP8 ? run_grouped<EPI_SCATTER, ELEM_FP8>(a, block_m, s)
+                           : run_grouped<EPI_SCATTER, ELEM_BF16>(a, block_m, s);
+}
+
+hipError_t launch_gemm_f32(const GemmArgs& a, int epi, hipStream_t s) {
+  const int ncols = epi == EPI_GATED ? 32 : 64;
+  const int64_t blocks = ((a.M + 63) / 64) * ((a.N + ncols - 1) / ncols);
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (epi == EPI_GATED) gemm_f32_kernel<EPI_GATED><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(a);
+  else if (epi == EPI_SCATTER) gemm_f32_kernel<EPI_SCATTER><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(a);
+  else gemm_f32_kernel<EPI_STORE_F32><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

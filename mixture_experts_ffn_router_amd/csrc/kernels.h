@@ -1,0 +1,68 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_route(const float* logits, int64_t T, int E, int K, int renorm, const float* pes,
+                        float* w_out, int32_t* ids_out, int out_stride, int n_shared, hipStream_t s);
+
+hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int bm_log2, int32_t* counts,
+                          int32_t* offsets, int32_t* sorted_slots, int32_t* block_expert,
+                          hipStream_t s);
+
+enum GemmEpi { EPI_GATED = 0, EPI_SCATTER = 1, EPI_STORE_F32 = 2, EPI_SCATTER_F32 = 3 };
+enum GemmElem { ELEM_F32 = 0, ELEM_BF16 = 1, ELEM_FP8 = 2 };
+
+// One grouped "NT" GEMM: C[r, n] = sum_k A[row(r), k] * B_e[n, k] for the rows r
+// of every row block, e = the block's expert.
+struct GemmArgs {
+  const void* A;              // activation rows, [*, Kdim], row stride lda (elements)
+  int64_t lda;
+  const int32_t* a_rows;      // row map for A: slot index per row (token = slot / row_div), -1 = pad;
+                              // NULL = identity rows
+  int32_t row_div;
+  int64_t M;                  // identity rows: number of valid rows; mapped rows: capacity
+  int64_t a_rows_alloc;       // rows of the A allocation (a_rows_alloc * lda * 2 < 2^31)
+  const int32_t* m_dev;       // device count of rows (padded total) or NULL (use M)
+  const int32_t* block_expert;  // expert per row block, NULL = expert 0
+  const void* B0;             // routed expert weights, expert stride bstride (elements)
+  const void* B1;             // weights of experts >= n_routed (shared), same stride
+  int64_t bstride;
+  int32_t n_routed;
+  const float* bscale0;       // FP8 per-output-channel scales, expert stride sstride
+  const float* bscale1;
+  int64_t sstride;
+  int32_t N;                  // output columns (gated: I, reading B rows n and I + n)
+  int32_t Kdim;
+  void* C;                    // output; row stride ldc (elements)
+  int64_t ldc;
+  const int32_t* c_rows;      // scatter epilogue: output row = c_rows[r] (skip if < 0)
+  const float* row_weight;    // scatter epilogue: weight per output row (slot), NULL = 1
+  int32_t act;                // gated epilogue activation
+  const float* row_scale;     // per-token factor on the accumulator (gated: on g and u; store:
+                              // on the value), indexed by the A row's token; NULL = 1
+  float c_scale = 1.f;        // constant factor on stored values (store epilogue)
+};
+
+// bf16 A; B bf16 or FP8 (ELEM_BF16 / ELEM_FP8).  block_m in {32, 64, 128, 256}.
+hipError_t launch_gemm_mfma(const GemmArgs& a, int epi, int belem, int block_m, hipStream_t s);
+// fp32 A and B (the fp32 layer).  block_m = 64.
+hipError_t launch_gemm_f32(const GemmArgs& a, int epi, hipStream_t s);
+
+// inv_rms[t] = 1/sqrt(mean(x_t^2) + eps); rows are materialised only where their
+// output pointer is non-NULL (router input, dense input, expert input).
+hipError_t launch_prenorm(const void* x, int elem, int64_t T, int H, float eps, float* inv_rms,
+                          const float* router_scale, const float* gamma_pre, const float* gamma_pre2,
+                          void* r_out, void* xn1_out, void* xn2_out, hipStream_t s);
+
+hipError_t launch_finalize(const void* ybuf, int yelem, int Kp, const float* dense_out,
+                           const float* gamma_post1, const float* gamma_post2, float eps, void* out,
+                           int oelem, float* out_f32, int64_t T, int H, hipStream_t s);
+
+hipError_t launch_gather_topk(const float* w_in, const int32_t* ids_in, int in_stride, int K, int64_t T,
+                              float* w_out, int32_t* ids_out, hipStream_t s);
+
+}  // namespace moe

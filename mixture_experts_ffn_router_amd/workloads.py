@@ -172,7 +172,10 @@ def make_layer(spec: LayerSpec, seed: int = 0, T: Optional[int] = None, x_only=F
     else:
         L["dense_w13"] = L["dense_w2"] = None
     if spec.random_gammas:
+        # test-only learned weights: router scale and input norms around 1; the
+        # post-norm weights below 1 keep the output near unit scale
         g = _rng(seed, _TID["gammas"]).uniform(0.5, 1.5, (5, H)).astype(np.float32)
+        g[3:] = (g[3:] - 0.5) * 0.4 + 0.3
         L["router_scale"] = torch.from_numpy(g[0].copy()) if spec.router_mode == "gemma" else None
         L["gammas"] = {k: torch.from_numpy(g[i + 1].copy())
                        for i, k in enumerate(["pre", "pre2", "post1", "post2"])}
