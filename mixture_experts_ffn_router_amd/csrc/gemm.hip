@@ -39,6 +39,8 @@
 //     the accumulator and the normalised rows are never rounded or stored.
 //
 // fp32 kernel (the fp32 layer): plain LDS-tiled FMA, 64x64 tile, same epilogues.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -94,18 +96,22 @@ __device__ __forceinline__ void dma16(rsrc_t r, void* dst, uint32_t voff, uint32
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, (int)voff, (int)soff, 0, 0);
 }
 
-// Tile order: blocks are dealt to the 8 XCDs round-robin, so block b runs on XCD b % 8.
-// Renumber so each XCD walks a contiguous range of logical tiles, and order logical tiles
-// in groups of GM row blocks x all column tiles (row block fastest): the ~32 tiles an
-// XCD runs at once then share GM row blocks of A and a few column tiles of B in its L2.
-__device__ __forceinline__ void tile_of_block(int64_t b, int64_t nblocks, int64_t mb_cap, int64_t nb_cnt,
-                                              int64_t& mb, int64_t& nb) {
-  constexpr int XCDS = 8, GM = 4;
-  int64_t lid = b;
-  if (nblocks % XCDS == 0) lid = (b % XCDS) * (nblocks / XCDS) + b / XCDS;
+// Tile order.  The grid is persistent: block b walks tiles t = b, b + G, ... with
+// G a multiple of 8, and blocks are dealt to the 8 XCDs round-robin, so XCD x
+// runs the tiles t = x (mod 8).  Renumber so each XCD walks a contiguous range of
+// logical tiles, and order logical tiles in groups of GM row blocks x all column
+// tiles (row block fastest): the ~32 tiles an XCD runs at once then share GM row
+// blocks of A and a few column tiles of B in its L2.  Only row blocks that hold
+// rows are counted, so no block idles on padding and the XCDs stay balanced.
+__device__ __forceinline__ int64_t xcd_logical(int64_t t, int64_t per_xcd, bool xcd_map) {
+  constexpr int XCDS = 8;
+  return xcd_map ? (t % XCDS) * per_xcd + t / XCDS : t;
+}
+__device__ __forceinline__ void tile_coords(int64_t lid, int64_t mbn, int64_t nb_cnt, int64_t& mb, int64_t& nb) {
+  constexpr int GM = 4;
   const int64_t per_group = GM * nb_cnt;
   const int64_t g = lid / per_group, w = lid % per_group;
-  const int64_t gm = min((int64_t)GM, mb_cap - g * GM);  // rows in this (possibly last) group
+  const int64_t gm = min((int64_t)GM, mbn - g * GM);  // rows in this (possibly last) group
   mb = g * GM + w % gm;
   nb = w / gm;
 }
@@ -168,13 +174,24 @@ void gemm_mfma_kernel(GemmArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   constexpr int NCOLS = GATED ? BN / 2 : BN;  // output columns per block
-  const int64_t mb_cap = (p.M + BM - 1) / BM;
-  const int64_t nb_cnt = (p.N + NCOLS - 1) / NCOLS;
-  int64_t mb, nbi;
-  tile_of_block(blockIdx.x, gridDim.x, mb_cap, nb_cnt, mb, nbi);
   const int64_t m_rows = p.m_dev ? (int64_t)(*p.m_dev) : p.M;
+  const int64_t mbn = (m_rows + BM - 1) / BM;  // row blocks holding rows
+  const int64_t nb_cnt = (p.N + NCOLS - 1) / NCOLS;
+  const int64_t ntiles = mbn * nb_cnt;
+  const bool xcd_map = gridDim.x % 8 == 0;
+  const int64_t per_xcd = (ntiles + 7) / 8;
+  const int64_t tend = xcd_map ? per_xcd * 8 : ntiles;
+  // Rows whose slot is -1 are padding: their operand loads are issued out of
+  // range (zero fill, no memory traffic), a wave whose rows are all padding skips
+  // its MFMAs, and nothing is stored for them.
+  const int32_t* pad_map = p.a_rows ? p.a_rows : p.c_rows;
+  for (int64_t t = blockIdx.x; t < tend; t += gridDim.x) {
+  const int64_t lid = xcd_logical(t, per_xcd, xcd_map);
+  if (lid >= ntiles) continue;  // uniform per block
+  int64_t mb, nbi;
+  tile_coords(lid, mbn, nb_cnt, mb, nbi);
+  __syncthreads();  // the previous tile's LDS reads are done in every wave
   const int64_t m0 = mb * BM;
-  if (m0 >= m_rows) return;
   const int n0 = (int)nbi * NCOLS;
   const int e = p.block_expert ? p.block_expert[mb] : 0;
   const bool routed = e < p.n_routed;
@@ -182,6 +199,7 @@ void gemm_mfma_kernel(GemmArgs p) {
   const uint8_t* Bbase = (const uint8_t*)(routed ? p.B0 : p.B1) + eoff * p.bstride * EB;
   const float* bscale = nullptr;
   if constexpr (FP8) bscale = (routed ? p.bscale0 : p.bscale1) + eoff * p.sstride;
+  const bool wave_live = m0 + wm * WM < m_rows && (!pad_map || pad_map[m0 + wm * WM] >= 0);
 
   const rsrc_t rsA = make_rsrc(p.A, (uint32_t)(p.a_rows_alloc * p.lda * 2));
   const rsrc_t rsB = make_rsrc(Bbase, (uint32_t)((int64_t)(GATED ? 2 * p.N : p.N) * p.Kdim * EB));
@@ -194,14 +212,13 @@ void gemm_mfma_kernel(GemmArgs p) {
   for (int i = 0; i < A_DMA; ++i) {
     const int r = (wave * A_DMA + i) * A_ROWS_PER_DMA + lane / A_CH;
     const int64_t grow = m0 + r;
+    const int slot = (pad_map && grow < p.M) ? pad_map[grow] : 0;
     int64_t tok;
-    if (p.a_rows) {
-      const int slot = grow < p.M ? p.a_rows[grow] : -1;
-      tok = slot >= 0 ? slot / p.row_div : 0;
-    } else {
-      tok = grow < p.M ? grow : p.M - 1;
-    }
-    a_off[i] = (uint32_t)(tok * p.lda * 2) + (uint32_t)((((lane % A_CH) ^ lds_swz<A_ROW>(r))) << 4);
+    if (p.a_rows) tok = slot >= 0 ? slot / p.row_div : 0;
+    else tok = grow < p.M ? grow : p.M - 1;
+    a_off[i] = (grow >= m_rows || slot < 0)
+                   ? 0x80000000u
+                   : (uint32_t)(tok * p.lda * 2) + (uint32_t)((((lane % A_CH) ^ lds_swz<A_ROW>(r))) << 4);
   }
   const int bl_row = lane / B_CH;  // row within a DMA group (B rows are 64 bytes: groups of 16 rows)
   static_assert(B_ROW == 64, "B DMA groups must start at multiples of 16 rows");
@@ -309,6 +326,16 @@ void gemm_mfma_kernel(GemmArgs p) {
   };
 
   // ---- pipeline: tiles kt+1 .. kt+NS-1 are in flight while tile kt computes.
+  // A wave whose rows are all padding runs the same DMA / barrier sequence
+  // without fragment reads or MFMAs.
+  auto pipeline = [&](auto live_tag) {
+    constexpr bool LIVE = decltype(live_tag)::value;
+    auto load_frags_l = [&](int b, int s_, Frags& f) {
+      if constexpr (LIVE) load_frags(b, s_, f);
+    };
+    auto mfmas_l = [&](const Frags& f) {
+      if constexpr (LIVE) mfmas(f);
+    };
   constexpr int R_SUB = TM * NA + TN;             // LDS reads per sub-step
   constexpr int M_SUB = TM * TN * (FP8 ? 2 : 1);  // MFMAs per sub-step
 #pragma unroll
@@ -316,7 +343,7 @@ void gemm_mfma_kernel(GemmArgs p) {
   wait_vmcnt<(NS - 2) * D_TILE>();  // this wave's part of tile 0
   __builtin_amdgcn_s_barrier();      // everyone's part of tile 0
   Frags f0, f1;
-  load_frags(0, 0, f0);
+  load_frags_l(0, 0, f0);
   int buf = 0;
   for (int kt = 0; kt < nk; ++kt) {
     const int nbuf = buf + 1 == NS ? 0 : buf + 1;
@@ -327,16 +354,16 @@ void gemm_mfma_kernel(GemmArgs p) {
     wait_lgkmcnt0();
     // Sub-step 1 fragments first: they have all of sub-step 0 to land, so the
     // lgkmcnt wait before the barrier finds them done.
-    load_frags(buf, 1, f1);
+    load_frags_l(buf, 1, f1);
     issue_dma(kt + NS - 1, buf == 0 ? NS - 1 : buf - 1);
-    mfmas(f0);
+    mfmas_l(f0);
     // Own reads of tile kt done and own DMA of tile kt+1 landed; the barrier
     // extends both to every wave.  Tiles kt+2 .. kt+NS-1 stay in flight.
     wait_lgkmcnt0();
     wait_vmcnt<(NS - 2) * D_TILE>();
     __builtin_amdgcn_s_barrier();
-    load_frags(nbuf, 0, f0);
-    mfmas(f1);
+    load_frags_l(nbuf, 0, f0);
+    mfmas_l(f1);
     // Issue order: sub-step 1 reads; sub-step 0 MFMAs with the DMAs between the
     // first of them; [barrier]; next tile's sub-step 0 reads between the first
     // sub-step 1 MFMAs.
@@ -356,12 +383,17 @@ void gemm_mfma_kernel(GemmArgs p) {
     buf = nbuf;
   }
 
+  };
+  if (wave_live) pipeline(std::true_type{});
+  else pipeline(std::false_type{});
+
   // ---- epilogue.  acc[i][j][v]: row = m0 + wm*WM + 32i + l32,
   //      col (tile-local) = 8*(v/4) + 4*hsel + (v%4)
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int64_t grow = m0 + wm * WM + 32 * i + l32;
     if (grow >= m_rows) continue;
+    if (!wave_live) continue;
     float rs = 1.f;
     if (p.row_scale) {
       int64_t tok = grow;
@@ -372,6 +404,7 @@ void gemm_mfma_kernel(GemmArgs p) {
       rs = p.row_scale[tok];
     }
     if constexpr (GATED) {
+      if (p.a_rows && p.a_rows[grow] < 0) continue;  // padding: never read back
       constexpr int TH = TN / 2;
       bf16_t* C = (bf16_t*)p.C + grow * p.ldc;
 #pragma unroll
@@ -437,6 +470,7 @@ void gemm_mfma_kernel(GemmArgs p) {
       }
     }
   }
+  }  // tile loop
 }
 
 // ------------------------------------------------------------------ fp32 path
@@ -544,16 +578,36 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
 }
 
 // ------------------------------------------------------------------ dispatch
+static int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI, int BELEM>
 static hipError_t run_mfma(const GemmArgs& a, hipStream_t s) {
   constexpr int NCOLS = EPI == EPI_GATED ? BN / 2 : BN;
+  constexpr int THREADS = 64 * WAVES_M * WAVES_N;
   const int64_t mb_cap = (a.M + BM - 1) / BM;
   const int64_t nb = (a.N + NCOLS - 1) / NCOLS;
-  const int64_t blocks = mb_cap * nb;
-  if (blocks <= 0) return hipSuccess;
-  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  gemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, EPI, BELEM>
-      <<<dim3((unsigned)blocks), dim3(64 * WAVES_M * WAVES_N), 0, s>>>(a);
+  const int64_t tiles = mb_cap * nb;  // upper bound; the kernel counts the real ones
+  if (tiles <= 0) return hipSuccess;
+  auto kern = gemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, EPI, BELEM>;
+  static int per_cu = 0;  // resident blocks per CU for this instantiation
+  if (!per_cu) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, THREADS, 0) != hipSuccess || n <= 0) n = 1;
+    per_cu = n;
+  }
+  const int64_t resident = (int64_t)device_cu_count() * per_cu;
+  const int64_t grid = tiles < resident ? tiles : resident;
+  kern<<<dim3((unsigned)grid), dim3(THREADS), 0, s>>>(a);
   return hipGetLastError();
 }
 
