@@ -143,9 +143,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N)
 __attribute__((amdgpu_waves_per_eu(WAVES_M * WAVES_N / 4, WAVES_M * WAVES_N / 4)))
 void gemm_mfma_kernel(GemmArgs p) {
   constexpr bool FP8 = BELEM == ELEM_FP8;
-  // bf16: 32-deep K tiles in 4 stages; fp8 weights: 64-deep K tiles in 3 stages
-  constexpr int BK = FP8 ? 64 : 32;
-  constexpr int NS = FP8 ? 3 : 4;
+  // 8 waves, bf16: ping-pong with register-staged loads, 64-deep K tiles in 2 stages.
+  // Otherwise LDS-DMA: bf16 32-deep K tiles in 4 stages; fp8 weights 64-deep in 3.
+  constexpr bool PPR = WAVES_M * WAVES_N == 8 && BELEM == ELEM_BF16;
+  constexpr int BK = (PPR || BELEM == ELEM_FP8) ? 64 : 32;
+  constexpr int NS = PPR ? 2 : (BELEM == ELEM_FP8 ? 3 : 4);
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr bool GATED = EPI == EPI_GATED;
@@ -204,49 +206,7 @@ void gemm_mfma_kernel(GemmArgs p) {
   const rsrc_t rsA = make_rsrc(p.A, (uint32_t)(p.a_rows_alloc * p.lda * 2));
   const rsrc_t rsB = make_rsrc(Bbase, (uint32_t)((int64_t)(GATED ? 2 * p.N : p.N) * p.Kdim * EB));
 
-  // ---- DMA source offsets.  Instruction i of this wave fills ROWS_PER_DMA
-  // consecutive tile rows; lane l writes row base + l / CH, physical chunk l % CH,
-  // which holds logical chunk (l % CH) ^ swz(row).
-  uint32_t a_off[A_DMA];
-#pragma unroll
-  for (int i = 0; i < A_DMA; ++i) {
-    const int r = (wave * A_DMA + i) * A_ROWS_PER_DMA + lane / A_CH;
-    const int64_t grow = m0 + r;
-    const int slot = (pad_map && grow < p.M) ? pad_map[grow] : 0;
-    int64_t tok;
-    if (p.a_rows) tok = slot >= 0 ? slot / p.row_div : 0;
-    else tok = grow < p.M ? grow : p.M - 1;
-    a_off[i] = (grow >= m_rows || slot < 0)
-                   ? 0x80000000u
-                   : (uint32_t)(tok * p.lda * 2) + (uint32_t)((((lane % A_CH) ^ lds_swz<A_ROW>(r))) << 4);
-  }
-  const int bl_row = lane / B_CH;  // row within a DMA group (B rows are 64 bytes: groups of 16 rows)
-  static_assert(B_ROW == 64, "B DMA groups must start at multiples of 16 rows");
-  const uint32_t b_voff = (uint32_t)(bl_row * p.Kdim * EB) + (uint32_t)(((lane % B_CH) ^ lds_swz<B_ROW>(bl_row)) << 4);
-  uint32_t b_soff[B_DMA];
-#pragma unroll
-  for (int i = 0; i < B_DMA; ++i) {
-    const int q0 = (wave * B_DMA + i) * B_ROWS_PER_DMA;
-    int brow;
-    if constexpr (GATED) brow = q0 < BN / 2 ? n0 + q0 : p.N + n0 + (q0 - BN / 2);
-    else brow = n0 + q0;
-    b_soff[i] = (uint32_t)((int64_t)brow * p.Kdim * EB);
-  }
   const int nk = p.Kdim / BK;
-  // Tile kt into stage buf; tiles past the end are issued with an out-of-range
-  // offset, which the buffer bound turns into zero fill without a memory access.
-  auto issue_dma = [&](int kt, int buf) {
-    uint8_t* sA = smem + buf * STAGE;
-    uint8_t* sB = sA + A_BYTES;
-    const bool live = kt < nk;
-#pragma unroll
-    for (int i = 0; i < A_DMA; ++i)
-      dma16(rsA, sA + (wave * A_DMA + i) * 1024, live ? a_off[i] : 0x80000000u, live ? (uint32_t)kt * A_ROW : 0u);
-#pragma unroll
-    for (int i = 0; i < B_DMA; ++i)
-      dma16(rsB, sB + (wave * B_DMA + i) * 1024, live ? b_voff : 0x80000000u,
-            live ? b_soff[i] + (uint32_t)kt * (uint32_t)B_ROW : 0u);
-  };
 
   // LDS row of the wave's B tile j (output-column tile)
   auto b_lds_row = [&](int j) {
@@ -330,6 +290,50 @@ void gemm_mfma_kernel(GemmArgs p) {
   // without fragment reads or MFMAs.
   auto pipeline = [&](auto live_tag) {
     constexpr bool LIVE = decltype(live_tag)::value;
+    // ---- DMA source offsets.  Instruction i of this wave fills ROWS_PER_DMA
+    // consecutive tile rows; lane l writes row base + l / CH, physical chunk l % CH,
+    // which holds logical chunk (l % CH) ^ swz(row).
+    uint32_t a_off[A_DMA];
+  #pragma unroll
+    for (int i = 0; i < A_DMA; ++i) {
+      const int r = (wave * A_DMA + i) * A_ROWS_PER_DMA + lane / A_CH;
+      const int64_t grow = m0 + r;
+      const int slot = (pad_map && grow < p.M) ? pad_map[grow] : 0;
+      int64_t tok;
+      if (p.a_rows) tok = slot >= 0 ? slot / p.row_div : 0;
+      else tok = grow < p.M ? grow : p.M - 1;
+      a_off[i] = (grow >= m_rows || slot < 0)
+                     ? 0x80000000u
+                     : (uint32_t)(tok * p.lda * 2) + (uint32_t)((((lane % A_CH) ^ lds_swz<A_ROW>(r))) << 4);
+    }
+    const int bl_row = lane / B_CH;  // row within a DMA group (B rows are 64 bytes: groups of 16 rows)
+    static_assert(PPR || B_ROW == 64, "B DMA groups must start at multiples of 16 rows");
+    const uint32_t b_voff = (uint32_t)(bl_row * p.Kdim * EB) + (uint32_t)(((lane % B_CH) ^ lds_swz<B_ROW>(bl_row)) << 4);
+    uint32_t b_soff[B_DMA];
+  #pragma unroll
+    for (int i = 0; i < B_DMA; ++i) {
+      const int q0 = (wave * B_DMA + i) * B_ROWS_PER_DMA;
+      int brow;
+      if constexpr (GATED) brow = q0 < BN / 2 ? n0 + q0 : p.N + n0 + (q0 - BN / 2);
+      else brow = n0 + q0;
+      b_soff[i] = (uint32_t)((int64_t)brow * p.Kdim * EB);
+    }
+    // Tile kt into stage buf; tiles past the end are issued with an out-of-range
+    // offset, which the buffer bound turns into zero fill without a memory access.
+    auto issue_dma = [&](int kt, int buf) {
+      uint8_t* sA = smem + buf * STAGE;
+      uint8_t* sB = sA + A_BYTES;
+      const bool live = kt < nk;
+  #pragma unroll
+      for (int i = 0; i < A_DMA; ++i)
+        dma16(rsA, sA + (wave * A_DMA + i) * 1024, live ? a_off[i] : 0x80000000u, live ? (uint32_t)kt * A_ROW : 0u);
+  #pragma unroll
+      for (int i = 0; i < B_DMA; ++i)
+        dma16(rsB, sB + (wave * B_DMA + i) * 1024, live ? b_voff : 0x80000000u,
+              live ? b_soff[i] + (uint32_t)kt * (uint32_t)B_ROW : 0u);
+    };
+
+
     auto load_frags_l = [&](int b, int s_, Frags& f) {
       if constexpr (LIVE) load_frags(b, s_, f);
     };
@@ -384,8 +388,145 @@ void gemm_mfma_kernel(GemmArgs p) {
   }
 
   };
-  if (wave_live) pipeline(std::true_type{});
-  else pipeline(std::false_type{});
+  // ---- ping-pong pipeline (8 waves, bf16): the two groups of 4 waves (one wave
+  // of each group per SIMD) run offset by one barrier phase.  In its memory
+  // phase a wave reads all fragments of the next K tile from LDS and issues its
+  // share of a later tile's DMA; in its compute phase it runs the MFMAs from
+  // registers only.  While one group computes, the other loads, so each SIMD's
+  // matrix pipe alternates between its two waves.
+  //   phase 2m   : group 0 loads tile m,     group 1 computes tile m-1
+  //   phase 2m+1 : group 0 computes tile m,  group 1 loads tile m
+  // Stage m % NS is read in phases 2m and 2m+1; the DMA issued in the memory
+  // phase of tile m fills the stage of tile m-1, which both groups are done with.
+  // The scheduler may not move anything (MFMAs included) across a phase boundary.
+  auto phase_barrier = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- ping-pong pipeline with register-staged loads (8 waves, bf16).
+  // The two groups of 4 waves (one wave of each group per SIMD) run offset by
+  // one barrier phase: in a memory phase a wave reads the fragments of the next
+  // half K tile (32 deep) from LDS; in a compute phase it runs that half tile's
+  // MFMAs from registers only.  While one group computes, the other loads, so each
+  // SIMD's matrix pipe alternates between its two waves.  Half tile h is loaded by
+  // group 0 in phase 2h and group 1 in phase 2h+1, and computed one phase later.
+  // Global -> LDS: each wave stages its 1/8 of a 64-deep K tile (8 KB: 8 loads
+  // of 16 bytes per lane over 128-byte row segments) in registers.  In the memory
+  // phase of the first half of tile j a wave writes its staged share of tile j+1
+  // into the other LDS stage (last read for tile j-1, one phase earlier) and
+  // issues the global loads of tile j+2, which then have four phases to land.
+  auto pingpong_reg = [&](auto live_tag) {
+    constexpr bool LIVE = decltype(live_tag)::value;
+    constexpr int NLA = A_BYTES / 1024 / NW, NLB = B_BYTES / 1024 / NW;  // 16-byte loads per lane
+    const int grp = wave >> 2;
+    // Global offsets (no swizzle) and LDS destinations (swizzled) of this lane's
+    // chunks.  Load i covers tile rows (wave*NL + i)*8 + lane/8, chunk lane%8.  Row
+    // bits 0-2 come from the lane and bit 3 is i & 1, so the LDS destination of
+    // load i is one of two bases plus i KiB; B rows of one wave stay in one
+    // half (gate or up), so B load i is load 0 plus i*8 weight rows.
+    static_assert(NLA % 2 == 0 && NLB % 2 == 0, "two LDS bases");
+    uint32_t ga[NLA];
+#pragma unroll
+    for (int i = 0; i < NLA; ++i) {
+      const int r = (wave * NLA + i) * 8 + (lane >> 3);
+      const int64_t grow = m0 + r;
+      const int slot = (pad_map && grow < p.M) ? pad_map[grow] : 0;
+      int64_t tok;
+      if (p.a_rows) tok = slot >= 0 ? slot / p.row_div : 0;
+      else tok = grow < p.M ? grow : p.M - 1;
+      ga[i] = (grow >= m_rows || slot < 0) ? 0x80000000u : (uint32_t)(tok * p.lda * 2) + ((lane & 7) << 4);
+    }
+    const int r0 = wave * NLA * 8 + (lane >> 3);  // bit 3 of r0 is 0 (wave*NLA*8 is a multiple of 16)
+    const int la0 = r0 * A_ROW + (((lane & 7) ^ lds_swz<A_ROW>(r0)) << 4);
+    const int la1 = (r0 + 8) * A_ROW + (((lane & 7) ^ lds_swz<A_ROW>(r0 + 8)) << 4) - 1024;
+    const int q0 = wave * NLB * 8 + (lane >> 3);
+    const int lb0 = q0 * B_ROW + (((lane & 7) ^ lds_swz<B_ROW>(q0)) << 4);
+    const int lb1 = (q0 + 8) * B_ROW + (((lane & 7) ^ lds_swz<B_ROW>(q0 + 8)) << 4) - 1024;
+    int brow0;
+    if constexpr (GATED) brow0 = q0 - (lane >> 3) < BN / 2 ? n0 + (q0 - (lane >> 3)) : p.N + n0 + (q0 - (lane >> 3) - BN / 2);
+    else brow0 = n0 + (q0 - (lane >> 3));
+    const uint32_t gb0 = (uint32_t)((int64_t)(brow0 + (lane >> 3)) * p.Kdim * 2) + ((lane & 7) << 4);
+    const uint32_t gb_step = (uint32_t)(8 * p.Kdim * 2);  // 8 weight rows
+    u32x4 sa[NLA], sbv[NLB];
+    auto gload = [&](int kt) {
+      const bool live = kt < nk;
+#pragma unroll
+      for (int i = 0; i < NLA; ++i)
+        sa[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rsA, live ? ga[i] : 0x80000000u, live ? kt * A_ROW : 0, 0));
+#pragma unroll
+      for (int i = 0; i < NLB; ++i)
+        sbv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rsB, live ? gb0 : 0x80000000u, live ? kt * B_ROW + i * gb_step : 0, 0));
+    };
+    auto lds_store = [&](int stage) {
+      uint8_t* st = smem + stage * STAGE;
+#pragma unroll
+      for (int i = 0; i < NLA; ++i) *(u32x4*)(st + ((i & 1) ? la1 : la0) + i * 1024) = sa[i];
+#pragma unroll
+      for (int i = 0; i < NLB; ++i) *(u32x4*)(st + A_BYTES + ((i & 1) ? lb1 : lb0) + i * 1024) = sbv[i];
+    };
+    bf16x8 fa[TM][2];
+    u32x4 fb[TN][2];
+    // prologue: tile 0 into stage 0, tile 1 in flight
+    gload(0);
+    wait_vmcnt<0>();
+    lds_store(0);
+    gload(1);
+    wait_lgkmcnt0();
+    phase_barrier();
+    if (grp == 1) phase_barrier();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int st = kt & 1;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        // memory phase
+        if (hh == 0) {
+          wait_vmcnt<0>();    // staged share of tile kt+1 has landed
+          lds_store(st ^ 1);  // the stage of tile kt-1: both groups are done with it
+          gload(kt + 2);
+        }
+        if constexpr (LIVE) {
+          const uint8_t* sa0 = smem + st * STAGE;
+          const uint8_t* sb0 = sa0 + A_BYTES;
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const int c = 2 * (2 * hh + s2) + hsel;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) fa[i][s2] = *(const bf16x8*)(sa0 + a_row_off[i] + ((c ^ swa) << 4));
+#pragma unroll
+            for (int j = 0; j < TN; ++j) fb[j][s2] = *(const u32x4*)(sb0 + b_row_off[j] + ((c ^ swb) << 4));
+          }
+        }
+        wait_lgkmcnt0();  // fragments in registers; this wave's LDS writes done
+        phase_barrier();
+        // compute phase
+        if constexpr (LIVE) {
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+              const bf16x8 bj = __builtin_bit_cast(bf16x8, fb[j][s2]);
+#pragma unroll
+              for (int i = 0; i < TM; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bj, fa[i][s2], acc[i][j], 0, 0, 0);
+            }
+        }
+        phase_barrier();
+      }
+    }
+    if (grp == 0) phase_barrier();  // same barrier count in both groups
+  };
+
+  if constexpr (PPR) {
+    if (wave_live) pingpong_reg(std::true_type{});
+    else pingpong_reg(std::false_type{});
+  } else {
+    if (wave_live) pipeline(std::true_type{});
+    else pipeline(std::false_type{});
+  }
 
   // ---- epilogue.  acc[i][j][v]: row = m0 + wm*WM + 32i + l32,
   //      col (tile-local) = 8*(v/4) + 4*hsel + (v%4)
