@@ -3,23 +3,29 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config mixtral] [--T N]
 
-One step is one moe_forward call (router logits -> routing -> permutation ->
-grouped gate/up GEMM + gated activation -> grouped down GEMM + weighted
-combine -> finalize) over one batch of T synthetic tokens whose inputs and
-weights are already resident in HBM.  The default workload is the Mixtral-style
-layer (T=4096, H=4096, E=8, top-2, I=14336, SwiGLU, bf16).
+One step is one moe_forward call over one batch of T synthetic tokens whose
+inputs and weights are already resident in HBM: router logits -> routing ->
+(grouped path: permutation -> grouped gate/up GEMM + gated activation -> grouped
+down GEMM + weighted combine -> finalize; decode path, T <= 16: fused weight-
+streaming kernels).  The default workload is the Mixtral-style layer (T=4096,
+H=4096, E=8, top-2, I=14336, SwiGLU, bf16).
+
+Decode-path workloads rotate over several copies of the layer whose experts are
+permuted differently (at least 4 copies and 512 MB of weights), so a step never
+finds the experts it reads in the 256 MB last-level cache from the step before.
 
 Prints one JSON line:
   value        tokens/s of the whole step (HIP events around K back-to-back steps)
   roofline     the dominant kernel's algorithmic FLOP (or bytes) per launch over its
                average duration, timed with HIP events that the library records on
                its launch stream between stages, against MI355X's published peak
-  cpu_baseline the float64 CPU oracle on a bounded row sample of the same workload
+  cpu_baseline the float64 CPU oracle on a bounded sample of the same workload
 """
 from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -27,6 +33,7 @@ import time
 METRIC = "MoE layer tokens/s; prefill TFLOP/s % MFMA peak; decode GB/s % HBM peak"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+MALL_BYTES = 256 << 20
 
 
 def parse():
@@ -36,36 +43,81 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mixtral")
     ap.add_argument("--T", type=int, default=None)
-    ap.add_argument("--cpu-rows", type=int, default=None, help="oracle row sample (default per config)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
 
-def stage_work(spec, T, counts=None):
-    """Algorithmic FLOP and HBM bytes per stage (padding and skipped experts not counted)."""
+def stage_work(spec, T, counts, path):
+    """Algorithmic FLOP and HBM bytes per stage of the library's stage events.
+    Padding and experts nobody picked are not counted; weights count once."""
     H, E, K, I = spec.H, spec.E, spec.K, spec.I
-    S, Is, Id = spec.n_shared, spec.I_shared, spec.I_dense
+    S, Id = spec.n_shared, spec.I_dense
     wb = 1 if spec.wdtype == "fp8" else (4 if spec.wdtype == "fp32" else 2)
     ab = 4 if spec.wdtype == "fp32" else 2
+    sb = 4 if spec.wdtype == "fp8" else 0  # fp32 scale per output channel
+    Kp = K + S
     rows = T * K
-    fl = {}
-    fl["router"] = 0 if spec.supplied_logits else 2 * T * E * H
-    fl["gate_up"] = 2 * rows * H * 2 * I + 2 * T * S * H * 2 * Is
-    fl["down"] = 2 * rows * I * H + 2 * T * S * Is * H
+    used = int((counts > 0).sum())
+    z = 0 if spec.supplied_logits else 1
+    fl = {s: 0 for s in ("router", "gate_up", "down", "dense_gate_up", "dense_down")}
+    fl["router"] = z * 2 * T * E * H
+    fl["gate_up"] = 2 * rows * H * 2 * I + 2 * T * S * H * 2 * I
+    fl["down"] = 2 * rows * I * H + 2 * T * S * I * H
     fl["dense_gate_up"] = 2 * T * H * 2 * Id
     fl["dense_down"] = 2 * T * Id * H
-    # weights actually touched: experts with at least one row
-    used = E if counts is None else int((counts > 0).sum())
+    w_up = used * 2 * I * (H * wb + sb) + S * 2 * I * H * ab
+    w_down = used * H * (I * wb + sb) + S * H * I * ab
     by = {}
-    by["gate_up"] = used * 2 * I * H * wb + S * 2 * Is * H * ab + T * H * ab + rows * I * ab
-    by["down"] = used * H * I * wb + S * H * Is * ab + rows * I * ab + (rows + T * S) * H * ab
-    by["router"] = 0 if spec.supplied_logits else E * H * ab + T * H * ab + T * E * 4
-    by["dense_gate_up"] = 2 * Id * H * ab + T * H * ab + T * Id * ab
-    by["dense_down"] = H * Id * ab + T * Id * ab + T * H * 4
+    if path == "decode":
+        # pre kernel: router + dense gate/up; up kernel: expert gate/up + dense down;
+        # down kernel: expert down + combine; finalize: post-norms (dense branch only)
+        fl = {"router": fl["router"] + fl["dense_gate_up"], "gate_up": fl["gate_up"] + fl["dense_down"],
+              "down": fl["down"], "dense_gate_up": 0, "dense_down": 0}
+        by["router"] = z * (E * H * ab + T * E * 4) + 2 * Id * H * ab + T * H * ab + T * Id * ab
+        by["gate_up"] = w_up + T * H * ab + T * Kp * I * ab + (H * Id * ab + T * Id * ab + T * H * 4 if Id else 0)
+        by["down"] = w_down + T * Kp * I * ab + T * H * (4 if Id else ab)
+        by["dense_gate_up"] = by["dense_down"] = 0
+        by["finalize"] = 2 * T * H * 4 + T * H * ab if Id else 0
+    else:
+        by["router"] = z * (E * H * ab + T * H * ab + T * E * 4)
+        by["gate_up"] = w_up + T * H * ab + rows * I * ab
+        by["down"] = w_down + rows * I * ab + (rows + T * S) * H * ab
+        by["dense_gate_up"] = 2 * Id * H * ab + T * H * ab + T * Id * ab
+        by["dense_down"] = H * Id * ab + T * Id * ab + T * H * 4
+        by["finalize"] = T * Kp * H * (4 if Id else ab) + T * H * ab
     return fl, by
 
 
-def cpu_baseline(L, rows_n):
+def rotated_sets(B, dl, path):
+    """Copies of the layer with the experts rolled along the expert axis, enough
+    that the weights a decode step reads were not read by the previous step."""
+    import torch
+    if path != "decode" or dl.desc.num_experts < 2:
+        return [dl]
+    t = dl.t
+    nbytes = sum(v.numel() * v.element_size() for v in t.values() if v is not None)
+    n = max(4, math.ceil(2 * MALL_BYTES / max(nbytes, 1)))
+    E = dl.desc.num_experts
+    sets = [dl]
+    for i in range(1, n):
+        shift = max(1, (i * E) // n)
+        c = {}
+        for k, v in t.items():
+            if v is None or k in ("x", "logits"):
+                c[k] = v
+            elif k in ("w13", "w2", "w13_scale", "w2_scale", "per_expert_scale"):
+                c[k] = torch.roll(v, shifts=shift, dims=0).contiguous()
+            else:
+                c[k] = v.clone()
+        sets.append(B.DeviceLayer(dl.desc, c))
+    return sets
+
+
+def cpu_baseline(L, seconds):
+    """The oracle on a row sample of the workload sized for about `seconds` of CPU
+    time (routing and permutation over all T rows; expert FFNs over the sample),
+    repeated when even all T rows take less."""
     import numpy as np
     from mixture_experts_ffn_router_amd import workloads as W
     from oracle import moe_oracle as O
@@ -75,17 +127,27 @@ def cpu_baseline(L, rows_n):
     except Exception:
         threads = None
     T = L["T"]
-    rows = np.sort(np.random.default_rng(0).choice(T, min(rows_n, T), replace=False))
     layer = W.oracle_layer(L)
     x = L["x"].float().numpy().astype(np.float64)
     logits = None if L["logits"] is None else L["logits"].numpy().astype(np.float64)
-    t0 = time.perf_counter()
-    O.moe_layer(x, layer, rows=rows, logits=logits)
-    dt = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+
+    def run(n, reps=1):
+        rows = np.sort(rng.choice(T, n, replace=False))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            O.moe_layer(x, layer, rows=rows, logits=logits)
+        return time.perf_counter() - t0
+
+    pilot = min(T, 16)
+    rate = pilot / max(run(pilot), 1e-6)  # rows per second (routing cost included)
+    n = int(min(T, max(pilot, rate * seconds)))
+    reps = 1 if n < T else max(1, int(seconds / max(n / rate, 1e-6)))
+    dt = run(n, reps)
     cores = len(os.sched_getaffinity(0))
-    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": threads or cores, "kind": "oracle",
-            "sample": f"{len(rows)} of {T} token rows through the experts (routing and permutation "
-                      f"over all {T}); {dt:.1f} s on {cores} host cores, numpy BLAS threads {threads}"}
+    return {"value": round(n * reps / dt, 2), "unit": "tokens/s", "cores": threads or cores, "kind": "oracle",
+            "sample": f"{n} of {T} token rows through the experts (routing over all {T}), {reps} time(s): "
+                      f"{dt:.1f} s on {cores} host cores, numpy BLAS threads {threads}"}
 
 
 def main():
@@ -104,12 +166,15 @@ def main():
     spec = spec.with_T(T)
     L = W.make_layer(spec, seed=0)
     dl = B.DeviceLayer.from_generated(L)
+    path = dl.path(T)
+    sets = rotated_sets(B, dl, path)
     act_dtype = dl.act_dtype
     out = torch.empty(T, spec.H, dtype=act_dtype, device="cuda")
     ws = torch.empty(dl.workspace_size(T), dtype=torch.uint8, device="cuda")
-    print(f"[bench] {spec.name} T={T}: warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        dl.forward(out=out, workspace=ws)
+    print(f"[bench] {spec.name} T={T} path={path} weight sets={len(sets)}: warmup {args.warmup}",
+          file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        sets[i % len(sets)].forward(out=out, workspace=ws)
     torch.cuda.synchronize()
 
     # timed region: K back-to-back steps
@@ -117,8 +182,8 @@ def main():
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record()
-    for _ in range(args.steps):
-        dl.forward(out=out, workspace=ws)
+    for i in range(args.steps):
+        sets[i % len(sets)].forward(out=out, workspace=ws)
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -138,18 +203,19 @@ def main():
     p0 = torch.cuda.Event(enable_timing=True)
     p1 = torch.cuda.Event(enable_timing=True)
     p0.record()
-    for row in evs:
-        dl.forward(out=out, workspace=ws, events=row)
+    for i, row in enumerate(evs):
+        sets[i % len(sets)].forward(out=out, workspace=ws, events=row)
     p1.record()
     torch.cuda.synchronize()
     prof_ms = p0.elapsed_time(p1) / args.steps
     stage_ms = {name: sum(row[i].elapsed_time(row[i + 1]) for row in evs) / args.steps
                 for i, name in enumerate(B.STAGES)}
 
-    fl, by = stage_work(spec, T, counts)
+    fl, by = stage_work(spec, T, counts, path)
     total_flop = sum(fl.values())
-    gemm_stages = [s for s in ("gate_up", "down", "dense_gate_up", "dense_down", "router") if fl[s] > 0]
-    dom = max(gemm_stages, key=lambda s: stage_ms[s])
+    total_bytes = sum(by.values())
+    cand = [s for s in ("gate_up", "down", "dense_gate_up", "dense_down", "router") if fl[s] > 0]
+    dom = max(cand, key=lambda s: stage_ms[s])
     dom_s = stage_ms[dom] / 1e3
     intensity = fl[dom] / max(by[dom], 1)
     # ridge point of MI355X: 2500e12 / 8e12 = 312 FLOP/byte
@@ -179,16 +245,18 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{spec.name} MoE FFN layer forward", "T": T, "hidden": spec.H,
                    "experts": spec.E, "top_k": spec.K, "inter": spec.I, "act": spec.act,
-                   "shared": spec.n_shared, "dense_inter": spec.I_dense},
+                   "shared": spec.n_shared, "dense_inter": spec.I_dense, "path": path,
+                   "weight_sets": len(sets)},
         "step_tflops": round(total_flop / (ms_per_step / 1e3) / 1e12, 2),
+        "step_gbps": round(total_bytes / (ms_per_step / 1e3) / 1e9, 1),
+        "experts_touched": int((counts > 0).sum()),
         "stages_ms": {k: round(v, 5) for k, v in stage_ms.items()},
         "profiled_ms_per_step": round(prof_ms, 5),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        rows_n = args.cpu_rows or (256 if T > 256 else T)
-        print(f"[bench] cpu oracle on {rows_n} rows", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(L, rows_n)
+        print(f"[bench] cpu oracle, about {args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

@@ -150,6 +150,7 @@ typedef struct {
 
 /*
  * Bytes of workspace moe_forward needs for T tokens (*bytes set on MOE_OK).
+ * Non-decreasing in T: a workspace sized for T serves every smaller T.
  */
 moe_status moe_forward_workspace_size(const moe_layer_desc* desc, int64_t T, size_t* bytes);
 
@@ -176,12 +177,26 @@ moe_status moe_forward_workspace_size(const moe_layer_desc* desc, int64_t T, siz
  * act_dtype F32); the gated intermediate and the per-slot expert outputs are
  * rounded to bf16 in the bf16 path; logits are fp32.
  *
+ * Two execution paths compute this same operation (moe_forward_path tells which
+ * one a call takes).  The grouped path permutes the routed rows and runs grouped
+ * GEMMs.  The decode path (T <= 16 bf16 tokens) streams each selected expert's
+ * weights once and applies them to all tokens together; it folds the routing
+ * weight into the gated intermediate before its bf16 rounding and sums the
+ * expert outputs of a token in fp32 before the single output rounding.
+ *
  * workspace: device memory of at least moe_forward_workspace_size() bytes,
  * 256-byte aligned, owned by the caller; contents on entry do not matter and
  * are clobbered.  Two calls that share a workspace must be stream-ordered.
  */
 moe_status moe_forward(const moe_layer_desc* desc, const moe_tensors* tensors, int64_t T,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Execution path moe_forward takes for T tokens ([LC] lesson 35: a decode
+ * token touches only its experts' weights, so the layer is bound by reading
+ * them).  Returns MOE_PATH_GROUPED, MOE_PATH_DECODE, or -1 for an invalid
+ * descriptor or T < 0. */
+typedef enum { MOE_PATH_GROUPED = 0, MOE_PATH_DECODE = 1 } moe_path;
+int32_t moe_forward_path(const moe_layer_desc* desc, int64_t T);
 
 /* Stages of moe_forward, in launch order (indices into the event array below). */
 typedef enum {
@@ -203,6 +218,8 @@ typedef enum {
  * `stream`: events[i] just before stage i and events[MOE_STAGE_COUNT] after the
  * last one, so hipEventElapsedTime(events[i], events[i+1]) is the time of stage
  * i.  A stage that does not run for this layer gets two back-to-back records.
+ * On the decode path the gate/up stage also runs the dense gate/up and the
+ * routing, and the down stage also runs the dense down and the combine.
  * It only records: nothing is synchronised.  For measurement.
  */
 moe_status moe_forward_profiled(const moe_layer_desc* desc, const moe_tensors* tensors, int64_t T,

@@ -48,7 +48,8 @@ class Tensors(C.Structure):
 
 
 EXPORTS = ["moe_status_string", "moe_last_error", "moe_route", "moe_permute_capacity", "moe_permute",
-           "moe_forward_workspace_size", "moe_forward", "moe_forward_profiled"]
+           "moe_forward_workspace_size", "moe_forward", "moe_forward_profiled", "moe_forward_path"]
+PATHS = {0: "grouped", 1: "decode"}
 STAGES = ["prenorm", "router", "route", "permute", "gate_up", "down", "dense_gate_up", "dense_down",
           "finalize"]
 
@@ -84,6 +85,8 @@ def load(path: str = LIB_PATH):
     lib.moe_forward_profiled.restype = C.c_int
     lib.moe_forward_profiled.argtypes = [C.POINTER(LayerDesc), C.POINTER(Tensors), C.c_int64, C.c_void_p,
                                          C.c_size_t, C.c_void_p, C.POINTER(C.c_void_p)]
+    lib.moe_forward_path.restype = C.c_int32
+    lib.moe_forward_path.argtypes = [C.POINTER(LayerDesc), C.c_int64]
     _lib = lib
     return lib
 
@@ -197,6 +200,13 @@ class DeviceLayer:
                  gamma_pre=d(g.get("pre")), gamma_pre2=d(g.get("pre2")),
                  gamma_post1=d(g.get("post1")), gamma_post2=d(g.get("post2")))
         return cls(desc, t)
+
+    def path(self, T):
+        """Which execution path moe_forward takes for T tokens: "grouped" or "decode"."""
+        r = load().moe_forward_path(C.byref(self.desc), T)
+        if r < 0:
+            raise ValueError("invalid layer descriptor or T")
+        return PATHS[r]
 
     def workspace_size(self, T):
         n = C.c_size_t(0)

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cmath>
 #include <cstring>
+#include <algorithm>
 
 #include "../../include/moe.h"
 #include "kernels.h"
@@ -57,8 +58,17 @@ int choose_block_m(const moe_layer_desc& d, int64_t T) {
   return avg >= 256 ? 256 : 64;
 }
 
+// Decode path: at most 16 bf16 tokens (one MFMA tile of token columns) whose
+// rows fit the decode kernels' LDS staging.
+bool use_decode(const moe_layer_desc& d, int64_t T) {
+  if (d.act_dtype != MOE_DT_BF16 || T < 1 || T > 16) return false;
+  const int lds_max = 160 * 1024;
+  return moe::decode_up_lds_bytes((int)T, d.hidden, d.top_k + d.n_shared, d.num_experts + d.n_shared) <= lds_max &&
+         moe::decode_pre_lds_bytes((int)T, d.hidden) <= lds_max;
+}
+
 struct Plan {
-  bool f32;
+  bool f32, decode;
   int Kp, Ep, bm;
   int64_t cap;
   bool need_logits, need_prenorm, gemma_router, dense;
@@ -66,6 +76,7 @@ struct Plan {
   bool y_f32;                    // per-slot expert outputs kept in fp32
   size_t o_logits, o_w, o_ids, o_counts, o_offsets, o_sorted, o_bexp, o_rms, o_r, o_xn1, o_xn2, o_h, o_y,
       o_dh, o_dout, total;
+  size_t o_rinfo, o_msum;  // decode path only
 };
 
 moe_status validate_desc(const moe_layer_desc* d) {
@@ -149,6 +160,19 @@ moe_status make_plan(const moe_layer_desc& d, const moe_tensors* t, int64_t T, P
   p.o_dh = take(p.dense ? (size_t)T * d.inter_dense * ae : 0);
   p.o_dout = take(p.dense ? (size_t)T * H * 4 : 0);
   p.total = o;
+  // The decode path lays out its own (smaller) buffers over the same workspace;
+  // the size reported stays that of the grouped path, so it grows with T.
+  p.decode = use_decode(d, T);
+  if (p.decode) {
+    o = 0;
+    p.o_logits = take(p.need_logits ? (size_t)T * d.num_experts * 4 : 0);
+    p.o_rinfo = take((size_t)(1 + 17 * p.Ep) * 4);
+    p.o_h = take((size_t)slots * d.inter * 2);
+    p.o_dh = take(p.dense ? (size_t)T * d.inter_dense * 2 : 0);
+    p.o_dout = take(p.dense ? (size_t)T * H * 4 : 0);
+    p.o_msum = take(p.dense ? (size_t)T * H * 4 : 0);
+    if (o > p.total) p.total = o;
+  }
   return MOE_OK;
 }
 
@@ -218,6 +242,11 @@ MOE_API moe_status moe_permute(const int32_t* topk_ids, int64_t T, int32_t K, in
   return MOE_OK;
 }
 
+MOE_API int32_t moe_forward_path(const moe_layer_desc* desc, int64_t T) {
+  if (validate_desc(desc) != MOE_OK || T < 0) return -1;
+  return use_decode(*desc, T) ? MOE_PATH_DECODE : MOE_PATH_GROUPED;
+}
+
 MOE_API moe_status moe_forward_workspace_size(const moe_layer_desc* desc, int64_t T, size_t* bytes) {
   g_err[0] = 0;
   moe_status s = validate_desc(desc);
@@ -251,6 +280,85 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
 
   hipStream_t st = (hipStream_t)stream;
   uint8_t* ws = (uint8_t*)workspace;
+  auto mark = [&](int stage) -> hipError_t {
+    return events ? hipEventRecord((hipEvent_t)events[stage], st) : hipSuccess;
+  };
+#define STAGE(i) HIP_TRY(mark(i), "event record")
+  if (p.decode) {
+    moe::DecodeArgs a{};
+    a.T = (int)T;
+    a.H = d.hidden;
+    a.E = d.num_experts;
+    a.K = d.top_k;
+    a.Kp = p.Kp;
+    a.Ep = p.Ep;
+    a.I = d.inter;
+    a.Id = d.inter_dense;
+    a.act = d.act;
+    a.dense_act = d.dense_act;
+    a.renorm = d.renormalize;
+    a.gemma_router = d.router_mode == MOE_ROUTER_GEMMA;
+    a.dense = p.dense;
+    a.eps = d.eps;
+    a.n_router_groups = p.need_logits ? (d.num_experts + 15) / 16 : 0;
+    // The dense gate/up runs in the up kernel while two of its blocks fit per CU
+    // (its weights then stream while the expert blocks route), else with the router.
+    const bool dense_in_up = moe::decode_up_blocks_per_cu((int)T, d.hidden, p.Kp, p.Ep) == 2;
+    a.n_dense_groups = p.dense && dense_in_up ? d.inter_dense / 16 : 0;
+    a.n_pre_dense_groups = p.dense && !dense_in_up ? d.inter_dense / 16 : 0;
+    a.max_active = (int)std::min<int64_t>(p.Ep, T * p.Kp);
+    a.n_up_blocks = a.max_active * (d.inter / 16);  // items; capped at launch
+    a.n_ddown_groups = p.dense ? d.hidden / 16 : 0;
+    a.x = t->x;
+    a.z = p.need_logits ? (t->logits_out ? t->logits_out : (float*)(ws + p.o_logits)) : const_cast<float*>(t->logits);
+    a.w_router = t->w_router;
+    a.router_scale = t->router_scale;
+    a.pes = t->per_expert_scale;
+    a.w13 = t->w13;
+    a.w2 = t->w2;
+    a.s13 = t->w13_scale;
+    a.s2 = t->w2_scale;
+    a.shared_w13 = t->shared_w13;
+    a.shared_w2 = t->shared_w2;
+    a.dense_w13 = t->dense_w13;
+    a.dense_w2 = t->dense_w2;
+    a.g_pre = t->gamma_pre;
+    a.g_pre2 = t->gamma_pre2;
+    a.hd = p.dense ? ws + p.o_dh : nullptr;
+    a.hbuf = ws + p.o_h;
+    a.dsum = p.dense ? (float*)(ws + p.o_dout) : nullptr;
+    a.msum = p.dense ? (float*)(ws + p.o_msum) : nullptr;
+    a.rinfo = (int*)(ws + p.o_rinfo);
+    a.out = t->out;
+    a.out_f32 = t->out_f32;
+    a.topk_w_out = t->topk_w_out;
+    a.topk_ids_out = t->topk_ids_out;
+    const bool fp8 = d.weight_dtype == MOE_DT_FP8_E4M3;
+    STAGE(MOE_STAGE_PRENORM);
+    STAGE(MOE_STAGE_ROUTER);
+    // router logits
+    HIP_TRY(moe::launch_decode_pre(a, st), "decode pre launch");
+    if (!p.need_logits && t->logits_out)
+      HIP_TRY(hipMemcpyAsync(t->logits_out, t->logits, (size_t)T * d.num_experts * 4, hipMemcpyDeviceToDevice, st),
+              "logits copy");
+    STAGE(MOE_STAGE_ROUTE);
+    STAGE(MOE_STAGE_PERMUTE);
+    STAGE(MOE_STAGE_GATE_UP);
+    // dense gate/up, routing + expert gate/up
+    HIP_TRY(moe::launch_decode_up(a, fp8, st), "decode up launch");
+    STAGE(MOE_STAGE_DOWN);
+    // dense down, expert down + combine
+    HIP_TRY(moe::launch_decode_down(a, fp8, st), "decode down launch");
+    STAGE(MOE_STAGE_DENSE_GATE_UP);
+    STAGE(MOE_STAGE_DENSE_DOWN);
+    STAGE(MOE_STAGE_FINALIZE);
+    if (p.dense)
+      HIP_TRY(moe::launch_finalize(a.msum, moe::ELEM_F32, 1, a.dsum, t->gamma_post1, t->gamma_post2, d.eps,
+                                   t->out, moe::ELEM_BF16, t->out_f32, T, d.hidden, st),
+              "finalize launch");
+    STAGE(MOE_STAGE_COUNT);
+    return MOE_OK;
+  }
   const int H = d.hidden, E = d.num_experts, K = d.top_k, I = d.inter;
   const int act_elem = p.f32 ? moe::ELEM_F32 : moe::ELEM_BF16;
   const int b_elem = d.weight_dtype == MOE_DT_FP8_E4M3 ? moe::ELEM_FP8 : moe::ELEM_BF16;
@@ -272,11 +380,6 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
   auto gemm = [&](const moe::GemmArgs& a, int epi, int belem, int bm) -> hipError_t {
     return p.f32 ? moe::launch_gemm_f32(a, epi, st) : moe::launch_gemm_mfma(a, epi, belem, bm, st);
   };
-  auto mark = [&](int stage) -> hipError_t {
-    return events ? hipEventRecord((hipEvent_t)events[stage], st) : hipSuccess;
-  };
-#define STAGE(i) HIP_TRY(mark(i), "event record")
-
   STAGE(MOE_STAGE_PRENORM);
   // 1. input norms (Gemma router preprocessing, pre_feedforward_layernorm / _2):
   //    1/rms per token; normalised rows only where a learned weight is given.

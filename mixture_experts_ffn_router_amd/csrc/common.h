@@ -31,61 +31,60 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // ---------------------------------------------------------------- wave64 reductions
-// Butterfly all-reduce: xor 1 and xor 2 by quad permutes, then the half-row
-// and row mirrors (every lane of a quad / half-row already holds the same
-// partial, so a mirror reaches the partner group), xor 16 by ds_swizzle, and
-// the two 32-lane halves through readlane.  Every lane ends with the result.
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
-}
-__device__ __forceinline__ uint32_t swz_xor16(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+// All-reduce over the 64 lanes with DPP moves only (no LDS round trip):
+// butterflies over xor 1 and xor 2 (quad permutes), then the half-row and row
+// mirrors leave every lane of a 16-lane row with the row's result; row_bcast:15
+// folds row 0 into row 1 and row 2 into row 3, row_bcast:31 folds rows 0-1 into
+// rows 2-3, so lane 63 ends with the result, which readlane makes uniform.
+// Rows a broadcast does not write receive the identity (`old`), so the same
+// sequence serves sums as well as max / min.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xF, false);
 }
 
 template <typename Op>
-__device__ __forceinline__ uint32_t wave_allreduce_u32(uint32_t v, Op op) {
-  v = op(v, dpp_u32<0xB1>(v));    // quad_perm [1,0,3,2]
-  v = op(v, dpp_u32<0x4E>(v));    // quad_perm [2,3,0,1]
-  v = op(v, dpp_u32<0x141>(v));   // row_half_mirror
-  v = op(v, dpp_u32<0x140>(v));   // row_mirror
-  v = op(v, swz_xor16(v));
-  uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
-  uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
-  return op(a, b);
+__device__ __forceinline__ uint32_t wave_allreduce_u32(uint32_t v, Op op, uint32_t identity) {
+  v = op(v, dpp_u32<0xB1>(v, identity));       // quad_perm [1,0,3,2]
+  v = op(v, dpp_u32<0x4E>(v, identity));       // quad_perm [2,3,0,1]
+  v = op(v, dpp_u32<0x141>(v, identity));      // row_half_mirror
+  v = op(v, dpp_u32<0x140>(v, identity));      // row_mirror
+  v = op(v, dpp_u32<0x142, 0xA>(v, identity)); // row_bcast:15 into rows 1, 3
+  v = op(v, dpp_u32<0x143, 0xC>(v, identity)); // row_bcast:31 into rows 2, 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  return wave_allreduce_u32(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+  return wave_allreduce_u32(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; }, 0u);
 }
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-  return wave_allreduce_u32(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+  return wave_allreduce_u32(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; }, 0xFFFFFFFFu);
 }
 __device__ __forceinline__ float wave_max_f32(float v) {
-  return __uint_as_float(wave_allreduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
-    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
-  }));
+  return __uint_as_float(wave_allreduce_u32(
+      __float_as_uint(v),
+      [](uint32_t a, uint32_t b) { return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b))); },
+      __float_as_uint(-INFINITY)));
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  return __uint_as_float(wave_allreduce_u32(
+      __float_as_uint(v),
+      [](uint32_t a, uint32_t b) { return __float_as_uint(__uint_as_float(a) + __uint_as_float(b)); }, 0u));
 }
 __device__ __forceinline__ double wave_sum_f64(double v) {
-  // same butterfly on the two 32-bit halves of each double
+  // the same moves on the two 32-bit halves of each double (identity +0.0 = all-zero bits)
   auto mv = [](double x, auto shuffle) {
     uint64_t u = __double_as_longlong(x);
     uint32_t lo = shuffle((uint32_t)u), hi = shuffle((uint32_t)(u >> 32));
     return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
   };
-  v += mv(v, [](uint32_t a) { return dpp_u32<0xB1>(a); });
-  v += mv(v, [](uint32_t a) { return dpp_u32<0x4E>(a); });
-  v += mv(v, [](uint32_t a) { return dpp_u32<0x141>(a); });
-  v += mv(v, [](uint32_t a) { return dpp_u32<0x140>(a); });
-  v += mv(v, [](uint32_t a) { return swz_xor16(a); });
-  double a = mv(v, [](uint32_t x) { return (uint32_t)__builtin_amdgcn_readlane((int)x, 0); });
-  double b = mv(v, [](uint32_t x) { return (uint32_t)__builtin_amdgcn_readlane((int)x, 32); });
-  return a + b;
-}
-__device__ __forceinline__ float wave_sum_f32(float v) {
-  return __uint_as_float(wave_allreduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
-    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
-  }));
+  v += mv(v, [](uint32_t a) { return dpp_u32<0xB1>(a, 0u); });
+  v += mv(v, [](uint32_t a) { return dpp_u32<0x4E>(a, 0u); });
+  v += mv(v, [](uint32_t a) { return dpp_u32<0x141>(a, 0u); });
+  v += mv(v, [](uint32_t a) { return dpp_u32<0x140>(a, 0u); });
+  v += mv(v, [](uint32_t a) { return dpp_u32<0x142, 0xA>(a, 0u); });
+  v += mv(v, [](uint32_t a) { return dpp_u32<0x143, 0xC>(a, 0u); });
+  return mv(v, [](uint32_t x) { return (uint32_t)__builtin_amdgcn_readlane((int)x, 63); });
 }
 
 // Total order on finite fp32 as uint32, with -0.0 mapped onto +0.0.
@@ -106,6 +105,38 @@ __device__ __forceinline__ float act_gelu_tanh(float a) {
   const float c = 0.7978845608028654f;  // sqrt(2/pi)
   float u = c * (a + 0.044715f * a * a * a);
   return a / (1.0f + expf(-2.0f * u));
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float apply_act(int act, float g) {
+  return act == 0 ? act_silu(g) : act_gelu_tanh(g);
+}
+
+// 8 fp8 (E4M3) codes in two dwords -> 8 bf16.  v_cvt_pk_f32_fp8 widens two codes
+// (word 0 or word 1 of a dword) to fp32; every E4M3 value has at most 4
+// significant bits, so the upper 16 bits of its fp32 pattern are exactly its
+// bf16 pattern, and one byte permute packs two of them.
+template <bool HI_WORD>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t src) {
+  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8(src, HI_WORD);
+  return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+}
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  u32x4 r;
+  r[0] = fp8x2_to_bf16x2<false>(lo);
+  r[1] = fp8x2_to_bf16x2<true>(lo);
+  r[2] = fp8x2_to_bf16x2<false>(hi);
+  r[3] = fp8x2_to_bf16x2<true>(hi);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Buffer resource over [base, base + bytes): loads past the end return 0.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // raw buffer: stride 0, num_records = bytes (loads past it return 0)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 }  // namespace moe

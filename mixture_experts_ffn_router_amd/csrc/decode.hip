@@ -1,0 +1,637 @@
+// Decode path of the MoE layer: a handful of tokens (T <= 16), where the layer
+// is bound by streaming the weights of the experts the tokens picked ("Gemma 4
+// 26B-A4B MoE walkthrough" section 7 tensor flow; llama.cpp lesson 35: only the
+// selected experts' weights are read, which is what makes a token cheap, and
+// decode is limited by memory bandwidth, not arithmetic).
+//
+// Every weight row is read once per call and applied to all tokens at once: the
+// MFMA v_mfma_f32_16x16x32_bf16 takes 16 weight rows as its A operand and up to
+// 16 token rows as its B operand (columns past T, or tokens that did not pick
+// the expert, are zero), so each 16x16 accumulator tile is 16 output features x
+// 16 tokens.  A block of 8 waves splits the reduction dimension in 8 and sums
+// the partial tiles through LDS in a fixed order.
+//
+// Launches (a fraction of the grouped path's nine):
+//   pre   router logits, 16 experts per block (skipped when logits are supplied);
+//   up    first the dense MLP's gate/up with its activation (16 hidden units per
+//         block; these need no routing, so their weights stream while the other
+//         blocks route), then blocks that each recompute the routing of the T
+//         tokens (a few hundred instructions per token), build the ascending
+//         list of active experts and walk (active expert, 16 hidden units)
+//         items: gate/up rows of that expert against the rows of the tokens that
+//         picked it, h = act(g) * u times the slot's routing weight, stored per
+//         slot in bf16.  Every block normalises the token rows it needs itself
+//         while staging them into LDS;
+//   down  first the dense MLP's down projection, then one block per 16 output
+//         features: the sum over active experts of W2_e h_e, where h_e already
+//         carries each token's weight, so the combine over a token's k slots
+//         happens inside the accumulator;
+//   finalize (dense branch only): the two post-norms and the branch sum.
+//
+// Decode time is mostly chains of dependent memory round trips inside a block,
+// so every wave issues all loads of its share of a weight tile in one batch,
+// before it stages the token rows when the tile is known in advance, and the
+// token rows are read once (into registers) while the routing is computed.
+//
+// Weights are addressed through buffer resources: a row past the end of the
+// tensor (router rows >= E) reads as zero.  FP8 weights are widened to bf16 in
+// registers (exact) and their per-output-channel scale is applied once per
+// expert to the reduced tile.
+#include "common.h"
+#include "kernels.h"
+#include "route_dev.h"
+
+namespace moe {
+
+#ifndef DECODE_DU_BF16
+#define DECODE_DU_BF16 2
+#endif
+#ifndef DECODE_DU_FP8
+#define DECODE_DU_FP8 6
+#endif
+#ifndef DECODE_DW3
+#define DECODE_DW3 8
+#endif
+// macro steps (64 reduction elements each) per load batch
+constexpr int DU_PRE = 6;                // router kernel: few blocks, one batch per wave
+constexpr int DU_BF16 = DECODE_DU_BF16;  // streaming kernels, bf16 weights
+constexpr int DU_FP8 = DECODE_DU_FP8;    // streaming kernels, fp8 weights
+constexpr int XCH = 8;  // 16-byte chunks per lane of a token row held in registers (4096 elements)
+
+// Lane l feeds row / token column l & 15 and reduction elements from lane group
+// g = l >> 4.  Within macro step m (elements 64m .. 64m + 63) MFMA j reads the
+// 8 elements starting at kchunk(m, j, g):
+//   bf16 weights: 64m + 32j + 8g   (each 16-byte load is one MFMA's operand)
+//   fp8 weights:  64m + 16g + 8j   (one 16-byte load holds both MFMAs' operands)
+// The assignment of reduction indices to MFMA slots is arbitrary as long as A
+// and B agree; these make every load 16 contiguous bytes.
+template <bool FP8>
+__device__ __forceinline__ int kchunk(int m, int j, int g) {
+  return FP8 ? 64 * m + 16 * g + 8 * j : 64 * m + 32 * j + 8 * g;
+}
+
+constexpr uint32_t OOB = 0x80000000u;  // a buffer offset past every tensor here: the load returns 0
+
+__device__ __forceinline__ u32x4 bload(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// acc[r] += A_r (16 weight rows) x B (token rows) over macro steps, in batches of DU.
+//   ra/aoff: weight tensor and the byte offset of this lane's weight row;
+//   BG = false: B rows in LDS (b_lds = this lane's token row, zero if !bvalid);
+//   BG = true:  B rows in global memory (rb/boff; boff past the end reads zero).
+template <bool FP8, int NR, bool BG, int DU>
+struct Stream {
+  static constexpr int LA = FP8 ? 1 : 2;  // 16-byte A loads per row group per macro step
+  static constexpr int EB = FP8 ? 1 : 2;
+  rsrc_t ra[NR];
+  uint32_t aoff[NR];
+  rsrc_t rb;
+  uint32_t boff;
+  int g;
+  u32x4 av[NR][DU][LA];
+  u32x4 bv[BG ? DU : 1][2];
+
+  __device__ __forceinline__ void load(int m, int m1) {
+#pragma unroll
+    for (int u = 0; u < DU; ++u) {
+      const bool live = m + u < m1;
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int j = 0; j < LA; ++j)
+          av[r][u][j] = bload(ra[r], live ? aoff[r] + (uint32_t)(kchunk<FP8>(m + u, j, g) * EB) : OOB);
+      if constexpr (BG) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bv[u][j] = bload(rb, live ? boff + (uint32_t)(kchunk<FP8>(m + u, j, g) * 2) : OOB);
+      }
+    }
+  }
+  // Steps past m1 run with zero weights (their loads fell outside the buffer)
+  // and B re-read from step m1 - 1, so a batch is branch-free.
+  __device__ __forceinline__ void compute(f32x4 (&acc)[NR], const bf16_t* b_lds, bool bvalid, int m, int m1) {
+#pragma unroll
+    for (int u = 0; u < DU; ++u) {
+      const int mu = m + u < m1 ? m + u : m1 - 1;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        bf16x8 b;
+        if constexpr (BG) {
+          b = __builtin_bit_cast(bf16x8, bv[u][j]);
+        } else {
+          const u32x4 raw = *(const u32x4*)(b_lds + kchunk<FP8>(mu, j, g));
+          b = __builtin_bit_cast(bf16x8, bvalid ? raw : u32x4{0u, 0u, 0u, 0u});
+        }
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          bf16x8 a;
+          if constexpr (FP8) {
+            const u32x4 q = av[r][u][0];
+            a = fp8x8_to_bf16x8(j ? q[2] : q[0], j ? q[3] : q[1]);
+          } else {
+            a = __builtin_bit_cast(bf16x8, av[r][u][j]);
+          }
+          acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[r], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // Macro steps [m0, m1); the first batch was already issued when first_loaded.
+  __device__ __forceinline__ void run(f32x4 (&acc)[NR], const bf16_t* b_lds, bool bvalid, int m0, int m1,
+                                      bool first_loaded) {
+    for (int m = m0; m < m1; m += DU) {
+      if (m != m0 || !first_loaded) load(m, m1);
+      __builtin_amdgcn_sched_barrier(0);  // the whole batch is issued before the first MFMA waits
+      compute(acc, b_lds, bvalid, m, m1);
+    }
+  }
+};
+
+// Split of the reduction over the NW waves of a block.
+template <int NW>
+__device__ __forceinline__ void wave_range(int ms, int wave, int& m0, int& m1) {
+  m0 = wave * ms / NW;
+  m1 = (wave + 1) * ms / NW;
+}
+
+// Partial tiles of all waves -> LDS.  Tile element (row rho, column t) sits in
+// lane t + 16 (rho / 4), register rho % 4 of the 16x16 accumulator.
+template <int NR>
+__device__ __forceinline__ void partials_to_lds(float* red, const f32x4 (&acc)[NR], int wave, int lane) {
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[((wave * NR + r) * 4 + v) * 64 + lane] = acc[r][v];
+}
+template <int NW, int NR>
+__device__ __forceinline__ float reduced(const float* red, int r, int rho, int t) {
+  const int lane = t + 16 * (rho >> 2), v = rho & 3;
+  float s = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) s += red[((w * NR + r) * 4 + v) * 64 + lane];
+  return s;
+}
+
+// ---------------------------------------------------------------- token rows -> LDS
+// Row pitch H + 8 elements: 16 lanes reading one 16-byte chunk of 16 different
+// rows hit distinct banks.  Lane chunk c of pass p covers elements
+// (p * XCH + c) * 512 + 8 lane .. + 8.
+struct RowRegs {
+  u32x4 q[XCH];
+};
+
+__device__ __forceinline__ void row_load(RowRegs& r, rsrc_t rx, int t, int H, int pass, int lane) {
+#pragma unroll
+  for (int c = 0; c < XCH; ++c) {
+    const int k = (pass * XCH + c) * 512 + lane * 8;
+    r.q[c] = bload(rx, k < H ? (uint32_t)((t * H + k) * 2) : OOB);
+  }
+}
+
+__device__ __forceinline__ float sumsq8(u32x4 q) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(q[i] << 16), hi = __uint_as_float(q[i] & 0xFFFF0000u);
+    s += lo * lo + hi * hi;
+  }
+  return s;
+}
+
+// Stage token t (one wave).  With norm, f = c / sqrt(mean(x_t^2) + eps):
+//   vec given: s[t][k] = bf16(x[t][k] * f * vec[k]), fac[t] = 1
+//              (a learned per-dimension weight has to be applied before the dot product);
+//   otherwise: s[t] = x[t] unchanged, fac[t] = f, applied in fp32 to the dot products
+//              (a norm without a weight is a per-token factor: x_t / rms_t . w = (x_t . w) / rms_t).
+// Without norm the row is copied and fac[t] = 1.  r holds pass 0 when preloaded.
+__device__ void stage_token(RowRegs& r, bool preloaded, rsrc_t rx, int t, int H, bool norm, float eps, float c,
+                            const float* __restrict__ vec, bf16_t* s, int pitch, float* fac, int lane) {
+  const int npass = (H + XCH * 512 - 1) / (XCH * 512);
+  bf16_t* sr = s + t * pitch;
+  const bool xform = norm && vec;
+  float ss = 0.f;
+  for (int p = 0; p < npass; ++p) {
+    if (p > 0 || !preloaded) row_load(r, rx, t, H, p, lane);
+#pragma unroll
+    for (int ch = 0; ch < XCH; ++ch) {
+      const int k = (p * XCH + ch) * 512 + lane * 8;
+      if (k < H) {
+        if (norm) ss += sumsq8(r.q[ch]);
+        if (!xform) *(u32x4*)(sr + k) = r.q[ch];
+      }
+    }
+  }
+  float f = 1.f;
+  if (norm) f = c / sqrtf(wave_sum_f32(ss) / (float)H + eps);
+  if (xform) {
+    for (int p = 0; p < npass; ++p) {
+      if (npass > 1) row_load(r, rx, t, H, p, lane);  // one pass: the row is still in registers
+#pragma unroll
+      for (int ch = 0; ch < XCH; ++ch) {
+        const int k = (p * XCH + ch) * 512 + lane * 8;
+        if (k < H) {
+          u32x4 o;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float lo = __uint_as_float(r.q[ch][i] << 16) * f * vec[k + 2 * i];
+            const float hi = __uint_as_float(r.q[ch][i] & 0xFFFF0000u) * f * vec[k + 2 * i + 1];
+            o[i] = pack_bf16x2(lo, hi);
+          }
+          *(u32x4*)(sr + k) = o;
+        }
+      }
+    }
+  }
+  if (lane == 0) fac[t] = xform ? 1.f : f;
+}
+
+__device__ __forceinline__ int find_slot(const int* s_ids, int Kp, int t, int e) {
+  for (int k = 0; k < Kp; ++k)
+    if (s_ids[t * Kp + k] == e) return t * Kp + k;
+  return -1;
+}
+
+constexpr int PW = 8;                          // waves per block of the pre and up kernels
+constexpr int DW3 = DECODE_DW3;                // waves per block of the down kernel
+constexpr int RED_FLOATS = PW * 2 * 4 * 64;    // partial tiles of up to two row groups
+
+__host__ __device__ __forceinline__ int stage_bytes(int T, int H) { return (T * (H + 8) * 2 + 15) / 16 * 16; }
+// up kernel: partial tiles, slot ids and weights, expert flags and list, active
+// count, per-token factors; then the staged rows
+__host__ __device__ __forceinline__ int up_small_bytes(int Kp, int Ep) {
+  return (RED_FLOATS * 4 + (32 * Kp + 2 * Ep + 1 + 16) * 4 + 15) / 16 * 16;
+}
+
+// Dense MLP gate/up for 16 hidden units.  It needs no routing: run by the up
+// kernel's leading blocks (their weights stream while the expert blocks route)
+// when two blocks fit per CU, else by the pre kernel after the router blocks.
+__device__ void dense_gate_up_tile(const DecodeArgs& a, uint8_t* dsm, int i0) {
+  const int T = a.T, H = a.H, Id = a.Id, pitch = H + 8;
+  bf16_t* sx = (bf16_t*)dsm;
+  float* red = (float*)(dsm + stage_bytes(T, H));
+  float* fac = red + RED_FLOATS;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, col = lane & 15;
+  const rsrc_t rx = make_rsrc(a.x, (uint32_t)(T * H * 2));
+  const bool bvalid = col < T;
+  const bf16_t* brow = sx + (bvalid ? col : 0) * pitch;
+  int m0, m1;
+  wave_range<PW>(H / 64, wave, m0, m1);
+  RowRegs xr;
+  if (wave < T) row_load(xr, rx, wave, H, 0, lane);
+  Stream<false, 2, false, DU_BF16> st;
+  st.ra[0] = st.ra[1] = make_rsrc(a.dense_w13, (uint32_t)((int64_t)2 * Id * H * 2));
+  st.aoff[0] = (uint32_t)((i0 + col) * H * 2);
+  st.aoff[1] = (uint32_t)((Id + i0 + col) * H * 2);
+  st.g = g;
+  if (m0 < m1) st.load(m0, m1);
+  for (int t = wave; t < T; t += PW) stage_token(xr, t == wave, rx, t, H, true, a.eps, 1.f, a.g_pre, sx, pitch, fac, lane);
+  __syncthreads();
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  st.run(acc, brow, bvalid, m0, m1, true);
+  partials_to_lds<2>(red, acc, wave, lane);
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int rho = threadIdx.x >> 4, t = threadIdx.x & 15;
+    if (t < T) {
+      const float gv = reduced<PW, 2>(red, 0, rho, t) * fac[t], uv = reduced<PW, 2>(red, 1, rho, t) * fac[t];
+      ((bf16_t*)a.hd)[t * Id + i0 + rho] = f32_to_bf16(apply_act(a.dense_act, gv) * uv);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- pre: router logits (+ dense gate/up)
+__global__ __launch_bounds__(PW * 64, 2) void decode_pre_kernel(DecodeArgs a) {
+  extern __shared__ __align__(16) uint8_t dsm[];
+  if ((int)blockIdx.x >= a.n_router_groups) {
+    dense_gate_up_tile(a, dsm, (blockIdx.x - a.n_router_groups) * 16);
+    return;
+  }
+  const int T = a.T, H = a.H, pitch = H + 8;
+  bf16_t* sx = (bf16_t*)dsm;
+  float* red = (float*)(dsm + stage_bytes(T, H));
+  float* fac = red + RED_FLOATS;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, col = lane & 15;
+  const rsrc_t rx = make_rsrc(a.x, (uint32_t)(T * H * 2));
+  const bool bvalid = col < T;
+  const bf16_t* brow = sx + (bvalid ? col : 0) * pitch;
+  int m0, m1;
+  wave_range<PW>(H / 64, wave, m0, m1);
+  RowRegs xr;
+  if (wave < T) row_load(xr, rx, wave, H, 0, lane);
+  const int e0 = blockIdx.x * 16;
+  Stream<false, 1, false, DU_PRE> st;
+  st.ra[0] = make_rsrc(a.w_router, (uint32_t)((int64_t)a.E * H * 2));
+  st.aoff[0] = (uint32_t)((e0 + col) * H * 2);  // rows >= E read zero
+  st.g = g;
+  if (m0 < m1) st.load(m0, m1);
+  for (int t = wave; t < T; t += PW)
+    stage_token(xr, t == wave, rx, t, H, a.gemma_router != 0, a.eps, a.gemma_router ? 1.0f / sqrtf((float)H) : 1.f,
+                a.gemma_router ? a.router_scale : nullptr, sx, pitch, fac, lane);
+  __syncthreads();
+  f32x4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
+  st.run(acc, brow, bvalid, m0, m1, true);
+  partials_to_lds<1>(red, acc, wave, lane);
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int rho = threadIdx.x >> 4, t = threadIdx.x & 15;
+    if (t < T && e0 + rho < a.E) a.z[t * a.E + e0 + rho] = reduced<PW, 1>(red, 0, rho, t) * fac[t];
+  }
+}
+
+// ---------------------------------------------------------------- up: dense gate/up, routing + expert gate/up
+template <int VPL, bool FP8>
+__global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
+  extern __shared__ __align__(16) uint8_t dsm[];
+  if ((int)blockIdx.x < a.n_dense_groups) {
+    dense_gate_up_tile(a, dsm, blockIdx.x * 16);
+    return;
+  }
+  const int blk = blockIdx.x - a.n_dense_groups;  // expert block
+  const int T = a.T, H = a.H, I = a.I, E = a.E, Kp = a.Kp, Ep = a.Ep, pitch = H + 8;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, col = lane & 15;
+  float* red = (float*)dsm;
+  int* s_ids = (int*)(dsm + RED_FLOATS * 4);
+  float* s_w = (float*)(s_ids + 16 * Kp);
+  int* s_flag = (int*)(s_w + 16 * Kp);
+  int* s_active = s_flag + Ep;
+  int* s_nact = s_active + Ep;
+  float* fac = (float*)(s_nact + 1);
+  bf16_t* sx = (bf16_t*)(dsm + up_small_bytes(Kp, Ep));
+  const rsrc_t rx = make_rsrc(a.x, (uint32_t)(T * H * 2));
+
+  // 1. token rows and logits in flight together, then the routing of the T
+  //    tokens (every block computes the same routing); wave w takes tokens w
+  //    and w + PW
+  const int t0 = wave, t1 = wave + PW;
+  RowRegs xr0, xr1;
+  if (t0 < T) row_load(xr0, rx, t0, H, 0, lane);
+  if (t1 < T) row_load(xr1, rx, t1, H, 0, lane);
+  TokenLogits<VPL> z0, z1;
+  if (t0 < T) z0 = load_logits<VPL>(a.z + t0 * E, E, lane);
+  if (t1 < T) z1 = load_logits<VPL>(a.z + t1 * E, E, lane);
+  for (int i = threadIdx.x; i < Ep; i += PW * 64) s_flag[i] = 0;
+  for (int t = t0; t < T && t <= t1; t += PW) {
+    float w;
+    int id;
+    route_logits<VPL>(t == t0 ? z0 : z1, E, a.K, a.renorm, a.pes, lane, w, id);
+    if (lane < a.K) {
+      s_ids[t * Kp + lane] = id;
+      s_w[t * Kp + lane] = w;
+    } else if (lane < Kp) {
+      s_ids[t * Kp + lane] = E + (lane - a.K);
+      s_w[t * Kp + lane] = 1.f;
+    }
+  }
+  // expert input rows: pre_feedforward_layernorm_2(x) with the dense branch, x otherwise
+  if (t0 < T) stage_token(xr0, true, rx, t0, H, a.dense != 0, a.eps, 1.f, a.dense ? a.g_pre2 : nullptr, sx, pitch, fac, lane);
+  if (t1 < T) stage_token(xr1, true, rx, t1, H, a.dense != 0, a.eps, 1.f, a.dense ? a.g_pre2 : nullptr, sx, pitch, fac, lane);
+  __syncthreads();
+  for (int i = threadIdx.x; i < T * Kp; i += PW * 64) s_flag[s_ids[i]] = 1;
+  __syncthreads();
+  if (wave == 0) {  // ascending list of the experts with at least one slot
+    int base = 0;
+    for (int j = 0; j < Ep; j += 64) {
+      const int e = j + lane;
+      const bool f = e < Ep && s_flag[e];
+      const uint64_t mask = __ballot(f);
+      if (f) s_active[base + __popcll(mask & ((1ull << lane) - 1ull))] = e;
+      base += __popcll(mask);
+    }
+    if (lane == 0) *s_nact = base;
+  }
+  __syncthreads();
+  const int n_act = *s_nact;
+
+  // 2. the first expert block publishes the routing for the down kernel and the caller
+  if (blk == 0) {
+    if (threadIdx.x == 0) a.rinfo[0] = n_act;
+    for (int i = threadIdx.x; i < n_act; i += PW * 64) a.rinfo[1 + i] = s_active[i];
+    for (int i = threadIdx.x; i < n_act * 16; i += PW * 64) {
+      const int t = i & 15;
+      a.rinfo[1 + Ep + i] = t < T ? find_slot(s_ids, Kp, t, s_active[i >> 4]) : -1;
+    }
+    for (int i = threadIdx.x; i < T * a.K; i += PW * 64) {
+      const int t = i / a.K, k = i % a.K;
+      if (a.topk_w_out) a.topk_w_out[i] = s_w[t * Kp + k];
+      if (a.topk_ids_out) a.topk_ids_out[i] = s_ids[t * Kp + k];
+    }
+  }
+
+  // 3. (active expert, 16 hidden units) items: a contiguous, balanced range per block
+  constexpr int WB = FP8 ? 1 : 2;
+  const int RG = I / 16, n_items = n_act * RG;
+  const int it0 = (int)((int64_t)blk * n_items / a.n_up_blocks);
+  const int it1 = (int)((int64_t)(blk + 1) * n_items / a.n_up_blocks);
+  int m0, m1;
+  wave_range<PW>(H / 64, wave, m0, m1);
+  for (int item = it0; item < it1; ++item) {
+    const int u = item / RG, i0 = (item % RG) * 16;
+    const int e = s_active[u];
+    float sg = 1.f, su = 1.f;  // fp8 per-output-channel scales of the epilogue's row, loaded early
+    if constexpr (FP8) {
+      if (threadIdx.x < 256) {
+        sg = a.s13[(int64_t)e * 2 * I + i0 + (threadIdx.x >> 4)];
+        su = a.s13[(int64_t)e * 2 * I + I + i0 + (threadIdx.x >> 4)];
+      }
+    }
+    const int slot_col = col < T ? find_slot(s_ids, Kp, col, e) : -1;
+    const bool bvalid = slot_col >= 0;
+    const bf16_t* brow = sx + (bvalid ? col : 0) * pitch;
+    const uint8_t* wbase = e < E ? (const uint8_t*)a.w13 + (int64_t)e * 2 * I * H * WB
+                                 : (const uint8_t*)a.shared_w13 + (int64_t)(e - E) * 2 * I * H * 2;
+    Stream<FP8, 2, false, FP8 ? DU_FP8 : DU_BF16> st;
+    st.ra[0] = st.ra[1] = make_rsrc(wbase, (uint32_t)((int64_t)2 * I * H * WB));
+    st.aoff[0] = (uint32_t)((i0 + col) * H * WB);
+    st.aoff[1] = (uint32_t)((I + i0 + col) * H * WB);
+    st.g = g;
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    st.run(acc, brow, bvalid, m0, m1, false);
+    partials_to_lds<2>(red, acc, wave, lane);
+    __syncthreads();
+    if (threadIdx.x < 256) {
+      const int rho = threadIdx.x >> 4, t = threadIdx.x & 15;
+      const int slot = t < T ? find_slot(s_ids, Kp, t, e) : -1;
+      if (slot >= 0) {
+        const float gv = reduced<PW, 2>(red, 0, rho, t) * fac[t] * sg;
+        const float uv = reduced<PW, 2>(red, 1, rho, t) * fac[t] * su;
+        const float h = apply_act(a.act, gv) * uv * s_w[slot];
+        ((bf16_t*)a.hbuf)[(int64_t)slot * I + i0 + rho] = f32_to_bf16(h);
+      }
+    }
+    __syncthreads();  // red is rewritten by the next item
+  }
+}
+
+// ---------------------------------------------------------------- down: dense down, expert down + combine
+template <bool FP8>
+__global__ __launch_bounds__(DW3 * 64) void decode_down_kernel(DecodeArgs a) {
+  __shared__ float red[DW3 * 4 * 64];
+  const int T = a.T, H = a.H, I = a.I, E = a.E, Ep = a.Ep;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, col = lane & 15;
+
+  if ((int)blockIdx.x < a.n_ddown_groups) {
+    // dense MLP down projection: 16 output features x T tokens, fp32 out
+    const int Id = a.Id, n0 = blockIdx.x * 16;
+    Stream<false, 1, true, DU_BF16> st;
+    st.ra[0] = make_rsrc(a.dense_w2, (uint32_t)((int64_t)H * Id * 2));
+    st.aoff[0] = (uint32_t)((n0 + col) * Id * 2);
+    st.rb = make_rsrc(a.hd, (uint32_t)(T * Id * 2));
+    st.boff = col < T ? (uint32_t)(col * Id * 2) : OOB;
+    st.g = g;
+    int m0, m1;
+    wave_range<DW3>(Id / 64, wave, m0, m1);
+    f32x4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
+    st.run(acc, nullptr, false, m0, m1, false);
+    partials_to_lds<1>(red, acc, wave, lane);
+    __syncthreads();
+    if (threadIdx.x < 256) {
+      const int rho = threadIdx.x >> 4, t = threadIdx.x & 15;
+      if (t < T) a.dsum[t * H + n0 + rho] = reduced<DW3, 1>(red, 0, rho, t);
+    }
+    return;
+  }
+
+  const int n0 = (blockIdx.x - a.n_ddown_groups) * 16;
+  // The routing summary of the up kernel; this wave's entries are read in the
+  // same round trip as the active count, assuming one unit per active expert
+  // (re-read otherwise).  Entries at or past the count are stale but in bounds.
+  const int us = wave < a.max_active ? wave : 0;
+  const int n_act = a.rinfo[0];
+  int e_spec = a.rinfo[1 + us];
+  int slot_spec = a.rinfo[1 + Ep + us * 16 + col];
+  const int MS = I / 64;
+  const int S = min((DW3 + n_act - 1) / n_act, MS);  // reduction splits per expert
+  const int n_units = n_act * S;
+  constexpr int WB = FP8 ? 1 : 2;
+  const rsrc_t rb = make_rsrc(a.hbuf, (uint32_t)((int64_t)T * a.Kp * I * 2));
+  f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+  for (int unit = wave; unit < n_units; unit += DW3) {
+    const int u = unit / S, s = unit % S;
+    const bool spec = u == us && unit == wave;
+    const int e = spec ? e_spec : a.rinfo[1 + u];
+    const int slot = spec ? slot_spec : a.rinfo[1 + Ep + u * 16 + col];
+    const uint8_t* wbase = e < E ? (const uint8_t*)a.w2 + (int64_t)e * H * I * WB
+                                 : (const uint8_t*)a.shared_w2 + (int64_t)(e - E) * H * I * 2;
+    Stream<FP8, 1, true, FP8 ? DU_FP8 : DU_BF16> st;
+    st.ra[0] = make_rsrc(wbase, (uint32_t)((int64_t)H * I * WB));
+    st.aoff[0] = (uint32_t)((n0 + col) * I * WB);
+    st.rb = rb;
+    st.boff = slot >= 0 ? (uint32_t)((int64_t)slot * I * 2) : OOB;
+    st.g = g;
+    f32x4 sc = {1.f, 1.f, 1.f, 1.f};  // fp8 per-output-channel scales of this lane's rows, loaded early
+    if constexpr (FP8) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sc[v] = a.s2[(int64_t)e * H + n0 + 4 * g + v];
+    }
+    f32x4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
+    st.run(acc, nullptr, false, s * MS / S, (s + 1) * MS / S, false);
+    if constexpr (FP8) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) tot[v] += sc[v] * acc[0][v];
+    } else {
+      tot += acc[0];
+    }
+  }
+  const f32x4 part[1] = {tot};
+  partials_to_lds<1>(red, part, wave, lane);
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int rho = threadIdx.x >> 4, t = threadIdx.x & 15;
+    if (t < T) {
+      const float v = reduced<DW3, 1>(red, 0, rho, t);
+      const int64_t o = (int64_t)t * H + n0 + rho;
+      if (a.msum) {
+        a.msum[o] = v;
+      } else {
+        ((bf16_t*)a.out)[o] = f32_to_bf16(v);
+        if (a.out_f32) a.out_f32[o] = v;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launches
+int decode_up_lds_bytes(int T, int H, int Kp, int Ep) {
+  // expert blocks; the dense gate/up blocks need stage_bytes + (RED_FLOATS + 16) * 4, which is less
+  return up_small_bytes(Kp, Ep) + stage_bytes(T, H);
+}
+int decode_pre_lds_bytes(int T, int H) { return stage_bytes(T, H) + (RED_FLOATS + 16) * 4; }
+
+template <typename F>
+static hipError_t allow_lds(F* f, int bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+hipError_t launch_decode_pre(const DecodeArgs& a, hipStream_t s) {
+  const int nb = a.n_router_groups + a.n_pre_dense_groups;
+  if (nb == 0) return hipSuccess;
+  const int lds = decode_pre_lds_bytes(a.T, a.H);
+  hipError_t e = allow_lds(decode_pre_kernel, lds);
+  if (e != hipSuccess) return e;
+  decode_pre_kernel<<<dim3(nb), dim3(PW * 64), lds, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int VPL, bool FP8>
+static hipError_t up_vpl(const DecodeArgs& a, int nb, int lds, hipStream_t s) {
+  hipError_t e = allow_lds(decode_up_kernel<VPL, FP8>, lds);
+  if (e != hipSuccess) return e;
+  decode_up_kernel<VPL, FP8><<<dim3(nb), dim3(PW * 64), lds, s>>>(a);
+  return hipGetLastError();
+}
+
+static int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+int decode_up_blocks_per_cu(int T, int H, int Kp, int Ep) {
+  return decode_up_lds_bytes(T, H, Kp, Ep) * 2 <= 160 * 1024 ? 2 : 1;
+}
+
+// a.n_up_blocks holds the number of (expert, 16 hidden units) items on entry;
+// the expert blocks walk them, sized so that they and the dense blocks are
+// resident together.
+hipError_t launch_decode_up(const DecodeArgs& args, bool fp8, hipStream_t s) {
+  DecodeArgs a = args;
+  const int lds = decode_up_lds_bytes(a.T, a.H, a.Kp, a.Ep);
+  const int slots = cu_count() * decode_up_blocks_per_cu(a.T, a.H, a.Kp, a.Ep);
+  const int room = slots - a.n_dense_groups > slots / 2 ? slots - a.n_dense_groups : slots / 2;
+  // as few blocks as keep the item count per block at its minimum, so that every
+  // block gets the same number of items when all experts the bound allows are active
+  const int per_block = (a.n_up_blocks + room - 1) / room;
+  a.n_up_blocks = (a.n_up_blocks + per_block - 1) / per_block;
+  const int nb = a.n_dense_groups + a.n_up_blocks;
+  const int vpl = a.E <= 64 ? 1 : a.E <= 128 ? 2 : a.E <= 256 ? 4 : 8;
+  if (fp8) {
+    switch (vpl) {
+      case 1: return up_vpl<1, true>(a, nb, lds, s);
+      case 2: return up_vpl<2, true>(a, nb, lds, s);
+      case 4: return up_vpl<4, true>(a, nb, lds, s);
+      default: return up_vpl<8, true>(a, nb, lds, s);
+    }
+  }
+  switch (vpl) {
+    case 1: return up_vpl<1, false>(a, nb, lds, s);
+    case 2: return up_vpl<2, false>(a, nb, lds, s);
+    case 4: return up_vpl<4, false>(a, nb, lds, s);
+    default: return up_vpl<8, false>(a, nb, lds, s);
+  }
+}
+
+hipError_t launch_decode_down(const DecodeArgs& a, bool fp8, hipStream_t s) {
+  const dim3 grid(a.n_ddown_groups + a.H / 16), block(DW3 * 64);
+  if (fp8) decode_down_kernel<true><<<grid, block, 0, s>>>(a);
+  else decode_down_kernel<false><<<grid, block, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -46,12 +46,6 @@
 
 namespace moe {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float apply_act(int act, float g) {
-  return act == 0 ? act_silu(g) : act_gelu_tanh(g);
-}
-
 template <int BELEM>
 struct BTraits;
 template <>
@@ -65,31 +59,7 @@ struct BTraits<ELEM_FP8> {
   static constexpr int ELEM_BYTES = 1;
 };
 
-// 8 fp8 (E4M3) codes in two dwords -> 8 bf16.  v_cvt_pk_f32_fp8 widens two codes
-// (word 0 or word 1 of a dword) to fp32; every E4M3 value has at most 4
-// significant bits, so the upper 16 bits of its fp32 pattern are exactly its
-// bf16 pattern, and one byte permute packs two of them.
-template <bool HI_WORD>
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t src) {
-  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8(src, HI_WORD);
-  return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
-}
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-  u32x4 r;
-  r[0] = fp8x2_to_bf16x2<false>(lo);
-  r[1] = fp8x2_to_bf16x2<true>(lo);
-  r[2] = fp8x2_to_bf16x2<false>(hi);
-  r[3] = fp8x2_to_bf16x2<true>(hi);
-  return __builtin_bit_cast(bf16x8, r);
-}
-
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  // raw buffer: stride 0, num_records = bytes (loads past it return 0)
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
 
 // 16 bytes per lane, global -> LDS: lane l's data lands at dst + 16 l (dst wave-uniform).
 __device__ __forceinline__ void dma16(rsrc_t r, void* dst, uint32_t voff, uint32_t soff) {

@@ -65,4 +65,49 @@ hipError_t launch_finalize(const void* ybuf, int yelem, int Kp, const float* den
 hipError_t launch_gather_topk(const float* w_in, const int32_t* ids_in, int in_stride, int K, int64_t T,
                               float* w_out, int32_t* ids_out, hipStream_t s);
 
+// Decode path (a few tokens, T <= 16): weights streamed once per call, all
+// tokens applied to each weight row together.
+struct DecodeArgs {
+  int T, H, E, K, Kp, Ep, I, Id;
+  int act, dense_act, renorm, gemma_router, dense;
+  float eps;
+  int n_router_groups;  // pre kernel: blocks computing 16 router logits each (0: logits supplied)
+  int n_pre_dense_groups;  // pre kernel: trailing blocks computing 16 dense hidden units each
+  int n_dense_groups;   // up kernel: leading blocks computing 16 dense hidden units each
+  int n_up_blocks;      // up kernel: blocks walking the (expert, 16 hidden units) items
+  int n_ddown_groups;   // down kernel: leading blocks computing 16 dense output features each
+  int max_active;       // min(Ep, T * Kp): bound on the number of active experts
+  const void* x;        // [T, H] bf16
+  float* z;             // [T, E] logits: written by the pre kernel or supplied
+  const void* w_router;
+  const float* router_scale;
+  const float* pes;
+  const void* w13;
+  const void* w2;
+  const float* s13;
+  const float* s2;
+  const void* shared_w13;
+  const void* shared_w2;
+  const void* dense_w13;
+  const void* dense_w2;
+  const float* g_pre;
+  const float* g_pre2;
+  void* hd;             // [T, Id] bf16 dense hidden
+  void* hbuf;           // [T * Kp, I] bf16 weighted expert hidden, per slot
+  float* dsum;          // [T, H] dense branch output
+  float* msum;          // [T, H] expert sum when post-norms follow, else NULL
+  int* rinfo;           // active count, active experts [Ep], slot per (active, token) [Ep][16]
+  void* out;            // [T, H] bf16 (when msum is NULL)
+  float* out_f32;
+  float* topk_w_out;
+  int32_t* topk_ids_out;
+};
+
+int decode_up_lds_bytes(int T, int H, int Kp, int Ep);
+int decode_pre_lds_bytes(int T, int H);
+int decode_up_blocks_per_cu(int T, int H, int Kp, int Ep);
+hipError_t launch_decode_pre(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_up(const DecodeArgs& a, bool fp8, hipStream_t s);
+hipError_t launch_decode_down(const DecodeArgs& a, bool fp8, hipStream_t s);
+
 }  // namespace moe

@@ -22,8 +22,8 @@ constexpr int PERM_STEP = PERM_THREADS * 4;
 
 __device__ __forceinline__ int block_sum_i32(int v, int* s_red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // wave reduction through the u32 butterfly (values are small non-negative ints)
-  v = (int)wave_allreduce_u32((uint32_t)v, [](uint32_t a, uint32_t b) { return a + b; });
+  // wave all-reduce on the u32 pattern (values are small non-negative ints)
+  v = (int)wave_allreduce_u32((uint32_t)v, [](uint32_t a, uint32_t b) { return a + b; }, 0u);
   if (lane == 0) s_red[wave] = v;
   __syncthreads();
   int tot = 0;

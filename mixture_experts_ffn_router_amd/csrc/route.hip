@@ -18,6 +18,7 @@
 // rounded once, so a weight is within about two fp32 ulps of exact.
 #include "common.h"
 #include "kernels.h"
+#include "route_dev.h"
 
 namespace moe {
 
@@ -31,64 +32,13 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // uniform per wave
-  const float* z = logits + t * (int64_t)E;
-
-  float v[VPL];
-  uint32_t key[VPL];
-  float lmax = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < VPL; ++j) {
-    int idx = lane + 64 * j;
-    if (idx < E) {
-      v[j] = z[idx];
-      key[j] = f32_order_key(v[j]);
-      lmax = fmaxf(lmax, v[j]);
-    } else {
-      v[j] = 0.f;
-      key[j] = 0u;  // below every finite key: never selected while K <= E
-    }
-  }
-  const float m = wave_max_f32(lmax);
-
-  double s_all = 1.0;
-  if (!renorm) {
-    double s = 0.0;
-#pragma unroll
-    for (int j = 0; j < VPL; ++j)
-      if (lane + 64 * j < E) s += (double)expf(v[j] - m);
-    s_all = wave_sum_f64(s);
-  }
-
-  uint32_t taken = 0;  // bit j: this lane's value j already selected
-  float my_e = 0.f;
-  int my_id = 0;
-  double denom = 0.0;
-  for (int k = 0; k < K; ++k) {
-    uint32_t bk = 0, bi = 0xFFFFFFFFu;
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      if (!((taken >> j) & 1u) && key[j] > bk) {  // j ascending: lowest index wins ties
-        bk = key[j];
-        bi = (uint32_t)(lane + 64 * j);
-      }
-    }
-    const uint32_t gk = wave_max_u32(bk);
-    const uint32_t gi = wave_min_u32(bk == gk ? bi : 0xFFFFFFFFu);
-    if ((int)(gi & 63u) == lane) taken |= 1u << (gi >> 6);
-    const float e = expf(f32_from_order_key(gk) - m);
-    denom += (double)e;  // slot order
-    if (lane == k) {
-      my_e = e;
-      my_id = (int)gi;
-    }
-  }
+  float w;
+  int id;
+  route_token<VPL>(logits + t * (int64_t)E, E, K, renorm, pes, lane, w, id);
   int64_t o = t * (int64_t)out_stride + lane;
   if (lane < K) {
-    const double d = renorm ? (denom > 0.0 ? denom : 1.0) : s_all;
-    double w = (double)my_e / d;
-    if (pes) w *= (double)pes[my_id];
-    w_out[o] = (float)w;
-    ids_out[o] = my_id;
+    w_out[o] = w;
+    ids_out[o] = id;
   } else if (lane < K + n_shared) {
     w_out[o] = 1.f;
     ids_out[o] = E + (lane - K);

@@ -132,9 +132,57 @@ def test_workspace_reuse_across_sizes(B):
     assert torch.equal(part, full[:37])
 
 
+# ------------------------------------------------------------------ decode path (T <= 16)
+DECODE = {
+    "plain_e8_k2": W.LayerSpec("dec_plain", 1, 256, 8, 2, 512, "silu", "bf16"),
+    "gemma_gammas": W.LayerSpec("dec_gemma", 1, 256, 16, 4, 128, "gelu_tanh", "bf16", router_mode="gemma",
+                                per_expert_scale="uniform", I_dense=192, random_gammas=True),
+    "gemma_plain_norms": W.LayerSpec("dec_gemma_i64", 1, 320, 16, 8, 192, "gelu_tanh", "bf16",
+                                     router_mode="gemma", per_expert_scale="uniform", I_dense=128),
+    "shared_no_renorm": W.LayerSpec("dec_deepseek", 1, 256, 8, 3, 128, "silu", "bf16", renorm=False,
+                                    n_shared=2, I_shared=128),
+    "fp8_supplied": W.LayerSpec("dec_fp8", 1, 256, 16, 4, 192, "gelu_tanh", "fp8", supplied_logits=True),
+    "e512_k8": W.LayerSpec("dec_e512", 1, 128, 512, 8, 64, "silu", "bf16"),
+    "single_expert": W.LayerSpec("dec_e1", 1, 128, 1, 1, 128, "gelu_tanh", "bf16"),
+    "h8192": W.LayerSpec("dec_h8192", 1, 8192, 4, 1, 128, "silu", "bf16"),
+}
+DECODE_T = {"h8192": (1, 8)}
+
+
+@pytest.mark.parametrize("name,T", [(n, t) for n in DECODE for t in DECODE_T.get(n, (1, 5, 16))],
+                         ids=[f"{n}-T{t}" for n in DECODE for t in DECODE_T.get(n, (1, 5, 16))])
+def test_decode_path_every_element(B, name, T):
+    L = W.make_layer(DECODE[name].with_T(T), seed=21 + T)
+    dl = B.DeviceLayer.from_generated(L)
+    assert dl.path(T) == "decode"
+    run_and_check(B, L)
+
+
+def test_decode_path_bounds(B):
+    """T <= 16 takes the decode path while the token rows fit its LDS staging."""
+    dl = B.DeviceLayer.from_generated(W.make_layer(DECODE["plain_e8_k2"], seed=1))
+    assert [dl.path(t) for t in (1, 16, 17, 4096)] == ["decode", "decode", "grouped", "grouped"]
+    big = B.DeviceLayer.from_generated(W.make_layer(DECODE["h8192"], seed=1))
+    assert big.path(8) == "decode" and big.path(16) == "grouped"
+    f32 = B.DeviceLayer.from_generated(W.make_layer(W.SPECS["tiny"].with_T(4), seed=1))
+    assert f32.path(4) == "grouped"
+
+
+def test_decode_deterministic_and_workspace_reuse(B):
+    L = W.make_layer(DECODE["gemma_gammas"].with_T(16), seed=5)
+    dl = B.DeviceLayer.from_generated(L)
+    ws = torch.empty(dl.workspace_size(16), dtype=torch.uint8, device="cuda")
+    a = dl.forward(workspace=ws).clone()
+    for _ in range(3):
+        assert torch.equal(dl.forward(workspace=ws), a)
+    # fewer tokens on the same workspace: a token's output does not depend on the others
+    part = dl.forward(x=dl.t["x"][:3].contiguous(), workspace=ws)
+    assert torch.equal(part, a[:3])
+
+
 # ------------------------------------------------------------------ full-size configurations
-FULL = [("tiny", 64), ("mixtral", 4096), ("gemma", 1), ("gemma", 16), ("gemma", 128),
-        ("gemma", 8192), ("deepseek", 16384), ("skewed_fp8", 1), ("skewed_fp8", 4096)]
+FULL = [("tiny", 64), ("mixtral", 1), ("mixtral", 4096), ("gemma", 1), ("gemma", 16), ("gemma", 128),
+        ("gemma", 8192), ("deepseek", 16), ("deepseek", 16384), ("skewed_fp8", 1), ("skewed_fp8", 4096)]
 
 
 def _rows(T, n=256):
