@@ -24,11 +24,14 @@ Prints one JSON line:
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
 import sys
 import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
 
 METRIC = "MoE layer tokens/s; prefill TFLOP/s % MFMA peak; decode GB/s % HBM peak"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
@@ -45,12 +48,54 @@ def parse():
     ap.add_argument("--T", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
 
 
-def stage_work(spec, T, counts, path):
+# Kernel sources whose change invalidates stored HBM byte counts, per path.
+KERNEL_SOURCES = {"grouped": ["gemm.hip"], "decode": ["decode.hip"]}
+
+
+def source_digest(path):
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[path]:
+        with open(os.path.join(ROOT, "mixture_experts_ffn_router_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload, kernel, path):
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy calibration), or None when
+    there is none or the kernel source changed since it was taken."""
+    f = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(f):
+        return None
+    with open(f) as fh:
+        rec = json.load(fh).get(f"{workload}/{kernel}")
+    if not rec or rec.get("source_digest") != source_digest(path):
+        return None
+    return rec["bytes_per_launch"]
+
+
+def copy_calibration():
+    """A plain device-to-device copy of 1 GiB, five times: its FETCH_SIZE and
+    WRITE_SIZE per dispatch against the 1 GiB it moves give the counters' scale."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "dispatches": 5}), flush=True)
+
+
+def stage_work(spec, T, counts, path, dense_stage=None):
     """Algorithmic FLOP and HBM bytes per stage of the library's stage events.
-    Padding and experts nobody picked are not counted; weights count once."""
+    Padding and experts nobody picked are not counted; weights count once.
+    dense_stage: decode path only, the stage whose launch runs the dense gate/up."""
     H, E, K, I = spec.H, spec.E, spec.K, spec.I
     S, Id = spec.n_shared, spec.I_dense
     wb = 1 if spec.wdtype == "fp8" else (4 if spec.wdtype == "fp32" else 2)
@@ -70,13 +115,18 @@ def stage_work(spec, T, counts, path):
     w_down = used * H * (I * wb + sb) + S * H * I * ab
     by = {}
     if path == "decode":
-        # pre kernel: router + dense gate/up; up kernel: expert gate/up + dense down;
-        # down kernel: expert down + combine; finalize: post-norms (dense branch only)
-        fl = {"router": fl["router"] + fl["dense_gate_up"], "gate_up": fl["gate_up"] + fl["dense_down"],
-              "down": fl["down"], "dense_gate_up": 0, "dense_down": 0}
-        by["router"] = z * (E * H * ab + T * E * 4) + 2 * Id * H * ab + T * H * ab + T * Id * ab
-        by["gate_up"] = w_up + T * H * ab + T * Kp * I * ab + (H * Id * ab + T * Id * ab + T * H * 4 if Id else 0)
-        by["down"] = w_down + T * Kp * I * ab + T * H * (4 if Id else ab)
+        # router launch: router logits; gate/up launch: routing + expert gate/up; down
+        # launch: dense down + expert down + combine; finalize: post-norms.  The dense
+        # gate/up rides with the router or the gate/up launch (dense_stage).
+        dgu_fl, dgu_by = fl["dense_gate_up"], 2 * Id * H * ab + T * H * ab + T * Id * ab
+        fl = {"router": fl["router"], "gate_up": fl["gate_up"], "down": fl["down"] + fl["dense_down"],
+              "dense_gate_up": 0, "dense_down": 0}
+        by["router"] = z * (E * H * ab + T * E * 4 + T * H * ab)
+        by["gate_up"] = w_up + T * H * ab + T * Kp * I * ab
+        by["down"] = w_down + T * Kp * I * ab + T * H * (4 if Id else ab) + (H * Id * ab + T * Id * ab + T * H * 4 if Id else 0)
+        if Id:
+            fl[dense_stage] += dgu_fl
+            by[dense_stage] += dgu_by
         by["dense_gate_up"] = by["dense_down"] = 0
         by["finalize"] = 2 * T * H * 4 + T * H * ab if Id else 0
     else:
@@ -156,6 +206,9 @@ def main():
         print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
     from mixture_experts_ffn_router_amd import binding as B
     from mixture_experts_ffn_router_amd import workloads as W
@@ -208,10 +261,19 @@ def main():
     p1.record()
     torch.cuda.synchronize()
     prof_ms = p0.elapsed_time(p1) / args.steps
-    stage_ms = {name: sum(row[i].elapsed_time(row[i + 1]) for row in evs) / args.steps
-                for i, name in enumerate(B.STAGES)}
+    raw_ms = {name: sum(row[i].elapsed_time(row[i + 1]) for row in evs) / args.steps
+              for i, name in enumerate(B.STAGES)}
+    # Each event record costs stream time of its own; measure two back-to-back
+    # records on the same stream and take that off every stage interval.
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a_, b_ in pairs:
+        a_.record()
+        b_.record()
+    torch.cuda.synchronize()
+    marker_ms = sorted(a_.elapsed_time(b_) for a_, b_ in pairs)[len(pairs) // 2]
+    stage_ms = {k: max(v - marker_ms, 0.0) if v > marker_ms * 1.5 else 0.0 for k, v in raw_ms.items()}
 
-    fl, by = stage_work(spec, T, counts, path)
+    fl, by = stage_work(spec, T, counts, path, dl.dense_gate_up_stage(T))
     total_flop = sum(fl.values())
     total_bytes = sum(by.values())
     cand = [s for s in ("gate_up", "down", "dense_gate_up", "dense_down", "router") if fl[s] > 0]
@@ -227,8 +289,14 @@ def main():
         achieved = by[dom] / dom_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    wl = f"{spec.name}_T{T}"
+    traffic = stored_traffic(wl, dom, path)
+    roof["traffic"] = traffic
     roof.update({"kernel": dom, "kernel_ms": round(stage_ms[dom], 5),
-                 "algorithmic_per_launch": fl[dom] if roof["bound"] == "mfma" else by[dom]})
+                 "algorithmic_per_launch": fl[dom] if roof["bound"] == "mfma" else by[dom],
+                 "algorithmic_bytes_per_launch": by[dom],
+                 "traffic_over_algorithmic": round(traffic / by[dom], 3) if traffic else None,
+                 "event_marker_ms": round(marker_ms, 5), "kernel_source_digest": source_digest(path)})
 
     line = {
         "metric": METRIC,
@@ -251,6 +319,7 @@ def main():
         "step_gbps": round(total_bytes / (ms_per_step / 1e3) / 1e9, 1),
         "experts_touched": int((counts > 0).sum()),
         "stages_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "stages_raw_ms": {k: round(v, 5) for k, v in raw_ms.items()},
         "profiled_ms_per_step": round(prof_ms, 5),
         "roofline": roof,
     }

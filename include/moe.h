@@ -198,6 +198,13 @@ moe_status moe_forward(const moe_layer_desc* desc, const moe_tensors* tensors, i
 typedef enum { MOE_PATH_GROUPED = 0, MOE_PATH_DECODE = 1 } moe_path;
 int32_t moe_forward_path(const moe_layer_desc* desc, int64_t T);
 
+/* Stage (MOE_STAGE_ROUTER or MOE_STAGE_GATE_UP) whose launch runs the dense
+ * MLP's gate/up on the decode path for T tokens: the gate/up launch while two of
+ * its blocks fit per CU with the staged token rows, else the router launch.
+ * -1 for an invalid descriptor, a layer without the dense branch, or a T that
+ * takes the grouped path.  For measurement (bytes per stage). */
+int32_t moe_decode_dense_gate_up_stage(const moe_layer_desc* desc, int64_t T);
+
 /* Stages of moe_forward, in launch order (indices into the event array below). */
 typedef enum {
   MOE_STAGE_PRENORM = 0,        /* 1/rms per token (+ rows with learned norm weights) */

@@ -48,7 +48,8 @@ class Tensors(C.Structure):
 
 
 EXPORTS = ["moe_status_string", "moe_last_error", "moe_route", "moe_permute_capacity", "moe_permute",
-           "moe_forward_workspace_size", "moe_forward", "moe_forward_profiled", "moe_forward_path"]
+           "moe_forward_workspace_size", "moe_forward", "moe_forward_profiled", "moe_forward_path",
+           "moe_decode_dense_gate_up_stage"]
 PATHS = {0: "grouped", 1: "decode"}
 STAGES = ["prenorm", "router", "route", "permute", "gate_up", "down", "dense_gate_up", "dense_down",
           "finalize"]
@@ -87,6 +88,8 @@ def load(path: str = LIB_PATH):
                                          C.c_size_t, C.c_void_p, C.POINTER(C.c_void_p)]
     lib.moe_forward_path.restype = C.c_int32
     lib.moe_forward_path.argtypes = [C.POINTER(LayerDesc), C.c_int64]
+    lib.moe_decode_dense_gate_up_stage.restype = C.c_int32
+    lib.moe_decode_dense_gate_up_stage.argtypes = [C.POINTER(LayerDesc), C.c_int64]
     _lib = lib
     return lib
 
@@ -207,6 +210,11 @@ class DeviceLayer:
         if r < 0:
             raise ValueError("invalid layer descriptor or T")
         return PATHS[r]
+
+    def dense_gate_up_stage(self, T):
+        """Stage name whose launch runs the dense gate/up on the decode path, or None."""
+        r = load().moe_decode_dense_gate_up_stage(C.byref(self.desc), T)
+        return None if r < 0 else STAGES[r]
 
     def workspace_size(self, T):
         n = C.c_size_t(0)

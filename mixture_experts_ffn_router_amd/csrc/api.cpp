@@ -247,6 +247,12 @@ MOE_API int32_t moe_forward_path(const moe_layer_desc* desc, int64_t T) {
   return use_decode(*desc, T) ? MOE_PATH_DECODE : MOE_PATH_GROUPED;
 }
 
+MOE_API int32_t moe_decode_dense_gate_up_stage(const moe_layer_desc* desc, int64_t T) {
+  if (validate_desc(desc) != MOE_OK || T < 0 || !use_decode(*desc, T) || desc->inter_dense == 0) return -1;
+  const int kp = desc->top_k + desc->n_shared, ep = desc->num_experts + desc->n_shared;
+  return moe::decode_up_blocks_per_cu((int)T, desc->hidden, kp, ep) == 2 ? MOE_STAGE_GATE_UP : MOE_STAGE_ROUTER;
+}
+
 MOE_API moe_status moe_forward_workspace_size(const moe_layer_desc* desc, int64_t T, size_t* bytes) {
   g_err[0] = 0;
   moe_status s = validate_desc(desc);
@@ -438,6 +444,7 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
     a.a_rows_alloc = T;
     a.m_dev = offsets + p.Ep;
     a.block_expert = bexp;
+    a.seg_off = offsets;
     a.B0 = t->w13;
     a.B1 = t->shared_w13;
     a.bstride = (int64_t)2 * I * H;
@@ -461,6 +468,7 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
     a.a_rows_alloc = p.cap;
     a.m_dev = offsets + p.Ep;
     a.block_expert = bexp;
+    a.seg_off = offsets;
     a.B0 = t->w2;
     a.B1 = t->shared_w2;
     a.bstride = (int64_t)H * I;

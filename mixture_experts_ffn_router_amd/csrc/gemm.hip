@@ -69,21 +69,39 @@ __device__ __forceinline__ void dma16(rsrc_t r, void* dst, uint32_t voff, uint32
 // Tile order.  The grid is persistent: block b walks tiles t = b, b + G, ... with
 // G a multiple of 8, and blocks are dealt to the 8 XCDs round-robin, so XCD x
 // runs the tiles t = x (mod 8).  Renumber so each XCD walks a contiguous range of
-// logical tiles, and order logical tiles in groups of GM row blocks x all column
-// tiles (row block fastest): the ~32 tiles an XCD runs at once then share GM row
-// blocks of A and a few column tiles of B in its L2.  Only row blocks that hold
-// rows are counted, so no block idles on padding and the XCDs stay balanced.
+// logical tiles.  Logical tiles are laid out segment by segment (a segment is
+// the row blocks of one expert, or all row blocks when rows are not grouped by
+// expert), each segment cut into near-equal chunks of at most GMAX row blocks,
+// and within a chunk the row block runs fastest: the tiles an XCD runs at once
+// are the chunk's row blocks times a few column tiles, so each weight tile is
+// read from memory once per chunk and the rest come from the XCD's L2.  A fixed
+// group height would straddle experts and stream their weights several times.
+// Only row blocks that hold rows are counted, so no block idles on padding and
+// the XCDs stay balanced.
 __device__ __forceinline__ int64_t xcd_logical(int64_t t, int64_t per_xcd, bool xcd_map) {
   constexpr int XCDS = 8;
   return xcd_map ? (t % XCDS) * per_xcd + t / XCDS : t;
 }
-__device__ __forceinline__ void tile_coords(int64_t lid, int64_t mbn, int64_t nb_cnt, int64_t& mb, int64_t& nb) {
-  constexpr int GM = 4;
-  const int64_t per_group = GM * nb_cnt;
-  const int64_t g = lid / per_group, w = lid % per_group;
-  const int64_t gm = min((int64_t)GM, mbn - g * GM);  // rows in this (possibly last) group
-  mb = g * GM + w % gm;
-  nb = w / gm;
+__device__ __forceinline__ void tile_coords(int64_t lid, int64_t mbn, int64_t nb_cnt, const int32_t* block_expert,
+                                            const int32_t* seg_off, int bm, int64_t& mb, int64_t& nb) {
+  constexpr int GMAX = 8;
+  // A chunk starting at row block s owns logical tiles [s * nb_cnt, (s + h) * nb_cnt),
+  // so lid / nb_cnt is a row block of lid's chunk, and of its segment.
+  const int64_t r = lid / nb_cnt;
+  int64_t f = 0, n = mbn;
+  if (block_expert) {
+    const int e = block_expert[r];
+    f = seg_off[e] / bm;
+    n = (seg_off[e + 1] - seg_off[e]) / bm;
+  }
+  const int64_t j = r - f, q = (n + GMAX - 1) / GMAX;  // block within the segment; chunks
+  int64_t c = j * q / n;                                // chunk c: segment blocks [c n / q, (c + 1) n / q)
+  while ((c + 1) * n / q <= j) ++c;
+  while (c * n / q > j) --c;
+  const int64_t c0 = c * n / q, h = (c + 1) * n / q - c0;
+  const int64_t local = lid - (f + c0) * nb_cnt;
+  mb = f + c0 + local % h;
+  nb = local / h;
 }
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14])
@@ -161,7 +179,7 @@ void gemm_mfma_kernel(GemmArgs p) {
   const int64_t lid = xcd_logical(t, per_xcd, xcd_map);
   if (lid >= ntiles) continue;  // uniform per block
   int64_t mb, nbi;
-  tile_coords(lid, mbn, nb_cnt, mb, nbi);
+  tile_coords(lid, mbn, nb_cnt, p.block_expert, p.seg_off, BM, mb, nbi);
   __syncthreads();  // the previous tile's LDS reads are done in every wave
   const int64_t m0 = mb * BM;
   const int n0 = (int)nbi * NCOLS;

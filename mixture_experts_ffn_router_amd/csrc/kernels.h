@@ -28,6 +28,7 @@ struct GemmArgs {
   int64_t a_rows_alloc;       // rows of the A allocation (a_rows_alloc * lda * 2 < 2^31)
   const int32_t* m_dev;       // device count of rows (padded total) or NULL (use M)
   const int32_t* block_expert;  // expert per row block, NULL = expert 0
+  const int32_t* seg_off;       // with block_expert: padded row offset of each expert [E + 1]
   const void* B0;             // routed expert weights, expert stride bstride (elements)
   const void* B1;             // weights of experts >= n_routed (shared), same stride
   int64_t bstride;
