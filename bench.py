@@ -263,15 +263,18 @@ def main():
     prof_ms = p0.elapsed_time(p1) / args.steps
     raw_ms = {name: sum(row[i].elapsed_time(row[i + 1]) for row in evs) / args.steps
               for i, name in enumerate(B.STAGES)}
-    # Each event record costs stream time of its own; measure two back-to-back
-    # records on the same stream and take that off every stage interval.
+    # Each event record costs stream time of its own (two back-to-back records on
+    # the stream, reported as event_marker_ms).  Stage intervals are kept as
+    # measured, so a stage's time is an upper bound on its kernel's duration: within
+    # about 1% of rocprofv3's average for millisecond kernels, a few us over it for
+    # the decode path's microsecond kernels.
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for a_, b_ in pairs:
         a_.record()
         b_.record()
     torch.cuda.synchronize()
     marker_ms = sorted(a_.elapsed_time(b_) for a_, b_ in pairs)[len(pairs) // 2]
-    stage_ms = {k: max(v - marker_ms, 0.0) if v > marker_ms * 1.5 else 0.0 for k, v in raw_ms.items()}
+    stage_ms = {k: (v if v > marker_ms * 1.5 else 0.0) for k, v in raw_ms.items()}  # empty stages: 0
 
     fl, by = stage_work(spec, T, counts, path, dl.dense_gate_up_stage(T))
     total_flop = sum(fl.values())
@@ -319,7 +322,6 @@ def main():
         "step_gbps": round(total_bytes / (ms_per_step / 1e3) / 1e9, 1),
         "experts_touched": int((counts > 0).sum()),
         "stages_ms": {k: round(v, 5) for k, v in stage_ms.items()},
-        "stages_raw_ms": {k: round(v, 5) for k, v in raw_ms.items()},
         "profiled_ms_per_step": round(prof_ms, 5),
         "roofline": roof,
     }
