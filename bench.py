@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mixtral")
     ap.add_argument("--T", type=int, default=None)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
@@ -166,8 +166,8 @@ def rotated_sets(B, dl, path):
 
 def cpu_baseline(L, seconds):
     """The oracle on a row sample of the workload sized for about `seconds` of CPU
-    time (routing and permutation over all T rows; expert FFNs over the sample),
-    repeated when even all T rows take less."""
+    time: routing over all T rows, the expert FFNs over the sample (repeated when
+    even all T rows take less)."""
     import numpy as np
     from mixture_experts_ffn_router_amd import workloads as W
     from oracle import moe_oracle as O
@@ -189,11 +189,18 @@ def cpu_baseline(L, seconds):
             O.moe_layer(x, layer, rows=rows, logits=logits)
         return time.perf_counter() - t0
 
-    pilot = min(T, 16)
-    rate = pilot / max(run(pilot), 1e-6)  # rows per second (routing cost included)
-    n = int(min(T, max(pilot, rate * seconds)))
-    reps = 1 if n < T else max(1, int(seconds / max(n / rate, 1e-6)))
-    dt = run(n, reps)
+    # Grow the sample (then repeat all T rows) by at most 8x per try until one run
+    # takes at least half the target; that run is the measurement.
+    n, reps = min(T, 16), 1
+    while True:
+        dt = run(n, reps)
+        if dt >= seconds / 2:
+            break
+        scale = min(8.0, seconds / max(dt, 1e-3))
+        if n < T:
+            n = min(T, max(n + 1, int(n * scale)))
+        else:
+            reps = max(reps + 1, int(reps * scale))
     cores = len(os.sched_getaffinity(0))
     return {"value": round(n * reps / dt, 2), "unit": "tokens/s", "cores": threads or cores, "kind": "oracle",
             "sample": f"{n} of {T} token rows through the experts (routing over all {T}), {reps} time(s): "
