@@ -76,7 +76,8 @@ struct Plan {
   bool y_f32;                    // per-slot expert outputs kept in fp32
   size_t o_logits, o_w, o_ids, o_counts, o_offsets, o_sorted, o_bexp, o_rms, o_r, o_xn1, o_xn2, o_h, o_y,
       o_dh, o_dout, total;
-  size_t o_rinfo, o_msum;  // decode path only
+  size_t o_rinfo, o_ypart;  // decode path only
+  int down_splits;
 };
 
 moe_status validate_desc(const moe_layer_desc* d) {
@@ -170,7 +171,8 @@ moe_status make_plan(const moe_layer_desc& d, const moe_tensors* t, int64_t T, P
     p.o_h = take((size_t)slots * d.inter * 2);
     p.o_dh = take(p.dense ? (size_t)T * d.inter_dense * 2 : 0);
     p.o_dout = take(p.dense ? (size_t)T * H * 4 : 0);
-    p.o_msum = take(p.dense ? (size_t)T * H * 4 : 0);
+    p.down_splits = moe::decode_down_splits((int)T, d.hidden, d.inter, p.dense);
+    p.o_ypart = take(p.dense || p.down_splits > 1 ? (size_t)T * p.down_splits * H * 4 : 0);
     if (o > p.total) p.total = o;
   }
   return MOE_OK;
@@ -333,7 +335,8 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
     a.hd = p.dense ? ws + p.o_dh : nullptr;
     a.hbuf = ws + p.o_h;
     a.dsum = p.dense ? (float*)(ws + p.o_dout) : nullptr;
-    a.msum = p.dense ? (float*)(ws + p.o_msum) : nullptr;
+    a.down_splits = p.down_splits;
+    a.ypart = p.dense || p.down_splits > 1 ? (float*)(ws + p.o_ypart) : nullptr;
     a.rinfo = (int*)(ws + p.o_rinfo);
     a.out = t->out;
     a.out_f32 = t->out_f32;
@@ -358,9 +361,9 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
     STAGE(MOE_STAGE_DENSE_GATE_UP);
     STAGE(MOE_STAGE_DENSE_DOWN);
     STAGE(MOE_STAGE_FINALIZE);
-    if (p.dense)
-      HIP_TRY(moe::launch_finalize(a.msum, moe::ELEM_F32, 1, a.dsum, t->gamma_post1, t->gamma_post2, d.eps,
-                                   t->out, moe::ELEM_BF16, t->out_f32, T, d.hidden, st),
+    if (a.ypart)
+      HIP_TRY(moe::launch_finalize(a.ypart, moe::ELEM_F32, p.down_splits, a.dsum, t->gamma_post1, t->gamma_post2,
+                                   d.eps, t->out, moe::ELEM_BF16, t->out_f32, T, d.hidden, st),
               "finalize launch");
     STAGE(MOE_STAGE_COUNT);
     return MOE_OK;

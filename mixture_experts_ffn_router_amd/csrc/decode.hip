@@ -22,11 +22,13 @@
 //         picked it, h = act(g) * u times the slot's routing weight, stored per
 //         slot in bf16.  Every block normalises the token rows it needs itself
 //         while staging them into LDS;
-//   down  first the dense MLP's down projection, then one block per 16 output
-//         features: the sum over active experts of W2_e h_e, where h_e already
+//   down  first the dense MLP's down projection, then blocks of 16 output
+//         features (times P parts of the reduction when there are few feature
+//         groups): the sum over active experts of W2_e h_e, where h_e already
 //         carries each token's weight, so the combine over a token's k slots
 //         happens inside the accumulator;
-//   finalize (dense branch only): the two post-norms and the branch sum.
+//   finalize (dense branch or P > 1): the sum of the P partial rows in a fixed
+//         order, then the two post-norms and the branch sum.
 //
 // Decode time is mostly chains of dependent memory round trips inside a block,
 // so every wave issues all loads of its share of a weight tile in one batch,
@@ -43,19 +45,11 @@
 
 namespace moe {
 
-#ifndef DECODE_DU_BF16
-#define DECODE_DU_BF16 2
-#endif
-#ifndef DECODE_DU_FP8
-#define DECODE_DU_FP8 6
-#endif
-#ifndef DECODE_DW3
-#define DECODE_DW3 8
-#endif
-// macro steps (64 reduction elements each) per load batch
-constexpr int DU_PRE = 6;                // router kernel: few blocks, one batch per wave
-constexpr int DU_BF16 = DECODE_DU_BF16;  // streaming kernels, bf16 weights
-constexpr int DU_FP8 = DECODE_DU_FP8;    // streaming kernels, fp8 weights
+// Macro steps (64 reduction elements each) per load batch (measured: short
+// batches with more resident waves stream bf16 weights best; fp8 prefers longer).
+constexpr int DU_PRE = 6;   // router kernel: few blocks, one batch per wave
+constexpr int DU_BF16 = 2;  // streaming kernels, bf16 weights
+constexpr int DU_FP8 = 6;   // streaming kernels, fp8 weights
 constexpr int XCH = 8;  // 16-byte chunks per lane of a token row held in registers (4096 elements)
 
 // Lane l feeds row / token column l & 15 and reduction elements from lane group
@@ -252,7 +246,7 @@ __device__ __forceinline__ int find_slot(const int* s_ids, int Kp, int t, int e)
 }
 
 constexpr int PW = 8;                          // waves per block of the pre and up kernels
-constexpr int DW3 = DECODE_DW3;                // waves per block of the down kernel
+constexpr int DW3 = 8;                         // waves per block of the down kernel
 constexpr int RED_FLOATS = PW * 2 * 4 * 64;    // partial tiles of up to two row groups
 
 __host__ __device__ __forceinline__ int stage_bytes(int T, int H) { return (T * (H + 8) * 2 + 15) / 16 * 16; }
@@ -491,7 +485,10 @@ __global__ __launch_bounds__(DW3 * 64) void decode_down_kernel(DecodeArgs a) {
     return;
   }
 
-  const int n0 = (blockIdx.x - a.n_ddown_groups) * 16;
+  // Block = (16 output features, part): the part takes 1/P of every expert's
+  // reduction range, so P blocks share a feature group when there are few groups.
+  const int ng = H / 16, gi = blockIdx.x - a.n_ddown_groups;
+  const int n0 = (gi % ng) * 16, part = gi / ng, P = a.down_splits;
   // The routing summary of the up kernel; this wave's entries are read in the
   // same round trip as the active count, assuming one unit per active expert
   // (re-read otherwise).  Entries at or past the count are stale but in bounds.
@@ -499,8 +496,8 @@ __global__ __launch_bounds__(DW3 * 64) void decode_down_kernel(DecodeArgs a) {
   const int n_act = a.rinfo[0];
   int e_spec = a.rinfo[1 + us];
   int slot_spec = a.rinfo[1 + Ep + us * 16 + col];
-  const int MS = I / 64;
-  const int S = min((DW3 + n_act - 1) / n_act, MS);  // reduction splits per expert
+  const int k0 = part * (I / 64) / P, MS = (part + 1) * (I / 64) / P - k0;  // this part's macro steps
+  const int S = min((DW3 + n_act - 1) / n_act, MS);  // further splits per expert over the waves
   const int n_units = n_act * S;
   constexpr int WB = FP8 ? 1 : 2;
   const rsrc_t rb = make_rsrc(a.hbuf, (uint32_t)((int64_t)T * a.Kp * I * 2));
@@ -524,7 +521,7 @@ __global__ __launch_bounds__(DW3 * 64) void decode_down_kernel(DecodeArgs a) {
       for (int v = 0; v < 4; ++v) sc[v] = a.s2[(int64_t)e * H + n0 + 4 * g + v];
     }
     f32x4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
-    st.run(acc, nullptr, false, s * MS / S, (s + 1) * MS / S, false);
+    st.run(acc, nullptr, false, k0 + s * MS / S, k0 + (s + 1) * MS / S, false);
     if constexpr (FP8) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) tot[v] += sc[v] * acc[0][v];
@@ -532,17 +529,17 @@ __global__ __launch_bounds__(DW3 * 64) void decode_down_kernel(DecodeArgs a) {
       tot += acc[0];
     }
   }
-  const f32x4 part[1] = {tot};
-  partials_to_lds<1>(red, part, wave, lane);
+  const f32x4 tile[1] = {tot};
+  partials_to_lds<1>(red, tile, wave, lane);
   __syncthreads();
   if (threadIdx.x < 256) {
     const int rho = threadIdx.x >> 4, t = threadIdx.x & 15;
     if (t < T) {
       const float v = reduced<DW3, 1>(red, 0, rho, t);
-      const int64_t o = (int64_t)t * H + n0 + rho;
-      if (a.msum) {
-        a.msum[o] = v;
+      if (a.ypart) {
+        a.ypart[((int64_t)t * P + part) * H + n0 + rho] = v;
       } else {
+        const int64_t o = (int64_t)t * H + n0 + rho;
         ((bf16_t*)a.out)[o] = f32_to_bf16(v);
         if (a.out_f32) a.out_f32[o] = v;
       }
@@ -627,8 +624,21 @@ hipError_t launch_decode_up(const DecodeArgs& args, bool fp8, hipStream_t s) {
   }
 }
 
+// Parts per output-feature group of the down kernel: enough blocks for about two
+// per CU, when a finalize runs anyway (dense branch) or the call has 4+ tokens
+// (a finalize launch then costs less than the idle CUs); at most one per 64-deep
+// step of the reduction.
+int decode_down_splits(int T, int H, int I, bool dense) {
+  if (!dense && T < 4) return 1;
+  const int ng = H / 16;
+  int P = (2 * cu_count() + ng - 1) / ng;
+  P = P < 1 ? 1 : (P > 4 ? 4 : P);
+  return P < I / 64 ? P : I / 64;
+}
+
 hipError_t launch_decode_down(const DecodeArgs& a, bool fp8, hipStream_t s) {
-  const dim3 grid(a.n_ddown_groups + a.H / 16), block(DW3 * 64);
+  if (a.down_splits < 1 || (a.down_splits > 1 && !a.ypart)) return hipErrorInvalidValue;
+  const dim3 grid(a.n_ddown_groups + a.H / 16 * a.down_splits), block(DW3 * 64);
   if (fp8) decode_down_kernel<true><<<grid, block, 0, s>>>(a);
   else decode_down_kernel<false><<<grid, block, 0, s>>>(a);
   return hipGetLastError();

@@ -96,9 +96,10 @@ struct DecodeArgs {
   void* hd;             // [T, Id] bf16 dense hidden
   void* hbuf;           // [T * Kp, I] bf16 weighted expert hidden, per slot
   float* dsum;          // [T, H] dense branch output
-  float* msum;          // [T, H] expert sum when post-norms follow, else NULL
+  float* ypart;         // [T, P, H] partial expert sums when a finalize follows, else NULL
+  int down_splits;      // P: parts of the reduction per output-feature group in the down kernel
   int* rinfo;           // active count, active experts [Ep], slot per (active, token) [Ep][16]
-  void* out;            // [T, H] bf16 (when msum is NULL)
+  void* out;            // [T, H] bf16 (when ypart is NULL)
   float* out_f32;
   float* topk_w_out;
   int32_t* topk_ids_out;
@@ -107,6 +108,7 @@ struct DecodeArgs {
 int decode_up_lds_bytes(int T, int H, int Kp, int Ep);
 int decode_pre_lds_bytes(int T, int H);
 int decode_up_blocks_per_cu(int T, int H, int Kp, int Ep);
+int decode_down_splits(int T, int H, int I, bool dense);
 hipError_t launch_decode_pre(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_up(const DecodeArgs& a, bool fp8, hipStream_t s);
 hipError_t launch_decode_down(const DecodeArgs& a, bool fp8, hipStream_t s);
