@@ -70,6 +70,7 @@ bool use_decode(const moe_layer_desc& d, int64_t T) {
 struct Plan {
   bool f32, decode;
   int Kp, Ep, bm;
+  int ks;  // reduction parts of the grouped down GEMM (per-slot rows per slot)
   int64_t cap;
   bool need_logits, need_prenorm, gemma_router, dense;
   bool mat_r, mat_xn1, mat_xn2;  // normalised rows that must be materialised (learned weight present)
@@ -138,6 +139,10 @@ moe_status make_plan(const moe_layer_desc& d, const moe_tensors* t, int64_t T, P
   // With the dense branch the MoE sum is RMS-normalised afterwards, which turns
   // its relative error into error at output scale: keep the per-slot rows fp32.
   p.y_f32 = p.f32 || p.dense;
+  // Split the down GEMM's reduction when its tiles would fill the CUs in few
+  // rounds (long reductions over few rows: the Mixtral-style layer); rows are
+  // estimated with half a block of padding per expert.
+  p.ks = p.f32 ? 1 : moe::gemm_scatter_k_splits(slots + (int64_t)p.Ep * (p.bm / 2), p.bm, d.hidden, d.inter);
   const size_t H = d.hidden;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -157,7 +162,7 @@ moe_status make_plan(const moe_layer_desc& d, const moe_tensors* t, int64_t T, P
   p.o_xn1 = take(p.mat_xn1 ? (size_t)T * H * ae : 0);
   p.o_xn2 = take(p.mat_xn2 ? (size_t)T * H * ae : 0);
   p.o_h = take((size_t)p.cap * d.inter * ae);
-  p.o_y = take((size_t)slots * H * (p.y_f32 ? 4 : ae));
+  p.o_y = take((size_t)slots * p.ks * H * (p.y_f32 ? 4 : ae));
   p.o_dh = take(p.dense ? (size_t)T * d.inter_dense * ae : 0);
   p.o_dout = take(p.dense ? (size_t)T * H * 4 : 0);
   p.total = o;
@@ -484,6 +489,7 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
     a.ldc = H;
     a.c_rows = sorted;
     a.row_weight = w;
+    a.k_splits = p.ks;
     HIP_TRY(gemm(a, (p.y_f32 && !p.f32) ? moe::EPI_SCATTER_F32 : moe::EPI_SCATTER, b_elem, p.bm),
             "down gemm launch");
   }
@@ -522,7 +528,7 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
   }
   STAGE(MOE_STAGE_FINALIZE);
   // 8. per-token combine in slot order (+ Gemma post-norms and branch sum)
-  HIP_TRY(moe::launch_finalize(y, p.y_f32 ? moe::ELEM_F32 : act_elem, p.Kp, dout, t->gamma_post1, t->gamma_post2, d.eps, t->out, act_elem,
+  HIP_TRY(moe::launch_finalize(y, p.y_f32 ? moe::ELEM_F32 : act_elem, p.Kp * p.ks, dout, t->gamma_post1, t->gamma_post2, d.eps, t->out, act_elem,
                                t->out_f32, T, H, st),
           "finalize launch");
   // 9. optional copies of the routing result

@@ -167,7 +167,8 @@ void gemm_mfma_kernel(GemmArgs p) {
   const int64_t m_rows = p.m_dev ? (int64_t)(*p.m_dev) : p.M;
   const int64_t mbn = (m_rows + BM - 1) / BM;  // row blocks holding rows
   const int64_t nb_cnt = (p.N + NCOLS - 1) / NCOLS;
-  const int64_t ntiles = mbn * nb_cnt;
+  const int KS = p.k_splits;  // reduction parts (scatter epilogues), the slowest tile index
+  const int64_t ntiles = mbn * nb_cnt * KS;
   const bool xcd_map = gridDim.x % 8 == 0;
   const int64_t per_xcd = (ntiles + 7) / 8;
   const int64_t tend = xcd_map ? per_xcd * 8 : ntiles;
@@ -179,7 +180,8 @@ void gemm_mfma_kernel(GemmArgs p) {
   const int64_t lid = xcd_logical(t, per_xcd, xcd_map);
   if (lid >= ntiles) continue;  // uniform per block
   int64_t mb, nbi;
-  tile_coords(lid, mbn, nb_cnt, p.block_expert, p.seg_off, BM, mb, nbi);
+  const int ks = (int)(lid / (mbn * nb_cnt));
+  tile_coords(lid % (mbn * nb_cnt), mbn, nb_cnt, p.block_expert, p.seg_off, BM, mb, nbi);
   __syncthreads();  // the previous tile's LDS reads are done in every wave
   const int64_t m0 = mb * BM;
   const int n0 = (int)nbi * NCOLS;
@@ -194,7 +196,9 @@ void gemm_mfma_kernel(GemmArgs p) {
   const rsrc_t rsA = make_rsrc(p.A, (uint32_t)(p.a_rows_alloc * p.lda * 2));
   const rsrc_t rsB = make_rsrc(Bbase, (uint32_t)((int64_t)(GATED ? 2 * p.N : p.N) * p.Kdim * EB));
 
-  const int nk = p.Kdim / BK;
+  // K tiles [kt0, kt0 + nk) of this reduction part
+  const int kt0 = ks * (p.Kdim / BK) / KS;
+  const int nk = (ks + 1) * (p.Kdim / BK) / KS - kt0;
 
   // LDS row of the wave's B tile j (output-column tile)
   auto b_lds_row = [&](int j) {
@@ -314,11 +318,11 @@ void gemm_mfma_kernel(GemmArgs p) {
       const bool live = kt < nk;
   #pragma unroll
       for (int i = 0; i < A_DMA; ++i)
-        dma16(rsA, sA + (wave * A_DMA + i) * 1024, live ? a_off[i] : 0x80000000u, live ? (uint32_t)kt * A_ROW : 0u);
+        dma16(rsA, sA + (wave * A_DMA + i) * 1024, live ? a_off[i] : 0x80000000u, live ? (uint32_t)(kt0 + kt) * A_ROW : 0u);
   #pragma unroll
       for (int i = 0; i < B_DMA; ++i)
         dma16(rsB, sB + (wave * B_DMA + i) * 1024, live ? b_voff : 0x80000000u,
-              live ? b_soff[i] + (uint32_t)kt * (uint32_t)B_ROW : 0u);
+              live ? b_soff[i] + (uint32_t)(kt0 + kt) * (uint32_t)B_ROW : 0u);
     };
 
 
@@ -443,11 +447,11 @@ void gemm_mfma_kernel(GemmArgs p) {
 #pragma unroll
       for (int i = 0; i < NLA; ++i)
         sa[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              rsA, live ? ga[i] : 0x80000000u, live ? kt * A_ROW : 0, 0));
+                                              rsA, live ? ga[i] : 0x80000000u, live ? (kt0 + kt) * A_ROW : 0, 0));
 #pragma unroll
       for (int i = 0; i < NLB; ++i)
         sbv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               rsB, live ? gb0 : 0x80000000u, live ? kt * B_ROW + i * gb_step : 0, 0));
+                                               rsB, live ? gb0 : 0x80000000u, live ? (kt0 + kt) * B_ROW + i * gb_step : 0, 0));
     };
     auto lds_store = [&](int stage) {
       uint8_t* st = smem + stage * STAGE;
@@ -562,6 +566,7 @@ void gemm_mfma_kernel(GemmArgs p) {
       const int slot = p.c_rows[grow];
       if (slot < 0) continue;
       const float w = p.row_weight ? p.row_weight[slot] : 1.f;
+      const int64_t orow = (int64_t)slot * KS + ks;  // the part's row of this slot
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
 #pragma unroll
@@ -578,9 +583,9 @@ void gemm_mfma_kernel(GemmArgs p) {
             uint2 pk;
             pk.x = pack_bf16x2(y[0], y[1]);
             pk.y = pack_bf16x2(y[2], y[3]);
-            *(uint2*)((bf16_t*)p.C + (int64_t)slot * p.ldc + col) = pk;
+            *(uint2*)((bf16_t*)p.C + orow * p.ldc + col) = pk;
           } else {
-            *(float4*)((float*)p.C + (int64_t)slot * p.ldc + col) = make_float4(y[0], y[1], y[2], y[3]);
+            *(float4*)((float*)p.C + orow * p.ldc + col) = make_float4(y[0], y[1], y[2], y[3]);
           }
         }
       }
@@ -762,7 +767,28 @@ static hipError_t run_grouped(const GemmArgs& a, int block_m, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// The 256-row configurations hold one block per CU (their LDS stages take most
+// of it), so a grid round is one tile per CU.  A part must keep at least 32 K
+// tiles so the pipeline's fill stays small against it.
+int gemm_scatter_k_splits(int64_t rows, int block_m, int N, int Kdim) {
+  if (block_m != 256 || rows <= 0) return 1;
+  const int bn = N % 256 == 0 ? 256 : 128;
+  const int64_t tiles = (rows + block_m - 1) / block_m * ((N + bn - 1) / bn);
+  const int64_t slots = device_cu_count();
+  int best = 1;
+  double best_rounds = 1e300;
+  for (int ks = 1; ks <= 4 && (Kdim / 64) / ks >= 32; ++ks) {
+    const double rounds = (double)((tiles * ks + slots - 1) / slots) / ks;  // in full-reduction tile times
+    if (rounds < best_rounds - 1e-9) {
+      best_rounds = rounds;
+      best = ks;
+    }
+  }
+  return best;
+}
+
 hipError_t launch_gemm_mfma(const GemmArgs& a, int epi, int belem, int block_m, hipStream_t s) {
+  if (a.k_splits < 1 || (a.k_splits > 1 && epi != EPI_SCATTER && epi != EPI_SCATTER_F32)) return hipErrorInvalidValue;
   if (epi == EPI_STORE_F32) {
     if (belem != ELEM_BF16) return hipErrorInvalidValue;
     if (block_m == 128) {
@@ -782,6 +808,7 @@ hipError_t launch_gemm_mfma(const GemmArgs& a, int epi, int belem, int block_m, 
 }
 
 hipError_t launch_gemm_f32(const GemmArgs& a, int epi, hipStream_t s) {
+  if (a.k_splits != 1) return hipErrorInvalidValue;
   const int ncols = epi == EPI_GATED ? 32 : 64;
   const int64_t blocks = ((a.M + 63) / 64) * ((a.N + ncols - 1) / ncols);
   if (blocks <= 0) return hipSuccess;

@@ -40,16 +40,21 @@ struct GemmArgs {
   int32_t Kdim;
   void* C;                    // output; row stride ldc (elements)
   int64_t ldc;
-  const int32_t* c_rows;      // scatter epilogue: output row = c_rows[r] (skip if < 0)
+  const int32_t* c_rows;      // scatter epilogue: output row = c_rows[r] * k_splits + part (skip if < 0)
   const float* row_weight;    // scatter epilogue: weight per output row (slot), NULL = 1
   int32_t act;                // gated epilogue activation
   const float* row_scale;     // per-token factor on the accumulator (gated: on g and u; store:
                               // on the value), indexed by the A row's token; NULL = 1
   float c_scale = 1.f;        // constant factor on stored values (store epilogue)
+  int32_t k_splits = 1;       // scatter epilogues (MFMA kernel): the reduction is cut into this many
+                              // parts, each stored to its own row; other epilogues need 1
 };
 
 // bf16 A; B bf16 or FP8 (ELEM_BF16 / ELEM_FP8).  block_m in {32, 64, 128, 256}.
 hipError_t launch_gemm_mfma(const GemmArgs& a, int epi, int belem, int block_m, hipStream_t s);
+// Reduction parts for a grouped scatter GEMM of about `rows` rows: the count in
+// 1..4 that wastes least of the last round of tiles on this device's CUs.
+int gemm_scatter_k_splits(int64_t rows, int block_m, int N, int Kdim);
 // fp32 A and B (the fp32 layer).  block_m = 64.
 hipError_t launch_gemm_f32(const GemmArgs& a, int epi, hipStream_t s);
 

@@ -84,6 +84,8 @@ SMALL = {
     "tiny_fp32_ragged": W.SPECS["tiny"].with_T(77),
     "bf16_ragged_bm64": W.LayerSpec("bf16_small", 300, 256, 8, 2, 512, "silu", "bf16"),
     "bf16_bm256": W.LayerSpec("bf16_bm256", 1100, 256, 4, 1, 512, "silu", "bf16"),
+    # few row blocks and a long down reduction: the down GEMM splits its reduction in parts
+    "bf16_down_split": W.LayerSpec("bf16_ksplit", 512, 256, 2, 1, 4096, "silu", "bf16"),
     "bf16_single_expert": W.LayerSpec("bf16_e1", 65, 128, 1, 1, 128, "gelu_tanh", "bf16"),
     "gemma_small": W.LayerSpec("gemma_small", 333, 256, 16, 4, 128, "gelu_tanh", "bf16",
                                router_mode="gemma", per_expert_scale="uniform", I_dense=192,
