@@ -50,12 +50,15 @@ int64_t permute_capacity(int64_t n_slots, int E, int bm) {
   return (n_slots + (int64_t)E * (bm - 1)) / bm * bm;
 }
 
-// Row-block height of the grouped GEMMs: 256-row blocks once an expert gets
-// enough rows on average to fill them, 64 otherwise; 64 for the fp32 layer.
+// Row-block height of the grouped GEMMs.  Every expert's rows are padded to a
+// whole block and a block costs about the same time however many of its rows
+// are real, so the height follows the rows an expert gets on average: 256
+// (256x256 tiles) from 1024 rows, 128 (128x512 tiles, the same per-wave shape)
+// from 128, else 64; 64 for the fp32 layer.
 int choose_block_m(const moe_layer_desc& d, int64_t T) {
   if (d.act_dtype == MOE_DT_F32) return 64;
   const int64_t avg = T * d.top_k / d.num_experts;
-  return avg >= 256 ? 256 : 64;
+  return avg >= 1024 ? 256 : (avg >= 128 ? 128 : 64);
 }
 
 // Decode path: at most 16 bf16 tokens (one MFMA tile of token columns) whose

@@ -756,6 +756,7 @@ static hipError_t run_grouped(const GemmArgs& a, int block_m, hipStream_t s) {
     if (N % 256 == 0) return run_mfma<256, 256, 4, 2, EPI, BELEM>(a, s);
     return run_mfma<256, 128, 4, 1, EPI, BELEM>(a, s);
   }
+  if (block_m == 128) return run_mfma<128, 512, 2, 4, EPI, BELEM>(a, s);
   if (block_m == 64) {
     if (EPI == EPI_GATED) {
       if (N % 128 == 0) return run_mfma<64, 256, 1, 4, EPI, BELEM>(a, s);

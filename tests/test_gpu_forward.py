@@ -83,9 +83,10 @@ SMALL = {
     "tiny_fp32": W.SPECS["tiny"],
     "tiny_fp32_ragged": W.SPECS["tiny"].with_T(77),
     "bf16_ragged_bm64": W.LayerSpec("bf16_small", 300, 256, 8, 2, 512, "silu", "bf16"),
-    "bf16_bm256": W.LayerSpec("bf16_bm256", 1100, 256, 4, 1, 512, "silu", "bf16"),
-    # few row blocks and a long down reduction: the down GEMM splits its reduction in parts
-    "bf16_down_split": W.LayerSpec("bf16_ksplit", 512, 256, 2, 1, 4096, "silu", "bf16"),
+    "bf16_bm128": W.LayerSpec("bf16_bm128", 1100, 256, 4, 1, 512, "silu", "bf16"),
+    # 256-row blocks; few row blocks and a long down reduction: the down GEMM splits
+    # its reduction in parts
+    "bf16_bm256_down_split": W.LayerSpec("bf16_ksplit", 2048, 256, 2, 1, 4096, "silu", "bf16"),
     "bf16_single_expert": W.LayerSpec("bf16_e1", 65, 128, 1, 1, 128, "gelu_tanh", "bf16"),
     "gemma_small": W.LayerSpec("gemma_small", 333, 256, 16, 4, 128, "gelu_tanh", "bf16",
                                router_mode="gemma", per_expert_scale="uniform", I_dense=192,
@@ -96,7 +97,9 @@ SMALL = {
                                   renorm=False, n_shared=2, I_shared=128),
     "fp8_small": W.LayerSpec("fp8_small", 257, 256, 16, 4, 192, "gelu_tanh", "fp8",
                              supplied_logits=True),
-    "fp8_small_bm256": W.LayerSpec("fp8_bm256", 1030, 256, 4, 1, 256, "silu", "fp8",
+    "fp8_small_bm128": W.LayerSpec("fp8_bm128", 1030, 256, 4, 1, 256, "silu", "fp8",
+                                   supplied_logits=True),
+    "fp8_small_bm256": W.LayerSpec("fp8_bm256", 2100, 256, 2, 1, 512, "gelu_tanh", "fp8",
                                    supplied_logits=True),
     "fp32_gemma_router": W.LayerSpec("fp32_gemma", 50, 128, 8, 3, 64, "gelu_tanh", "fp32",
                                      router_mode="gemma", I_dense=64, random_gammas=True),
