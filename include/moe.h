@@ -5,7 +5,11 @@
  * Conventions for every entry point:
  *   - All tensors are dense, row-major, contiguous device pointers (HIP device
  *     memory the caller owns).  The library allocates no device memory and keeps
- *     no state between calls; calls on different streams are independent.
+ *     no data between calls; calls on different streams are independent.  The
+ *     one thing it keeps: moe_forward creates, on first need per host thread and
+ *     device, a second stream (default priority, non-blocking) and two events,
+ *     held until the process ends; a layer's dense branch runs on that stream,
+ *     ordered with the caller's stream by those events (see moe_forward).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work
  *     is enqueued asynchronously on it; the call returns once it is enqueued.
  *   - Arguments are validated on the host before anything is launched.  A bad
@@ -176,6 +180,11 @@ moe_status moe_forward_workspace_size(const moe_layer_desc* desc, int64_t T, siz
  * Precision: bf16 operands with fp32 accumulation (fp32 throughout for
  * act_dtype F32); the gated intermediate and the per-slot expert outputs are
  * rounded to bf16 in the bf16 path; logits are fp32.
+ *
+ * On the grouped path the dense branch runs on the library's second stream
+ * between an event recorded on `stream` after the input norms and a wait of
+ * `stream` before the finalize, so it overlaps routing, permutation and the
+ * grouped GEMMs; moe_forward_profiled keeps it on `stream`.
  *
  * Two execution paths compute this same operation (moe_forward_path tells which
  * one a call takes).  The grouped path permutes the routed rows and runs grouped

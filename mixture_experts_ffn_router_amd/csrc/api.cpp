@@ -37,6 +37,31 @@ moe_status hip_fail(hipError_t e, const char* what) {
     if (_e != hipSuccess) return hip_fail(_e, what); \
   } while (0)
 
+// A second stream per host thread and device, created on first use and kept
+// until the process ends: the dense MLP branch of a layer runs on it, between a
+// fork event recorded on the caller's stream after the input norms and a join
+// event the caller's stream waits for before the finalize, so it fills the CUs
+// that routing, permutation and the tails of the grouped GEMMs leave idle.
+// Default priority, non-blocking, ordered only by those events.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool tried = false, ok = false;
+};
+SideStream* side_stream() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  thread_local SideStream per_device[64];
+  SideStream& x = per_device[dev];
+  if (!x.tried) {
+    x.tried = true;
+    x.ok = hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) == hipSuccess &&
+           hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) == hipSuccess &&
+           hipEventCreateWithFlags(&x.join, hipEventDisableTiming) == hipSuccess;
+  }
+  return x.ok ? &x : nullptr;
+}
+
 constexpr size_t ALIGN = 256;
 size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
@@ -394,9 +419,47 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
   void* dh = p.dense ? ws + p.o_dh : nullptr;
   float* dout = p.dense ? (float*)(ws + p.o_dout) : nullptr;
 
-  auto gemm = [&](const moe::GemmArgs& a, int epi, int belem, int bm) -> hipError_t {
-    return p.f32 ? moe::launch_gemm_f32(a, epi, st) : moe::launch_gemm_mfma(a, epi, belem, bm, st);
+  auto gemm_on = [&](const moe::GemmArgs& a, int epi, int belem, int bm, hipStream_t s) -> hipError_t {
+    return p.f32 ? moe::launch_gemm_f32(a, epi, s) : moe::launch_gemm_mfma(a, epi, belem, bm, s);
   };
+  auto gemm = [&](const moe::GemmArgs& a, int epi, int belem, int bm) -> hipError_t {
+    return gemm_on(a, epi, belem, bm, st);
+  };
+  // parallel dense MLP (Gemma): dense_out = MLP(xn1) in fp32, on stream s
+  auto dense_branch = [&](hipStream_t s, bool marks) -> moe_status {
+    const int dbm = T >= 1024 ? 256 : 64;
+    moe::GemmArgs a{};
+    a.A = p.mat_xn1 ? xn1 : t->x;
+    if (!p.mat_xn1) a.row_scale = inv_rms;
+    a.lda = H;
+    a.M = T;
+    a.a_rows_alloc = T;
+    a.B0 = t->dense_w13;
+    a.n_routed = 1;
+    a.N = d.inter_dense;
+    a.Kdim = H;
+    a.C = dh;
+    a.ldc = d.inter_dense;
+    a.act = d.dense_act;
+    HIP_TRY(gemm_on(a, moe::EPI_GATED, moe::ELEM_BF16, dbm, s), "dense gate/up gemm launch");
+    if (marks) STAGE(MOE_STAGE_DENSE_DOWN);
+    moe::GemmArgs b{};
+    b.A = dh;
+    b.lda = d.inter_dense;
+    b.M = T;
+    b.a_rows_alloc = T;
+    b.B0 = t->dense_w2;
+    b.n_routed = 1;
+    b.N = H;
+    b.Kdim = d.inter_dense;
+    b.C = dout;
+    b.ldc = H;
+    HIP_TRY(gemm_on(b, moe::EPI_STORE_F32, moe::ELEM_BF16, dbm, s), "dense down gemm launch");
+    return MOE_OK;
+  };
+  // Overlap the dense branch with the MoE path unless stages are being timed.
+  SideStream* side = p.dense && !events ? side_stream() : nullptr;
+
   STAGE(MOE_STAGE_PRENORM);
   // 1. input norms (Gemma router preprocessing, pre_feedforward_layernorm / _2):
   //    1/rms per token; normalised rows only where a learned weight is given.
@@ -404,6 +467,13 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
     HIP_TRY(moe::launch_prenorm(t->x, act_elem, T, H, d.eps, inv_rms, t->router_scale, t->gamma_pre,
                                 t->gamma_pre2, r_in, xn1, xn2, st),
             "prenorm launch");
+  if (side) {
+    HIP_TRY(hipEventRecord(side->fork, st), "fork event");
+    HIP_TRY(hipStreamWaitEvent(side->s, side->fork, 0), "fork wait");
+    s = dense_branch(side->s, false);
+    if (s != MOE_OK) return s;
+    HIP_TRY(hipEventRecord(side->join, side->s), "join event");
+  }
 
   STAGE(MOE_STAGE_ROUTER);
   // 2. router logits (fp32)
@@ -497,38 +567,14 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
             "down gemm launch");
   }
   STAGE(MOE_STAGE_DENSE_GATE_UP);
-  // 7. parallel dense MLP (Gemma): dense_out = MLP(xn1) in fp32
-  if (!p.dense) STAGE(MOE_STAGE_DENSE_DOWN);
-  if (p.dense) {
-    const int dbm = T >= 1024 ? 256 : 64;
-    moe::GemmArgs a{};
-    a.A = p.mat_xn1 ? xn1 : t->x;
-    if (!p.mat_xn1) a.row_scale = inv_rms;
-    a.lda = H;
-    a.M = T;
-    a.a_rows_alloc = T;
-    a.B0 = t->dense_w13;
-    a.n_routed = 1;
-    a.N = d.inter_dense;
-    a.Kdim = H;
-    a.C = dh;
-    a.ldc = d.inter_dense;
-    a.act = d.dense_act;
-    HIP_TRY(gemm(a, moe::EPI_GATED, moe::ELEM_BF16, dbm), "dense gate/up gemm launch");
+  // 7. parallel dense MLP (Gemma), here when it did not run on the side stream
+  if (p.dense && !side) {
+    s = dense_branch(st, true);
+    if (s != MOE_OK) return s;
+  } else {
     STAGE(MOE_STAGE_DENSE_DOWN);
-    moe::GemmArgs b{};
-    b.A = dh;
-    b.lda = d.inter_dense;
-    b.M = T;
-    b.a_rows_alloc = T;
-    b.B0 = t->dense_w2;
-    b.n_routed = 1;
-    b.N = H;
-    b.Kdim = d.inter_dense;
-    b.C = dout;
-    b.ldc = H;
-    HIP_TRY(gemm(b, moe::EPI_STORE_F32, moe::ELEM_BF16, dbm), "dense down gemm launch");
   }
+  if (side) HIP_TRY(hipStreamWaitEvent(st, side->join, 0), "join wait");
   STAGE(MOE_STAGE_FINALIZE);
   // 8. per-token combine in slot order (+ Gemma post-norms and branch sum)
   HIP_TRY(moe::launch_finalize(y, p.y_f32 ? moe::ELEM_F32 : act_elem, p.Kp * p.ks, dout, t->gamma_post1, t->gamma_post2, d.eps, t->out, act_elem,
