@@ -98,7 +98,8 @@ bool use_decode(const moe_layer_desc& d, int64_t T) {
 struct Plan {
   bool f32, decode;
   int Kp, Ep, bm;
-  int ks;  // reduction parts of the grouped down GEMM (per-slot rows per slot)
+  int ks;    // reduction parts of the grouped down GEMM (per-slot rows per slot)
+  int ks_r;  // reduction parts of the router GEMM (partial logit planes, summed by the route kernel)
   int64_t cap;
   bool need_logits, need_prenorm, gemma_router, dense;
   bool mat_r, mat_xn1, mat_xn2;  // normalised rows that must be materialised (learned weight present)
@@ -194,6 +195,15 @@ moe_status make_plan(const moe_layer_desc& d, const moe_tensors* t, int64_t T, P
   p.o_dh = take(p.dense ? (size_t)T * d.inter_dense * ae : 0);
   p.o_dout = take(p.dense ? (size_t)T * H * 4 : 0);
   p.total = o;
+  // The router GEMM has few output tiles (T/128 x E/128) and a reduction over all
+  // of H: split it so the tiles cover the CUs.  Its partial planes live in the
+  // expert hidden buffer h, which is first written after routing.
+  p.ks_r = 1;
+  if (p.need_logits && !p.f32) {
+    p.ks_r = moe::gemm_store_k_splits(T, d.num_experts, d.hidden);
+    const size_t h_bytes = (size_t)p.cap * d.inter * ae;
+    while (p.ks_r > 1 && (size_t)p.ks_r * T * d.num_experts * 4 > h_bytes) --p.ks_r;
+  }
   // The decode path lays out its own (smaller) buffers over the same workspace;
   // the size reported stays that of the grouped path, so it grows with T.
   p.decode = use_decode(d, T);
@@ -480,6 +490,7 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
   const float* z = t->logits;
   if (p.need_logits) {
     float* zo = t->logits_out ? t->logits_out : (float*)(ws + p.o_logits);
+    if (p.ks_r > 1) zo = (float*)h;  // [ks_r, T, E] partial planes
     moe::GemmArgs a{};
     a.A = p.mat_r ? r_in : t->x;
     a.lda = H;
@@ -495,6 +506,7 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
     a.Kdim = H;
     a.C = zo;
     a.ldc = E;
+    a.k_splits = p.ks_r;
     HIP_TRY(gemm(a, moe::EPI_STORE_F32, moe::ELEM_BF16, 128), "router gemm launch");
     z = zo;
   } else if (t->logits_out) {
@@ -504,7 +516,8 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
 
   STAGE(MOE_STAGE_ROUTE);
   // 3. routing weights and ids (shared experts appended as ids E.., weight 1)
-  HIP_TRY(moe::launch_route(z, T, E, K, d.renormalize, t->per_expert_scale, w, ids, p.Kp, d.n_shared, st),
+  HIP_TRY(moe::launch_route(z, T, E, K, d.renormalize, t->per_expert_scale, w, ids, p.Kp, d.n_shared, st,
+                            p.ks_r, T * E, t->logits_out),
           "route launch");
 
   STAGE(MOE_STAGE_PERMUTE);

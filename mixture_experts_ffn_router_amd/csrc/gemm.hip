@@ -7,18 +7,20 @@
 // expert-major row list; e = the block's expert.  Both operands are
 // K-contiguous ("NT"), which is what the MFMA operand layout wants.
 //
-// bf16 MFMA kernel (v_mfma_f32_32x32x16_bf16), 256 threads = 4 waves:
-//   * BM x BN output tile; K tiles of 32 (bf16) in 4 LDS stages, or 64 (fp8
-//     weights) in 3, filled by buffer loads that write LDS directly (no staging
-//     registers).  Tiles kt+1 .. kt+NS-1 are in flight while tile kt computes;
-//     the waits are explicit vmcnt counts, so only the oldest tile is waited for.
-//     Buffer resources bound each operand, so a load past the end returns 0.
+// bf16 MFMA kernel (v_mfma_f32_32x32x16_bf16), 4 or 8 waves:
+//   * BM x BN output tile; every operand tile reaches LDS through buffer loads
+//     that write LDS directly (no staging registers).  8 waves with bf16 weights
+//     ping-pong over 64-deep K tiles in 2 stages (see pingpong_dma64).  Otherwise
+//     a software pipeline: K tiles of 32 (bf16) in 4 LDS stages, or 64 (fp8
+//     weights) in 3; tiles kt+1 .. kt+NS-1 are in flight while tile kt computes,
+//     and the waits are explicit vmcnt counts, so only the oldest tile is waited
+//     for.  Buffer resources bound each operand, so a load past the end returns 0.
 //   * LDS rows of 64 / 128 bytes; the 16-byte chunk index is XORed with a
 //     function of the row so the 16 lanes of each ds_read_b128 phase hit
 //     distinct banks.
-//   * Fragments are double-buffered in registers: the LDS reads of the next
-//     sub-step (including the first of the next tile, right after the barrier)
-//     are in flight while the MFMAs of this one run.
+//   * Software pipeline: fragments are double-buffered in registers, the LDS
+//     reads of the next sub-step (including the first of the next tile, right
+//     after the barrier) in flight while the MFMAs of this one run.
 //   * A rows are gathered straight from x through the row map (no permuted copy
 //     of the activations); B rows come from the block's expert.
 //   * The MFMA is issued as B x A, so each lane's accumulator holds 4
@@ -131,11 +133,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N)
 __attribute__((amdgpu_waves_per_eu(WAVES_M * WAVES_N / 4, WAVES_M * WAVES_N / 4)))
 void gemm_mfma_kernel(GemmArgs p) {
   constexpr bool FP8 = BELEM == ELEM_FP8;
-  // 8 waves, bf16: ping-pong with register-staged loads, 64-deep K tiles in 2 stages.
-  // Otherwise LDS-DMA: bf16 32-deep K tiles in 4 stages; fp8 weights 64-deep in 3.
-  constexpr bool PPR = WAVES_M * WAVES_N == 8 && BELEM == ELEM_BF16;
-  constexpr int BK = (PPR || BELEM == ELEM_FP8) ? 64 : 32;
-  constexpr int NS = PPR ? 2 : (BELEM == ELEM_FP8 ? 3 : 4);
+  // All operands reach LDS by DMA (buffer_load ... lds).  8 waves, bf16: ping-pong
+  // over 64-deep K tiles in 2 stages.  Otherwise a software pipeline: bf16 32-deep
+  // K tiles in 4 stages; fp8 weights 64-deep in 3.
+  constexpr bool PP = WAVES_M * WAVES_N == 8 && BELEM == ELEM_BF16;
+  constexpr int BK = (PP || BELEM == ELEM_FP8) ? 64 : 32;
+  constexpr int NS = PP ? 2 : (BELEM == ELEM_FP8 ? 3 : 4);
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr bool GATED = EPI == EPI_GATED;
@@ -227,7 +230,7 @@ void gemm_mfma_kernel(GemmArgs p) {
   // every fragment row of this lane is l32 modulo 32
   const int swa = lds_swz<A_ROW>(l32), swb = lds_swz<B_ROW>(l32);
 
-  // Two sub-steps per K tile: bf16 16 k each; fp8 32 k each (one 16-byte B read
+  // Sub-steps of a K tile: bf16 16 k each; fp8 32 k each (one 16-byte B read
   // feeds two MFMAs, see below).
   constexpr int NA = FP8 ? 2 : 1;
   struct Frags {
@@ -280,13 +283,17 @@ void gemm_mfma_kernel(GemmArgs p) {
   // ---- pipeline: tiles kt+1 .. kt+NS-1 are in flight while tile kt computes.
   // A wave whose rows are all padding runs the same DMA / barrier sequence
   // without fragment reads or MFMAs.
-  auto pipeline = [&](auto live_tag) {
-    constexpr bool LIVE = decltype(live_tag)::value;
-    // ---- DMA source offsets.  Instruction i of this wave fills ROWS_PER_DMA
-    // consecutive tile rows; lane l writes row base + l / CH, physical chunk l % CH,
-    // which holds logical chunk (l % CH) ^ swz(row).
+  // ---- LDS-DMA source offsets.  Instruction i of this wave fills ROWS_PER_DMA
+  // consecutive tile rows; lane l writes row base + l / CH, physical chunk l % CH,
+  // which holds logical chunk (l % CH) ^ swz(row).
+  struct DmaPlan {
     uint32_t a_off[A_DMA];
-  #pragma unroll
+    uint32_t b_voff[2];  // by bit 3 of the group's first row (128-byte rows swizzle on it)
+    uint32_t b_soff[B_DMA];
+  };
+  auto dma_plan = [&]() {
+    DmaPlan d;
+#pragma unroll
     for (int i = 0; i < A_DMA; ++i) {
       const int r = (wave * A_DMA + i) * A_ROWS_PER_DMA + lane / A_CH;
       const int64_t grow = m0 + r;
@@ -294,38 +301,47 @@ void gemm_mfma_kernel(GemmArgs p) {
       int64_t tok;
       if (p.a_rows) tok = slot >= 0 ? slot / p.row_div : 0;
       else tok = grow < p.M ? grow : p.M - 1;
-      a_off[i] = (grow >= m_rows || slot < 0)
-                     ? 0x80000000u
-                     : (uint32_t)(tok * p.lda * 2) + (uint32_t)((((lane % A_CH) ^ lds_swz<A_ROW>(r))) << 4);
+      d.a_off[i] = (grow >= m_rows || slot < 0)
+                       ? 0x80000000u
+                       : (uint32_t)(tok * p.lda * 2) + (uint32_t)((((lane % A_CH) ^ lds_swz<A_ROW>(r))) << 4);
     }
-    const int bl_row = lane / B_CH;  // row within a DMA group (B rows are 64 bytes: groups of 16 rows)
-    static_assert(PPR || B_ROW == 64, "B DMA groups must start at multiples of 16 rows");
-    const uint32_t b_voff = (uint32_t)(bl_row * p.Kdim * EB) + (uint32_t)(((lane % B_CH) ^ lds_swz<B_ROW>(bl_row)) << 4);
-    uint32_t b_soff[B_DMA];
-  #pragma unroll
+    // row within a DMA group (groups of 16 rows of 64 bytes or 8 rows of 128 bytes,
+    // starting at multiples of their size: the swizzle of row q0 + bl_row depends
+    // on bl_row and, for 128-byte rows, on bit 3 of q0)
+    const int bl_row = lane / B_CH;
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      d.b_voff[k] = (uint32_t)(bl_row * p.Kdim * EB) +
+                    (uint32_t)(((lane % B_CH) ^ lds_swz<B_ROW>(bl_row + 8 * k)) << 4);
+#pragma unroll
     for (int i = 0; i < B_DMA; ++i) {
       const int q0 = (wave * B_DMA + i) * B_ROWS_PER_DMA;
       int brow;
       if constexpr (GATED) brow = q0 < BN / 2 ? n0 + q0 : p.N + n0 + (q0 - BN / 2);
       else brow = n0 + q0;
-      b_soff[i] = (uint32_t)((int64_t)brow * p.Kdim * EB);
+      d.b_soff[i] = (uint32_t)((int64_t)brow * p.Kdim * EB);
     }
-    // Tile kt into stage buf; tiles past the end are issued with an out-of-range
-    // offset, which the buffer bound turns into zero fill without a memory access.
-    auto issue_dma = [&](int kt, int buf) {
-      uint8_t* sA = smem + buf * STAGE;
-      uint8_t* sB = sA + A_BYTES;
-      const bool live = kt < nk;
-  #pragma unroll
-      for (int i = 0; i < A_DMA; ++i)
-        dma16(rsA, sA + (wave * A_DMA + i) * 1024, live ? a_off[i] : 0x80000000u, live ? (uint32_t)(kt0 + kt) * A_ROW : 0u);
-  #pragma unroll
-      for (int i = 0; i < B_DMA; ++i)
-        dma16(rsB, sB + (wave * B_DMA + i) * 1024, live ? b_voff : 0x80000000u,
-              live ? b_soff[i] + (uint32_t)(kt0 + kt) * (uint32_t)B_ROW : 0u);
-    };
+    return d;
+  };
+  // Tile kt into stage buf; tiles past the end are issued with an out-of-range
+  // offset, which the buffer bound turns into zero fill without a memory access.
+  auto issue_dma = [&](const DmaPlan& d, int kt, int buf) {
+    static_assert(B_ROWS_PER_DMA % 8 == 0, "B DMA groups must start at multiples of 8 rows");
+    uint8_t* sA = smem + buf * STAGE;
+    uint8_t* sB = sA + A_BYTES;
+    const bool live = kt < nk;
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i)
+      dma16(rsA, sA + (wave * A_DMA + i) * 1024, live ? d.a_off[i] : 0x80000000u, live ? (uint32_t)(kt0 + kt) * A_ROW : 0u);
+#pragma unroll
+    for (int i = 0; i < B_DMA; ++i)
+      dma16(rsB, sB + (wave * B_DMA + i) * 1024, live ? d.b_voff[(((wave * B_DMA + i) * B_ROWS_PER_DMA) >> 3) & 1] : 0x80000000u,
+            live ? d.b_soff[i] + (uint32_t)(kt0 + kt) * (uint32_t)B_ROW : 0u);
+  };
 
-
+  auto pipeline = [&](auto live_tag) {
+    constexpr bool LIVE = decltype(live_tag)::value;
+    const DmaPlan dp = dma_plan();
     auto load_frags_l = [&](int b, int s_, Frags& f) {
       if constexpr (LIVE) load_frags(b, s_, f);
     };
@@ -335,7 +351,7 @@ void gemm_mfma_kernel(GemmArgs p) {
   constexpr int R_SUB = TM * NA + TN;             // LDS reads per sub-step
   constexpr int M_SUB = TM * TN * (FP8 ? 2 : 1);  // MFMAs per sub-step
 #pragma unroll
-  for (int t = 0; t < NS - 1; ++t) issue_dma(t, t);
+  for (int t = 0; t < NS - 1; ++t) issue_dma(dp, t, t);
   wait_vmcnt<(NS - 2) * D_TILE>();  // this wave's part of tile 0
   __builtin_amdgcn_s_barrier();      // everyone's part of tile 0
   Frags f0, f1;
@@ -351,7 +367,7 @@ void gemm_mfma_kernel(GemmArgs p) {
     // Sub-step 1 fragments first: they have all of sub-step 0 to land, so the
     // lgkmcnt wait before the barrier finds them done.
     load_frags_l(buf, 1, f1);
-    issue_dma(kt + NS - 1, buf == 0 ? NS - 1 : buf - 1);
+    issue_dma(dp, kt + NS - 1, buf == 0 ? NS - 1 : buf - 1);
     mfmas_l(f0);
     // Own reads of tile kt done and own DMA of tile kt+1 landed; the barrier
     // extends both to every wave.  Tiles kt+2 .. kt+NS-1 stay in flight.
@@ -380,141 +396,75 @@ void gemm_mfma_kernel(GemmArgs p) {
   }
 
   };
-  // ---- ping-pong pipeline (8 waves, bf16): the two groups of 4 waves (one wave
-  // of each group per SIMD) run offset by one barrier phase.  In its memory
-  // phase a wave reads all fragments of the next K tile from LDS and issues its
-  // share of a later tile's DMA; in its compute phase it runs the MFMAs from
+  // ---- ping-pong (8 waves, bf16): the two groups of 4 waves (one wave of each
+  // group per SIMD) run offset by one barrier phase.  In a memory phase a wave
+  // reads the fragments of half a K tile (32 deep) from LDS and issues its share
+  // of a later tile's DMA; in a compute phase it runs that half tile's MFMAs from
   // registers only.  While one group computes, the other loads, so each SIMD's
-  // matrix pipe alternates between its two waves.
-  //   phase 2m   : group 0 loads tile m,     group 1 computes tile m-1
-  //   phase 2m+1 : group 0 computes tile m,  group 1 loads tile m
-  // Stage m % NS is read in phases 2m and 2m+1; the DMA issued in the memory
-  // phase of tile m fills the stage of tile m-1, which both groups are done with.
-  // The scheduler may not move anything (MFMAs included) across a phase boundary.
+  // matrix pipe alternates between its two waves.  The scheduler may not move
+  // anything (MFMAs included) across a phase boundary.
   auto phase_barrier = [] {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // ---- ping-pong pipeline with register-staged loads (8 waves, bf16).
-  // The two groups of 4 waves (one wave of each group per SIMD) run offset by
-  // one barrier phase: in a memory phase a wave reads the fragments of the next
-  // half K tile (32 deep) from LDS; in a compute phase it runs that half tile's
-  // MFMAs from registers only.  While one group computes, the other loads, so each
-  // SIMD's matrix pipe alternates between its two waves.  Half tile h is loaded by
-  // group 0 in phase 2h and group 1 in phase 2h+1, and computed one phase later.
-  // Global -> LDS: each wave stages its 1/8 of a 64-deep K tile (8 KB: 8 loads
-  // of 16 bytes per lane over 128-byte row segments) in registers.  In the memory
-  // phase of the first half of tile j a wave writes its staged share of tile j+1
-  // into the other LDS stage (last read for tile j-1, one phase earlier) and
-  // issues the global loads of tile j+2, which then have four phases to land.
-  auto pingpong_reg = [&](auto live_tag) {
+  // 64-deep K tiles in 2 LDS stages; 64-deep so each DMA lane fetches 16 bytes of
+  // a 128-byte row piece and an instruction covers whole cache lines (32-deep
+  // tiles in more stages halve the pieces and cost L2 bandwidth).  Each K tile
+  // takes four phases: group 0 reads half 0 of tile t in phase 4t and
+  // half 1 in phase 4t+2, computing each in the next phase; group 1 runs one phase
+  // behind.  The stage of tile t-1 is free once group 1 has read its half 1
+  // (phase 4t-1): group 1 issues its share of tile t+1 right after those reads,
+  // group 0 at the start of phase 4t.  Each wave waits for its own share in its
+  // last phase before phase 4t+4, where tile t+1 is first read (group 0 at the
+  // end of its compute phase 4t+3, group 1 at the end of its memory phase 4t+3);
+  // the barrier closing phase 4t+3 makes every share visible.
+  auto pingpong_dma64 = [&](auto live_tag) {
     constexpr bool LIVE = decltype(live_tag)::value;
-    constexpr int NLA = A_BYTES / 1024 / NW, NLB = B_BYTES / 1024 / NW;  // 16-byte loads per lane
     const int grp = wave >> 2;
-    // Global offsets (no swizzle) and LDS destinations (swizzled) of this lane's
-    // chunks.  Load i covers tile rows (wave*NL + i)*8 + lane/8, chunk lane%8.  Row
-    // bits 0-2 come from the lane and bit 3 is i & 1, so the LDS destination of
-    // load i is one of two bases plus i KiB; B rows of one wave stay in one
-    // half (gate or up), so B load i is load 0 plus i*8 weight rows.
-    static_assert(NLA % 2 == 0 && NLB % 2 == 0, "two LDS bases");
-    uint32_t ga[NLA];
-#pragma unroll
-    for (int i = 0; i < NLA; ++i) {
-      const int r = (wave * NLA + i) * 8 + (lane >> 3);
-      const int64_t grow = m0 + r;
-      const int slot = (pad_map && grow < p.M) ? pad_map[grow] : 0;
-      int64_t tok;
-      if (p.a_rows) tok = slot >= 0 ? slot / p.row_div : 0;
-      else tok = grow < p.M ? grow : p.M - 1;
-      ga[i] = (grow >= m_rows || slot < 0) ? 0x80000000u : (uint32_t)(tok * p.lda * 2) + ((lane & 7) << 4);
+    const DmaPlan dp = dma_plan();
+    Frags f[2];
+    issue_dma(dp, 0, 0);
+    if (grp == 1) {
+      issue_dma(dp, 1, 1);
+      wait_vmcnt<D_TILE>();  // this wave's part of tile 0
+    } else {
+      wait_vmcnt<0>();
     }
-    const int r0 = wave * NLA * 8 + (lane >> 3);  // bit 3 of r0 is 0 (wave*NLA*8 is a multiple of 16)
-    const int la0 = r0 * A_ROW + (((lane & 7) ^ lds_swz<A_ROW>(r0)) << 4);
-    const int la1 = (r0 + 8) * A_ROW + (((lane & 7) ^ lds_swz<A_ROW>(r0 + 8)) << 4) - 1024;
-    const int q0 = wave * NLB * 8 + (lane >> 3);
-    const int lb0 = q0 * B_ROW + (((lane & 7) ^ lds_swz<B_ROW>(q0)) << 4);
-    const int lb1 = (q0 + 8) * B_ROW + (((lane & 7) ^ lds_swz<B_ROW>(q0 + 8)) << 4) - 1024;
-    int brow0;
-    if constexpr (GATED) brow0 = q0 - (lane >> 3) < BN / 2 ? n0 + (q0 - (lane >> 3)) : p.N + n0 + (q0 - (lane >> 3) - BN / 2);
-    else brow0 = n0 + (q0 - (lane >> 3));
-    const uint32_t gb0 = (uint32_t)((int64_t)(brow0 + (lane >> 3)) * p.Kdim * 2) + ((lane & 7) << 4);
-    const uint32_t gb_step = (uint32_t)(8 * p.Kdim * 2);  // 8 weight rows
-    u32x4 sa[NLA], sbv[NLB];
-    auto gload = [&](int kt) {
-      const bool live = kt < nk;
-#pragma unroll
-      for (int i = 0; i < NLA; ++i)
-        sa[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              rsA, live ? ga[i] : 0x80000000u, live ? (kt0 + kt) * A_ROW : 0, 0));
-#pragma unroll
-      for (int i = 0; i < NLB; ++i)
-        sbv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               rsB, live ? gb0 : 0x80000000u, live ? (kt0 + kt) * B_ROW + i * gb_step : 0, 0));
-    };
-    auto lds_store = [&](int stage) {
-      uint8_t* st = smem + stage * STAGE;
-#pragma unroll
-      for (int i = 0; i < NLA; ++i) *(u32x4*)(st + ((i & 1) ? la1 : la0) + i * 1024) = sa[i];
-#pragma unroll
-      for (int i = 0; i < NLB; ++i) *(u32x4*)(st + A_BYTES + ((i & 1) ? lb1 : lb0) + i * 1024) = sbv[i];
-    };
-    bf16x8 fa[TM][2];
-    u32x4 fb[TN][2];
-    // prologue: tile 0 into stage 0, tile 1 in flight
-    gload(0);
-    wait_vmcnt<0>();
-    lds_store(0);
-    gload(1);
-    wait_lgkmcnt0();
     phase_barrier();
     if (grp == 1) phase_barrier();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int st = kt & 1;
+    for (int t = 0; t < nk; ++t) {
+      const int st = t & 1;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         // memory phase
-        if (hh == 0) {
-          wait_vmcnt<0>();    // staged share of tile kt+1 has landed
-          lds_store(st ^ 1);  // the stage of tile kt-1: both groups are done with it
-          gload(kt + 2);
-        }
+        if (hh == 0 && grp == 0 && t + 1 < nk) issue_dma(dp, t + 1, st ^ 1);
         if constexpr (LIVE) {
-          const uint8_t* sa0 = smem + st * STAGE;
-          const uint8_t* sb0 = sa0 + A_BYTES;
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            const int c = 2 * (2 * hh + s2) + hsel;
-#pragma unroll
-            for (int i = 0; i < TM; ++i) fa[i][s2] = *(const bf16x8*)(sa0 + a_row_off[i] + ((c ^ swa) << 4));
-#pragma unroll
-            for (int j = 0; j < TN; ++j) fb[j][s2] = *(const u32x4*)(sb0 + b_row_off[j] + ((c ^ swb) << 4));
-          }
+          load_frags(st, 2 * hh, f[0]);
+          load_frags(st, 2 * hh + 1, f[1]);
         }
-        wait_lgkmcnt0();  // fragments in registers; this wave's LDS writes done
+        wait_lgkmcnt0();
+        if (hh == 1 && grp == 1) {
+          wait_vmcnt<0>();                           // own share of tile t+1 has landed
+          if (t + 2 < nk) issue_dma(dp, t + 2, st);  // every wave is done with tile t
+        }
         phase_barrier();
         // compute phase
         if constexpr (LIVE) {
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-              const bf16x8 bj = __builtin_bit_cast(bf16x8, fb[j][s2]);
-#pragma unroll
-              for (int i = 0; i < TM; ++i)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bj, fa[i][s2], acc[i][j], 0, 0, 0);
-            }
+          mfmas(f[0]);
+          mfmas(f[1]);
         }
+        if (hh == 1 && grp == 0) wait_vmcnt<0>();  // own share of tile t+1 has landed
         phase_barrier();
       }
     }
     if (grp == 0) phase_barrier();  // same barrier count in both groups
   };
 
-  if constexpr (PPR) {
-    if (wave_live) pingpong_reg(std::true_type{});
-    else pingpong_reg(std::false_type{});
+  if constexpr (PP) {
+    if (wave_live) pingpong_dma64(std::true_type{});
+    else pingpong_dma64(std::false_type{});
   } else {
     if (wave_live) pipeline(std::true_type{});
     else pipeline(std::false_type{});
@@ -590,7 +540,7 @@ void gemm_mfma_kernel(GemmArgs p) {
         }
       }
     } else {
-      float* C = (float*)p.C + grow * p.ldc;
+      float* C = (float*)p.C + ((int64_t)ks * p.M + grow) * p.ldc;  // part ks's plane of [KS, M, ldc]
       const float f = rs * p.c_scale;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
@@ -730,7 +680,7 @@ static hipError_t run_mfma(const GemmArgs& a, hipStream_t s) {
   constexpr int THREADS = 64 * WAVES_M * WAVES_N;
   const int64_t mb_cap = (a.M + BM - 1) / BM;
   const int64_t nb = (a.N + NCOLS - 1) / NCOLS;
-  const int64_t tiles = mb_cap * nb;  // upper bound; the kernel counts the real ones
+  const int64_t tiles = mb_cap * nb * a.k_splits;  // upper bound; the kernel counts the real ones
   if (tiles <= 0) return hipSuccess;
   auto kern = gemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, EPI, BELEM>;
   static int per_cu = 0;  // resident blocks per CU for this instantiation
@@ -788,8 +738,19 @@ int gemm_scatter_k_splits(int64_t rows, int block_m, int N, int Kdim) {
   return best;
 }
 
+// Reduction parts for a store GEMM over identity rows (the router): enough tiles
+// for about two per CU, each part keeping at least 8 K tiles of 32.
+int gemm_store_k_splits(int64_t M, int N, int Kdim) {
+  if (M <= 0 || N <= 0) return 1;
+  const int64_t tiles = (M + 127) / 128 * ((N + (N <= 64 ? 63 : 127)) / (N <= 64 ? 64 : 128));
+  int ks = (int)((2 * device_cu_count() + tiles - 1) / tiles);
+  ks = ks < 1 ? 1 : (ks > 8 ? 8 : ks);
+  while (ks > 1 && (Kdim / 32) / ks < 8) --ks;
+  return ks;
+}
+
 hipError_t launch_gemm_mfma(const GemmArgs& a, int epi, int belem, int block_m, hipStream_t s) {
-  if (a.k_splits < 1 || (a.k_splits > 1 && epi != EPI_SCATTER && epi != EPI_SCATTER_F32)) return hipErrorInvalidValue;
+  if (a.k_splits < 1 || (a.k_splits > 1 && epi == EPI_GATED)) return hipErrorInvalidValue;
   if (epi == EPI_STORE_F32) {
     if (belem != ELEM_BF16) return hipErrorInvalidValue;
     if (block_m == 128) {

@@ -6,8 +6,11 @@
 
 namespace moe {
 
+// logits: nparts planes of [T, E] (part_stride elements apart) summed in order;
+// with more than one part, sum_out (if not NULL) receives the summed logits.
 hipError_t launch_route(const float* logits, int64_t T, int E, int K, int renorm, const float* pes,
-                        float* w_out, int32_t* ids_out, int out_stride, int n_shared, hipStream_t s);
+                        float* w_out, int32_t* ids_out, int out_stride, int n_shared, hipStream_t s,
+                        int nparts = 1, int64_t part_stride = 0, float* sum_out = nullptr);
 
 hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int bm_log2, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_slots, int32_t* block_expert,
@@ -46,8 +49,9 @@ struct GemmArgs {
   const float* row_scale;     // per-token factor on the accumulator (gated: on g and u; store:
                               // on the value), indexed by the A row's token; NULL = 1
   float c_scale = 1.f;        // constant factor on stored values (store epilogue)
-  int32_t k_splits = 1;       // scatter epilogues (MFMA kernel): the reduction is cut into this many
-                              // parts, each stored to its own row; other epilogues need 1
+  int32_t k_splits = 1;       // MFMA kernel, scatter and store epilogues: the reduction is cut into
+                              // this many parts, each stored to its own row (scatter: row slot*KS+part)
+                              // or plane (store: C[part][row]); the gated epilogue needs 1
 };
 
 // bf16 A; B bf16 or FP8 (ELEM_BF16 / ELEM_FP8).  block_m in {32, 64, 128, 256}.
@@ -55,6 +59,7 @@ hipError_t launch_gemm_mfma(const GemmArgs& a, int epi, int belem, int block_m, 
 // Reduction parts for a grouped scatter GEMM of about `rows` rows: the count in
 // 1..4 that wastes least of the last round of tiles on this device's CUs.
 int gemm_scatter_k_splits(int64_t rows, int block_m, int N, int Kdim);
+int gemm_store_k_splits(int64_t M, int N, int Kdim);
 // fp32 A and B (the fp32 layer).  block_m = 64.
 hipError_t launch_gemm_f32(const GemmArgs& a, int epi, hipStream_t s);
 

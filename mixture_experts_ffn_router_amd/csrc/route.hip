@@ -28,13 +28,26 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
                                                     const float* __restrict__ pes,
                                                     float* __restrict__ w_out,
                                                     int32_t* __restrict__ ids_out, int out_stride,
-                                                    int n_shared) {
+                                                    int n_shared, int nparts, int64_t part_stride,
+                                                    float* __restrict__ sum_out) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // uniform per wave
+  // the logits of token t: partial sums of the router GEMM's reduction parts, in part order
+  TokenLogits<VPL> z = load_logits<VPL>(logits + t * (int64_t)E, E, lane);
+  for (int q = 1; q < nparts; ++q) {
+    const TokenLogits<VPL> zq = load_logits<VPL>(logits + q * part_stride + t * (int64_t)E, E, lane);
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) z.v[j] += zq.v[j];
+  }
+  if (sum_out && nparts > 1) {
+#pragma unroll
+    for (int j = 0; j < VPL; ++j)
+      if (lane + 64 * j < E) sum_out[t * (int64_t)E + lane + 64 * j] = z.v[j];
+  }
   float w;
   int id;
-  route_token<VPL>(logits + t * (int64_t)E, E, K, renorm, pes, lane, w, id);
+  route_logits<VPL>(z, E, K, renorm, pes, lane, w, id);
   int64_t o = t * (int64_t)out_stride + lane;
   if (lane < K) {
     w_out[o] = w;
@@ -47,17 +60,17 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 
 hipError_t launch_route(const float* logits, int64_t T, int E, int K, int renorm, const float* pes,
                         float* w_out, int32_t* ids_out, int out_stride, int n_shared,
-                        hipStream_t s) {
+                        hipStream_t s, int nparts, int64_t part_stride, float* sum_out) {
   if (T == 0) return hipSuccess;
   dim3 grid((unsigned)((T + 3) / 4)), block(256);
   if (E <= 64)
-    route_kernel<1><<<grid, block, 0, s>>>(logits, T, E, K, renorm, pes, w_out, ids_out, out_stride, n_shared);
+    route_kernel<1><<<grid, block, 0, s>>>(logits, T, E, K, renorm, pes, w_out, ids_out, out_stride, n_shared, nparts, part_stride, sum_out);
   else if (E <= 128)
-    route_kernel<2><<<grid, block, 0, s>>>(logits, T, E, K, renorm, pes, w_out, ids_out, out_stride, n_shared);
+    route_kernel<2><<<grid, block, 0, s>>>(logits, T, E, K, renorm, pes, w_out, ids_out, out_stride, n_shared, nparts, part_stride, sum_out);
   else if (E <= 256)
-    route_kernel<4><<<grid, block, 0, s>>>(logits, T, E, K, renorm, pes, w_out, ids_out, out_stride, n_shared);
+    route_kernel<4><<<grid, block, 0, s>>>(logits, T, E, K, renorm, pes, w_out, ids_out, out_stride, n_shared, nparts, part_stride, sum_out);
   else
-    route_kernel<8><<<grid, block, 0, s>>>(logits, T, E, K, renorm, pes, w_out, ids_out, out_stride, n_shared);
+    route_kernel<8><<<grid, block, 0, s>>>(logits, T, E, K, renorm, pes, w_out, ids_out, out_stride, n_shared, nparts, part_stride, sum_out);
   return hipGetLastError();
 }
 

@@ -87,6 +87,11 @@ SMALL = {
     # 256-row blocks; few row blocks and a long down reduction: the down GEMM splits
     # its reduction in parts
     "bf16_bm256_down_split": W.LayerSpec("bf16_ksplit", 2048, 256, 2, 1, 4096, "silu", "bf16"),
+    # H = 1024: the router GEMM splits its reduction into partial logit planes
+    # that the route kernel sums
+    "bf16_router_split": W.LayerSpec("bf16_rsplit", 200, 1024, 8, 2, 128, "silu", "bf16"),
+    "gemma_router_split": W.LayerSpec("gemma_rsplit", 150, 1024, 32, 4, 128, "gelu_tanh", "bf16",
+                                      router_mode="gemma", per_expert_scale="uniform", I_dense=128),
     "bf16_single_expert": W.LayerSpec("bf16_e1", 65, 128, 1, 1, 128, "gelu_tanh", "bf16"),
     "gemma_small": W.LayerSpec("gemma_small", 333, 256, 16, 4, 128, "gelu_tanh", "bf16",
                                router_mode="gemma", per_expert_scale="uniform", I_dense=192,
