@@ -139,6 +139,29 @@ def stage_work(spec, T, counts, path, dense_stage=None):
     return fl, by
 
 
+def launched_stages(spec, path, dense_stage, raw_ms, marker_ms):
+    """The library stages that launch work for this layer (the others hold only
+    their event record)."""
+    supplied, dense = spec.supplied_logits, spec.I_dense > 0
+    if path == "decode":
+        st = {"gate_up", "down"}
+        if not supplied or (dense and dense_stage == "router"):
+            st.add("router")
+        # finalize: with the dense branch, or when the down kernel splits its
+        # reduction (chosen inside the library from the device's CU count)
+        if dense or raw_ms["finalize"] > marker_ms + 1e-3:
+            st.add("finalize")
+        return st
+    st = {"route", "permute", "gate_up", "down", "finalize"}
+    if (spec.router_mode == "gemma" and not supplied) or dense:
+        st.add("prenorm")
+    if not supplied:
+        st.add("router")
+    if dense:
+        st |= {"dense_gate_up", "dense_down"}
+    return st
+
+
 def rotated_sets(B, dl, path):
     """Copies of the layer with the experts rolled along the expert axis, enough
     that the weights a decode step reads were not read by the previous step."""
@@ -281,7 +304,8 @@ def main():
         b_.record()
     torch.cuda.synchronize()
     marker_ms = sorted(a_.elapsed_time(b_) for a_, b_ in pairs)[len(pairs) // 2]
-    stage_ms = {k: (v if v > marker_ms * 1.5 else 0.0) for k, v in raw_ms.items()}  # empty stages: 0
+    launched = launched_stages(spec, path, dl.dense_gate_up_stage(T), raw_ms, marker_ms)
+    stage_ms = {k: (v if k in launched else 0.0) for k, v in raw_ms.items()}  # empty stages: 0
 
     fl, by = stage_work(spec, T, counts, path, dl.dense_gate_up_stage(T))
     total_flop = sum(fl.values())

@@ -9,12 +9,12 @@
 //
 // bf16 MFMA kernel (v_mfma_f32_32x32x16_bf16), 4 or 8 waves:
 //   * BM x BN output tile; every operand tile reaches LDS through buffer loads
-//     that write LDS directly (no staging registers).  8 waves with bf16 weights
-//     ping-pong over 64-deep K tiles in 2 stages (see pingpong_dma64).  Otherwise
-//     a software pipeline: K tiles of 32 (bf16) in 4 LDS stages, or 64 (fp8
-//     weights) in 3; tiles kt+1 .. kt+NS-1 are in flight while tile kt computes,
-//     and the waits are explicit vmcnt counts, so only the oldest tile is waited
-//     for.  Buffer resources bound each operand, so a load past the end returns 0.
+//     that write LDS directly (no staging registers), in K tiles of 64.  8 waves
+//     ping-pong over 2 stages (see pingpong_dma64).  4 waves run a software
+//     pipeline over up to 4 stages: tiles kt+1 .. kt+NS-1 are in flight while
+//     tile kt computes, and the waits are explicit vmcnt counts, so only the
+//     oldest tile is waited for.  Buffer resources bound each operand, so a load
+//     past the end returns 0.
 //   * LDS rows of 64 / 128 bytes; the 16-byte chunk index is XORed with a
 //     function of the row so the 16 lanes of each ds_read_b128 phase hit
 //     distinct banks.
@@ -133,12 +133,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N)
 __attribute__((amdgpu_waves_per_eu(WAVES_M * WAVES_N / 4, WAVES_M * WAVES_N / 4)))
 void gemm_mfma_kernel(GemmArgs p) {
   constexpr bool FP8 = BELEM == ELEM_FP8;
-  // All operands reach LDS by DMA (buffer_load ... lds).  8 waves, bf16: ping-pong
-  // over 64-deep K tiles in 2 stages.  Otherwise a software pipeline: bf16 32-deep
-  // K tiles in 4 stages; fp8 weights 64-deep in 3.
-  constexpr bool PP = WAVES_M * WAVES_N == 8 && BELEM == ELEM_BF16;
-  constexpr int BK = (PP || BELEM == ELEM_FP8) ? 64 : 32;
-  constexpr int NS = PP ? 2 : (BELEM == ELEM_FP8 ? 3 : 4);
+  // All operand tiles reach LDS by DMA (buffer_load ... lds) in 64-deep K tiles,
+  // so each lane fetches 16 bytes of a 128-byte bf16 row piece (fp8: 64-byte
+  // pieces) and an instruction covers whole cache lines.  8 waves: ping-pong in
+  // 2 stages.  4 waves: software pipeline in up to 4 stages (as many as fit).
+  constexpr bool PP = WAVES_M * WAVES_N == 8;
+  constexpr int BK = 64;
+  constexpr int STAGE_B = BM * BK * 2 + BN * BK * BTraits<BELEM>::ELEM_BYTES;
+  constexpr int NS = PP ? 2 : (160 * 1024 / STAGE_B < 4 ? 160 * 1024 / STAGE_B : 4);
+  static_assert(PP || NS >= 3, "the pipeline keeps at least two tiles in flight");
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr bool GATED = EPI == EPI_GATED;
@@ -350,42 +353,55 @@ void gemm_mfma_kernel(GemmArgs p) {
     };
   constexpr int R_SUB = TM * NA + TN;             // LDS reads per sub-step
   constexpr int M_SUB = TM * TN * (FP8 ? 2 : 1);  // MFMAs per sub-step
+  constexpr int SUBS = BK / (FP8 ? 32 : 16);      // sub-steps per K tile
+  static_assert(SUBS == 2 || SUBS == 4, "2 or 4 sub-steps");
 #pragma unroll
   for (int t = 0; t < NS - 1; ++t) issue_dma(dp, t, t);
   wait_vmcnt<(NS - 2) * D_TILE>();  // this wave's part of tile 0
   __builtin_amdgcn_s_barrier();      // everyone's part of tile 0
-  Frags f0, f1;
-  load_frags_l(0, 0, f0);
+  Frags f[2];
+  load_frags_l(0, 0, f[0]);
   int buf = 0;
   for (int kt = 0; kt < nk; ++kt) {
     const int nbuf = buf + 1 == NS ? 0 : buf + 1;
-    // Refill the stage that held tile kt-1: every wave finished reading it
-    // before the barrier of the previous iteration.
-    // Sub-step 0 fragments were read half a tile ago; waiting for them here
-    // (before new reads) keeps the wait from covering the reads issued next.
-    wait_lgkmcnt0();
-    // Sub-step 1 fragments first: they have all of sub-step 0 to land, so the
-    // lgkmcnt wait before the barrier finds them done.
-    load_frags_l(buf, 1, f1);
-    issue_dma(dp, kt + NS - 1, buf == 0 ? NS - 1 : buf - 1);
-    mfmas_l(f0);
+    // Sub-step s < SUBS-1: read the fragments of sub-step s+1 while the MFMAs of
+    // sub-step s run.  Sub-step s's fragments were read a sub-step ago; waiting
+    // for them first (before new reads) keeps the wait from covering the reads
+    // issued next.  Sub-step 0 also refills the stage that held tile kt-1: every
+    // wave finished reading it before the barrier of the previous iteration.
+    auto sub_step = [&](auto s_c) {
+      constexpr int S = decltype(s_c)::value;
+      wait_lgkmcnt0();
+      load_frags_l(buf, S + 1, f[(S + 1) & 1]);
+      if constexpr (S == 0) issue_dma(dp, kt + NS - 1, buf == 0 ? NS - 1 : buf - 1);
+      mfmas_l(f[S & 1]);
+      // issue order: the reads, then the MFMAs (with the DMAs between the first
+      // of them in sub-step 0)
+      __builtin_amdgcn_sched_group_barrier(0x100, R_SUB, 0);   // DS read
+      if constexpr (S == 0) {
+#pragma unroll
+        for (int q = 0; q < D_TILE; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM (LDS DMA)
+        }
+        if (M_SUB > D_TILE) __builtin_amdgcn_sched_group_barrier(0x008, M_SUB - D_TILE, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, M_SUB, 0);
+      }
+    };
+    sub_step(std::integral_constant<int, 0>{});
+    if constexpr (SUBS == 4) {
+      sub_step(std::integral_constant<int, 1>{});
+      sub_step(std::integral_constant<int, 2>{});
+    }
     // Own reads of tile kt done and own DMA of tile kt+1 landed; the barrier
     // extends both to every wave.  Tiles kt+2 .. kt+NS-1 stay in flight.
     wait_lgkmcnt0();
     wait_vmcnt<(NS - 2) * D_TILE>();
     __builtin_amdgcn_s_barrier();
-    load_frags_l(nbuf, 0, f0);
-    mfmas_l(f1);
-    // Issue order: sub-step 1 reads; sub-step 0 MFMAs with the DMAs between the
-    // first of them; [barrier]; next tile's sub-step 0 reads between the first
-    // sub-step 1 MFMAs.
-    __builtin_amdgcn_sched_group_barrier(0x100, R_SUB, 0);   // DS read
-#pragma unroll
-    for (int q = 0; q < D_TILE; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // VMEM (LDS DMA)
-    }
-    if (M_SUB > D_TILE) __builtin_amdgcn_sched_group_barrier(0x008, M_SUB - D_TILE, 0);
+    // last sub-step, with the next tile's sub-step 0 reads between its MFMAs
+    load_frags_l(nbuf, 0, f[0]);
+    mfmas_l(f[1]);
 #pragma unroll
     for (int q = 0; q < R_SUB; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -396,11 +412,12 @@ void gemm_mfma_kernel(GemmArgs p) {
   }
 
   };
-  // ---- ping-pong (8 waves, bf16): the two groups of 4 waves (one wave of each
+  // ---- ping-pong (8 waves): the two groups of 4 waves (one wave of each
   // group per SIMD) run offset by one barrier phase.  In a memory phase a wave
   // reads the fragments of half a K tile (32 deep) from LDS and issues its share
   // of a later tile's DMA; in a compute phase it runs that half tile's MFMAs from
-  // registers only.  While one group computes, the other loads, so each SIMD's
+  // registers only (fp8 weights: with their conversion to bf16).  While one group
+  // computes, the other loads, so each SIMD's
   // matrix pipe alternates between its two waves.  The scheduler may not move
   // anything (MFMAs included) across a phase boundary.
   auto phase_barrier = [] {
@@ -409,9 +426,8 @@ void gemm_mfma_kernel(GemmArgs p) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // 64-deep K tiles in 2 LDS stages; 64-deep so each DMA lane fetches 16 bytes of
-  // a 128-byte row piece and an instruction covers whole cache lines (32-deep
-  // tiles in more stages halve the pieces and cost L2 bandwidth).  Each K tile
+  // 64-deep K tiles in 2 LDS stages (32-deep tiles in more stages would halve
+  // the row pieces each DMA lane fetches and cost L2 bandwidth).  Each K tile
   // takes four phases: group 0 reads half 0 of tile t in phase 4t and
   // half 1 in phase 4t+2, computing each in the next phase; group 1 runs one phase
   // behind.  The stage of tile t-1 is free once group 1 has read its half 1
@@ -434,6 +450,7 @@ void gemm_mfma_kernel(GemmArgs p) {
     }
     phase_barrier();
     if (grp == 1) phase_barrier();
+    constexpr int SPH = BK / (FP8 ? 32 : 16) / 2;  // sub-steps per half tile
     for (int t = 0; t < nk; ++t) {
       const int st = t & 1;
 #pragma unroll
@@ -441,8 +458,8 @@ void gemm_mfma_kernel(GemmArgs p) {
         // memory phase
         if (hh == 0 && grp == 0 && t + 1 < nk) issue_dma(dp, t + 1, st ^ 1);
         if constexpr (LIVE) {
-          load_frags(st, 2 * hh, f[0]);
-          load_frags(st, 2 * hh + 1, f[1]);
+#pragma unroll
+          for (int q = 0; q < SPH; ++q) load_frags(st, SPH * hh + q, f[q]);
         }
         wait_lgkmcnt0();
         if (hh == 1 && grp == 1) {
@@ -452,8 +469,8 @@ void gemm_mfma_kernel(GemmArgs p) {
         phase_barrier();
         // compute phase
         if constexpr (LIVE) {
-          mfmas(f[0]);
-          mfmas(f[1]);
+#pragma unroll
+          for (int q = 0; q < SPH; ++q) mfmas(f[q]);
         }
         if (hh == 1 && grp == 0) wait_vmcnt<0>();  // own share of tile t+1 has landed
         phase_barrier();
