@@ -116,14 +116,20 @@ __global__ __launch_bounds__(NT) void finalize_kernel(const TY* __restrict__ ybu
   const int ng = H / 8;
   float m[G][8];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const int idx = threadIdx.x + g * NT;
+  for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int q = 0; q < 8; ++q) m[g][q] = 0.f;
-    if (idx < ng) {
-      for (int j = 0; j < Kp; ++j) {  // slot order
+  // Sum in slot order; the slot loop is outside so one slot's loads for all of
+  // this thread's groups (and, unrolled, the next slots') are in flight together.
+#pragma unroll 4
+  for (int j = 0; j < Kp; ++j) {
+    const TY* yr = ybuf + (t * Kp + j) * H;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int idx = threadIdx.x + g * NT;
+      if (idx < ng) {
         float v[8];
-        ld8(ybuf + (t * Kp + j) * H + idx * 8, v);
+        ld8(yr + idx * 8, v);
 #pragma unroll
         for (int q = 0; q < 8; ++q) m[g][q] += v[q];
       }

@@ -6,8 +6,9 @@
 // Two launches, one workgroup (16 waves) per expert in each:
 //   count:   expert e counts the slots whose id is e;
 //   scatter: expert e sums the padded sizes of experts < e to find its segment,
-//            then walks the ids in order, 4096 slots per step, and compacts the
-//            matching flat slot indices.  A thread owns 4 consecutive slots;
+//            then walks the ids in order, 4096 slots per step (the next step's
+//            ids loaded while this one is ranked), and compacts the matching
+//            flat slot indices.  A thread owns 4 consecutive slots;
 //            its rank inside the step is an exclusive prefix of per-thread
 //            match counts (0..4), taken from three ballots (one per bit of the
 //            count) and per-wave totals in LDS, so the order is deterministic
@@ -32,15 +33,34 @@ __device__ __forceinline__ int block_sum_i32(int v, int* s_red) {
   return tot;
 }
 
+// ids f0 .. f0+3 (-1 past n, not read); one 16-byte load when the ids are
+// 16-byte aligned and all four exist.
+__device__ __forceinline__ int4 load_ids4(const int32_t* __restrict__ ids, int64_t n, int64_t f0, bool vec) {
+  if (vec && f0 + 3 < n) return *(const int4*)(ids + f0);
+  int4 r;
+  r.x = f0 < n ? ids[f0] : -1;
+  r.y = f0 + 1 < n ? ids[f0 + 1] : -1;
+  r.z = f0 + 2 < n ? ids[f0 + 2] : -1;
+  r.w = f0 + 3 < n ? ids[f0 + 3] : -1;
+  return r;
+}
+__device__ __forceinline__ uint32_t match4(int4 v, int e) {
+  return (uint32_t)(v.x == e) | ((uint32_t)(v.y == e) << 1) | ((uint32_t)(v.z == e) << 2) | ((uint32_t)(v.w == e) << 3);
+}
+
 __global__ __launch_bounds__(PERM_THREADS) void permute_count_kernel(const int32_t* __restrict__ ids,
-                                                                     int64_t n, int32_t* __restrict__ counts) {
+                                                                     int64_t n, int32_t* __restrict__ counts,
+                                                                     bool vec) {
   __shared__ int s_red[PERM_THREADS / 64];
   const int e = blockIdx.x;
   int c = 0;
-  for (int64_t f = (int64_t)threadIdx.x * 4; f < n; f += PERM_STEP) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (f + q < n && ids[f + q] == e) ++c;
+  // the next step's ids are loaded before this step's are counted
+  int64_t f = (int64_t)threadIdx.x * 4;
+  int4 cur = load_ids4(ids, n, f, vec);
+  for (; f < n; f += PERM_STEP) {
+    const int4 nxt = load_ids4(ids, n, f + PERM_STEP, vec);
+    c += __popc(match4(cur, e));
+    cur = nxt;
   }
   c = block_sum_i32(c, s_red);
   if (threadIdx.x == 0) counts[e] = c;
@@ -48,7 +68,8 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_count_kernel(const int32
 
 __global__ __launch_bounds__(PERM_THREADS) void permute_scatter_kernel(
     const int32_t* __restrict__ ids, int64_t n, int E, int bm_log2, const int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slots, int32_t* __restrict__ block_expert) {
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slots, int32_t* __restrict__ block_expert,
+    bool vec) {
   __shared__ int s_red[PERM_THREADS / 64];
   __shared__ int s_wtot[PERM_THREADS / 64];
   const int e = blockIdx.x;
@@ -68,12 +89,12 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_scatter_kernel(
 
   const uint64_t lt = (1ull << lane) - 1ull;
   int running = 0;
+  int4 cur = load_ids4(ids, n, (int64_t)tid * 4, vec);
   for (int64_t base = 0; base < n; base += PERM_STEP) {
     const int64_t f0 = base + (int64_t)tid * 4;
-    uint32_t bits = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (f0 + q < n && ids[f0 + q] == e) bits |= 1u << q;
+    const int4 nxt = load_ids4(ids, n, f0 + PERM_STEP, vec);  // next step, in flight meanwhile
+    const uint32_t bits = match4(cur, e);
+    cur = nxt;
     const int c = __popc(bits);
     const uint64_t b0 = __ballot(c & 1), b1 = __ballot(c & 2), b2 = __ballot(c & 4);
     const int wprefix = __popcll(b0 & lt) + 2 * __popcll(b1 & lt) + 4 * __popcll(b2 & lt);
@@ -99,11 +120,12 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_scatter_kernel(
 hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int bm_log2, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_slots, int32_t* block_expert,
                           hipStream_t s) {
-  permute_count_kernel<<<E, PERM_THREADS, 0, s>>>(ids, n, counts);
+  const bool vec = ((uintptr_t)ids & 15) == 0;
+  permute_count_kernel<<<E, PERM_THREADS, 0, s>>>(ids, n, counts, vec);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   permute_scatter_kernel<<<E, PERM_THREADS, 0, s>>>(ids, n, E, bm_log2, counts, offsets, sorted_slots,
-                                                    block_expert);
+                                                    block_expert, vec);
   return hipGetLastError();
 }
 
