@@ -164,7 +164,18 @@ void gemm_mfma_kernel(GemmArgs p) {
                 "stage must split into 1 KiB DMA instructions over the waves");
   static_assert(!GATED || ((BN / 2) % B_ROWS_PER_DMA == 0), "DMA groups must not straddle gate/up");
   static_assert(NS * STAGE <= 160 * 1024, "LDS");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+  constexpr int NCOLS_ = EPI == EPI_GATED ? BN / 2 : BN;
+  constexpr int EOESZ = (EPI == EPI_GATED || EPI == EPI_SCATTER) ? 2 : 4;
+  constexpr int EROWB = NCOLS_ * EOESZ + 4 * EOESZ;  // staged output row (padded)
+  constexpr int EPASS = (BM * (EROWB + 4) + 160 * 1024 - 1) / (160 * 1024);
+  constexpr int PROWS = BM / EPASS;
+  // staged rows + their output row indices (gated and fp32 scatter epilogues
+  // store directly)
+  constexpr int EPI_LDS = (EPI == EPI_GATED || EPI == EPI_SCATTER_F32) ? 0 : PROWS * EROWB + PROWS * 4;
+  static_assert(WAVES_M % EPASS == 0 && EPI_LDS <= 160 * 1024, "epilogue passes of whole wave rows");
+  constexpr int SMEM = NS * STAGE > EPI_LDS ? NS * STAGE : EPI_LDS;
+  constexpr int THREADS = 64 * WAVES_M * WAVES_N;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
@@ -489,12 +500,11 @@ void gemm_mfma_kernel(GemmArgs p) {
 
   // ---- epilogue.  acc[i][j][v]: row = m0 + wm*WM + 32i + l32,
   //      col (tile-local) = 8*(v/4) + 4*hsel + (v%4)
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int64_t grow = m0 + wm * WM + 32 * i + l32;
-    if (grow >= m_rows) continue;
-    if (!wave_live) continue;
+  // Per-row factors of the tile row grow: token factor (row_scale) and, for the
+  // scatter epilogue, the routing weight of its slot.
+  auto row_factor = [&](int64_t grow) {
     float rs = 1.f;
+    if (grow >= m_rows) return rs;  // past the rows: nothing is stored for it
     if (p.row_scale) {
       int64_t tok = grow;
       if (p.a_rows) {
@@ -503,9 +513,118 @@ void gemm_mfma_kernel(GemmArgs p) {
       }
       rs = p.row_scale[tok];
     }
-    if constexpr (GATED) {
+    if constexpr (EPI == EPI_SCATTER || EPI == EPI_SCATTER_F32) {
+      const int slot = p.c_rows[grow];
+      rs = (slot >= 0 && p.row_weight) ? p.row_weight[slot] : 1.f;
+    } else if constexpr (EPI == EPI_STORE_F32) {
+      rs *= p.c_scale;
+    }
+    return rs;
+  };
+  // The 4 output values of acc[i][j][4*g4 .. 4*g4+3] (j < TN/2 for gated)
+  // at tile-local column col, with factor rs.
+  auto out4 = [&](int i, int j, int g4, int col, float rs, float* v) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (GATED) {
+        constexpr int TH = TN / 2;
+        float gv = acc[i][j][4 * g4 + q] * rs, uv = acc[i][j + TH][4 * g4 + q] * rs;
+        if constexpr (FP8) {
+          gv *= bscale[n0 + col + q];
+          uv *= bscale[p.N + n0 + col + q];
+        }
+        v[q] = apply_act(p.act, gv) * uv;
+      } else {
+        v[q] = acc[i][j][4 * g4 + q] * rs;
+        if constexpr (FP8) v[q] *= bscale[n0 + col + q];
+      }
+    }
+  };
+  // Output row of tile row grow, or -1 when nothing is stored for it.
+  auto out_row = [&](int64_t grow) -> int64_t {
+    if (grow >= m_rows) return -1;
+    if constexpr (GATED) return (p.a_rows && p.a_rows[grow] < 0) ? -1 : grow;  // padding: never read back
+    else if constexpr (EPI == EPI_SCATTER || EPI == EPI_SCATTER_F32) {
+      const int slot = p.c_rows[grow];
+      return slot < 0 ? -1 : (int64_t)slot * KS + ks;  // the part's row of this slot
+    } else {
+      return (int64_t)ks * p.M + grow;  // part ks's plane of [KS, M, ldc]
+    }
+  };
+  constexpr int OESZ = (GATED || EPI == EPI_SCATTER) ? 2 : 4;  // output element bytes
+  constexpr int CPL = 16 / OESZ;                               // output elements per 16 bytes
+  // The bf16 scatter and the fp32 store epilogues stage their tile in LDS
+  // (below); it needs 16-byte aligned output rows and column groups: always so
+  // for the scatter epilogue (checked at launch), not for the router's logits
+  // (E columns).  The gated and fp32 scatter epilogues store directly (8 / 16
+  // bytes per lane, 16 / 32 contiguous bytes per row): staging them measured
+  // no faster.
+  bool staged = EPI == EPI_SCATTER || EPI == EPI_STORE_F32;
+  if constexpr (EPI == EPI_STORE_F32 && !PP)
+    staged = (p.N % CPL) == 0 && (p.ldc % CPL) == 0 && (((uintptr_t)p.C & 15) == 0);
+  if (staged) {
+    // Stage the tile's outputs in LDS, row-major (rows padded by 4 elements, so
+    // the 32 rows a fragment store spans hit distinct banks), then copy whole
+    // rows out with 16-byte stores on consecutive lanes: the MFMA layout would
+    // store 32 rows x 16-32 bytes per instruction.  Tiles larger than LDS go
+    // in passes of whole wave rows.
+    wait_vmcnt<0>();  // no DMA (zero fill past the last K tile) still writing LDS
+    __syncthreads();  // every wave done reading the pipeline's stages
+#pragma unroll 1
+    for (int pass = 0; pass < EPASS; ++pass) {
+      if (pass) __syncthreads();  // the previous pass's rows are copied out
+      if (wave_live && wm / (WAVES_M / EPASS) == pass) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int rl = wm * WM + 32 * i + l32 - pass * PROWS;  // row in this pass
+          const float rs = row_factor(m0 + wm * WM + 32 * i + l32);
+#pragma unroll
+          for (int j = 0; j < (GATED ? TN / 2 : TN); ++j) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const int col = (GATED ? wn * (WN / 2) : wn * WN) + 32 * j + 8 * g4 + 4 * hsel;
+              float v[4] = {0.f, 0.f, 0.f, 0.f};
+              if (n0 + col < p.N) out4(i, j, g4, col, rs, v);  // columns past N: not stored
+              uint8_t* d = smem + rl * EROWB + col * OESZ;
+              if constexpr (OESZ == 2) {
+                uint2 pk;
+                pk.x = pack_bf16x2(v[0], v[1]);
+                pk.y = pack_bf16x2(v[2], v[3]);
+                *(uint2*)d = pk;
+              } else {
+                *(float4*)d = make_float4(v[0], v[1], v[2], v[3]);
+              }
+            }
+          }
+        }
+      }
+      // output row of each staged row (one row-map lookup per row), kept in LDS
+      // after the staged rows
+      int32_t* s_orow = (int32_t*)(smem + PROWS * EROWB);
+      for (int r = tid; r < PROWS; r += THREADS) s_orow[r] = (int32_t)out_row(m0 + pass * PROWS + r);
+      __syncthreads();
+      constexpr int CHR = NCOLS * OESZ / 16;  // 16-byte chunks per row
+      for (int idx = tid; idx < PROWS * CHR; idx += THREADS) {
+        const int r = idx / CHR, c = idx - r * CHR;
+        const int col = n0 + c * CPL;
+        const int32_t orow = s_orow[r];
+        if (orow < 0 || col >= p.N) continue;
+        *(uint4*)((uint8_t*)p.C + ((int64_t)orow * p.ldc + col) * OESZ) = *(const uint4*)(smem + r * EROWB + c * 16);
+      }
+    }
+  } else if constexpr (GATED) {
+    // h = act(g) * u, 4 consecutive bf16 outputs (8 bytes) per lane and store
+    constexpr int TH = TN / 2;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int64_t grow = m0 + wm * WM + 32 * i + l32;
+      if (grow >= m_rows || !wave_live) continue;
       if (p.a_rows && p.a_rows[grow] < 0) continue;  // padding: never read back
-      constexpr int TH = TN / 2;
+      float rs = 1.f;
+      if (p.row_scale) {
+        const int slot = p.a_rows ? p.a_rows[grow] : 0;
+        rs = p.row_scale[p.a_rows ? slot / p.row_div : grow];
+      }
       bf16_t* C = (bf16_t*)p.C + grow * p.ldc;
 #pragma unroll
       for (int j = 0; j < TH; ++j) {
@@ -516,12 +635,12 @@ void gemm_mfma_kernel(GemmArgs p) {
           float h[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            float g = acc[i][j][4 * g4 + q] * rs, u = acc[i][j + TH][4 * g4 + q] * rs;
+            float gv = acc[i][j][4 * g4 + q] * rs, uv = acc[i][j + TH][4 * g4 + q] * rs;
             if constexpr (FP8) {
-              g *= bscale[col + q];
-              u *= bscale[p.N + col + q];
+              gv *= bscale[col + q];
+              uv *= bscale[p.N + col + q];
             }
-            h[q] = apply_act(p.act, g) * u;
+            h[q] = apply_act(p.act, gv) * uv;
           }
           uint2 pk;
           pk.x = pack_bf16x2(h[0], h[1]);
@@ -529,44 +648,34 @@ void gemm_mfma_kernel(GemmArgs p) {
           *(uint2*)(C + col) = pk;
         }
       }
-    } else if constexpr (EPI == EPI_SCATTER || EPI == EPI_SCATTER_F32) {
-      const int slot = p.c_rows[grow];
-      if (slot < 0) continue;
-      const float w = p.row_weight ? p.row_weight[slot] : 1.f;
-      const int64_t orow = (int64_t)slot * KS + ks;  // the part's row of this slot
+    }
+  } else if constexpr (EPI == EPI_SCATTER_F32 || (EPI == EPI_STORE_F32 && !PP)) {
+    // Direct fp32 stores: 4 consecutive outputs per lane (16 bytes) when the row
+    // is aligned for it (always for the scatter epilogue), else one element at
+    // a time (the router's logits).
+    const bool vec = EPI == EPI_SCATTER_F32 || ((p.N % 4) == 0 && (p.ldc % 4) == 0 && (((uintptr_t)p.C & 15) == 0));
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int64_t grow = m0 + wm * WM + 32 * i + l32;
+      const int64_t orow = wave_live ? out_row(grow) : -1;
+      if (orow < 0) continue;
+      const float rs = row_factor(grow);
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const int col = n0 + wn * WN + 32 * j + 8 * g4 + 4 * hsel;
-          if (col >= p.N) continue;
-          float y[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            y[q] = acc[i][j][4 * g4 + q] * w;
-            if constexpr (FP8) y[q] *= bscale[col + q];
-          }
-          if constexpr (EPI == EPI_SCATTER) {
-            uint2 pk;
-            pk.x = pack_bf16x2(y[0], y[1]);
-            pk.y = pack_bf16x2(y[2], y[3]);
-            *(uint2*)((bf16_t*)p.C + orow * p.ldc + col) = pk;
+          const int col = wn * WN + 32 * j + 8 * g4 + 4 * hsel;
+          if (n0 + col >= p.N) continue;
+          float v[4];
+          out4(i, j, g4, col, rs, v);
+          float* d = (float*)p.C + orow * p.ldc + n0 + col;
+          if (vec) {
+            *(float4*)d = make_float4(v[0], v[1], v[2], v[3]);
           } else {
-            *(float4*)((float*)p.C + orow * p.ldc + col) = make_float4(y[0], y[1], y[2], y[3]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (n0 + col + q < p.N) d[q] = v[q];
           }
-        }
-      }
-    } else {
-      float* C = (float*)p.C + ((int64_t)ks * p.M + grow) * p.ldc;  // part ks's plane of [KS, M, ldc]
-      const float f = rs * p.c_scale;
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int col = n0 + wn * WN + 32 * j + 8 * g4 + 4 * hsel;
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (col + q < p.N) C[col + q] = acc[i][j][4 * g4 + q] * f;
         }
       }
     }
@@ -768,6 +877,13 @@ int gemm_store_k_splits(int64_t M, int N, int Kdim) {
 
 hipError_t launch_gemm_mfma(const GemmArgs& a, int epi, int belem, int block_m, hipStream_t s) {
   if (a.k_splits < 1 || (a.k_splits > 1 && epi == EPI_GATED)) return hipErrorInvalidValue;
+  // Gated and scatter epilogues store groups of 4 or 8 consecutive outputs
+  // (8 or 16 bytes), and so does the store epilogue of 256-row blocks (possibly
+  // an 8-wave tile); the 4-wave store tiles of 64- and 128-row blocks also take
+  // unaligned outputs.
+  const int cpl = epi == EPI_GATED || epi == EPI_SCATTER ? 8 : 4;
+  const bool aligned = a.N % cpl == 0 && a.ldc % cpl == 0 && ((uintptr_t)a.C & 15) == 0;
+  if (!aligned && (epi != EPI_STORE_F32 || block_m == 256)) return hipErrorInvalidValue;
   if (epi == EPI_STORE_F32) {
     if (belem != ELEM_BF16) return hipErrorInvalidValue;
     if (block_m == 128) {

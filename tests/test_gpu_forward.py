@@ -98,6 +98,12 @@ SMALL = {
                                random_gammas=True),
     "gemma_small_i64": W.LayerSpec("gemma_i64", 130, 320, 16, 8, 192, "gelu_tanh", "bf16",
                                    router_mode="gemma", per_expert_scale="uniform", I_dense=128),
+    # dense branch -> fp32 per-slot rows; 256- and 128-row blocks stage the
+    # scatter epilogue's output tile in LDS in two passes
+    "gemma_dense_bm256": W.LayerSpec("gemma_bm256", 2048, 256, 2, 1, 256, "gelu_tanh", "bf16",
+                                     router_mode="gemma", per_expert_scale="uniform", I_dense=128),
+    "gemma_dense_bm128": W.LayerSpec("gemma_bm128", 600, 512, 4, 1, 128, "gelu_tanh", "bf16",
+                                     router_mode="gemma", per_expert_scale="uniform", I_dense=192),
     "deepseek_small": W.LayerSpec("deepseek_small", 200, 256, 8, 3, 128, "silu", "bf16",
                                   renorm=False, n_shared=2, I_shared=128),
     "fp8_small": W.LayerSpec("fp8_small", 257, 256, 16, 4, 192, "gelu_tanh", "fp8",
