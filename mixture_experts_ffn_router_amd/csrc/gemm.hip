@@ -443,7 +443,7 @@ void gemm_mfma_kernel(GemmArgs p) {
   // half 1 in phase 4t+2, computing each in the next phase; group 1 runs one phase
   // behind.  The stage of tile t-1 is free once group 1 has read its half 1
   // (phase 4t-1): group 1 issues its share of tile t+1 right after those reads,
-  // group 0 at the start of phase 4t.  Each wave waits for its own share in its
+  // group 0 in phase 4t, after its fragment reads.  Each wave waits for its own share in its
   // last phase before phase 4t+4, where tile t+1 is first read (group 0 at the
   // end of its compute phase 4t+3, group 1 at the end of its memory phase 4t+3);
   // the barrier closing phase 4t+3 makes every share visible.
@@ -466,12 +466,13 @@ void gemm_mfma_kernel(GemmArgs p) {
       const int st = t & 1;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        // memory phase
-        if (hh == 0 && grp == 0 && t + 1 < nk) issue_dma(dp, t + 1, st ^ 1);
+        // memory phase: fragment reads first, so they do not queue behind the
+        // DMA's LDS writes
         if constexpr (LIVE) {
 #pragma unroll
           for (int q = 0; q < SPH; ++q) load_frags(st, SPH * hh + q, f[q]);
         }
+        if (hh == 0 && grp == 0 && t + 1 < nk) issue_dma(dp, t + 1, st ^ 1);
         wait_lgkmcnt0();
         if (hh == 1 && grp == 1) {
           wait_vmcnt<0>();                           // own share of tile t+1 has landed
