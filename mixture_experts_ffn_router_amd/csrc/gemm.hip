@@ -439,14 +439,14 @@ void gemm_mfma_kernel(GemmArgs p) {
 
   // 64-deep K tiles in 2 LDS stages (32-deep tiles in more stages would halve
   // the row pieces each DMA lane fetches and cost L2 bandwidth).  Each K tile
-  // takes four phases: group 0 reads half 0 of tile t in phase 4t and
-  // half 1 in phase 4t+2, computing each in the next phase; group 1 runs one phase
-  // behind.  The stage of tile t-1 is free once group 1 has read its half 1
-  // (phase 4t-1): group 1 issues its share of tile t+1 right after those reads,
-  // group 0 in phase 4t, after its fragment reads.  Each wave waits for its own share in its
-  // last phase before phase 4t+4, where tile t+1 is first read (group 0 at the
-  // end of its compute phase 4t+3, group 1 at the end of its memory phase 4t+3);
-  // the barrier closing phase 4t+3 makes every share visible.
+  // takes four phases: group 0 reads half 0 of tile t in phase 4t and half 1 in
+  // phase 4t+2, computing each in the next phase; group 1 runs one phase behind.
+  // The stage of tile t-1 is free once group 1 has read its half 1 (phase
+  // 4t-1): group 1 issues its share of tile t+1 right after those reads, group 0
+  // in phase 4t, after its fragment reads.  Each wave waits for its own share in
+  // its last phase before phase 4t+4, where tile t+1 is first read (group 0 at
+  // the end of its compute phase 4t+3, group 1 at the end of its memory phase
+  // 4t+3); the barrier closing phase 4t+3 makes every share visible.
   auto pingpong_dma64 = [&](auto live_tag) {
     constexpr bool LIVE = decltype(live_tag)::value;
     const int grp = wave >> 2;
