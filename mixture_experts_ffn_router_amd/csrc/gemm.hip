@@ -822,15 +822,23 @@ static hipError_t run_mfma(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// A tile ncols output columns wide is worth it when its last column block idles
+// at most a tenth of N past N, and the tiles still number at least one per CU
+// (rows: the row capacity, an upper bound; times the reduction parts).
+static bool wide_fits(const GemmArgs& a, int block_m, int ncols) {
+  const int64_t N = a.N;
+  if (((N + ncols - 1) / ncols * ncols - N) * 10 > N) return false;
+  return (a.M + block_m - 1) / block_m * ((N + ncols - 1) / ncols) * a.k_splits >= (int64_t)device_cu_count();
+}
+
 template <int EPI, int BELEM>
 static hipError_t run_grouped(const GemmArgs& a, int block_m, hipStream_t s) {
   const int N = a.N;
   if (block_m == 256) {
-    if (EPI == EPI_GATED) {
-      if (N % 128 == 0) return run_mfma<256, 256, 4, 2, EPI, BELEM>(a, s);
-      return run_mfma<256, 128, 4, 1, EPI, BELEM>(a, s);
-    }
-    if (N % 256 == 0) return run_mfma<256, 256, 4, 2, EPI, BELEM>(a, s);
+    // 8-wave 256x256 tiles (gated: 128 output columns) unless they would idle
+    // too many columns; a ragged last column block reads zeros past the weights
+    // and stores nothing past N.
+    if (wide_fits(a, 256, EPI == EPI_GATED ? 128 : 256)) return run_mfma<256, 256, 4, 2, EPI, BELEM>(a, s);
     return run_mfma<256, 128, 4, 1, EPI, BELEM>(a, s);
   }
   if (block_m == 128) return run_mfma<128, 512, 2, 4, EPI, BELEM>(a, s);
