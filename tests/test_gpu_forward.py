@@ -112,6 +112,19 @@ SMALL = {
                                    supplied_logits=True),
     "fp8_small_bm256": W.LayerSpec("fp8_bm256", 2100, 256, 2, 1, 512, "gelu_tanh", "fp8",
                                    supplied_logits=True),
+    # limits and shape corners of the grouped path: the most experts (E=512: 4
+    # router column tiles, 8 logits per route lane, 512 permutation blocks), the
+    # widest rows (H=8192: router reduction in 8 parts of 32 K tiles, finalize at
+    # full width), every expert selected (k=E), logit rows that are not 16-byte
+    # aligned (E=6: the router's direct-store epilogue), and a dense gate/up wide
+    # enough for ragged 8-wave tiles (2112 = 16.5 x 128 output columns)
+    "bf16_e512": W.LayerSpec("bf16_e512", 200, 128, 512, 8, 64, "silu", "bf16"),
+    "bf16_h8192": W.LayerSpec("bf16_h8192", 300, 8192, 4, 2, 128, "silu", "bf16"),
+    "bf16_k_equals_e": W.LayerSpec("bf16_keqe", 100, 256, 4, 4, 128, "gelu_tanh", "bf16",
+                                   per_expert_scale="uniform"),
+    "bf16_e6": W.LayerSpec("bf16_e6", 150, 256, 6, 2, 128, "silu", "bf16"),
+    "gemma_dense_wide": W.LayerSpec("gemma_wide", 4096, 256, 2, 1, 128, "gelu_tanh", "bf16",
+                                    router_mode="gemma", per_expert_scale="uniform", I_dense=2112),
     "fp32_gemma_router": W.LayerSpec("fp32_gemma", 50, 128, 8, 3, 64, "gelu_tanh", "fp32",
                                      router_mode="gemma", I_dense=64, random_gammas=True),
 }
