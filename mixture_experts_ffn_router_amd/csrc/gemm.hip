@@ -24,7 +24,7 @@
 //   * A rows are gathered straight from x through the row map (no permuted copy
 //     of the activations); B rows come from the block's expert.
 //   * The MFMA is issued as B x A, so each lane's accumulator holds 4
-//     consecutive output columns of one row: epilogue stores are 8 bytes.
+//     consecutive output columns of one row (8- or 16-byte direct stores).
 //   * Gated epilogue: the B tile holds BN/2 gate rows (w1) and the matching
 //     BN/2 up rows (w3), so the gate and up accumulators of a lane cover the
 //     same (row, col); h = act(g) * u is formed in registers and stored bf16.
@@ -32,7 +32,9 @@
 //   * Scatter epilogue (down projection): y = acc * routing weight of the row's
 //     slot, stored (bf16, or fp32 when the branch is renormalised afterwards)
 //     at the slot's row of the per-slot buffer; pad rows are skipped.  The
-//     per-token sum happens in the finalize kernel in slot order.
+//     per-token sum happens in the finalize kernel in slot order.  The bf16
+//     scatter and the fp32 store epilogues stage the tile in LDS and copy whole
+//     rows out with 16-byte stores on consecutive lanes.
 //   * FP8 B (OCP E4M3 codes, W8A16): B rows are 64 bytes in LDS, widened to bf16
 //     in registers (exact), and the per-output-channel scale is applied in the
 //     epilogue: sum_k x_k (q_kn s_n) = s_n sum_k x_k q_kn.
@@ -52,12 +54,10 @@ template <int BELEM>
 struct BTraits;
 template <>
 struct BTraits<ELEM_BF16> {
-  static constexpr int ROW_BYTES = 128;  // 64 bf16
   static constexpr int ELEM_BYTES = 2;
 };
 template <>
 struct BTraits<ELEM_FP8> {
-  static constexpr int ROW_BYTES = 64;  // 64 fp8
   static constexpr int ELEM_BYTES = 1;
 };
 
@@ -164,9 +164,9 @@ void gemm_mfma_kernel(GemmArgs p) {
                 "stage must split into 1 KiB DMA instructions over the waves");
   static_assert(!GATED || ((BN / 2) % B_ROWS_PER_DMA == 0), "DMA groups must not straddle gate/up");
   static_assert(NS * STAGE <= 160 * 1024, "LDS");
-  constexpr int NCOLS_ = EPI == EPI_GATED ? BN / 2 : BN;
-  constexpr int EOESZ = (EPI == EPI_GATED || EPI == EPI_SCATTER) ? 2 : 4;
-  constexpr int EROWB = NCOLS_ * EOESZ + 4 * EOESZ;  // staged output row (padded)
+  constexpr int NCOLS = GATED ? BN / 2 : BN;  // output columns per block
+  constexpr int OESZ = (GATED || EPI == EPI_SCATTER) ? 2 : 4;  // output element bytes
+  constexpr int EROWB = NCOLS * OESZ + 4 * OESZ;  // staged output row (padded)
   constexpr int EPASS = (BM * (EROWB + 4) + 160 * 1024 - 1) / (160 * 1024);
   constexpr int PROWS = BM / EPASS;
   // staged rows + their output row indices (gated and fp32 scatter epilogues
@@ -180,11 +180,10 @@ void gemm_mfma_kernel(GemmArgs p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  constexpr int NCOLS = GATED ? BN / 2 : BN;  // output columns per block
   const int64_t m_rows = p.m_dev ? (int64_t)(*p.m_dev) : p.M;
   const int64_t mbn = (m_rows + BM - 1) / BM;  // row blocks holding rows
   const int64_t nb_cnt = (p.N + NCOLS - 1) / NCOLS;
-  const int KS = p.k_splits;  // reduction parts (scatter epilogues), the slowest tile index
+  const int KS = p.k_splits;  // reduction parts (scatter and store epilogues), the slowest tile index
   const int64_t ntiles = mbn * nb_cnt * KS;
   const bool xcd_map = gridDim.x % 8 == 0;
   const int64_t per_xcd = (ntiles + 7) / 8;
@@ -552,8 +551,7 @@ void gemm_mfma_kernel(GemmArgs p) {
       return (int64_t)ks * p.M + grow;  // part ks's plane of [KS, M, ldc]
     }
   };
-  constexpr int OESZ = (GATED || EPI == EPI_SCATTER) ? 2 : 4;  // output element bytes
-  constexpr int CPL = 16 / OESZ;                               // output elements per 16 bytes
+  constexpr int CPL = 16 / OESZ;  // output elements per 16 bytes
   // The bf16 scatter and the fp32 store epilogues stage their tile in LDS
   // (below); it needs 16-byte aligned output rows and column groups: always so
   // for the scatter epilogue (checked at launch), not for the router's logits
