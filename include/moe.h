@@ -126,7 +126,10 @@ typedef struct {
   float eps;             /* RMSNorm epsilon (router preprocessing and Gemma norms) */
 } moe_layer_desc;
 
-/* Tensors of one forward call (device pointers unless noted). */
+/* Tensors of one forward call (device pointers unless noted).  The matrix
+ * tensors (x, w_router, w13, w2, shared and dense weights, out, out_f32) must be
+ * 16-byte aligned, else MOE_INVALID_ARG; the vectors and routing outputs need
+ * only their element alignment. */
 typedef struct {
   const void* x;                  /* [T, H] act_dtype */
   const float* logits;            /* [T, E] fp32 router logits, or NULL: computed from x */

@@ -231,6 +231,16 @@ moe_status validate_tensors(const moe_layer_desc& d, const moe_tensors* t) {
     return fail(MOE_INVALID_ARG, "n_shared > 0 needs shared_w13 and shared_w2");
   if (d.inter_dense && (!t->dense_w13 || !t->dense_w2))
     return fail(MOE_INVALID_ARG, "inter_dense > 0 needs dense_w13 and dense_w2");
+  // Matrix operands are moved in 16-byte pieces (LDS DMA, vector loads and stores).
+  const struct {
+    const void* p;
+    const char* name;
+  } mats[] = {{t->x, "x"},          {t->w_router, "w_router"},     {t->w13, "w13"},
+              {t->w2, "w2"},        {t->shared_w13, "shared_w13"}, {t->shared_w2, "shared_w2"},
+              {t->dense_w13, "dense_w13"}, {t->dense_w2, "dense_w2"}, {t->out, "out"},
+              {t->out_f32, "out_f32"}};
+  for (const auto& m : mats)
+    if ((uintptr_t)m.p % 16) return fail(MOE_INVALID_ARG, "%s must be 16-byte aligned", m.name);
   return MOE_OK;
 }
 

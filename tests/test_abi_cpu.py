@@ -110,6 +110,11 @@ def test_forward_rejects_missing_tensors_and_small_workspace():
     assert st == B.MOE_INVALID_ARG and b"aligned" in lib.moe_last_error()
     st = lib.moe_forward(C.byref(d), None, 16, fake, 1 << 40, None)
     assert st == B.MOE_INVALID_ARG
+    for name in ("x", "w13", "w2", "out", "w_router"):  # matrix operands move in 16-byte pieces
+        bad = B.Tensors(x=fake, w13=fake, w2=fake, out=fake, w_router=fake)
+        setattr(bad, name, fake + 8)
+        st = lib.moe_forward(C.byref(d), C.byref(bad), 16, fake, 1 << 40, None)
+        assert st == B.MOE_INVALID_ARG and name.encode() in lib.moe_last_error() and b"aligned" in lib.moe_last_error()
     d8 = _desc(weight_dtype=B.DT_FP8)
     st = lib.moe_forward(C.byref(d8), C.byref(ts), 16, fake, 1 << 40, None)
     assert st == B.MOE_INVALID_ARG and b"scale" in lib.moe_last_error()
