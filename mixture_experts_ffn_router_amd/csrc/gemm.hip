@@ -440,21 +440,82 @@ void gemm_mfma_kernel(GemmArgs p) {
   // the row pieces each DMA lane fetches and cost L2 bandwidth).  Each K tile
   // takes four phases: group 0 reads half 0 of tile t in phase 4t and half 1 in
   // phase 4t+2, computing each in the next phase; group 1 runs one phase behind.
-  // The stage of tile t-1 is free once group 1 has read its half 1 (phase
-  // 4t-1): group 1 issues its share of tile t+1 right after those reads, group 0
-  // in phase 4t, after its fragment reads.  Each wave waits for its own share in
-  // its last phase before phase 4t+4, where tile t+1 is first read (group 0 at
-  // the end of its compute phase 4t+3, group 1 at the end of its memory phase
-  // 4t+3); the barrier closing phase 4t+3 makes every share visible.
+  // A stage is refilled in parts, each written only when no wave can still read
+  // it.  Group 0's wave rows (the lower half of the A tile) are read by group 0
+  // alone, last in phase 4t-2 for tile t-1: group 1 refills them for tile t+1 in
+  // phase 4t-1, right after its own reads (which never touch those rows), so
+  // those loads get four phases.  Group 1's A rows and the B tile are read by
+  // group 1 until phase 4t-1: group 0 refills group 1's A rows and the first
+  // half of the B rows in phase 4t, group 1 the second half of the B rows in
+  // phase 4t+1, each after its fragment reads (of the other stage).  Each wave
+  // waits for its own parts in its last phase before phase 4t+4, where tile
+  // t+1 is first read (group 0 at the end of its compute phase 4t+3, group 1 at
+  // the end of its memory phase 4t+3); the barrier closing phase 4t+3 makes
+  // every part visible.
   auto pingpong_dma64 = [&](auto live_tag) {
     constexpr bool LIVE = decltype(live_tag)::value;
-    const int grp = wave >> 2;
-    const DmaPlan dp = dma_plan();
+    const int grp = wave >> 2, gw = wave & 3;
+    constexpr int NA = A_BYTES / 1024, NB = B_BYTES / 1024;  // 1 KiB DMA instructions per stage
+    constexpr int AH = NA / 8;   // A instructions per wave for one half of the A tile
+    constexpr int BH = NB / 8;   // B instructions per wave for one half of the B tile
+    static_assert(AH * 8 == NA && BH * 8 == NB, "DMA parts must split evenly over 4 waves");
+    static_assert(4 % WAVES_N == 0 && WAVES_M == 2 * (4 / WAVES_N) && (NA / 2) * A_ROWS_PER_DMA == BM / 2,
+                  "each group's wave rows are one half of the A tile (group 0 the lower)");
+    // This wave's A instructions: group 1 the lower half of the A tile (group
+    // 0's wave rows), group 0 the upper half; B instructions: group 0 the first
+    // half of the B tile, group 1 the second.
+    const int ia0 = (grp == 1 ? 0 : NA / 2) + gw * AH;
+    const int ib0 = (grp == 1 ? NB / 2 : 0) + gw * BH;
+    uint32_t a_off[AH], b_soff[BH], b_voff[2];
+#pragma unroll
+    for (int i = 0; i < AH; ++i) {
+      const int r = (ia0 + i) * A_ROWS_PER_DMA + lane / A_CH;
+      const int64_t grow = m0 + r;
+      const int slot = (pad_map && grow < p.M) ? pad_map[grow] : 0;
+      int64_t tok;
+      if (p.a_rows) tok = slot >= 0 ? slot / p.row_div : 0;
+      else tok = grow < p.M ? grow : p.M - 1;
+      a_off[i] = (grow >= m_rows || slot < 0)
+                     ? 0x80000000u
+                     : (uint32_t)(tok * p.lda * 2) + (uint32_t)((((lane % A_CH) ^ lds_swz<A_ROW>(r))) << 4);
+    }
+    {
+      const int bl_row = lane / B_CH;
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        b_voff[k] = (uint32_t)(bl_row * p.Kdim * EB) +
+                    (uint32_t)(((lane % B_CH) ^ lds_swz<B_ROW>(bl_row + 8 * k)) << 4);
+#pragma unroll
+      for (int i = 0; i < BH; ++i) {
+        const int q0 = (ib0 + i) * B_ROWS_PER_DMA;
+        int brow;
+        if constexpr (GATED) brow = q0 < BN / 2 ? n0 + q0 : p.N + n0 + (q0 - BN / 2);
+        else brow = n0 + q0;
+        b_soff[i] = (uint32_t)((int64_t)brow * p.Kdim * EB);
+      }
+    }
+    // this wave's A part / B part of tile kt into stage buf (past the end: zero fill)
+    auto issue_a = [&](int kt, int buf) {
+      uint8_t* sA = smem + buf * STAGE;
+      const bool live = kt < nk;
+#pragma unroll
+      for (int i = 0; i < AH; ++i)
+        dma16(rsA, sA + (ia0 + i) * 1024, live ? a_off[i] : 0x80000000u, live ? (uint32_t)(kt0 + kt) * A_ROW : 0u);
+    };
+    auto issue_b = [&](int kt, int buf) {
+      uint8_t* sB = smem + buf * STAGE + A_BYTES;
+      const bool live = kt < nk;
+#pragma unroll
+      for (int i = 0; i < BH; ++i)
+        dma16(rsB, sB + (ib0 + i) * 1024, live ? b_voff[(((ib0 + i) * B_ROWS_PER_DMA) >> 3) & 1] : 0x80000000u,
+              live ? b_soff[i] + (uint32_t)(kt0 + kt) * (uint32_t)B_ROW : 0u);
+    };
     Frags f[2];
-    issue_dma(dp, 0, 0);
+    issue_a(0, 0);
+    issue_b(0, 0);
     if (grp == 1) {
-      issue_dma(dp, 1, 1);
-      wait_vmcnt<D_TILE>();  // this wave's part of tile 0
+      issue_a(1, 1);
+      wait_vmcnt<AH>();  // this wave's parts of tile 0
     } else {
       wait_vmcnt<0>();
     }
@@ -471,11 +532,14 @@ void gemm_mfma_kernel(GemmArgs p) {
 #pragma unroll
           for (int q = 0; q < SPH; ++q) load_frags(st, SPH * hh + q, f[q]);
         }
-        if (hh == 0 && grp == 0 && t + 1 < nk) issue_dma(dp, t + 1, st ^ 1);
+        if (hh == 0 && t + 1 < nk) {
+          if (grp == 0) issue_a(t + 1, st ^ 1);  // group 1's rows of tile t+1
+          issue_b(t + 1, st ^ 1);                // this group's half of the B rows
+        }
         wait_lgkmcnt0();
         if (hh == 1 && grp == 1) {
-          wait_vmcnt<0>();                           // own share of tile t+1 has landed
-          if (t + 2 < nk) issue_dma(dp, t + 2, st);  // every wave is done with tile t
+          wait_vmcnt<0>();                     // own parts of tile t+1 have landed
+          if (t + 2 < nk) issue_a(t + 2, st);  // group 0's rows of tile t: read for the last time in phase 4t+2
         }
         phase_barrier();
         // compute phase
@@ -483,7 +547,7 @@ void gemm_mfma_kernel(GemmArgs p) {
 #pragma unroll
           for (int q = 0; q < SPH; ++q) mfmas(f[q]);
         }
-        if (hh == 1 && grp == 0) wait_vmcnt<0>();  // own share of tile t+1 has landed
+        if (hh == 1 && grp == 0) wait_vmcnt<0>();  // own parts of tile t+1 have landed
         phase_barrier();
       }
     }
