@@ -54,6 +54,9 @@ class LayerSpec:
     I_dense: int = 0             # > 0: Gemma-style parallel dense MLP with post-norms
     supplied_logits: bool = False    # True: logits N(0,1) + Zipf bias, no router weights
     random_gammas: bool = False      # test-only: non-unit norm / router scales
+    scoring: str = "softmax"     # "softmax" over all experts | "sigmoid" per expert
+    n_groups: int = 0            # > 1: group-limited routing over this many expert groups
+    topk_groups: int = 0         # groups picked per token when n_groups > 1
 
     def with_T(self, T):
         return dataclasses.replace(self, T=T)
@@ -72,11 +75,16 @@ SPECS = {
                           renorm=False, n_shared=2, I_shared=1408),
     "skewed_fp8": LayerSpec("skewed_fp8", 4096, 2816, 128, 8, 704, "gelu_tanh", "fp8",
                             supplied_logits=True),
+    # DeepSeek-V3 routing shape (256 routed experts + 1 shared, 8 per token) with sigmoid
+    # scoring and expert groups, on the DeepSeek-MoE layer's hidden and expert widths
+    "deepseek_v3": LayerSpec("deepseek_v3", 8192, 2048, 256, 8, 1408, "silu", "bf16",
+                             n_shared=1, I_shared=1408, scoring="sigmoid", n_groups=8,
+                             topk_groups=4),
 }
 
 # token counts the pages' configurations name for each layer shape
 T_VALUES = {"tiny": [64], "mixtral": [4096], "gemma": [1, 16, 128, 8192],
-            "deepseek": [16384], "skewed_fp8": [1, 4096]}
+            "deepseek": [16384], "skewed_fp8": [1, 4096], "deepseek_v3": [1, 16, 8192]}
 
 
 def _rng(seed, *key):
@@ -204,7 +212,8 @@ def oracle_layer(L):
         return t.float().numpy()
 
     d = dict(E=spec.E, K=spec.K, act=spec.act, renorm=spec.renorm,
-             router_mode=spec.router_mode, w_router=f(L["w_router"]),
+             scoring=spec.scoring, n_groups=max(spec.n_groups, 1),
+             topk_groups=max(spec.topk_groups, 1), router_mode=spec.router_mode, w_router=f(L["w_router"]),
              router_scale=f(L["router_scale"]), per_expert_scale=f(L["per_expert_scale"]),
              w13=f(L["w13"]), w2=f(L["w2"]), w13_scale=f(L["w13_scale"]),
              w2_scale=f(L["w2_scale"]))

@@ -22,7 +22,8 @@ the order and notation of the pages it follows:
 * "MOE Inference" (gaohongy.github.io): gated FFN (Act(x w1) * (x w3)) w2 with
   the merged w13.
 * llama.cpp visual guide, lesson 35 (MoE): softmax / argsort_top_k / get_rows /
-  normalise routing; mul_mat_id sparse expert matmuls; shared experts.
+  normalise routing, sigmoid scoring, expert groups; mul_mat_id sparse expert
+  matmuls; shared experts.
 * sglang PR #24696 summary: per-expert FP8 weights with a weight_scale per
   projection.
 
@@ -136,21 +137,30 @@ def router_logits(x, w_router, mode="plain", router_scale=None, eps=RMS_EPS):
 # Routing maths (Gemma 4 walkthrough §4-§5; vLLM Gemma4MoE routing function)
 # ----------------------------------------------------------------------------
 
-def select_topk(z, k):
+def select_topk(z, k, allowed=None):
     """Indices of the k largest logits per row, largest first.
 
     Selection is on the logits, not on probabilities (§4: top-k only touches
     the raw logits).  Slot order is descending value, as in the worked example
     whose ids come out as [3, 2].  Reading for ties (unstated on the pages):
     the lower expert index wins, and -0.0 equals +0.0.  A stable argsort of -z
-    gives exactly that order."""
+    gives exactly that order.
+
+    `allowed` (bool [T, E], optional) restricts the candidates of each row
+    (group-limited routing); each row must allow at least k experts."""
     z = _f64(z)
     if not np.all(np.isfinite(z)):
         raise ValueError("router logits must be finite")
     E = z.shape[-1]
     if not 1 <= k <= E:
         raise ValueError("need 1 <= k <= E")
-    return np.argsort(-z, axis=-1, kind="stable")[..., :k]
+    if allowed is None:
+        return np.argsort(-z, axis=-1, kind="stable")[..., :k]
+    allowed = np.asarray(allowed, dtype=bool)
+    if np.any(allowed.sum(axis=-1) < k):
+        raise ValueError("fewer than k experts allowed")
+    # masked experts sort after every allowed one; the stable sort keeps index order
+    return np.argsort(np.where(allowed, -z, np.inf), axis=-1, kind="stable")[..., :k]
 
 
 def softmax_all(z):
@@ -160,11 +170,46 @@ def softmax_all(z):
     return e / e.sum(axis=-1, keepdims=True)
 
 
-def route(z, k, renormalize=True, per_expert_scale=None):
+def sigmoid_scores(z):
+    """Sigmoid scoring, 1 / (1 + exp(-z)) per expert, each independent of the
+    others (llama.cpp lesson 35: some models turn the router scores into
+    probabilities with a sigmoid in place of the softmax)."""
+    z = _f64(z)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def group_mask(z, n_groups, topk_groups):
+    """Experts each token may select under group-limited routing (llama.cpp
+    lesson 35: with very many experts they are split into groups; a token first
+    picks groups, then its experts inside the picked groups).
+
+    Readings (the page names the two counts, n_expert_groups and n_group_used,
+    and nothing more): the groups are n_groups equal, contiguous ranges of
+    expert ids; a group's score is the largest logit among its experts (the
+    same group order as the largest probability, since both scorings are
+    increasing); the topk_groups groups with the largest scores are picked,
+    ties to the lower group index.  Returns bool [T, E]."""
+    z = _f64(z)
+    T, E = z.shape
+    if n_groups < 1 or E % n_groups:
+        raise ValueError("n_groups must divide E")
+    if not 1 <= topk_groups <= n_groups:
+        raise ValueError("need 1 <= topk_groups <= n_groups")
+    gsz = E // n_groups
+    gscore = z.reshape(T, n_groups, gsz).max(axis=-1)
+    picked = np.argsort(-gscore, axis=-1, kind="stable")[:, :topk_groups]
+    gallowed = np.zeros((T, n_groups), dtype=bool)
+    np.put_along_axis(gallowed, picked, True, axis=-1)
+    return np.repeat(gallowed, gsz, axis=-1)
+
+
+def route(z, k, renormalize=True, per_expert_scale=None, scoring="softmax", n_groups=1,
+          topk_groups=1):
     """Routing weights and ids, in the order of §4-§5:
 
-    1. ids = top-k of the logits;
-    2. p = softmax over all E;
+    1. ids = top-k of the logits (with n_groups > 1: among the experts of the
+       picked groups, see group_mask);
+    2. p = softmax over all E, or the per-expert sigmoid (scoring="sigmoid");
     3. indicator [T, E] with exactly k ones per row;
     4. gate = indicator * p;
     5. renormalise by the row sum (a non-positive sum is replaced by 1);
@@ -172,11 +217,18 @@ def route(z, k, renormalize=True, per_expert_scale=None):
     6. gather the k selected weights in slot order;
     7. multiply by per_expert_scale[ids] (ones when None).
 
+    Both scorings are strictly increasing in the logit, so selecting on the
+    logits selects the k largest probabilities (llama.cpp lesson 35 sorts the
+    probabilities; the Gemma walkthrough §4 the logits).
+
     Returns (weights [T, k] float64, ids [T, k] int64)."""
     z = _f64(z)
     T, E = z.shape
-    ids = select_topk(z, k)
-    p = softmax_all(z)
+    if scoring not in ("softmax", "sigmoid"):
+        raise ValueError(f"unknown scoring {scoring!r}")
+    allowed = group_mask(z, n_groups, topk_groups) if n_groups > 1 else None
+    ids = select_topk(z, k, allowed)
+    p = softmax_all(z) if scoring == "softmax" else sigmoid_scores(z)
     indicator = np.zeros((T, E))
     np.put_along_axis(indicator, ids, 1.0, axis=-1)
     gate = indicator * p
@@ -281,6 +333,7 @@ def moe_layer(x, layer, rows=None, logits=None):
 
     `layer` is a dict with:
       E, K, act, renorm, router_mode ('plain'|'gemma'),
+      scoring ('softmax'|'sigmoid'), n_groups, topk_groups (group-limited routing),
       w_router [E,H] or None (then `logits` must be given),
       router_scale [H] or None, per_expert_scale [E] or None,
       w13 [E,2I,H], w2 [E,H,I] (+ w13_scale [E,2I], w2_scale [E,H] for FP8 codes),
@@ -312,7 +365,9 @@ def moe_layer(x, layer, rows=None, logits=None):
         logits = router_logits(x, layer["w_router"], layer.get("router_mode", "plain"),
                                layer.get("router_scale"), eps)
     z = _f64(logits)
-    w, ids = route(z, K, layer.get("renorm", True), layer.get("per_expert_scale"))
+    w, ids = route(z, K, layer.get("renorm", True), layer.get("per_expert_scale"),
+                   layer.get("scoring", "softmax"), layer.get("n_groups", 1),
+                   layer.get("topk_groups", 1))
     counts, offsets, order = permutation(ids, E)
     dense = layer.get("dense")
     if dense is not None:

@@ -34,8 +34,8 @@ def test_highest_index_tie_break_is_caught(monkeypatch):
 
 def test_missing_renorm_is_caught(monkeypatch):
     orig = O.route
-    monkeypatch.setattr(O, "route", lambda z, k, renormalize=True, per_expert_scale=None:
-                        orig(z, k, False, per_expert_scale))
+    monkeypatch.setattr(O, "route", lambda z, k, renormalize=True, per_expert_scale=None, *rest:
+                        orig(z, k, False, per_expert_scale, *rest))
     _fails(P.test_closed_form_softmax_over_selected, 8, 2)
     _fails(P.test_worked_example_from_page)
 
@@ -43,8 +43,8 @@ def test_missing_renorm_is_caught(monkeypatch):
 def test_scale_indexed_by_slot_is_caught(monkeypatch):
     orig = O.route
 
-    def bad(z, k, renormalize=True, per_expert_scale=None):
-        w, ids = orig(z, k, renormalize, None)
+    def bad(z, k, renormalize=True, per_expert_scale=None, *rest):
+        w, ids = orig(z, k, renormalize, None, *rest)
         if per_expert_scale is not None:
             w = w * np.asarray(per_expert_scale)[:k][None, :]
         return w, ids
@@ -65,3 +65,29 @@ def test_dropped_cubic_term_in_gelu_is_caught(monkeypatch):
     monkeypatch.setattr(O, "gelu_tanh", lambda a: 0.5 * a * (1 + np.tanh(np.sqrt(2 / np.pi) * a)))
     monkeypatch.setitem(O.ACTIVATIONS, "gelu_tanh", O.gelu_tanh)
     _fails(P.test_activations_match_torch)
+
+
+def test_group_score_by_sum_is_caught(monkeypatch):
+    def bad(z, n_groups, topk_groups):
+        z = np.asarray(z, dtype=np.float64)
+        T, E = z.shape
+        gsz = E // n_groups
+        picked = np.argsort(-z.reshape(T, n_groups, gsz).sum(-1), axis=-1, kind="stable")[:, :topk_groups]
+        m = np.zeros((T, n_groups), dtype=bool)
+        np.put_along_axis(m, picked, True, axis=-1)
+        return np.repeat(m, gsz, axis=-1)
+    monkeypatch.setattr(O, "group_mask", bad)
+    _fails(P.test_group_limited_worked_case)
+    _fails(P.test_group_limited_topk_brute_force, 16, 4, 2, 3)
+
+
+def test_higher_group_index_tie_break_is_caught(monkeypatch):
+    orig = O.group_mask
+    monkeypatch.setattr(O, "group_mask", lambda z, G, KG: orig(np.asarray(z)[:, ::-1], G, KG)[:, ::-1])
+    _fails(P.test_group_limited_worked_case)
+
+
+def test_sigmoid_sign_error_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "sigmoid_scores", lambda z: 1.0 / (1.0 + np.exp(np.asarray(z, dtype=np.float64))))
+    _fails(P.test_sigmoid_scores_match_library_and_closed_forms)
+    _fails(P.test_sigmoid_route_sorts_probabilities, True)

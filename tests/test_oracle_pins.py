@@ -5,6 +5,7 @@ the pages print, a closed form the pages derive, an invariant they state, a
 brute-force evaluation through torch.nn.functional in float64, or a library
 routine (scipy softmax, numpy stable argsort, torch's float8_e4m3fn).
 """
+import itertools
 import math
 import os
 
@@ -99,6 +100,90 @@ def test_topk_brute_force_with_ties_and_signed_zero():
             ref = sorted(range(9), key=lambda e: (-float(z[r, e]) + 0.0, e))[:k]
             assert ids[r].tolist() == ref
     assert O.select_topk(z[:1], 4)[0].tolist() == [4, 5, 0, 1]
+
+
+# ------------------------------------------------------------ routing variants (llama.cpp lesson 35)
+
+def test_sigmoid_scores_match_library_and_closed_forms():
+    rng = np.random.default_rng(20)
+    z = rng.standard_normal((50, 16)) * 6
+    np.testing.assert_allclose(O.sigmoid_scores(z), scipy.special.expit(z), rtol=1e-15, atol=0)
+    assert O.sigmoid_scores(np.zeros((1, 1)))[0, 0] == 0.5
+    np.testing.assert_allclose(O.sigmoid_scores(-z), 1.0 - O.sigmoid_scores(z), atol=1e-15)
+
+
+@pytest.mark.parametrize("renorm", [True, False])
+def test_sigmoid_route_sorts_probabilities(renorm):
+    """The page's order of operations, through torch: probabilities first
+    (torch.sigmoid), a stable descending sort of them, gather, L1-normalise."""
+    rng = np.random.default_rng(21)
+    z = rng.standard_normal((300, 64)) * 2
+    K = 6
+    w, ids = O.route(z, K, renormalize=renorm, scoring="sigmoid")
+    p = torch.sigmoid(torch.from_numpy(z))
+    order = torch.sort(p, dim=-1, descending=True, stable=True).indices[:, :K]
+    assert np.array_equal(ids, order.numpy())
+    g = torch.gather(p, 1, order)
+    if renorm:
+        g = F.normalize(g, p=1, dim=-1)
+    np.testing.assert_allclose(w, g.numpy(), rtol=1e-13, atol=0)
+
+
+def _brute_groups(zrow, G, KG):
+    """The KG groups whose best logits have the largest sum, over every
+    combination (distinct logits make the set unique)."""
+    gsz = len(zrow) // G
+    best = [max(zrow[g * gsz:(g + 1) * gsz]) for g in range(G)]
+    return set(max(itertools.combinations(range(G), KG), key=lambda c: sum(best[i] for i in c)))
+
+
+@pytest.mark.parametrize("E,G,KG,K", [(16, 4, 2, 3), (32, 8, 3, 5), (12, 6, 1, 2)])
+def test_group_limited_topk_brute_force(E, G, KG, K):
+    rng = np.random.default_rng(22)
+    z = rng.standard_normal((200, E))
+    w, ids = O.route(z, K, True, None, "softmax", G, KG)
+    gsz = E // G
+    for r in range(z.shape[0]):
+        picked = _brute_groups(z[r].tolist(), G, KG)
+        cand = [e for e in range(E) if e // gsz in picked]
+        assert ids[r].tolist() == sorted(cand, key=lambda e: -z[r, e])[:K]
+    # renormalised: the softmax over the selected logits (the full denominator cancels)
+    zs = np.take_along_axis(z, ids, axis=-1)
+    np.testing.assert_allclose(w, scipy.special.softmax(zs, axis=-1), rtol=1e-13, atol=0)
+
+
+def test_group_limited_worked_case():
+    """Hand-checked.  Groups {0,1} {2,3} {4,5} {6,7} have best logits 5, 4, 4.5, 0;
+    groups 0 and 2 are picked, so expert 2 (the third largest logit) is out of
+    reach and the third slot goes to expert 1 (tied with expert 5 at -9)."""
+    z = np.array([[5.0, -9.0, 4.0, 0.0, 4.5, -9.0, 0.0, 0.0]])
+    assert O.route(z, 3, True, None, "softmax", 4, 2)[1][0].tolist() == [0, 4, 1]
+    assert O.route(z, 3)[1][0].tolist() == [0, 4, 2]
+    # tied group scores (groups 0 and 1 both 1.0): the lower group index is picked
+    z = np.array([[1.0, 0.0, 0.0, 1.0, 2.0, 2.0, -1.0, -1.0]])
+    assert O.route(z, 4, True, None, "sigmoid", 4, 2)[1][0].tolist() == [4, 5, 0, 1]
+    assert O.route(z, 4, True, None, "sigmoid")[1][0].tolist() == [4, 5, 0, 3]
+
+
+def test_group_limited_reduces_to_plain_topk():
+    """One expert per group with k groups picked, or every group picked, is the
+    plain top-k (ties included)."""
+    rng = np.random.default_rng(23)
+    z = _rand_logits(rng, 300, 16, ties=True)
+    for G, KG, K in [(16, 4, 4), (4, 4, 3), (8, 8, 8)]:
+        for scoring in ("softmax", "sigmoid"):
+            a = O.route(z, K, True, None, scoring, G, KG)
+            b = O.route(z, K, True, None, scoring)
+            assert np.array_equal(a[1], b[1])
+            np.testing.assert_array_equal(a[0], b[0])
+
+
+def test_group_limited_rejects_too_few_candidates():
+    z = np.zeros((1, 8))
+    with pytest.raises(ValueError):
+        O.route(z, 5, True, None, "softmax", 4, 2)  # 2 groups of 2 experts < 5
+    with pytest.raises(ValueError):
+        O.route(z, 2, True, None, "softmax", 3, 1)  # 3 does not divide 8
 
 
 def test_nonfinite_logits_rejected():
