@@ -347,7 +347,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{spec.name} MoE FFN layer forward", "T": T, "hidden": spec.H,
                    "experts": spec.E, "top_k": spec.K, "inter": spec.I, "act": spec.act,
-                   "shared": spec.n_shared, "dense_inter": spec.I_dense, "path": path,
+                   "shared": spec.n_shared, "dense_inter": spec.I_dense, "scoring": spec.scoring,
+                   "groups": [spec.n_groups, spec.topk_groups] if spec.n_groups > 1 else None, "path": path,
                    "weight_sets": len(sets)},
         "step_tflops": round(total_flop / (ms_per_step / 1e3) / 1e12, 2),
         "step_gbps": round(total_bytes / (ms_per_step / 1e3) / 1e9, 1),

@@ -48,6 +48,9 @@ typedef enum {
 typedef enum { MOE_ACT_SILU = 0, MOE_ACT_GELU_TANH = 1 } moe_act;
 typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1, MOE_DT_FP8_E4M3 = 2 } moe_dtype;
 typedef enum { MOE_ROUTER_PLAIN = 0, MOE_ROUTER_GEMMA = 1 } moe_router_mode;
+/* How the router turns logits into routing probabilities ([LC] routing: a
+ * softmax, or in some models a sigmoid). */
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_scoring;
 
 /* Human-readable name of a status code (static storage). */
 const char* moe_status_string(moe_status s);
@@ -55,26 +58,38 @@ const char* moe_status_string(moe_status s);
 const char* moe_last_error(void);
 
 /*
- * moe_route - softmax over all experts, top-k, renormalisation and the
- * per-expert scale fold, one token per wavefront.
+ * moe_route - softmax over all experts (or a sigmoid per expert), top-k,
+ * renormalisation and the per-expert scale fold, one token per wavefront.
  *
  * Defined by [G4] section 4 (routing maths) and section 5 (per-expert scale),
  * and the routing function of Gemma4MoE in [VD]; [LC] routing (softmax ->
- * argsort_top_k -> get_rows -> normalise) is the same with unit scales.
+ * argsort_top_k -> get_rows -> normalise) is the same with unit scales, and
+ * [LC] names the two variants taken here: sigmoid scoring, and expert groups
+ * (groups picked first, then experts inside the picked groups).
  * For each token t:
- *   ids[t, 0..K-1] = the K largest logits, largest first; ties go to the lower
- *                    expert index and -0.0 equals +0.0;
- *   renorm != 0:     w[t, j] = exp(z_ids_j) / sum_{i<K} exp(z_ids_i)
- *                    (= softmax over all E, masked to the top-K, renormalised);
- *   renorm == 0:     w[t, j] = softmax over all E at ids_j;
+ *   candidates      = all E experts; with n_groups > 1, the experts form n_groups
+ *                     equal contiguous ranges, a range scores its largest logit,
+ *                     and only the topk_groups best ranges (ties to the lower
+ *                     range) are candidates;
+ *   ids[t, 0..K-1]  = the K largest candidate logits, largest first; ties go to
+ *                     the lower expert index and -0.0 equals +0.0;
+ *   p_e             = softmax over all E at e (scoring SOFTMAX), or
+ *                     1 / (1 + exp(-z_e)) (scoring SIGMOID);
+ *   renorm != 0:     w[t, j] = p_ids_j / sum_{i<K} p_ids_i
+ *                    (softmax: = exp(z_ids_j) / sum_{i<K} exp(z_ids_i));
+ *   renorm == 0:     w[t, j] = p_ids_j;
  *   then             w[t, j] *= per_expert_scale[ids_j]   (1 when NULL).
  *
  *   logits            [T, E] fp32, finite (non-finite logits give undefined ids).
+ *   scoring           moe_scoring.
+ *   n_groups          0 or 1: no groups; else 2..64, dividing E.
+ *   topk_groups       with n_groups > 1: 1..n_groups, and topk_groups * E / n_groups >= K.
  *   per_expert_scale  [E] fp32 or NULL.
  *   topk_w            [T, K] fp32 out.   topk_ids [T, K] int32 out.
  * Limits: 1 <= K <= E <= 512, K <= 64.  T >= 0.
  */
 moe_status moe_route(const float* logits, int64_t T, int32_t E, int32_t K, int32_t renorm,
+                     int32_t scoring, int32_t n_groups, int32_t topk_groups,
                      const float* per_expert_scale, float* topk_w, int32_t* topk_ids,
                      void* stream);
 
@@ -124,6 +139,9 @@ typedef struct {
   int32_t inter_dense;   /* > 0: parallel dense MLP of this I with Gemma post-norms; 0: none */
   int32_t dense_act;     /* moe_act of the dense MLP */
   float eps;             /* RMSNorm epsilon (router preprocessing and Gemma norms) */
+  int32_t scoring;       /* moe_scoring (see moe_route) */
+  int32_t n_groups;      /* expert groups for group-limited routing: 0 or 1 = none, else 2..64 */
+  int32_t topk_groups;   /* groups picked per token when n_groups > 1 */
 } moe_layer_desc;
 
 /* Tensors of one forward call (device pointers unless noted).  The matrix

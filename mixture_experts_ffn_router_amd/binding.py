@@ -20,6 +20,7 @@ MOE_OK, MOE_INVALID_ARG, MOE_UNSUPPORTED, MOE_WORKSPACE_TOO_SMALL, MOE_HIP_ERROR
 ACT = {"silu": 0, "gelu_tanh": 1}
 DT_F32, DT_BF16, DT_FP8 = 0, 1, 2
 ROUTER_PLAIN, ROUTER_GEMMA = 0, 1
+SCORING = {"softmax": 0, "sigmoid": 1}
 
 
 class MoEError(RuntimeError):
@@ -37,7 +38,8 @@ class LayerDesc(C.Structure):
                 ("inter", C.c_int32), ("act", C.c_int32), ("act_dtype", C.c_int32),
                 ("weight_dtype", C.c_int32), ("renormalize", C.c_int32), ("router_mode", C.c_int32),
                 ("n_shared", C.c_int32), ("inter_dense", C.c_int32), ("dense_act", C.c_int32),
-                ("eps", C.c_float)]
+                ("eps", C.c_float), ("scoring", C.c_int32), ("n_groups", C.c_int32),
+                ("topk_groups", C.c_int32)]
 
 
 class Tensors(C.Structure):
@@ -71,7 +73,8 @@ def load(path: str = LIB_PATH):
     lib.moe_last_error.restype = C.c_char_p
     lib.moe_last_error.argtypes = []
     lib.moe_route.restype = C.c_int
-    lib.moe_route.argtypes = [C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
+    lib.moe_route.argtypes = [C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                              C.c_int32, C.c_int32, C.c_void_p,
                               C.c_void_p, C.c_void_p, C.c_void_p]
     lib.moe_permute_capacity.restype = C.c_int64
     lib.moe_permute_capacity.argtypes = [C.c_int64, C.c_int32, C.c_int32, C.c_int32]
@@ -124,7 +127,8 @@ def _dev(t, name, dtype=None, shape=None):
 # ----------------------------------------------------------------------------- moe_route
 
 def route(logits: torch.Tensor, k: int, renormalize: bool = True,
-          per_expert_scale: Optional[torch.Tensor] = None, out=None):
+          per_expert_scale: Optional[torch.Tensor] = None, out=None, scoring: str = "softmax",
+          n_groups: int = 0, topk_groups: int = 0):
     """moe_route: (topk_w fp32 [T,k], topk_ids int32 [T,k]) from fp32 logits [T,E]."""
     lib = load()
     T, E = logits.shape
@@ -135,7 +139,8 @@ def route(logits: torch.Tensor, k: int, renormalize: bool = True,
         ids = torch.empty(T, k, dtype=torch.int32, device=logits.device)
     else:
         w, ids = out
-    _check(lib.moe_route(_ptr(logits), T, E, k, int(bool(renormalize)), _ptr(per_expert_scale),
+    _check(lib.moe_route(_ptr(logits), T, E, k, int(bool(renormalize)), SCORING[scoring], n_groups,
+                         topk_groups, _ptr(per_expert_scale),
                          _ptr(w), _ptr(ids), _stream()))
     return w, ids
 
@@ -189,7 +194,8 @@ class DeviceLayer:
                          renormalize=int(spec.renorm),
                          router_mode=ROUTER_GEMMA if spec.router_mode == "gemma" else ROUTER_PLAIN,
                          n_shared=spec.n_shared, inter_dense=spec.I_dense, dense_act=ACT[spec.act],
-                         eps=eps)
+                         eps=eps, scoring=SCORING[spec.scoring], n_groups=spec.n_groups,
+                         topk_groups=spec.topk_groups)
 
         def d(t):
             return None if t is None else t.to(device, non_blocking=False).contiguous()

@@ -110,6 +110,28 @@ struct Plan {
   int down_splits;
 };
 
+// Routing options of a layer or a moe_route call, checked and filled in.
+moe_status route_opts(int32_t E, int32_t K, int32_t renorm, int32_t scoring, int32_t n_groups,
+                      int32_t topk_groups, moe::RouteOpts& o) {
+  if (scoring != MOE_SCORE_SOFTMAX && scoring != MOE_SCORE_SIGMOID)
+    return fail(MOE_INVALID_ARG, "unknown scoring %d", scoring);
+  if (n_groups < 0) return fail(MOE_INVALID_ARG, "n_groups %d < 0", n_groups);
+  if (n_groups > 64) return fail(MOE_UNSUPPORTED, "n_groups %d > 64", n_groups);
+  if (n_groups > 1) {
+    if (E % n_groups) return fail(MOE_INVALID_ARG, "n_groups %d does not divide num_experts %d", n_groups, E);
+    if (topk_groups < 1 || topk_groups > n_groups)
+      return fail(MOE_INVALID_ARG, "topk_groups %d outside [1, n_groups = %d]", topk_groups, n_groups);
+    if ((int64_t)topk_groups * (E / n_groups) < K)
+      return fail(MOE_INVALID_ARG, "top_k %d exceeds the %d experts of the picked groups", K,
+                  topk_groups * (E / n_groups));
+  }
+  o.renorm = renorm != 0;
+  o.scoring = scoring;
+  o.groups = n_groups > 1 ? n_groups : 1;
+  o.topk_groups = n_groups > 1 ? topk_groups : 1;
+  return MOE_OK;
+}
+
 moe_status validate_desc(const moe_layer_desc* d) {
   if (!d) return fail(MOE_INVALID_ARG, "desc is NULL");
   if (d->hidden <= 0 || d->num_experts <= 0 || d->top_k <= 0 || d->inter <= 0)
@@ -137,7 +159,15 @@ moe_status validate_desc(const moe_layer_desc* d) {
   if (d->router_mode != MOE_ROUTER_PLAIN && d->router_mode != MOE_ROUTER_GEMMA)
     return fail(MOE_INVALID_ARG, "unknown router mode %d", d->router_mode);
   if (!(d->eps >= 0.f)) return fail(MOE_INVALID_ARG, "eps must be >= 0");
-  return MOE_OK;
+  moe::RouteOpts o;
+  return route_opts(d->num_experts, d->top_k, d->renormalize, d->scoring, d->n_groups, d->topk_groups, o);
+}
+
+// The routing options of a validated layer.
+moe::RouteOpts layer_route_opts(const moe_layer_desc& d) {
+  moe::RouteOpts o;
+  route_opts(d.num_experts, d.top_k, d.renormalize, d.scoring, d.n_groups, d.topk_groups, o);
+  return o;
 }
 
 moe_status make_plan(const moe_layer_desc& d, const moe_tensors* t, int64_t T, Plan& p) {
@@ -260,15 +290,18 @@ MOE_API const char* moe_status_string(moe_status s) {
 MOE_API const char* moe_last_error(void) { return g_err; }
 
 MOE_API moe_status moe_route(const float* logits, int64_t T, int32_t E, int32_t K, int32_t renorm,
+                             int32_t scoring, int32_t n_groups, int32_t topk_groups,
                              const float* per_expert_scale, float* topk_w, int32_t* topk_ids, void* stream) {
   g_err[0] = 0;
   if (T < 0) return fail(MOE_INVALID_ARG, "T < 0");
   if (E < 1 || K < 1 || K > E) return fail(MOE_INVALID_ARG, "need 1 <= K <= E (K=%d, E=%d)", K, E);
   if (E > 512 || K > 64) return fail(MOE_UNSUPPORTED, "E <= 512 and K <= 64 are supported");
+  moe::RouteOpts o;
+  if (moe_status st = route_opts(E, K, renorm, scoring, n_groups, topk_groups, o)) return st;
   if (T == 0) return MOE_OK;
   if (!logits || !topk_w || !topk_ids) return fail(MOE_INVALID_ARG, "logits, topk_w and topk_ids are required");
   if (T > ((int64_t)1 << 32)) return fail(MOE_UNSUPPORTED, "T too large");
-  HIP_TRY(moe::launch_route(logits, T, E, K, renorm, per_expert_scale, topk_w, topk_ids, K, 0,
+  HIP_TRY(moe::launch_route(logits, T, E, K, o, per_expert_scale, topk_w, topk_ids, K, 0,
                             (hipStream_t)stream),
           "route launch");
   return MOE_OK;
@@ -357,7 +390,7 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
     a.Id = d.inter_dense;
     a.act = d.act;
     a.dense_act = d.dense_act;
-    a.renorm = d.renormalize;
+    a.route = layer_route_opts(d);
     a.gemma_router = d.router_mode == MOE_ROUTER_GEMMA;
     a.dense = p.dense;
     a.eps = d.eps;
@@ -526,7 +559,7 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
 
   STAGE(MOE_STAGE_ROUTE);
   // 3. routing weights and ids (shared experts appended as ids E.., weight 1)
-  HIP_TRY(moe::launch_route(z, T, E, K, d.renormalize, t->per_expert_scale, w, ids, p.Kp, d.n_shared, st,
+  HIP_TRY(moe::launch_route(z, T, E, K, layer_route_opts(d), t->per_expert_scale, w, ids, p.Kp, d.n_shared, st,
                             p.ks_r, T * E, t->logits_out),
           "route launch");
 

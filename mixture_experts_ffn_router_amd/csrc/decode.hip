@@ -288,7 +288,7 @@ __device__ void dense_gate_up_tile(const DecodeArgs& a, uint8_t* dsm, int i0) {
     const int rho = threadIdx.x >> 4, t = threadIdx.x & 15;
     if (t < T) {
       const float gv = reduced<PW, 2>(red, 0, rho, t) * fac[t], uv = reduced<PW, 2>(red, 1, rho, t) * fac[t];
-      ((bf16_t*)a.hd)[t * Id + i0 + rho] = f32_to_bf16(apply_act(a.dense_act, gv) * uv);
+      ((bf16_t*)a.hd)[t * Id + i0 + rho] = f32_to_bf16(apply_act_bf16(a.dense_act, gv) * uv);
     }
   }
 }
@@ -367,7 +367,7 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
   for (int t = t0; t < T && t <= t1; t += PW) {
     float w;
     int id;
-    route_logits<VPL>(t == t0 ? z0 : z1, E, a.K, a.renorm, a.pes, lane, w, id);
+    route_logits<VPL>(t == t0 ? z0 : z1, E, a.K, a.route, a.pes, lane, w, id);
     if (lane < a.K) {
       s_ids[t * Kp + lane] = id;
       s_w[t * Kp + lane] = w;
@@ -448,7 +448,7 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
       if (slot >= 0) {
         const float gv = reduced<PW, 2>(red, 0, rho, t) * fac[t] * sg;
         const float uv = reduced<PW, 2>(red, 1, rho, t) * fac[t] * su;
-        const float h = apply_act(a.act, gv) * uv * s_w[slot];
+        const float h = apply_act_bf16(a.act, gv) * uv * s_w[slot];
         ((bf16_t*)a.hbuf)[(int64_t)slot * I + i0 + rho] = f32_to_bf16(h);
       }
     }

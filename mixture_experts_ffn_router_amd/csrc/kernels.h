@@ -6,9 +6,21 @@
 
 namespace moe {
 
+// Routing options.  renorm: divide the selected weights by their sum.  scoring:
+// softmax over all experts or a sigmoid per expert.  groups > 1: the experts form
+// `groups` equal contiguous ranges and only the topk_groups ranges with the
+// largest best logit are candidates.
+enum RouteScoring { SCORE_SOFTMAX = 0, SCORE_SIGMOID = 1 };
+struct RouteOpts {
+  int renorm = 1;
+  int scoring = SCORE_SOFTMAX;
+  int groups = 1;
+  int topk_groups = 1;
+};
+
 // logits: nparts planes of [T, E] (part_stride elements apart) summed in order;
 // with more than one part, sum_out (if not NULL) receives the summed logits.
-hipError_t launch_route(const float* logits, int64_t T, int E, int K, int renorm, const float* pes,
+hipError_t launch_route(const float* logits, int64_t T, int E, int K, const RouteOpts& o, const float* pes,
                         float* w_out, int32_t* ids_out, int out_stride, int n_shared, hipStream_t s,
                         int nparts = 1, int64_t part_stride = 0, float* sum_out = nullptr);
 
@@ -80,7 +92,8 @@ hipError_t launch_gather_topk(const float* w_in, const int32_t* ids_in, int in_s
 // tokens applied to each weight row together.
 struct DecodeArgs {
   int T, H, E, K, Kp, Ep, I, Id;
-  int act, dense_act, renorm, gemma_router, dense;
+  int act, dense_act, gemma_router, dense;
+  RouteOpts route;
   float eps;
   int n_router_groups;  // pre kernel: blocks computing 16 router logits each (0: logits supplied)
   int n_pre_dense_groups;  // pre kernel: trailing blocks computing 16 dense hidden units each

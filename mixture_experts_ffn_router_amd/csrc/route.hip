@@ -1,6 +1,7 @@
 // Routing: softmax over all experts, top-k, renormalisation, per-expert
 // scale fold ("Gemma 4 26B-A4B MoE walkthrough" sections 4-5; the routing
-// function of Gemma4MoE in the vLLM gemma4 API docs).
+// function of Gemma4MoE in the vLLM gemma4 API docs), with the variants of the
+// llama.cpp MoE lesson: sigmoid scoring and expert groups.
 //
 // One wavefront per token.  Lane l holds the logits of experts l, l+64, ...
 // Selection runs K rounds of a wave-wide arg-max on the key (value desc,
@@ -16,6 +17,9 @@
 // is exp(z_k - m) / sum_{all E} exp(z_j - m).  The exponentials are fp32;
 // the sums, the division and the scale product are carried in fp64 and
 // rounded once, so a weight is within about two fp32 ulps of exact.
+// Sigmoid scoring selects on the logits too (the sigmoid is increasing) and
+// evaluates 1 / (1 + exp(-z)) of the K selected logits in fp64.  Expert groups
+// clear the keys of the experts outside the picked groups before the top-k.
 #include "common.h"
 #include "kernels.h"
 #include "route_dev.h"
@@ -24,7 +28,7 @@ namespace moe {
 
 template <int VPL>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int64_t T,
-                                                    int E, int K, int renorm,
+                                                    int E, int K, RouteOpts ro,
                                                     const float* __restrict__ pes,
                                                     float* __restrict__ w_out,
                                                     int32_t* __restrict__ ids_out, int out_stride,
@@ -47,7 +51,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   }
   float w;
   int id;
-  route_logits<VPL>(z, E, K, renorm, pes, lane, w, id);
+  route_logits<VPL>(z, E, K, ro, pes, lane, w, id);
   int64_t o = t * (int64_t)out_stride + lane;
   if (lane < K) {
     w_out[o] = w;
@@ -58,19 +62,19 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   }
 }
 
-hipError_t launch_route(const float* logits, int64_t T, int E, int K, int renorm, const float* pes,
+hipError_t launch_route(const float* logits, int64_t T, int E, int K, const RouteOpts& o, const float* pes,
                         float* w_out, int32_t* ids_out, int out_stride, int n_shared,
                         hipStream_t s, int nparts, int64_t part_stride, float* sum_out) {
   if (T == 0) return hipSuccess;
   dim3 grid((unsigned)((T + 3) / 4)), block(256);
   if (E <= 64)
-    route_kernel<1><<<grid, block, 0, s>>>(logits, T, E, K, renorm, pes, w_out, ids_out, out_stride, n_shared, nparts, part_stride, sum_out);
+    route_kernel<1><<<grid, block, 0, s>>>(logits, T, E, K, o, pes, w_out, ids_out, out_stride, n_shared, nparts, part_stride, sum_out);
   else if (E <= 128)
-    route_kernel<2><<<grid, block, 0, s>>>(logits, T, E, K, renorm, pes, w_out, ids_out, out_stride, n_shared, nparts, part_stride, sum_out);
+    route_kernel<2><<<grid, block, 0, s>>>(logits, T, E, K, o, pes, w_out, ids_out, out_stride, n_shared, nparts, part_stride, sum_out);
   else if (E <= 256)
-    route_kernel<4><<<grid, block, 0, s>>>(logits, T, E, K, renorm, pes, w_out, ids_out, out_stride, n_shared, nparts, part_stride, sum_out);
+    route_kernel<4><<<grid, block, 0, s>>>(logits, T, E, K, o, pes, w_out, ids_out, out_stride, n_shared, nparts, part_stride, sum_out);
   else
-    route_kernel<8><<<grid, block, 0, s>>>(logits, T, E, K, renorm, pes, w_out, ids_out, out_stride, n_shared, nparts, part_stride, sum_out);
+    route_kernel<8><<<grid, block, 0, s>>>(logits, T, E, K, o, pes, w_out, ids_out, out_stride, n_shared, nparts, part_stride, sum_out);
   return hipGetLastError();
 }
 

@@ -4,6 +4,7 @@
 #pragma once
 
 #include "common.h"
+#include "kernels.h"
 
 namespace moe {
 
@@ -24,8 +25,43 @@ __device__ __forceinline__ TokenLogits<VPL> load_logits(const float* __restrict_
   return r;
 }
 
+// Group-limited routing (llama.cpp MoE lesson: experts split into groups, groups
+// picked first): the experts form G equal contiguous ranges; a range's score is
+// its largest key (the same order as its largest logit or probability).  The KG
+// best ranges are picked, ties to the lower range, and every other expert's key
+// is cleared to 0, below every real key, so the top-k never takes it while K is
+// at most the number of experts in the picked ranges.
 template <int VPL>
-__device__ __forceinline__ void route_logits(const TokenLogits<VPL>& zl, int E, int K, int renorm,
+__device__ __forceinline__ void mask_groups(uint32_t (&key)[VPL], int E, int G, int KG, int lane) {
+  const int gsz = E / G;
+  uint32_t gkey = 0u;  // lane g < G: the best key of range g
+  for (int g = 0; g < G; ++g) {
+    uint32_t b = 0u;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int idx = lane + 64 * j;
+      if (idx < E && idx / gsz == g && key[j] > b) b = key[j];
+    }
+    b = wave_max_u32(b);
+    if (lane == g) gkey = b;
+  }
+  uint64_t picked = 0;  // the same on every lane
+  for (int r = 0; r < KG; ++r) {
+    const bool open = lane < G && !((picked >> lane) & 1ull);
+    const uint32_t c = open ? gkey : 0u;
+    const uint32_t gk = wave_max_u32(c);
+    const uint32_t gi = wave_min_u32(open && c == gk ? (uint32_t)lane : 0xFFFFFFFFu);
+    picked |= 1ull << gi;
+  }
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const int idx = lane + 64 * j;
+    if (idx < E && !((picked >> (idx / gsz)) & 1ull)) key[j] = 0u;
+  }
+}
+
+template <int VPL>
+__device__ __forceinline__ void route_logits(const TokenLogits<VPL>& zl, int E, int K, const RouteOpts& o,
                                              const float* __restrict__ pes, int lane, float& w_slot,
                                              int& id_slot) {
   float v[VPL];
@@ -42,10 +78,12 @@ __device__ __forceinline__ void route_logits(const TokenLogits<VPL>& zl, int E, 
       key[j] = 0u;  // below every finite key: never selected while K <= E
     }
   }
-  const float m = wave_max_f32(lmax);
+  if (o.groups > 1) mask_groups<VPL>(key, E, o.groups, o.topk_groups, lane);
+  const bool sigmoid = o.scoring == SCORE_SIGMOID;
+  const float m = sigmoid ? 0.f : wave_max_f32(lmax);
 
-  double s_all = 1.0;
-  if (!renorm) {
+  double s_all = 1.0;  // softmax without renormalisation: the sum over all E
+  if (!o.renorm && !sigmoid) {
     double s = 0.0;
 #pragma unroll
     for (int j = 0; j < VPL; ++j)
@@ -54,7 +92,7 @@ __device__ __forceinline__ void route_logits(const TokenLogits<VPL>& zl, int E, 
   }
 
   uint32_t taken = 0;  // bit j: this lane's value j already selected
-  float my_e = 0.f;
+  double my_e = 0.0;
   int my_id = 0;
   double denom = 0.0;
   for (int k = 0; k < K; ++k) {
@@ -69,8 +107,10 @@ __device__ __forceinline__ void route_logits(const TokenLogits<VPL>& zl, int E, 
     const uint32_t gk = wave_max_u32(bk);
     const uint32_t gi = wave_min_u32(bk == gk ? bi : 0xFFFFFFFFu);
     if ((int)(gi & 63u) == lane) taken |= 1u << (gi >> 6);
-    const float e = expf(f32_from_order_key(gk) - m);
-    denom += (double)e;  // slot order
+    const float zk = f32_from_order_key(gk);
+    // softmax: fp32 exp(z - max); sigmoid: 1 / (1 + exp(-z)) in fp64
+    const double e = sigmoid ? 1.0 / (1.0 + exp(-(double)zk)) : (double)expf(zk - m);
+    denom += e;  // slot order
     if (lane == k) {
       my_e = e;
       my_id = (int)gi;
@@ -79,19 +119,12 @@ __device__ __forceinline__ void route_logits(const TokenLogits<VPL>& zl, int E, 
   w_slot = 0.f;
   id_slot = 0;
   if (lane < K) {
-    const double d = renorm ? (denom > 0.0 ? denom : 1.0) : s_all;
-    double w = (double)my_e / d;
+    const double d = o.renorm ? (denom > 0.0 ? denom : 1.0) : s_all;
+    double w = my_e / d;
     if (pes) w *= (double)pes[my_id];
     w_slot = (float)w;
     id_slot = my_id;
   }
-}
-
-template <int VPL>
-__device__ __forceinline__ void route_token(const float* __restrict__ z, int E, int K, int renorm,
-                                            const float* __restrict__ pes, int lane, float& w_slot,
-                                            int& id_slot) {
-  route_logits<VPL>(load_logits<VPL>(z, E, lane), E, K, renorm, pes, lane, w_slot, id_slot);
 }
 
 }  // namespace moe

@@ -78,6 +78,13 @@ def _ws(desc, T):
     (dict(router_mode=5), B.MOE_INVALID_ARG),
     (dict(eps=-1.0), B.MOE_INVALID_ARG),
     (dict(top_k=60, num_experts=128, n_shared=8), B.MOE_UNSUPPORTED),
+    (dict(scoring=2), B.MOE_INVALID_ARG),
+    (dict(n_groups=-1), B.MOE_INVALID_ARG),
+    (dict(n_groups=3), B.MOE_INVALID_ARG),                 # does not divide E = 8
+    (dict(n_groups=4, topk_groups=0), B.MOE_INVALID_ARG),
+    (dict(n_groups=4, topk_groups=5), B.MOE_INVALID_ARG),
+    (dict(n_groups=4, topk_groups=1, top_k=3), B.MOE_INVALID_ARG),  # 2 candidates < 3
+    (dict(num_experts=128, top_k=2, n_groups=128, topk_groups=2), B.MOE_UNSUPPORTED),
 ])
 def test_bad_descriptors_rejected(kw, status):
     st, _ = _ws(_desc(**kw), 16)
@@ -125,11 +132,17 @@ def test_forward_rejects_missing_tensors_and_small_workspace():
 def test_route_and_permute_validation():
     lib = _lib()
     fake = 0x1000
-    assert lib.moe_route(fake, 4, 8, 9, 1, None, fake, fake, None) == B.MOE_INVALID_ARG
-    assert lib.moe_route(fake, 4, 600, 2, 1, None, fake, fake, None) == B.MOE_UNSUPPORTED
-    assert lib.moe_route(fake, -1, 8, 2, 1, None, fake, fake, None) == B.MOE_INVALID_ARG
-    assert lib.moe_route(None, 0, 8, 2, 1, None, None, None, None) == B.MOE_OK
-    assert lib.moe_route(None, 4, 8, 2, 1, None, fake, fake, None) == B.MOE_INVALID_ARG
+    assert lib.moe_route(fake, 4, 8, 9, 1, 0, 0, 0, None, fake, fake, None) == B.MOE_INVALID_ARG
+    assert lib.moe_route(fake, 4, 600, 2, 1, 0, 0, 0, None, fake, fake, None) == B.MOE_UNSUPPORTED
+    assert lib.moe_route(fake, -1, 8, 2, 1, 0, 0, 0, None, fake, fake, None) == B.MOE_INVALID_ARG
+    assert lib.moe_route(None, 0, 8, 2, 1, 0, 0, 0, None, None, None, None) == B.MOE_OK
+    assert lib.moe_route(None, 4, 8, 2, 1, 0, 0, 0, None, fake, fake, None) == B.MOE_INVALID_ARG
+    # routing options are checked before anything else, T = 0 included
+    assert lib.moe_route(None, 0, 8, 2, 1, 2, 0, 0, None, None, None, None) == B.MOE_INVALID_ARG
+    assert lib.moe_route(None, 0, 8, 2, 1, 1, 3, 1, None, None, None, None) == B.MOE_INVALID_ARG
+    assert lib.moe_route(None, 0, 8, 5, 1, 1, 4, 2, None, None, None, None) == B.MOE_INVALID_ARG
+    assert lib.moe_route(None, 0, 8, 4, 1, 1, 4, 2, None, None, None, None) == B.MOE_OK
+    assert lib.moe_route(None, 0, 8, 2, 1, 0, 1, 0, None, None, None, None) == B.MOE_OK  # 1 group = none
     assert lib.moe_permute(fake, 4, 2, 8, 48, fake, fake, fake, fake, None) == B.MOE_INVALID_ARG
     assert lib.moe_permute(fake, 4, 2, 8, 512, fake, fake, fake, fake, None) == B.MOE_INVALID_ARG
     assert lib.moe_permute(fake, 4, 0, 8, 64, fake, fake, fake, fake, None) == B.MOE_INVALID_ARG

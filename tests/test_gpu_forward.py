@@ -127,6 +127,14 @@ SMALL = {
                                     router_mode="gemma", per_expert_scale="uniform", I_dense=2112),
     "fp32_gemma_router": W.LayerSpec("fp32_gemma", 50, 128, 8, 3, 64, "gelu_tanh", "fp32",
                                      router_mode="gemma", I_dense=64, random_gammas=True),
+    # sigmoid scoring and expert groups, with a shared expert / without renormalisation
+    "v3_sigmoid_groups": W.LayerSpec("v3_small", 300, 256, 32, 4, 128, "silu", "bf16", n_shared=1,
+                                     I_shared=128, scoring="sigmoid", n_groups=8, topk_groups=2),
+    "softmax_groups_norenorm": W.LayerSpec("grp_norenorm", 200, 256, 64, 6, 128, "silu", "bf16",
+                                           renorm=False, per_expert_scale="uniform", n_groups=4,
+                                           topk_groups=2),
+    "fp32_sigmoid_groups": W.LayerSpec("fp32_v3", 40, 128, 16, 3, 64, "silu", "fp32",
+                                       scoring="sigmoid", n_groups=4, topk_groups=2),
 }
 
 
@@ -174,6 +182,8 @@ DECODE = {
     "e512_k8": W.LayerSpec("dec_e512", 1, 128, 512, 8, 64, "silu", "bf16"),
     "single_expert": W.LayerSpec("dec_e1", 1, 128, 1, 1, 128, "gelu_tanh", "bf16"),
     "h8192": W.LayerSpec("dec_h8192", 1, 8192, 4, 1, 128, "silu", "bf16"),
+    "v3_sigmoid_groups": W.LayerSpec("dec_v3", 1, 256, 32, 4, 128, "silu", "bf16", n_shared=1,
+                                     I_shared=128, scoring="sigmoid", n_groups=8, topk_groups=2),
 }
 DECODE_T = {"h8192": (1, 8)}
 
@@ -211,7 +221,8 @@ def test_decode_deterministic_and_workspace_reuse(B):
 
 # ------------------------------------------------------------------ full-size configurations
 FULL = [("tiny", 64), ("mixtral", 1), ("mixtral", 4096), ("gemma", 1), ("gemma", 16), ("gemma", 128),
-        ("gemma", 8192), ("deepseek", 16), ("deepseek", 16384), ("skewed_fp8", 1), ("skewed_fp8", 4096)]
+        ("gemma", 8192), ("deepseek", 16), ("deepseek", 16384), ("skewed_fp8", 1), ("skewed_fp8", 4096),
+        ("deepseek_v3", 1), ("deepseek_v3", 16), ("deepseek_v3", 8192)]
 
 
 def _rows(T, n=256):

@@ -32,12 +32,12 @@ def _logits(T, E, seed, kind="normal"):
     return z
 
 
-def _check_route(B, z, K, renorm=True, scale=None):
+def _check_route(B, z, K, renorm=True, scale=None, scoring="softmax", G=0, KG=0):
     zt = torch.from_numpy(z).cuda()
     st = None if scale is None else torch.from_numpy(scale).cuda()
-    w, ids = B.route(zt, K, renorm, st)
+    w, ids = B.route(zt, K, renorm, st, scoring=scoring, n_groups=G, topk_groups=KG)
     torch.cuda.synchronize()
-    wr, idr = O.route(z.astype(np.float64), K, renorm, scale)
+    wr, idr = O.route(z.astype(np.float64), K, renorm, scale, scoring, max(G, 1), max(KG, 1))
     assert np.array_equal(ids.cpu().numpy(), idr), "topk_ids differ"
     assert_weights_close(w.cpu().numpy(), wr)
 
@@ -56,6 +56,28 @@ def test_route_scale_and_renorm(B, renorm):
     z = _logits(517, E, seed=3, kind="skewed")
     scale = np.random.default_rng(4).uniform(0.5, 1.5, E).astype(np.float32)
     _check_route(B, z, K, renorm, scale)
+
+
+# sigmoid scoring and expert groups (llama.cpp MoE lesson): group ranges that
+# straddle lanes (25, 32 experts), one expert per group, the 64-group limit
+@pytest.mark.parametrize("E,K,G,KG", [(256, 8, 8, 4), (64, 6, 8, 3), (96, 8, 3, 1), (200, 10, 8, 2),
+                                      (16, 4, 16, 4), (512, 16, 64, 8), (8, 2, 0, 0)])
+@pytest.mark.parametrize("scoring,renorm", [("sigmoid", True), ("sigmoid", False), ("softmax", False)])
+@pytest.mark.parametrize("kind", ["normal", "ties"])
+def test_route_sigmoid_and_groups(B, E, K, G, KG, scoring, renorm, kind):
+    z = _logits(1003, E, seed=E * 11 + K + G, kind=kind)
+    scale = np.random.default_rng(E).uniform(0.5, 1.5, E).astype(np.float32)
+    _check_route(B, z, K, renorm, scale, scoring, G, KG)
+
+
+def test_route_groups_tied_group_scores(B):
+    """Groups whose best logits tie: the lower group is picked (hand-checked row
+    from the oracle's pins), on every token of a 4-token batch."""
+    z = np.tile(np.array([[1.0, 0.0, 0.0, 1.0, 2.0, 2.0, -1.0, -1.0]], dtype=np.float32), (4, 1))
+    zt = torch.from_numpy(z).cuda()
+    w, ids = B.route(zt, 4, True, scoring="sigmoid", n_groups=4, topk_groups=2)
+    assert ids.cpu().tolist() == [[4, 5, 0, 1]] * 4
+    _check_route(B, z, 4, True, None, "sigmoid", 4, 2)
 
 
 @pytest.mark.parametrize("T", [0, 1, 2, 3, 4, 5, 4097])
