@@ -19,16 +19,15 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
   return __uint_as_float(((uint32_t)v) << 16);
 }
 
-// Round-to-nearest-even fp32 -> bf16 (inputs are finite).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
-
+// Round-to-nearest-even fp32 -> bf16: gfx950's v_cvt_pk_bf16_f32 (two values
+// per instruction; NaN stays NaN, overflow rounds to infinity).
+typedef float f32x2_cvt __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_cvt __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const f32x2_cvt v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_cvt));
 }
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return (bf16_t)(pack_bf16x2(f, 0.f) & 0xFFFFu); }
 
 // ---------------------------------------------------------------- wave64 reductions
 // All-reduce over the 64 lanes with DPP moves only (no LDS round trip):
@@ -111,6 +110,19 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float apply_act(int act, float g) {
   return act == 0 ? act_silu(g) : act_gelu_tanh(g);
+}
+
+// The same activations for results rounded to bf16 next (8 significant bits):
+// both are g * sigmoid(t) (SiLU: t = g; GELU-tanh: t = 2c(g + 0.044715 g^3)),
+// and the sigmoid is taken from the hardware base-2 exponential and reciprocal
+// (v_exp_f32, v_rcp_f32, about 1 ulp each).  A few fp32 ulps in all, against
+// the 2^-9 relative step of the rounding that follows; about a quarter of the
+// instructions of the correctly rounded exponential and division.  Limits:
+// t -> -inf gives g * 0, t -> +inf gives g.
+__device__ __forceinline__ float apply_act_bf16(int act, float g) {
+  const float t = act == 0 ? g : 1.5957691216057308f * (g + 0.044715f * g * g * g);  // 2 sqrt(2/pi)
+  const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * t);                   // e^-t
+  return g * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 // 8 fp8 (E4M3) codes in two dwords -> 8 bf16.  v_cvt_pk_f32_fp8 widens two codes

@@ -597,7 +597,7 @@ void gemm_mfma_kernel(GemmArgs p) {
           gv *= bscale[n0 + col + q];
           uv *= bscale[p.N + n0 + col + q];
         }
-        v[q] = apply_act(p.act, gv) * uv;
+        v[q] = apply_act_bf16(p.act, gv) * uv;
       } else {
         v[q] = acc[i][j][4 * g4 + q] * rs;
         if constexpr (FP8) v[q] *= bscale[n0 + col + q];
@@ -682,10 +682,13 @@ void gemm_mfma_kernel(GemmArgs p) {
     for (int i = 0; i < TM; ++i) {
       const int64_t grow = m0 + wm * WM + 32 * i + l32;
       if (grow >= m_rows || !wave_live) continue;
-      if (p.a_rows && p.a_rows[grow] < 0) continue;  // padding: never read back
+      // Padding rows (slot -1) hold zeros (their A rows load as zeros) and are
+      // stored like the others, so no row-map lookup waits here unless a
+      // per-token factor needs the row's token.
       float rs = 1.f;
       if (p.row_scale) {
         const int slot = p.a_rows ? p.a_rows[grow] : 0;
+        if (slot < 0) continue;  // padding: never read back
         rs = p.row_scale[p.a_rows ? slot / p.row_div : grow];
       }
       bf16_t* C = (bf16_t*)p.C + grow * p.ldc;
@@ -703,7 +706,7 @@ void gemm_mfma_kernel(GemmArgs p) {
               gv *= bscale[col + q];
               uv *= bscale[p.N + col + q];
             }
-            h[q] = apply_act(p.act, gv) * uv;
+            h[q] = apply_act_bf16(p.act, gv) * uv;
           }
           uint2 pk;
           pk.x = pack_bf16x2(h[0], h[1]);
