@@ -57,6 +57,7 @@ class LayerSpec:
     scoring: str = "softmax"     # "softmax" over all experts | "sigmoid" per expert
     n_groups: int = 0            # > 1: group-limited routing over this many expert groups
     topk_groups: int = 0         # groups picked per token when n_groups > 1
+    act_quant: Optional[str] = None  # "fp8_dynamic": FP8 activations (needs FP8 weights)
 
     def with_T(self, T):
         return dataclasses.replace(self, T=T)
@@ -80,11 +81,17 @@ SPECS = {
     "deepseek_v3": LayerSpec("deepseek_v3", 8192, 2048, 256, 8, 1408, "silu", "bf16",
                              n_shared=1, I_shared=1408, scoring="sigmoid", n_groups=8,
                              topk_groups=4),
+    # FP8 weights and dynamically quantised FP8 activations (W8A8)
+    "mixtral_w8a8": LayerSpec("mixtral_w8a8", 4096, 4096, 8, 2, 14336, "silu", "fp8",
+                              act_quant="fp8_dynamic"),
+    "skewed_w8a8": LayerSpec("skewed_w8a8", 4096, 2816, 128, 8, 704, "gelu_tanh", "fp8",
+                             supplied_logits=True, act_quant="fp8_dynamic"),
 }
 
 # token counts the pages' configurations name for each layer shape
 T_VALUES = {"tiny": [64], "mixtral": [4096], "gemma": [1, 16, 128, 8192],
-            "deepseek": [16384], "skewed_fp8": [1, 4096], "deepseek_v3": [1, 16, 8192]}
+            "deepseek": [16384], "skewed_fp8": [1, 4096], "deepseek_v3": [1, 16, 8192],
+            "mixtral_w8a8": [4096], "skewed_w8a8": [1, 4096]}
 
 
 def _rng(seed, *key):
@@ -213,7 +220,8 @@ def oracle_layer(L):
 
     d = dict(E=spec.E, K=spec.K, act=spec.act, renorm=spec.renorm,
              scoring=spec.scoring, n_groups=max(spec.n_groups, 1),
-             topk_groups=max(spec.topk_groups, 1), router_mode=spec.router_mode, w_router=f(L["w_router"]),
+             topk_groups=max(spec.topk_groups, 1), act_quant=spec.act_quant,
+             router_mode=spec.router_mode, w_router=f(L["w_router"]),
              router_scale=f(L["router_scale"]), per_expert_scale=f(L["per_expert_scale"]),
              w13=f(L["w13"]), w2=f(L["w2"]), w13_scale=f(L["w13_scale"]),
              w2_scale=f(L["w2_scale"]))

@@ -25,7 +25,7 @@ the order and notation of the pages it follows:
   normalise routing, sigmoid scoring, expert groups; mul_mat_id sparse expert
   matmuls; shared experts.
 * sglang PR #24696 summary: per-expert FP8 weights with a weight_scale per
-  projection.
+  projection; "FP8-Dynamic" checkpoints (activations quantised at run time).
 
 Readings where the pages are silent are listed in the repository's design
 notes and repeated at the function that takes them.  Every function here is
@@ -102,6 +102,63 @@ def decode_e4m3fn(codes):
     mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
     val = np.where(s == 1, -mag, mag)
     return np.where((e == 15) & (m == 7), np.nan, val)
+
+
+def _e4m3fn_values():
+    """The 127 non-negative finite E4M3 values, by code 0..126, ascending."""
+    return decode_e4m3fn(np.arange(127, dtype=np.uint8))
+
+
+def encode_e4m3fn(x):
+    """Nearest OCP E4M3 ("fn") code of each float32 value, ties to the even code
+    (the one whose last mantissa bit is 0), magnitudes beyond 448 saturating to
+    448, the sign kept (negative values that round to zero give -0).  Written
+    from the format's definition: a search over the ascending table of the
+    representable magnitudes."""
+    x = np.asarray(x, dtype=np.float32)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("values to encode must be finite")
+    vals = _e4m3fn_values()
+    mag = np.minimum(np.abs(x).astype(np.float64), vals[-1])
+    hi = np.clip(np.searchsorted(vals, mag, side="left"), 0, 126)  # first value >= mag
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = mag - vals[lo], vals[hi] - mag
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)  # -0 for negatives rounding to 0
+
+
+def quantize_rows_fp8(a):
+    """Dynamic per-row FP8 quantisation of an activation matrix, the scheme of
+    the "FP8-Dynamic" checkpoints named on the sglang PR page (activations
+    quantised at run time, one scale per token row).
+
+    Readings (the page names the scheme, not its arithmetic): scale = the row's
+    largest magnitude / 448 (the largest E4M3 value), 1 for an all-zero row;
+    code = nearest E4M3 of value / scale.  Both steps in float32, the precision
+    the kernel takes these decisions in, so that the codes are a function of
+    the float32 inputs alone.  Returns (codes uint8 [R, C], scales float32 [R])."""
+    a = np.asarray(a, dtype=np.float32)
+    amax = np.abs(a).max(axis=-1)
+    scale = (amax / np.float32(448.0)).astype(np.float32)
+    scale = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    codes = encode_e4m3fn((a / scale[:, None]).astype(np.float32))
+    return codes, scale
+
+
+def fp8_roundtrip_rows(a):
+    """The activation a GEMM sees after dynamic FP8 quantisation: codes x scale."""
+    codes, scale = quantize_rows_fp8(a)
+    return decode_e4m3fn(codes) * scale.astype(np.float64)[:, None]
+
+
+def round_bf16(a):
+    """Round float64 values to the nearest bfloat16 (ties to even), returned as
+    float64: the storage precision of the gated intermediate in the bf16 layer."""
+    f = np.asarray(a, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
 # ----------------------------------------------------------------------------
@@ -269,22 +326,33 @@ def permutation(ids, E):
 # Expert FFN ("MOE Inference" gated FFN; Gemma 4 walkthrough §6)
 # ----------------------------------------------------------------------------
 
-def gated_ffn(xrows, w13, w2, act):
+def gated_ffn(xrows, w13, w2, act, act_quant=None):
     """(Act(x w1) * (x w3)) w2 for a block of rows.
 
     w13 has shape [2I, H]: rows [0, I) are the gate projection w1, rows
     [I, 2I) the up projection w3 (vLLM load_weights: gate_proj is shard w1,
-    up_proj shard w3, both [I, H]); w2 has shape [H, I] (down_proj)."""
+    up_proj shard w3, both [I, H]); w2 has shape [H, I] (down_proj).
+
+    act_quant="fp8_dynamic": each projection's input rows are quantised as in
+    quantize_rows_fp8 first: x before gate/up, and h, as stored (rounded to
+    bf16), before the down projection."""
     xrows = _f64(xrows)
     w13 = _f64(w13)
     I = w13.shape[0] // 2
+    if act_quant == "fp8_dynamic":
+        xrows = fp8_roundtrip_rows(xrows)
+    elif act_quant is not None:
+        raise ValueError(f"unknown activation quantisation {act_quant!r}")
     g = xrows @ w13[:I].T
     u = xrows @ w13[I:].T
     h = activation(act)(g) * u
+    if act_quant == "fp8_dynamic":
+        h = fp8_roundtrip_rows(round_bf16(h))
     return h @ _f64(w2).T
 
 
-def moe_combine(xe, weights, ids, w13, w2, act, rows=None, w13_scale=None, w2_scale=None):
+def moe_combine(xe, weights, ids, w13, w2, act, rows=None, w13_scale=None, w2_scale=None,
+                act_quant=None):
     """Sparse MoE output for the selected rows: out_t = sum_j w[t,j] * FFN_{ids[t,j]}(xe_t).
 
     Only the selected experts are evaluated (llama.cpp lesson 35: mul_mat_id
@@ -311,7 +379,7 @@ def moe_combine(xe, weights, ids, w13, w2, act, rows=None, w13_scale=None, w2_sc
             continue
         W13 = _expert_weight(w13, w13_scale, e)
         W2 = _expert_weight(w2, w2_scale, e)
-        y[ri, ji] = gated_ffn(xe[rows[ri]], W13, W2, act)
+        y[ri, ji] = gated_ffn(xe[rows[ri]], W13, W2, act, act_quant)
     out = np.zeros((len(rows), H))
     for j in range(k):  # slot order
         out += weights[rows, j][:, None] * y[:, j]
@@ -334,6 +402,7 @@ def moe_layer(x, layer, rows=None, logits=None):
     `layer` is a dict with:
       E, K, act, renorm, router_mode ('plain'|'gemma'),
       scoring ('softmax'|'sigmoid'), n_groups, topk_groups (group-limited routing),
+      act_quant (None | 'fp8_dynamic': routed experts' inputs quantised per row),
       w_router [E,H] or None (then `logits` must be given),
       router_scale [H] or None, per_expert_scale [E] or None,
       w13 [E,2I,H], w2 [E,H,I] (+ w13_scale [E,2I], w2_scale [E,H] for FP8 codes),
@@ -375,7 +444,7 @@ def moe_layer(x, layer, rows=None, logits=None):
     else:
         xe = x
     moe = moe_combine(xe, w, ids, layer["w13"], layer["w2"], layer["act"], rows,
-                      layer.get("w13_scale"), layer.get("w2_scale"))
+                      layer.get("w13_scale"), layer.get("w2_scale"), layer.get("act_quant"))
     shared = layer.get("shared")
     if shared is not None:
         sw13, sw2 = shared

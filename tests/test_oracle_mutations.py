@@ -7,9 +7,9 @@ from oracle import moe_oracle as O
 import tests.test_oracle_pins as P
 
 
-def _swapped_gate_up(xrows, w13, w2, act):
+def _swapped_gate_up(xrows, w13, w2, act, act_quant=None):
     I = w13.shape[0] // 2
-    return O.__dict__["_orig_gated_ffn"](xrows, np.concatenate([w13[I:], w13[:I]]), w2, act)
+    return O.__dict__["_orig_gated_ffn"](xrows, np.concatenate([w13[I:], w13[:I]]), w2, act, act_quant)
 
 
 def _fails(fn, *a, **k):
@@ -91,3 +91,32 @@ def test_sigmoid_sign_error_is_caught(monkeypatch):
     monkeypatch.setattr(O, "sigmoid_scores", lambda z: 1.0 / (1.0 + np.exp(np.asarray(z, dtype=np.float64))))
     _fails(P.test_sigmoid_scores_match_library_and_closed_forms)
     _fails(P.test_sigmoid_route_sorts_probabilities, True)
+
+
+def test_fp8_scale_for_wrong_maximum_is_caught(monkeypatch):
+    def bad(a):
+        a = np.asarray(a, dtype=np.float32)
+        scale = (np.abs(a).max(axis=-1) / np.float32(240.0)).astype(np.float32)
+        scale = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+        return O.encode_e4m3fn((a / scale[:, None]).astype(np.float32)), scale
+    monkeypatch.setattr(O, "quantize_rows_fp8", bad)
+    _fails(P.test_dynamic_fp8_rows_properties)
+    _fails(P.test_fp8_dynamic_ffn_matches_torch_composition)
+
+
+def test_truncating_e4m3_encode_is_caught(monkeypatch):
+    orig = O.encode_e4m3fn
+
+    def bad(x):
+        x = np.asarray(x, dtype=np.float32)
+        c = orig(x)
+        back = O.decode_e4m3fn(c)
+        over = np.abs(back) > np.abs(x)  # rounded away from zero: step back (truncation)
+        return np.where(over & ((c & 0x7F) > 0), c - 1, c).astype(np.uint8)
+    monkeypatch.setattr(O, "encode_e4m3fn", bad)
+    _fails(P.test_e4m3_encode_matches_torch_including_ties)
+
+
+def test_h_quantised_without_bf16_rounding_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "round_bf16", lambda a: np.asarray(a, dtype=np.float64))
+    _fails(P.test_fp8_dynamic_ffn_matches_torch_composition)

@@ -320,6 +320,77 @@ def test_fp8_decode_all_codes_match_torch():
     assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
 
 
+def test_e4m3_encode_matches_torch_including_ties():
+    """Nearest-even E4M3 encoding against torch's float8_e4m3fn conversion: every
+    representable value, every midpoint between neighbours (ties), a dense sweep,
+    values near zero of both signs, and saturation above 448."""
+    vals = torch.arange(0, 127, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    mids = (vals[:-1] + vals[1:]) / 2
+    x = np.concatenate([vals, -vals, mids, -mids, np.linspace(-460, 460, 40001),
+                        np.linspace(-0.003, 0.003, 601)]).astype(np.float32)
+    ref = torch.from_numpy(np.clip(x, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.encode_e4m3fn(x), ref)
+    assert O.encode_e4m3fn(np.array([1e6, -1e6], dtype=np.float32)).tolist() == [0x7E, 0xFE]
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(30)
+    a = np.concatenate([rng.standard_normal(20000) * 10, rng.standard_normal(2000) * 1e-30])
+    ref = torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(O.round_bf16(a), ref.astype(np.float64))
+
+
+def test_dynamic_fp8_rows_properties():
+    """Per row: the largest magnitude maps to +-448 exactly; every value comes back
+    within half an E4M3 step (relative 2^-4 above the subnormal range, absolute
+    2^-10 scale below it); scaling a row by a power of two keeps its codes; an
+    all-zero row has scale 1 and zero codes."""
+    rng = np.random.default_rng(31)
+    a = (rng.standard_normal((64, 300)) * rng.uniform(0.01, 100, (64, 1))).astype(np.float32)
+    a[5] = 0.0
+    codes, scale = O.quantize_rows_fp8(a)
+    nz = np.arange(64) != 5
+    arg = np.abs(a).argmax(axis=1)
+    assert np.all((codes[nz, arg[nz]] & 0x7F) == 0x7E)
+    assert scale[5] == 1.0 and not codes[5].any()
+    back = O.decode_e4m3fn(codes) * scale[:, None].astype(np.float64)
+    err = np.abs(back - a)
+    bound = np.maximum(np.abs(a) * 2.0 ** -4, scale[:, None] * 2.0 ** -10)
+    assert np.all(err <= bound * (1 + 1e-6))
+    c2, s2 = O.quantize_rows_fp8(a * np.float32(8.0))
+    assert np.array_equal(c2, codes) and np.array_equal(s2[nz], scale[nz] * 8)
+
+
+def test_fp8_dynamic_ffn_matches_torch_composition():
+    """The W8A8 expert FFN through torch, one library step at a time: per-row scale,
+    float8_e4m3fn conversion of x / scale, float64 matmuls, bfloat16 rounding of h,
+    the same quantisation of h, the down projection."""
+    rng = np.random.default_rng(32)
+    H, I, R = 64, 48, 40
+    x = rng.standard_normal((R, H)).astype(np.float32)
+    w13 = rng.standard_normal((2 * I, H)) / 8
+    w2 = rng.standard_normal((H, I)) / 7
+
+    def tq(a):  # torch: per-row dynamic FP8
+        a = torch.as_tensor(a, dtype=torch.float32)
+        s = a.abs().amax(dim=1) / 448.0
+        s = torch.where(s > 0, s, torch.ones_like(s))
+        q = (a / s[:, None]).to(torch.float8_e4m3fn)
+        return q.double() * s.double()[:, None]
+
+    xq = tq(x)
+    W13 = torch.from_numpy(w13)
+    g, u = xq @ W13[:I].T, xq @ W13[I:].T
+    h = F.silu(g) * u
+    hq = tq(h.to(torch.bfloat16).float())
+    ref = (hq @ torch.from_numpy(w2).T).numpy()
+    got = O.gated_ffn(x, w13, w2, "silu", act_quant="fp8_dynamic")
+    np.testing.assert_allclose(got, ref, rtol=1e-9, atol=1e-12)
+    # and it is an approximation of the unquantised FFN, not a different function
+    plain = O.gated_ffn(x, w13, w2, "silu")
+    assert np.sqrt(np.mean((got - plain) ** 2) / np.mean(plain ** 2)) < 0.1
+
+
 def test_fp8_layer_equals_decoded_bf16_layer():
     """The FP8 path is the plain layer on decode(q) * s."""
     rng = np.random.default_rng(10)
