@@ -35,6 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 
 METRIC = "MoE layer tokens/s; prefill TFLOP/s % MFMA peak; decode GB/s % HBM peak"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA (the FP8-activation layers' contraction)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 MALL_BYTES = 256 << 20
 
@@ -133,6 +134,9 @@ def stage_work(spec, T, counts, path, dense_stage=None):
         by["router"] = z * (E * H * ab + T * H * ab + T * E * 4)
         by["gate_up"] = w_up + T * H * ab + rows * I * ab
         by["down"] = w_down + rows * I * ab + (rows + T * S) * H * ab
+        if spec.act_quant:  # + the row quantisation of x and h: codes written and read back
+            by["gate_up"] += 2 * T * H
+            by["down"] += 2 * rows * I
         by["dense_gate_up"] = 2 * Id * H * ab + T * H * ab + T * Id * ab
         by["dense_down"] = H * Id * ab + T * Id * ab + T * H * 4
         by["finalize"] = T * Kp * H * (4 if Id else ab) + T * H * ab
@@ -314,11 +318,12 @@ def main():
     dom = max(cand, key=lambda s: stage_ms[s])
     dom_s = stage_ms[dom] / 1e3
     intensity = fl[dom] / max(by[dom], 1)
-    # ridge point of MI355X: 2500e12 / 8e12 = 312 FLOP/byte
-    if intensity >= PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3:
+    # ridge point of MI355X: 2500e12 / 8e12 = 312 FLOP/byte (bf16); fp8: 625
+    peak_mfma = PEAK_FP8_TFLOPS if spec.act_quant and dom in ("gate_up", "down") else PEAK_BF16_TFLOPS
+    if intensity >= peak_mfma / PEAK_HBM_GBS * 1e3:
         achieved = fl[dom] / dom_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_mfma, "unit": "TFLOP/s",
+                "frac": round(achieved / peak_mfma, 4), "traffic": None}
     else:
         achieved = by[dom] / dom_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -343,12 +348,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"fp32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 activations"}[spec.wdtype],
+        "dtype": ("fp8-e4m3 weights and activations (per-row dynamic activation scales)" if spec.act_quant else
+                  {"fp32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 activations"}[spec.wdtype]),
         "data": "synthetic",
         "config": {"workload": f"{spec.name} MoE FFN layer forward", "T": T, "hidden": spec.H,
                    "experts": spec.E, "top_k": spec.K, "inter": spec.I, "act": spec.act,
                    "shared": spec.n_shared, "dense_inter": spec.I_dense, "scoring": spec.scoring,
-                   "groups": [spec.n_groups, spec.topk_groups] if spec.n_groups > 1 else None, "path": path,
+                   "groups": [spec.n_groups, spec.topk_groups] if spec.n_groups > 1 else None,
+                   "act_quant": spec.act_quant, "path": path,
                    "weight_sets": len(sets)},
         "step_tflops": round(total_flop / (ms_per_step / 1e3) / 1e12, 2),
         "step_gbps": round(total_bytes / (ms_per_step / 1e3) / 1e9, 1),

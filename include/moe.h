@@ -51,6 +51,9 @@ typedef enum { MOE_ROUTER_PLAIN = 0, MOE_ROUTER_GEMMA = 1 } moe_router_mode;
 /* How the router turns logits into routing probabilities ([LC] routing: a
  * softmax, or in some models a sigmoid). */
 typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_scoring;
+/* Activation quantisation of the routed experts' GEMM inputs ([SG]: the
+ * "FP8-Dynamic" checkpoints quantise activations at run time, per token). */
+typedef enum { MOE_ACT_QUANT_NONE = 0, MOE_ACT_QUANT_FP8_DYNAMIC = 1 } moe_act_quant;
 
 /* Human-readable name of a status code (static storage). */
 const char* moe_status_string(moe_status s);
@@ -142,6 +145,8 @@ typedef struct {
   int32_t scoring;       /* moe_scoring (see moe_route) */
   int32_t n_groups;      /* expert groups for group-limited routing: 0 or 1 = none, else 2..64 */
   int32_t topk_groups;   /* groups picked per token when n_groups > 1 */
+  int32_t act_quant;     /* moe_act_quant: MOE_ACT_QUANT_FP8_DYNAMIC needs FP8 weights, bf16 x,
+                            no dense branch and inter <= 16384 (see moe_forward) */
 } moe_layer_desc;
 
 /* Tensors of one forward call (device pointers unless noted).  The matrix
@@ -191,6 +196,11 @@ moe_status moe_forward_workspace_size(const moe_layer_desc* desc, int64_t T, siz
  *            (gated FFN, [MI]; activation SiLU [LC] or GELU-tanh [G4] section 6);
  *            x_e = RMSNorm(x) * gamma_pre2 when the dense branch is present, else x;
  *            FP8 weights: W = decode_e4m3(q) * scale[e, n] ([SG]);
+ *            FP8 activations (act_quant, [SG] FP8-Dynamic): the GEMM inputs x_e and
+ *            h are each quantised per row first, scale = max|row| / 448 (1 for a
+ *            zero row), code = E4M3 nearest-even of value / scale (fp32), h as
+ *            stored in bf16; the products run on FP8 x FP8 MFMAs and the row and
+ *            channel scales multiply the accumulators;
  *   moe_t  = sum_j w[t,j] y_{t,j}              (weighted combine, [G4] section 7);
  *   shared experts: moe_t += sum_s FFN_s(x_t) with weight 1 ([LC] shared expert);
  *   dense branch (inter_dense > 0, [G4] section 1):
@@ -208,7 +218,7 @@ moe_status moe_forward_workspace_size(const moe_layer_desc* desc, int64_t T, siz
  * grouped GEMMs; moe_forward_profiled keeps it on `stream`.
  *
  * Two execution paths compute this same operation (moe_forward_path tells which
- * one a call takes).  The grouped path permutes the routed rows and runs grouped
+ * one a call takes; layers with FP8 activations always take the grouped path).  The grouped path permutes the routed rows and runs grouped
  * GEMMs.  The decode path (T <= 16 bf16 tokens) streams each selected expert's
  * weights once and applies them to all tokens together; it folds the routing
  * weight into the gated intermediate before its bf16 rounding and sums the

@@ -21,6 +21,7 @@ ACT = {"silu": 0, "gelu_tanh": 1}
 DT_F32, DT_BF16, DT_FP8 = 0, 1, 2
 ROUTER_PLAIN, ROUTER_GEMMA = 0, 1
 SCORING = {"softmax": 0, "sigmoid": 1}
+ACT_QUANT = {None: 0, "fp8_dynamic": 1}
 
 
 class MoEError(RuntimeError):
@@ -39,7 +40,7 @@ class LayerDesc(C.Structure):
                 ("weight_dtype", C.c_int32), ("renormalize", C.c_int32), ("router_mode", C.c_int32),
                 ("n_shared", C.c_int32), ("inter_dense", C.c_int32), ("dense_act", C.c_int32),
                 ("eps", C.c_float), ("scoring", C.c_int32), ("n_groups", C.c_int32),
-                ("topk_groups", C.c_int32)]
+                ("topk_groups", C.c_int32), ("act_quant", C.c_int32)]
 
 
 class Tensors(C.Structure):
@@ -195,7 +196,7 @@ class DeviceLayer:
                          router_mode=ROUTER_GEMMA if spec.router_mode == "gemma" else ROUTER_PLAIN,
                          n_shared=spec.n_shared, inter_dense=spec.I_dense, dense_act=ACT[spec.act],
                          eps=eps, scoring=SCORING[spec.scoring], n_groups=spec.n_groups,
-                         topk_groups=spec.topk_groups)
+                         topk_groups=spec.topk_groups, act_quant=ACT_QUANT[spec.act_quant])
 
         def d(t):
             return None if t is None else t.to(device, non_blocking=False).contiguous()

@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_mi355x.so")
-SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm.hip", "norm.hip", "decode.hip"]
+SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm.hip", "norm.hip", "decode.hip", "quant.hip"]
 ARCH = "gfx950"
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-fvisibility=hidden", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -83,13 +83,14 @@ int64_t permute_capacity(int64_t n_slots, int E, int bm) {
 int choose_block_m(const moe_layer_desc& d, int64_t T) {
   if (d.act_dtype == MOE_DT_F32) return 64;
   const int64_t avg = T * d.top_k / d.num_experts;
+  if (d.act_quant) return avg >= 1024 ? 256 : 128;  // FP8 activations: 8-wave tiles only
   return avg >= 1024 ? 256 : (avg >= 128 ? 128 : 64);
 }
 
 // Decode path: at most 16 bf16 tokens (one MFMA tile of token columns) whose
 // rows fit the decode kernels' LDS staging.
 bool use_decode(const moe_layer_desc& d, int64_t T) {
-  if (d.act_dtype != MOE_DT_BF16 || T < 1 || T > 16) return false;
+  if (d.act_dtype != MOE_DT_BF16 || d.act_quant || T < 1 || T > 16) return false;
   const int lds_max = 160 * 1024;
   return moe::decode_up_lds_bytes((int)T, d.hidden, d.top_k + d.n_shared, d.num_experts + d.n_shared) <= lds_max &&
          moe::decode_pre_lds_bytes((int)T, d.hidden) <= lds_max;
@@ -104,6 +105,8 @@ struct Plan {
   bool need_logits, need_prenorm, gemma_router, dense;
   bool mat_r, mat_xn1, mat_xn2;  // normalised rows that must be materialised (learned weight present)
   bool y_f32;                    // per-slot expert outputs kept in fp32
+  bool aq;                       // FP8 activations: x and h quantised per row
+  size_t o_xq, o_xs, o_hq, o_hs;  // their codes and scales
   size_t o_logits, o_w, o_ids, o_counts, o_offsets, o_sorted, o_bexp, o_rms, o_r, o_xn1, o_xn2, o_h, o_y,
       o_dh, o_dout, total;
   size_t o_rinfo, o_ypart;  // decode path only
@@ -159,6 +162,14 @@ moe_status validate_desc(const moe_layer_desc* d) {
   if (d->router_mode != MOE_ROUTER_PLAIN && d->router_mode != MOE_ROUTER_GEMMA)
     return fail(MOE_INVALID_ARG, "unknown router mode %d", d->router_mode);
   if (!(d->eps >= 0.f)) return fail(MOE_INVALID_ARG, "eps must be >= 0");
+  if (d->act_quant != MOE_ACT_QUANT_NONE && d->act_quant != MOE_ACT_QUANT_FP8_DYNAMIC)
+    return fail(MOE_INVALID_ARG, "unknown act_quant %d", d->act_quant);
+  if (d->act_quant) {
+    if (d->weight_dtype != MOE_DT_FP8_E4M3 || d->act_dtype != MOE_DT_BF16)
+      return fail(MOE_UNSUPPORTED, "FP8 activations need FP8 expert weights and bf16 x");
+    if (d->inter_dense) return fail(MOE_UNSUPPORTED, "FP8 activations with the dense branch");
+    if (d->inter > 16384) return fail(MOE_UNSUPPORTED, "FP8 activations need inter <= 16384");
+  }
   moe::RouteOpts o;
   return route_opts(d->num_experts, d->top_k, d->renormalize, d->scoring, d->n_groups, d->topk_groups, o);
 }
@@ -198,6 +209,7 @@ moe_status make_plan(const moe_layer_desc& d, const moe_tensors* t, int64_t T, P
   // With the dense branch the MoE sum is RMS-normalised afterwards, which turns
   // its relative error into error at output scale: keep the per-slot rows fp32.
   p.y_f32 = p.f32 || p.dense;
+  p.aq = d.act_quant != MOE_ACT_QUANT_NONE;
   // Split the down GEMM's reduction when its tiles would fill the CUs in few
   // rounds (long reductions over few rows: the Mixtral-style layer); rows are
   // estimated with half a block of padding per expert.
@@ -224,6 +236,10 @@ moe_status make_plan(const moe_layer_desc& d, const moe_tensors* t, int64_t T, P
   p.o_y = take((size_t)slots * p.ks * H * (p.y_f32 ? 4 : ae));
   p.o_dh = take(p.dense ? (size_t)T * d.inter_dense * ae : 0);
   p.o_dout = take(p.dense ? (size_t)T * H * 4 : 0);
+  p.o_xq = take(p.aq ? (size_t)T * H : 0);
+  p.o_xs = take(p.aq ? (size_t)T * 4 : 0);
+  p.o_hq = take(p.aq ? (size_t)p.cap * d.inter : 0);
+  p.o_hs = take(p.aq ? (size_t)p.cap * 4 : 0);
   p.total = o;
   // The router GEMM has few output tiles (T/128 x E/128) and a reduction over all
   // of H: split it so the tiles cover the CUs.  Its partial planes live in the
@@ -456,7 +472,11 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
   }
   const int H = d.hidden, E = d.num_experts, K = d.top_k, I = d.inter;
   const int act_elem = p.f32 ? moe::ELEM_F32 : moe::ELEM_BF16;
-  const int b_elem = d.weight_dtype == MOE_DT_FP8_E4M3 ? moe::ELEM_FP8 : moe::ELEM_BF16;
+  const int b_elem = p.aq ? moe::ELEM_FP8X8 : (d.weight_dtype == MOE_DT_FP8_E4M3 ? moe::ELEM_FP8 : moe::ELEM_BF16);
+  uint8_t* xq = p.aq ? (uint8_t*)(ws + p.o_xq) : nullptr;
+  float* xs = p.aq ? (float*)(ws + p.o_xs) : nullptr;
+  uint8_t* hq = p.aq ? (uint8_t*)(ws + p.o_hq) : nullptr;
+  float* hs = p.aq ? (float*)(ws + p.o_hs) : nullptr;
   float* w = (float*)(ws + p.o_w);
   int32_t* ids = (int32_t*)(ws + p.o_ids);
   int32_t* counts = (int32_t*)(ws + p.o_counts);
@@ -570,10 +590,17 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
 
   STAGE(MOE_STAGE_GATE_UP);
   // 5. grouped gate/up GEMM + gated activation -> h [cap, I]
+  //    (FP8 activations: x quantised per token first, its scale a row factor)
+  if (p.aq)
+    HIP_TRY(moe::launch_quant_rows_fp8(t->x, T, H, H, nullptr, nullptr, xq, H, xs, st), "x quantisation launch");
   {
     moe::GemmArgs a{};
     a.A = p.mat_xn2 ? xn2 : t->x;
     if (p.dense && !p.mat_xn2) a.row_scale = inv_rms;
+    if (p.aq) {
+      a.A = xq;
+      a.row_scale = xs;
+    }
     a.lda = H;
     a.a_rows = sorted;
     a.row_div = p.Kp;
@@ -597,9 +624,14 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
   }
   STAGE(MOE_STAGE_DOWN);
   // 6. grouped down GEMM, scaled by the routing weight, scattered to per-slot rows
+  //    (FP8 activations: h quantised per padded row, padding rows to zeros)
+  if (p.aq)
+    HIP_TRY(moe::launch_quant_rows_fp8(h, p.cap, I, I, sorted, offsets + p.Ep, hq, I, hs, st),
+            "h quantisation launch");
   {
     moe::GemmArgs a{};
-    a.A = h;
+    a.A = p.aq ? (const void*)hq : h;
+    a.row_scale = hs;
     a.lda = I;
     a.M = p.cap;
     a.a_rows_alloc = p.cap;

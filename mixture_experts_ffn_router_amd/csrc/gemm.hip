@@ -60,8 +60,14 @@ template <>
 struct BTraits<ELEM_FP8> {
   static constexpr int ELEM_BYTES = 1;
 };
+template <>
+struct BTraits<ELEM_FP8X8> {
+  static constexpr int ELEM_BYTES = 1;
+};
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x8 __attribute__((ext_vector_type(8)));
 
 // 16 bytes per lane, global -> LDS: lane l's data lands at dst + 16 l (dst wave-uniform).
 __device__ __forceinline__ void dma16(rsrc_t r, void* dst, uint32_t voff, uint32_t soff) {
@@ -132,14 +138,19 @@ template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI, int BELEM>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N)
 __attribute__((amdgpu_waves_per_eu(WAVES_M * WAVES_N / 4, WAVES_M * WAVES_N / 4)))
 void gemm_mfma_kernel(GemmArgs p) {
-  constexpr bool FP8 = BELEM == ELEM_FP8;
+  constexpr bool FP8 = BELEM == ELEM_FP8;    // FP8 B widened to bf16 (W8A16)
+  constexpr bool A8 = BELEM == ELEM_FP8X8;   // FP8 A and B: v_mfma_f32_32x32x64_f8f6f4
+  constexpr bool WSC = FP8 || A8;            // per-output-channel weight scales
+  constexpr int EA = A8 ? 1 : 2;             // A element bytes
   // All operand tiles reach LDS by DMA (buffer_load ... lds) in 64-deep K tiles,
   // so each lane fetches 16 bytes of a 128-byte bf16 row piece (fp8: 64-byte
   // pieces) and an instruction covers whole cache lines.  8 waves: ping-pong in
   // 2 stages.  4 waves: software pipeline in up to 4 stages (as many as fit).
   constexpr bool PP = WAVES_M * WAVES_N == 8;
-  constexpr int BK = 64;
-  constexpr int STAGE_B = BM * BK * 2 + BN * BK * BTraits<BELEM>::ELEM_BYTES;
+  // 64-deep K tiles (128-byte bf16 rows); FP8 x FP8: 128-deep (128-byte rows too)
+  constexpr int BK = A8 ? 128 : 64;
+  static_assert(!A8 || PP, "FP8 activations run on the 8-wave ping-pong tiles");
+  constexpr int STAGE_B = BM * BK * EA + BN * BK * BTraits<BELEM>::ELEM_BYTES;
   constexpr int NS = PP ? 2 : (160 * 1024 / STAGE_B < 4 ? 160 * 1024 / STAGE_B : 4);
   static_assert(PP || NS >= 3, "the pipeline keeps at least two tiles in flight");
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -150,7 +161,7 @@ void gemm_mfma_kernel(GemmArgs p) {
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(TM >= 1 && TN >= 1, "wave tile");
   static_assert(!GATED || (TN % 2 == 0), "gated needs gate/up tile pairs");
-  constexpr int A_ROW = BK * 2;
+  constexpr int A_ROW = BK * EA;
   constexpr int B_ROW = BK * EB;
   constexpr int A_BYTES = BM * A_ROW;
   constexpr int B_BYTES = BN * B_ROW;
@@ -206,15 +217,18 @@ void gemm_mfma_kernel(GemmArgs p) {
   const int64_t eoff = routed ? (int64_t)e : (int64_t)(e - p.n_routed);
   const uint8_t* Bbase = (const uint8_t*)(routed ? p.B0 : p.B1) + eoff * p.bstride * EB;
   const float* bscale = nullptr;
-  if constexpr (FP8) bscale = (routed ? p.bscale0 : p.bscale1) + eoff * p.sstride;
+  if constexpr (WSC) bscale = (routed ? p.bscale0 : p.bscale1) + eoff * p.sstride;
   const bool wave_live = m0 + wm * WM < m_rows && (!pad_map || pad_map[m0 + wm * WM] >= 0);
 
-  const rsrc_t rsA = make_rsrc(p.A, (uint32_t)(p.a_rows_alloc * p.lda * 2));
+  const rsrc_t rsA = make_rsrc(p.A, (uint32_t)(p.a_rows_alloc * p.lda * EA));
   const rsrc_t rsB = make_rsrc(Bbase, (uint32_t)((int64_t)(GATED ? 2 * p.N : p.N) * p.Kdim * EB));
 
-  // K tiles [kt0, kt0 + nk) of this reduction part
-  const int kt0 = ks * (p.Kdim / BK) / KS;
-  const int nk = (ks + 1) * (p.Kdim / BK) / KS - kt0;
+  // K tiles [kt0, kt0 + nk) of this reduction part.  FP8 x FP8 with Kdim % 128
+  // == 64 ends in a half tile (ktail): its chunks past Kdim load as zeros.
+  const int nkt = (p.Kdim + BK - 1) / BK;
+  const int ktail = (p.Kdim % BK) ? nkt - 1 : -1;
+  const int kt0 = ks * nkt / KS;
+  const int nk = (ks + 1) * nkt / KS - kt0;
 
   // LDS row of the wave's B tile j (output-column tile)
   auto b_lds_row = [&](int j) {
@@ -246,13 +260,35 @@ void gemm_mfma_kernel(GemmArgs p) {
   // Sub-steps of a K tile: bf16 16 k each; fp8 32 k each (one 16-byte B read
   // feeds two MFMAs, see below).
   constexpr int NA = FP8 ? 2 : 1;
-  struct Frags {
+  struct FragsW {
     bf16x8 a[TM][NA];
     u32x4 b[TN];
   };
+  // FP8 x FP8 sub-step s (64 deep): each lane holds 32 bytes of its row, bytes
+  // [64s + 32hsel, +32) (chunks 4s + 2hsel and 4s + 2hsel + 1), the same bytes
+  // for A and B, so the instruction pairs matching k.
+  struct Frags8 {
+    u32x8 a[TM];
+    u32x8 b[TN];
+  };
+  using Frags = std::conditional_t<A8, Frags8, FragsW>;
   auto load_frags = [&](int buf, int s, Frags& f) {
     const uint8_t* sa = smem + buf * STAGE;
     const uint8_t* sb = sa + A_BYTES;
+    if constexpr (A8) {
+      const int c = 4 * s + 2 * hsel;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        f.a[i].lo = *(const u32x4*)(sa + a_row_off[i] + ((c ^ swa) << 4));
+        f.a[i].hi = *(const u32x4*)(sa + a_row_off[i] + (((c + 1) ^ swa) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        f.b[j].lo = *(const u32x4*)(sb + b_row_off[j] + ((c ^ swb) << 4));
+        f.b[j].hi = *(const u32x4*)(sb + b_row_off[j] + (((c + 1) ^ swb) << 4));
+      }
+      return;
+    } else {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       if constexpr (!FP8) {
@@ -272,8 +308,22 @@ void gemm_mfma_kernel(GemmArgs p) {
       const int c = 2 * s + hsel;
       f.b[j] = *(const u32x4*)(sb + b_row_off[j] + ((c ^ swb) << 4));
     }
+    }
   };
   auto mfmas = [&](const Frags& f) {
+    if constexpr (A8) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const i32x8 bj = __builtin_bit_cast(i32x8, f.b[j]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const i32x8 ai = __builtin_bit_cast(i32x8, f.a[i]);
+          // E4M3 x E4M3 (format selectors 0), no block scales
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bj, ai, acc[i][j], 0, 0, 0, 0, 0, 0);
+        }
+      }
+      return;
+    } else {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       if constexpr (!FP8) {
@@ -290,6 +340,7 @@ void gemm_mfma_kernel(GemmArgs p) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b2, f.a[i][1], acc[i][j], 0, 0, 0);
         }
       }
+    }
     }
   };
 
@@ -316,7 +367,7 @@ void gemm_mfma_kernel(GemmArgs p) {
       else tok = grow < p.M ? grow : p.M - 1;
       d.a_off[i] = (grow >= m_rows || slot < 0)
                        ? 0x80000000u
-                       : (uint32_t)(tok * p.lda * 2) + (uint32_t)((((lane % A_CH) ^ lds_swz<A_ROW>(r))) << 4);
+                       : (uint32_t)(tok * p.lda * EA) + (uint32_t)((((lane % A_CH) ^ lds_swz<A_ROW>(r))) << 4);
     }
     // row within a DMA group (groups of 16 rows of 64 bytes or 8 rows of 128 bytes,
     // starting at multiples of their size: the swizzle of row q0 + bl_row depends
@@ -477,8 +528,17 @@ void gemm_mfma_kernel(GemmArgs p) {
       else tok = grow < p.M ? grow : p.M - 1;
       a_off[i] = (grow >= m_rows || slot < 0)
                      ? 0x80000000u
-                     : (uint32_t)(tok * p.lda * 2) + (uint32_t)((((lane % A_CH) ^ lds_swz<A_ROW>(r))) << 4);
+                     : (uint32_t)(tok * p.lda * EA) + (uint32_t)((((lane % A_CH) ^ lds_swz<A_ROW>(r))) << 4);
     }
+    // A half K tile (FP8 x FP8, Kdim % 128 == 64): chunks at or past Kdim load as
+    // zeros.  The global chunk of A instruction i / B instruction i in this lane:
+    const int tail_ch = (p.Kdim % BK) * EA / 16;
+    auto a_chunk = [&](int i) {
+      return (lane % A_CH) ^ lds_swz<A_ROW>((ia0 + i) * A_ROWS_PER_DMA + lane / A_CH);
+    };
+    auto b_chunk = [&](int i) {
+      return (lane % B_CH) ^ lds_swz<B_ROW>(lane / B_CH + 8 * ((((ib0 + i) * B_ROWS_PER_DMA) >> 3) & 1));
+    };
     {
       const int bl_row = lane / B_CH;
 #pragma unroll
@@ -498,17 +558,23 @@ void gemm_mfma_kernel(GemmArgs p) {
     auto issue_a = [&](int kt, int buf) {
       uint8_t* sA = smem + buf * STAGE;
       const bool live = kt < nk;
+      const bool tail = A8 && kt0 + kt == ktail;
 #pragma unroll
-      for (int i = 0; i < AH; ++i)
-        dma16(rsA, sA + (ia0 + i) * 1024, live ? a_off[i] : 0x80000000u, live ? (uint32_t)(kt0 + kt) * A_ROW : 0u);
+      for (int i = 0; i < AH; ++i) {
+        const bool on = live && !(tail && a_chunk(i) >= tail_ch);
+        dma16(rsA, sA + (ia0 + i) * 1024, on ? a_off[i] : 0x80000000u, live ? (uint32_t)(kt0 + kt) * A_ROW : 0u);
+      }
     };
     auto issue_b = [&](int kt, int buf) {
       uint8_t* sB = smem + buf * STAGE + A_BYTES;
       const bool live = kt < nk;
+      const bool tail = A8 && kt0 + kt == ktail;
 #pragma unroll
-      for (int i = 0; i < BH; ++i)
-        dma16(rsB, sB + (ib0 + i) * 1024, live ? b_voff[(((ib0 + i) * B_ROWS_PER_DMA) >> 3) & 1] : 0x80000000u,
+      for (int i = 0; i < BH; ++i) {
+        const bool on = live && !(tail && b_chunk(i) >= tail_ch);
+        dma16(rsB, sB + (ib0 + i) * 1024, on ? b_voff[(((ib0 + i) * B_ROWS_PER_DMA) >> 3) & 1] : 0x80000000u,
               live ? b_soff[i] + (uint32_t)(kt0 + kt) * (uint32_t)B_ROW : 0u);
+      }
     };
     Frags f[2];
     issue_a(0, 0);
@@ -521,7 +587,7 @@ void gemm_mfma_kernel(GemmArgs p) {
     }
     phase_barrier();
     if (grp == 1) phase_barrier();
-    constexpr int SPH = BK / (FP8 ? 32 : 16) / 2;  // sub-steps per half tile
+    constexpr int SPH = A8 ? 1 : BK / (FP8 ? 32 : 16) / 2;  // sub-steps per half tile
     for (int t = 0; t < nk; ++t) {
       const int st = t & 1;
 #pragma unroll
@@ -579,7 +645,7 @@ void gemm_mfma_kernel(GemmArgs p) {
     }
     if constexpr (EPI == EPI_SCATTER || EPI == EPI_SCATTER_F32) {
       const int slot = p.c_rows[grow];
-      rs = (slot >= 0 && p.row_weight) ? p.row_weight[slot] : 1.f;
+      rs *= (slot >= 0 && p.row_weight) ? p.row_weight[slot] : 1.f;  // (x the A row's scale, if any)
     } else if constexpr (EPI == EPI_STORE_F32) {
       rs *= p.c_scale;
     }
@@ -593,14 +659,14 @@ void gemm_mfma_kernel(GemmArgs p) {
       if constexpr (GATED) {
         constexpr int TH = TN / 2;
         float gv = acc[i][j][4 * g4 + q] * rs, uv = acc[i][j + TH][4 * g4 + q] * rs;
-        if constexpr (FP8) {
+        if constexpr (WSC) {
           gv *= bscale[n0 + col + q];
           uv *= bscale[p.N + n0 + col + q];
         }
         v[q] = apply_act_bf16(p.act, gv) * uv;
       } else {
         v[q] = acc[i][j][4 * g4 + q] * rs;
-        if constexpr (FP8) v[q] *= bscale[n0 + col + q];
+        if constexpr (WSC) v[q] *= bscale[n0 + col + q];
       }
     }
   };
@@ -702,7 +768,7 @@ void gemm_mfma_kernel(GemmArgs p) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             float gv = acc[i][j][4 * g4 + q] * rs, uv = acc[i][j + TH][4 * g4 + q] * rs;
-            if constexpr (FP8) {
+            if constexpr (WSC) {
               gv *= bscale[col + q];
               uv *= bscale[p.N + col + q];
             }
@@ -965,6 +1031,17 @@ hipError_t launch_gemm_mfma(const GemmArgs& a, int epi, int belem, int block_m, 
       return run_mfma<128, 128, 2, 2, EPI_STORE_F32, ELEM_BF16>(a, s);
     }
     return run_grouped<EPI_STORE_F32, ELEM_BF16>(a, block_m, s);
+  }
+  if (belem == ELEM_FP8X8) {
+    // FP8 activations: 8-wave tiles only, K a multiple of 64 (a final half tile is masked)
+    if (a.Kdim % 64 || (epi != EPI_GATED && epi != EPI_SCATTER)) return hipErrorInvalidValue;
+    if (block_m == 256)
+      return epi == EPI_GATED ? run_mfma<256, 256, 4, 2, EPI_GATED, ELEM_FP8X8>(a, s)
+                              : run_mfma<256, 256, 4, 2, EPI_SCATTER, ELEM_FP8X8>(a, s);
+    if (block_m == 128)
+      return epi == EPI_GATED ? run_mfma<128, 512, 2, 4, EPI_GATED, ELEM_FP8X8>(a, s)
+                              : run_mfma<128, 512, 2, 4, EPI_SCATTER, ELEM_FP8X8>(a, s);
+    return hipErrorInvalidValue;
   }
   if (epi == EPI_GATED)
     return belem == ELEM_FP8 ? run_grouped<EPI_GATED, ELEM_FP8>(a, block_m, s)

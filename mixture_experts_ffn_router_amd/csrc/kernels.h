@@ -29,7 +29,8 @@ hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int bm_log2, int
                           hipStream_t s);
 
 enum GemmEpi { EPI_GATED = 0, EPI_SCATTER = 1, EPI_STORE_F32 = 2, EPI_SCATTER_F32 = 3 };
-enum GemmElem { ELEM_F32 = 0, ELEM_BF16 = 1, ELEM_FP8 = 2 };
+// B element type; ELEM_FP8X8: A and B both FP8 (E4M3), the per-row A scale in row_scale
+enum GemmElem { ELEM_F32 = 0, ELEM_BF16 = 1, ELEM_FP8 = 2, ELEM_FP8X8 = 3 };
 
 // One grouped "NT" GEMM: C[r, n] = sum_k A[row(r), k] * B_e[n, k] for the rows r
 // of every row block, e = the block's expert.
@@ -80,6 +81,15 @@ hipError_t launch_gemm_f32(const GemmArgs& a, int epi, hipStream_t s);
 hipError_t launch_prenorm(const void* x, int elem, int64_t T, int H, float eps, float* inv_rms,
                           const float* router_scale, const float* gamma_pre, const float* gamma_pre2,
                           void* r_out, void* xn1_out, void* xn2_out, hipStream_t s);
+
+// Dynamic per-row FP8 quantisation: scale[r] = max|in[r,:]| / 448 (1 for a zero
+// row), codes[r,:] = E4M3 nearest-even of in[r,:] / scale[r].  in: bf16 rows of C
+// elements (C % 8 == 0, C <= 16384), row stride ld_in; rows r >= *m_dev (when
+// given) are left alone, rows with row_map[r] < 0 (when given) get zero codes
+// and scale 1.
+hipError_t launch_quant_rows_fp8(const void* in, int64_t R, int C, int64_t ld_in, const int32_t* row_map,
+                                 const int32_t* m_dev, uint8_t* codes, int64_t ld_out, float* scales,
+                                 hipStream_t s);
 
 hipError_t launch_finalize(const void* ybuf, int yelem, int Kp, const float* dense_out,
                            const float* gamma_post1, const float* gamma_post2, float eps, void* out,

@@ -85,6 +85,10 @@ def _ws(desc, T):
     (dict(n_groups=4, topk_groups=5), B.MOE_INVALID_ARG),
     (dict(n_groups=4, topk_groups=1, top_k=3), B.MOE_INVALID_ARG),  # 2 candidates < 3
     (dict(num_experts=128, top_k=2, n_groups=128, topk_groups=2), B.MOE_UNSUPPORTED),
+    (dict(act_quant=2), B.MOE_INVALID_ARG),
+    (dict(act_quant=1), B.MOE_UNSUPPORTED),                              # bf16 weights
+    (dict(act_quant=1, weight_dtype=B.DT_FP8, inter_dense=64), B.MOE_UNSUPPORTED),
+    (dict(act_quant=1, weight_dtype=B.DT_FP8, inter=16448), B.MOE_UNSUPPORTED),
 ])
 def test_bad_descriptors_rejected(kw, status):
     st, _ = _ws(_desc(**kw), 16)
@@ -155,3 +159,15 @@ def test_permute_capacity():
     assert lib.moe_permute_capacity(1, 1, 1, 16) == 16
     assert lib.moe_permute_capacity(4, 2, 8, 48) == -1
     assert lib.moe_permute_capacity(-1, 2, 8, 64) == -1
+
+
+def test_fp8_activation_layers_take_the_grouped_path():
+    lib = _lib()
+    d = _desc(act_quant=1, weight_dtype=B.DT_FP8)
+    assert [lib.moe_forward_path(C.byref(d), t) for t in (1, 4, 16, 4096)] == [0, 0, 0, 0]
+    d0 = _desc(weight_dtype=B.DT_FP8)
+    assert lib.moe_forward_path(C.byref(d0), 4) == 1
+    # the workspace holds the codes and scales of x and h as well
+    st0, n0 = _ws(d0, 4096)
+    st1, n1 = _ws(d, 4096)
+    assert st0 == st1 == B.MOE_OK and n1 > n0 + 4096 * 256

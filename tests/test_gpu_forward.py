@@ -135,6 +135,16 @@ SMALL = {
                                            topk_groups=2),
     "fp32_sigmoid_groups": W.LayerSpec("fp32_v3", 40, 128, 16, 3, 64, "silu", "fp32",
                                        scoring="sigmoid", n_groups=4, topk_groups=2),
+    # FP8 activations (W8A8): FP8 x FP8 MFMAs on 128- and 256-row tiles, reductions
+    # ending in a half K tile (I = 192, H = 320), a three-token batch on the grouped path
+    "w8a8_small": W.LayerSpec("w8a8_small", 300, 256, 16, 4, 192, "gelu_tanh", "fp8",
+                              supplied_logits=True, act_quant="fp8_dynamic"),
+    "w8a8_router_h_tail": W.LayerSpec("w8a8_htail", 500, 320, 8, 2, 256, "silu", "fp8",
+                                      per_expert_scale="uniform", act_quant="fp8_dynamic"),
+    "w8a8_bm256": W.LayerSpec("w8a8_bm256", 2100, 256, 2, 1, 512, "silu", "fp8",
+                              act_quant="fp8_dynamic"),
+    "w8a8_three_tokens": W.LayerSpec("w8a8_t3", 3, 128, 8, 2, 128, "gelu_tanh", "fp8",
+                                     supplied_logits=True, act_quant="fp8_dynamic"),
 }
 
 
@@ -222,7 +232,8 @@ def test_decode_deterministic_and_workspace_reuse(B):
 # ------------------------------------------------------------------ full-size configurations
 FULL = [("tiny", 64), ("mixtral", 1), ("mixtral", 4096), ("gemma", 1), ("gemma", 16), ("gemma", 128),
         ("gemma", 8192), ("deepseek", 16), ("deepseek", 16384), ("skewed_fp8", 1), ("skewed_fp8", 4096),
-        ("deepseek_v3", 1), ("deepseek_v3", 16), ("deepseek_v3", 8192)]
+        ("deepseek_v3", 1), ("deepseek_v3", 16), ("deepseek_v3", 8192),
+        ("mixtral_w8a8", 4096), ("skewed_w8a8", 1), ("skewed_w8a8", 4096)]
 
 
 def _rows(T, n=256):
