@@ -134,9 +134,13 @@ def stage_work(spec, T, counts, path, dense_stage=None):
         by["router"] = z * (E * H * ab + T * H * ab + T * E * 4)
         by["gate_up"] = w_up + T * H * ab + rows * I * ab
         by["down"] = w_down + rows * I * ab + (rows + T * S) * H * ab
-        if spec.act_quant:  # + the row quantisation of x and h: codes written and read back
-            by["gate_up"] += 2 * T * H
-            by["down"] += 2 * rows * I
+        if spec.act_quant:
+            # the GEMMs read 1-byte codes; the quantisations read bf16 rows and write
+            # codes and one fp32 scale per row
+            by["gate_up"] -= T * H * (ab - 1)
+            by["down"] -= rows * I * (ab - 1)
+            by["quant_x"] = T * H * ab + T * H + T * 4
+            by["quant_h"] = rows * I * ab + rows * I + rows * 4
         by["dense_gate_up"] = 2 * Id * H * ab + T * H * ab + T * Id * ab
         by["dense_down"] = H * Id * ab + T * Id * ab + T * H * 4
         by["finalize"] = T * Kp * H * (4 if Id else ab) + T * H * ab
@@ -157,6 +161,8 @@ def launched_stages(spec, path, dense_stage, raw_ms, marker_ms):
             st.add("finalize")
         return st
     st = {"route", "permute", "gate_up", "down", "finalize"}
+    if spec.act_quant:
+        st |= {"quant_x", "quant_h"}
     if (spec.router_mode == "gemma" and not supplied) or dense:
         st.add("prenorm")
     if not supplied:

@@ -251,12 +251,14 @@ typedef enum {
   MOE_STAGE_ROUTER = 1,         /* router logits GEMM */
   MOE_STAGE_ROUTE = 2,          /* moe_route */
   MOE_STAGE_PERMUTE = 3,        /* moe_permute */
-  MOE_STAGE_GATE_UP = 4,        /* grouped gate/up GEMM + gated activation */
-  MOE_STAGE_DOWN = 5,           /* grouped down GEMM + routing-weight scatter */
-  MOE_STAGE_DENSE_GATE_UP = 6,  /* dense MLP gate/up GEMM */
-  MOE_STAGE_DENSE_DOWN = 7,     /* dense MLP down GEMM */
-  MOE_STAGE_FINALIZE = 8,       /* per-token combine, post-norms, output rounding */
-  MOE_STAGE_COUNT = 9
+  MOE_STAGE_QUANT_X = 4,        /* FP8 activations: per-token quantisation of x */
+  MOE_STAGE_GATE_UP = 5,        /* grouped gate/up GEMM + gated activation */
+  MOE_STAGE_QUANT_H = 6,        /* FP8 activations: per-row quantisation of h */
+  MOE_STAGE_DOWN = 7,           /* grouped down GEMM + routing-weight scatter */
+  MOE_STAGE_DENSE_GATE_UP = 8,  /* dense MLP gate/up GEMM */
+  MOE_STAGE_DENSE_DOWN = 9,     /* dense MLP down GEMM */
+  MOE_STAGE_FINALIZE = 10,      /* per-token combine, post-norms, output rounding */
+  MOE_STAGE_COUNT = 11
 } moe_stage;
 
 /*

@@ -54,8 +54,8 @@ EXPORTS = ["moe_status_string", "moe_last_error", "moe_route", "moe_permute_capa
            "moe_forward_workspace_size", "moe_forward", "moe_forward_profiled", "moe_forward_path",
            "moe_decode_dense_gate_up_stage"]
 PATHS = {0: "grouped", 1: "decode"}
-STAGES = ["prenorm", "router", "route", "permute", "gate_up", "down", "dense_gate_up", "dense_down",
-          "finalize"]
+STAGES = ["prenorm", "router", "route", "permute", "quant_x", "gate_up", "quant_h", "down", "dense_gate_up",
+          "dense_down", "finalize"]
 
 _lib = None
 

@@ -454,9 +454,11 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
               "logits copy");
     STAGE(MOE_STAGE_ROUTE);
     STAGE(MOE_STAGE_PERMUTE);
+    STAGE(MOE_STAGE_QUANT_X);
     STAGE(MOE_STAGE_GATE_UP);
     // dense gate/up, routing + expert gate/up
     HIP_TRY(moe::launch_decode_up(a, fp8, st), "decode up launch");
+    STAGE(MOE_STAGE_QUANT_H);
     STAGE(MOE_STAGE_DOWN);
     // dense down, expert down + combine
     HIP_TRY(moe::launch_decode_down(a, fp8, st), "decode down launch");
@@ -588,11 +590,12 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
   HIP_TRY(moe::launch_permute(ids, T * p.Kp, p.Ep, log2_exact(p.bm), counts, offsets, sorted, bexp, st),
           "permute launch");
 
-  STAGE(MOE_STAGE_GATE_UP);
+  STAGE(MOE_STAGE_QUANT_X);
   // 5. grouped gate/up GEMM + gated activation -> h [cap, I]
   //    (FP8 activations: x quantised per token first, its scale a row factor)
   if (p.aq)
     HIP_TRY(moe::launch_quant_rows_fp8(t->x, T, H, H, nullptr, nullptr, xq, H, xs, st), "x quantisation launch");
+  STAGE(MOE_STAGE_GATE_UP);
   {
     moe::GemmArgs a{};
     a.A = p.mat_xn2 ? xn2 : t->x;
@@ -622,12 +625,13 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
     a.act = d.act;
     HIP_TRY(gemm(a, moe::EPI_GATED, b_elem, p.bm), "gate/up gemm launch");
   }
-  STAGE(MOE_STAGE_DOWN);
+  STAGE(MOE_STAGE_QUANT_H);
   // 6. grouped down GEMM, scaled by the routing weight, scattered to per-slot rows
   //    (FP8 activations: h quantised per padded row, padding rows to zeros)
   if (p.aq)
     HIP_TRY(moe::launch_quant_rows_fp8(h, p.cap, I, I, sorted, offsets + p.Ep, hq, I, hs, st),
             "h quantisation launch");
+  STAGE(MOE_STAGE_DOWN);
   {
     moe::GemmArgs a{};
     a.A = p.aq ? (const void*)hq : h;

@@ -248,3 +248,23 @@ def _rows(T, n=256):
 def test_full_size_configs(B, name, T):
     L = W.make_layer(W.SPECS[name].with_T(T), seed=0)
     run_and_check(B, L, rows=_rows(T))
+
+
+@pytest.mark.parametrize("name,T", [("w8a8_small", 300), ("gemma_small", 333), ("gemma_small", 4)],
+                         ids=["w8a8-grouped", "gemma-grouped", "gemma-decode"])
+def test_profiled_forward_same_output_and_every_stage_recorded(B, name, T):
+    """moe_forward_profiled computes the same output as moe_forward and records
+    one event before each stage, in launch order, and one after the last."""
+    L = W.make_layer(SMALL[name].with_T(T), seed=5)
+    dl = B.DeviceLayer.from_generated(L)
+    ref = dl.forward().clone()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(B.STAGES) + 1)]
+    for e in evs:  # torch creates the HIP event on its first record
+        e.record()
+    out = dl.forward(events=evs)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(len(B.STAGES))]
+    assert all(v >= 0 for v in ms), ms
+    launched = {"gate_up", "down"} | ({"quant_x", "quant_h"} if SMALL[name].act_quant else set())
+    assert all(ms[B.STAGES.index(s)] > 0 for s in launched), dict(zip(B.STAGES, ms))
