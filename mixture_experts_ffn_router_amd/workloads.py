@@ -58,6 +58,7 @@ class LayerSpec:
     n_groups: int = 0            # > 1: group-limited routing over this many expert groups
     topk_groups: int = 0         # groups picked per token when n_groups > 1
     act_quant: Optional[str] = None  # "fp8_dynamic": FP8 activations (needs FP8 weights)
+    block_tail: bool = False     # the FFN block's post_feedforward_layernorm and residual add
 
     def with_T(self, T):
         return dataclasses.replace(self, T=T)
@@ -189,11 +190,11 @@ def make_layer(spec: LayerSpec, seed: int = 0, T: Optional[int] = None, x_only=F
     if spec.random_gammas:
         # test-only learned weights: router scale and input norms around 1; the
         # post-norm weights below 1 keep the output near unit scale
-        g = _rng(seed, _TID["gammas"]).uniform(0.5, 1.5, (5, H)).astype(np.float32)
+        g = _rng(seed, _TID["gammas"]).uniform(0.5, 1.5, (6, H)).astype(np.float32)
         g[3:] = (g[3:] - 0.5) * 0.4 + 0.3
         L["router_scale"] = torch.from_numpy(g[0].copy()) if spec.router_mode == "gemma" else None
         L["gammas"] = {k: torch.from_numpy(g[i + 1].copy())
-                       for i, k in enumerate(["pre", "pre2", "post1", "post2"])}
+                       for i, k in enumerate(["pre", "pre2", "post1", "post2", "post_ff"])}
     else:
         L["router_scale"] = None
         L["gammas"] = None
@@ -226,6 +227,8 @@ def oracle_layer(L):
              w13=f(L["w13"]), w2=f(L["w2"]), w13_scale=f(L["w13_scale"]),
              w2_scale=f(L["w2_scale"]))
     d["shared"] = None if L["shared_w13"] is None else (f(L["shared_w13"]), f(L["shared_w2"]))
+    d["block_tail"] = spec.block_tail
+    d["gamma_post_ff"] = f((L["gammas"] or {}).get("post_ff"))
     if L["dense_w13"] is not None:
         g = L["gammas"] or {}
         d["dense"] = dict(w13=f(L["dense_w13"]), w2=f(L["dense_w2"]),

@@ -403,6 +403,8 @@ def moe_layer(x, layer, rows=None, logits=None):
       E, K, act, renorm, router_mode ('plain'|'gemma'),
       scoring ('softmax'|'sigmoid'), n_groups, topk_groups (group-limited routing),
       act_quant (None | 'fp8_dynamic': routed experts' inputs quantised per row),
+      block_tail (True: the FFN block's tail, post_feedforward_layernorm with weight
+      gamma_post_ff (ones when None) and the residual add),
       w_router [E,H] or None (then `logits` must be given),
       router_scale [H] or None, per_expert_scale [E] or None,
       w13 [E,2I,H], w2 [E,H,I] (+ w13_scale [E,2I], w2_scale [E,H] for FP8 codes),
@@ -421,7 +423,8 @@ def moe_layer(x, layer, rows=None, logits=None):
       Gemma: out = post_norm_1(MLP(pre_norm(x))) + post_norm_2(moe)
       others: out = moe
     The decoder layer's final post_feedforward_layernorm and residual add are
-    outside the FFN layer (reading).
+    outside the FFN layer (reading) unless block_tail asks for them:
+      out = x + post_feedforward_layernorm(out).
 
     Returns dict(out [len(rows),H], logits [T,E], weights [T,K], ids [T,K],
     counts [E], offsets [E+1], order [T*K])."""
@@ -456,5 +459,9 @@ def moe_layer(x, layer, rows=None, logits=None):
         out = rmsnorm(d, dense.get("gamma_post1"), eps) + rmsnorm(moe, dense.get("gamma_post2"), eps)
     else:
         out = moe
+    if layer.get("block_tail"):
+        # the rest of the FFN block (Gemma 4 walkthrough §1): post_feedforward_layernorm
+        # of the merged branches, then the residual add (the layer input is the residual)
+        out = x[rows] + rmsnorm(out, layer.get("gamma_post_ff"), eps)
     return dict(out=out, logits=z, weights=w, ids=ids, counts=counts, offsets=offsets,
                 order=order)

@@ -120,3 +120,15 @@ def test_truncating_e4m3_encode_is_caught(monkeypatch):
 def test_h_quantised_without_bf16_rounding_is_caught(monkeypatch):
     monkeypatch.setattr(O, "round_bf16", lambda a: np.asarray(a, dtype=np.float64))
     _fails(P.test_fp8_dynamic_ffn_matches_torch_composition)
+
+
+def test_block_tail_without_residual_is_caught(monkeypatch):
+    orig = O.moe_layer
+
+    def bad(x, layer, rows=None, logits=None):
+        r = orig(x, dict(layer, block_tail=False), rows, logits)
+        if layer.get("block_tail"):
+            r["out"] = O.rmsnorm(r["out"], layer.get("gamma_post_ff"))  # residual dropped
+        return r
+    monkeypatch.setattr(O, "moe_layer", bad)
+    _fails(P.test_gemma_branch_matches_torch_composition)

@@ -489,8 +489,13 @@ def test_gemma_branch_matches_torch_composition():
     d = _torch_ffn(F.rms_norm(xt, (H,), weight=T_(g["gamma_pre"]), eps=eps), T_(dw13), T_(dw2),
                    "gelu_tanh")
     ref = (F.rms_norm(d, (H,), weight=T_(g["gamma_post1"]), eps=eps) +
-           F.rms_norm(moe, (H,), weight=T_(g["gamma_post2"]), eps=eps)).numpy()
-    np.testing.assert_allclose(got["out"], ref, rtol=1e-10, atol=1e-11)
+           F.rms_norm(moe, (H,), weight=T_(g["gamma_post2"]), eps=eps))
+    np.testing.assert_allclose(got["out"], ref.numpy(), rtol=1e-10, atol=1e-11)
+    # the whole FFN block: post_feedforward_layernorm of the sum, then + residual
+    gff = rng.uniform(0.5, 1.5, H)
+    blk = O.moe_layer(x, dict(L, block_tail=True, gamma_post_ff=gff))["out"]
+    ref_blk = xt + F.rms_norm(ref, (H,), weight=T_(gff), eps=eps)
+    np.testing.assert_allclose(blk, ref_blk.numpy(), rtol=1e-10, atol=1e-11)
 
 
 def test_row_subset_matches_full():
