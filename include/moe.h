@@ -147,6 +147,8 @@ typedef struct {
   int32_t topk_groups;   /* groups picked per token when n_groups > 1 */
   int32_t act_quant;     /* moe_act_quant: MOE_ACT_QUANT_FP8_DYNAMIC needs FP8 weights, bf16 x,
                             no dense branch and inter <= 16384 (see moe_forward) */
+  int32_t block_tail;    /* 1: also the FFN block's tail, out = x + RMSNorm(out) * gamma_post_ff
+                            ([G4] section 1); 0: the layer output alone */
 } moe_layer_desc;
 
 /* Tensors of one forward call (device pointers unless noted).  The matrix
@@ -176,6 +178,7 @@ typedef struct {
   float* topk_w_out;              /* optional [T, K] */
   int32_t* topk_ids_out;          /* optional [T, K] */
   float* out_f32;                 /* optional [T, H] fp32: the output before its final rounding to act_dtype */
+  const float* gamma_post_ff;     /* [H] post_feedforward_layernorm weight (block_tail), NULL = ones */
 } moe_tensors;
 
 /*
@@ -206,7 +209,8 @@ moe_status moe_forward_workspace_size(const moe_layer_desc* desc, int64_t T, siz
  *   dense branch (inter_dense > 0, [G4] section 1):
  *            out = RMSNorm(MLP(RMSNorm(x)*gamma_pre))*gamma_post1 + RMSNorm(moe)*gamma_post2;
  *   otherwise out = moe.
- * The decoder layer's final post-norm and residual add are not part of it.
+ *   block_tail (the rest of the FFN block, [G4] section 1): out = x + RMSNorm(out) * gamma_post_ff,
+ *   computed in fp32 before the single output rounding.
  *
  * Precision: bf16 operands with fp32 accumulation (fp32 throughout for
  * act_dtype F32); the gated intermediate and the per-slot expert outputs are

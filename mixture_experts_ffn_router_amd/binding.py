@@ -40,14 +40,15 @@ class LayerDesc(C.Structure):
                 ("weight_dtype", C.c_int32), ("renormalize", C.c_int32), ("router_mode", C.c_int32),
                 ("n_shared", C.c_int32), ("inter_dense", C.c_int32), ("dense_act", C.c_int32),
                 ("eps", C.c_float), ("scoring", C.c_int32), ("n_groups", C.c_int32),
-                ("topk_groups", C.c_int32), ("act_quant", C.c_int32)]
+                ("topk_groups", C.c_int32), ("act_quant", C.c_int32), ("block_tail", C.c_int32)]
 
 
 class Tensors(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in (
         "x", "logits", "w_router", "router_scale", "per_expert_scale", "w13", "w2", "w13_scale",
         "w2_scale", "shared_w13", "shared_w2", "dense_w13", "dense_w2", "gamma_pre", "gamma_pre2",
-        "gamma_post1", "gamma_post2", "out", "logits_out", "topk_w_out", "topk_ids_out", "out_f32")]
+        "gamma_post1", "gamma_post2", "out", "logits_out", "topk_w_out", "topk_ids_out", "out_f32",
+        "gamma_post_ff")]
 
 
 EXPORTS = ["moe_status_string", "moe_last_error", "moe_route", "moe_permute_capacity", "moe_permute",
@@ -196,7 +197,8 @@ class DeviceLayer:
                          router_mode=ROUTER_GEMMA if spec.router_mode == "gemma" else ROUTER_PLAIN,
                          n_shared=spec.n_shared, inter_dense=spec.I_dense, dense_act=ACT[spec.act],
                          eps=eps, scoring=SCORING[spec.scoring], n_groups=spec.n_groups,
-                         topk_groups=spec.topk_groups, act_quant=ACT_QUANT[spec.act_quant])
+                         topk_groups=spec.topk_groups, act_quant=ACT_QUANT[spec.act_quant],
+                         block_tail=int(spec.block_tail))
 
         def d(t):
             return None if t is None else t.to(device, non_blocking=False).contiguous()
@@ -208,7 +210,8 @@ class DeviceLayer:
                  shared_w13=d(L["shared_w13"]), shared_w2=d(L["shared_w2"]),
                  dense_w13=d(L["dense_w13"]), dense_w2=d(L["dense_w2"]),
                  gamma_pre=d(g.get("pre")), gamma_pre2=d(g.get("pre2")),
-                 gamma_post1=d(g.get("post1")), gamma_post2=d(g.get("post2")))
+                 gamma_post1=d(g.get("post1")), gamma_post2=d(g.get("post2")),
+                 gamma_post_ff=d(g.get("post_ff")) if spec.block_tail else None)
         return cls(desc, t)
 
     def path(self, T):
@@ -259,10 +262,10 @@ class DeviceLayer:
         ts = Tensors(x=_ptr(x), logits=_ptr(logits), out=_ptr(out),
                      logits_out=_ptr(extra.get("logits")), topk_w_out=_ptr(extra.get("topk_w")),
                      topk_ids_out=_ptr(extra.get("topk_ids")), out_f32=_ptr(extra.get("out_f32")),
-                     **{k: _ptr(t[k]) for k in (
+                     **{k: _ptr(t.get(k)) for k in (
                          "w_router", "router_scale", "per_expert_scale", "w13", "w2", "w13_scale",
                          "w2_scale", "shared_w13", "shared_w2", "dense_w13", "dense_w2", "gamma_pre",
-                         "gamma_pre2", "gamma_post1", "gamma_post2")})
+                         "gamma_pre2", "gamma_post1", "gamma_post2", "gamma_post_ff")})
         if events is None:
             _check(lib.moe_forward(C.byref(self.desc), C.byref(ts), T, _ptr(workspace), workspace.numel(),
                                    _stream()))

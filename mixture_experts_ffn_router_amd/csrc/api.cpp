@@ -162,6 +162,7 @@ moe_status validate_desc(const moe_layer_desc* d) {
   if (d->router_mode != MOE_ROUTER_PLAIN && d->router_mode != MOE_ROUTER_GEMMA)
     return fail(MOE_INVALID_ARG, "unknown router mode %d", d->router_mode);
   if (!(d->eps >= 0.f)) return fail(MOE_INVALID_ARG, "eps must be >= 0");
+  if (d->block_tail != 0 && d->block_tail != 1) return fail(MOE_INVALID_ARG, "block_tail must be 0 or 1");
   if (d->act_quant != MOE_ACT_QUANT_NONE && d->act_quant != MOE_ACT_QUANT_FP8_DYNAMIC)
     return fail(MOE_INVALID_ARG, "unknown act_quant %d", d->act_quant);
   if (d->act_quant) {
@@ -261,7 +262,7 @@ moe_status make_plan(const moe_layer_desc& d, const moe_tensors* t, int64_t T, P
     p.o_dh = take(p.dense ? (size_t)T * d.inter_dense * 2 : 0);
     p.o_dout = take(p.dense ? (size_t)T * H * 4 : 0);
     p.down_splits = moe::decode_down_splits((int)T, d.hidden, d.inter, p.dense);
-    p.o_ypart = take(p.dense || p.down_splits > 1 ? (size_t)T * p.down_splits * H * 4 : 0);
+    p.o_ypart = take(p.dense || p.down_splits > 1 || d.block_tail ? (size_t)T * p.down_splits * H * 4 : 0);
     if (o > p.total) p.total = o;
   }
   return MOE_OK;
@@ -438,7 +439,7 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
     a.hbuf = ws + p.o_h;
     a.dsum = p.dense ? (float*)(ws + p.o_dout) : nullptr;
     a.down_splits = p.down_splits;
-    a.ypart = p.dense || p.down_splits > 1 ? (float*)(ws + p.o_ypart) : nullptr;
+    a.ypart = p.dense || p.down_splits > 1 || d.block_tail ? (float*)(ws + p.o_ypart) : nullptr;
     a.rinfo = (int*)(ws + p.o_rinfo);
     a.out = t->out;
     a.out_f32 = t->out_f32;
@@ -467,7 +468,8 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
     STAGE(MOE_STAGE_FINALIZE);
     if (a.ypart)
       HIP_TRY(moe::launch_finalize(a.ypart, moe::ELEM_F32, p.down_splits, a.dsum, t->gamma_post1, t->gamma_post2,
-                                   d.eps, t->out, moe::ELEM_BF16, t->out_f32, T, d.hidden, st),
+                                   d.eps, t->out, moe::ELEM_BF16, t->out_f32, T, d.hidden, st,
+                                   d.block_tail ? t->x : nullptr, t->gamma_post_ff),
               "finalize launch");
     STAGE(MOE_STAGE_COUNT);
     return MOE_OK;
@@ -670,7 +672,7 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
   STAGE(MOE_STAGE_FINALIZE);
   // 8. per-token combine in slot order (+ Gemma post-norms and branch sum)
   HIP_TRY(moe::launch_finalize(y, p.y_f32 ? moe::ELEM_F32 : act_elem, p.Kp * p.ks, dout, t->gamma_post1, t->gamma_post2, d.eps, t->out, act_elem,
-                               t->out_f32, T, H, st),
+                               t->out_f32, T, H, st, d.block_tail ? t->x : nullptr, t->gamma_post_ff),
           "finalize launch");
   // 9. optional copies of the routing result
   if (t->topk_w_out || t->topk_ids_out)

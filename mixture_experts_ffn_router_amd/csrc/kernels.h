@@ -91,9 +91,12 @@ hipError_t launch_quant_rows_fp8(const void* in, int64_t R, int C, int64_t ld_in
                                  const int32_t* m_dev, uint8_t* codes, int64_t ld_out, float* scales,
                                  hipStream_t s);
 
+// resid (when given, the layer input in the output type): out = resid +
+// RMSNorm(out) * gamma_post_ff (ones when NULL), the FFN block's tail.
 hipError_t launch_finalize(const void* ybuf, int yelem, int Kp, const float* dense_out,
                            const float* gamma_post1, const float* gamma_post2, float eps, void* out,
-                           int oelem, float* out_f32, int64_t T, int H, hipStream_t s);
+                           int oelem, float* out_f32, int64_t T, int H, hipStream_t s,
+                           const void* resid = nullptr, const float* gamma_post_ff = nullptr);
 
 hipError_t launch_gather_topk(const float* w_in, const int32_t* ids_in, int in_stride, int K, int64_t T,
                               float* w_out, int32_t* ids_out, hipStream_t s);

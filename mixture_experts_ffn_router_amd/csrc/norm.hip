@@ -14,7 +14,10 @@
 //   moe = sum_{j < Kp} ybuf[t, j, :]   in slot order, fp32;
 //   out = RMSNorm(dense_out[t]) * gamma_post1 + RMSNorm(moe) * gamma_post2  (dense branch)
 //   out = moe                                                              (otherwise)
-// The per-slot rows were already multiplied by their routing weights.
+//   out = x[t] + RMSNorm(out) * gamma_post_ff       (the FFN block's tail, when asked:
+//         post_feedforward_layernorm and the residual add of section 1)
+// The per-slot rows were already multiplied by their routing weights; out is
+// rounded once, at the end.
 #include "common.h"
 #include "kernels.h"
 
@@ -109,7 +112,9 @@ __global__ __launch_bounds__(NT) void finalize_kernel(const TY* __restrict__ ybu
                                                       const float* __restrict__ dense_out,
                                                       const float* __restrict__ g1, const float* __restrict__ g2,
                                                       float eps, TO* __restrict__ out,
-                                                      float* __restrict__ out_f32, int H) {
+                                                      float* __restrict__ out_f32, int H, bool tail,
+                                                      const TO* __restrict__ resid,
+                                                      const float* __restrict__ gff) {
   __shared__ float s_red[NT / 64];
   constexpr int G = 4;  // H <= NT * 8 * G
   const int64_t t = blockIdx.x;
@@ -135,47 +140,69 @@ __global__ __launch_bounds__(NT) void finalize_kernel(const TY* __restrict__ ybu
       }
     }
   }
+  // o: the layer output of this thread's groups
+  float o[G][8];
   if (dense_out == nullptr) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) o[g][q] = m[g][q];
+  } else {
+    float d[G][8];
+    float ssm = 0.f, ssd = 0.f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int idx = threadIdx.x + g * NT;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) d[g][q] = 0.f;
+      if (idx < ng) {
+        ld8(dense_out + t * H + idx * 8, d[g]);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          ssm += m[g][q] * m[g][q];
+          ssd += d[g][q] * d[g][q];
+        }
+      }
+    }
+    ssm = block_sum_f32(ssm, s_red);
+    ssd = block_sum_f32(ssd, s_red);
+    const float im = 1.0f / sqrtf(ssm / (float)H + eps);
+    const float id = 1.0f / sqrtf(ssd / (float)H + eps);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int idx = threadIdx.x + g * NT;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int i = idx * 8 + q;
+        o[g][q] = idx < ng ? d[g][q] * id * (g1 ? g1[i] : 1.f) + m[g][q] * im * (g2 ? g2[i] : 1.f) : 0.f;
+      }
+    }
+  }
+  if (tail) {
+    float ss = 0.f;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) ss += o[g][q] * o[g][q];  // zero past H
+    ss = block_sum_f32(ss, s_red);
+    const float io = 1.0f / sqrtf(ss / (float)H + eps);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int idx = threadIdx.x + g * NT;
       if (idx < ng) {
-        st8(out + t * H + idx * 8, m[g]);
-        if (out_f32) st8(out_f32 + t * H + idx * 8, m[g]);
+        float r[8];
+        ld8(resid + t * H + idx * 8, r);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) o[g][q] = r[q] + o[g][q] * io * (gff ? gff[idx * 8 + q] : 1.f);
       }
     }
-    return;
   }
-  float d[G][8];
-  float ssm = 0.f, ssd = 0.f;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const int idx = threadIdx.x + g * NT;
     if (idx < ng) {
-      ld8(dense_out + t * H + idx * 8, d[g]);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        ssm += m[g][q] * m[g][q];
-        ssd += d[g][q] * d[g][q];
-      }
-    }
-  }
-  ssm = block_sum_f32(ssm, s_red);
-  ssd = block_sum_f32(ssd, s_red);
-  const float im = 1.0f / sqrtf(ssm / (float)H + eps);
-  const float id = 1.0f / sqrtf(ssd / (float)H + eps);
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const int idx = threadIdx.x + g * NT;
-    if (idx < ng) {
-      float o[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int i = idx * 8 + q;
-        o[q] = d[g][q] * id * (g1 ? g1[i] : 1.f) + m[g][q] * im * (g2 ? g2[i] : 1.f);
-      }
-      st8(out + t * H + idx * 8, o);
-      if (out_f32) st8(out_f32 + t * H + idx * 8, o);
+      st8(out + t * H + idx * 8, o[g]);
+      if (out_f32) st8(out_f32 + t * H + idx * 8, o[g]);
     }
   }
 }
@@ -208,19 +235,24 @@ hipError_t launch_prenorm(const void* x, int elem, int64_t T, int H, float eps, 
 
 hipError_t launch_finalize(const void* ybuf, int yelem, int Kp, const float* dense_out,
                            const float* gamma_post1, const float* gamma_post2, float eps, void* out,
-                           int oelem, float* out_f32, int64_t T, int H, hipStream_t s) {
+                           int oelem, float* out_f32, int64_t T, int H, hipStream_t s, const void* resid,
+                           const float* gamma_post_ff) {
   if (T == 0) return hipSuccess;
   if (H > NT * 32 || H % 8) return hipErrorInvalidValue;
+  const bool tail = resid != nullptr;
   dim3 g((unsigned)T), b(NT);
   if (yelem == ELEM_F32 && oelem == ELEM_F32)
     finalize_kernel<float, float><<<g, b, 0, s>>>((const float*)ybuf, Kp, dense_out, gamma_post1,
-                                                  gamma_post2, eps, (float*)out, out_f32, H);
+                                                  gamma_post2, eps, (float*)out, out_f32, H, tail,
+                                                  (const float*)resid, gamma_post_ff);
   else if (yelem == ELEM_BF16 && oelem == ELEM_BF16)
     finalize_kernel<bf16_t, bf16_t><<<g, b, 0, s>>>((const bf16_t*)ybuf, Kp, dense_out, gamma_post1,
-                                                    gamma_post2, eps, (bf16_t*)out, out_f32, H);
+                                                    gamma_post2, eps, (bf16_t*)out, out_f32, H, tail,
+                                                    (const bf16_t*)resid, gamma_post_ff);
   else if (yelem == ELEM_F32 && oelem == ELEM_BF16)
     finalize_kernel<float, bf16_t><<<g, b, 0, s>>>((const float*)ybuf, Kp, dense_out, gamma_post1,
-                                                   gamma_post2, eps, (bf16_t*)out, out_f32, H);
+                                                   gamma_post2, eps, (bf16_t*)out, out_f32, H, tail,
+                                                   (const bf16_t*)resid, gamma_post_ff);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -86,6 +86,7 @@ def _ws(desc, T):
     (dict(n_groups=4, topk_groups=1, top_k=3), B.MOE_INVALID_ARG),  # 2 candidates < 3
     (dict(num_experts=128, top_k=2, n_groups=128, topk_groups=2), B.MOE_UNSUPPORTED),
     (dict(act_quant=2), B.MOE_INVALID_ARG),
+    (dict(block_tail=2), B.MOE_INVALID_ARG),
     (dict(act_quant=1), B.MOE_UNSUPPORTED),                              # bf16 weights
     (dict(act_quant=1, weight_dtype=B.DT_FP8, inter_dense=64), B.MOE_UNSUPPORTED),
     (dict(act_quant=1, weight_dtype=B.DT_FP8, inter=16448), B.MOE_UNSUPPORTED),

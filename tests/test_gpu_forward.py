@@ -145,6 +145,13 @@ SMALL = {
                               act_quant="fp8_dynamic"),
     "w8a8_three_tokens": W.LayerSpec("w8a8_t3", 3, 128, 8, 2, 128, "gelu_tanh", "fp8",
                                      supplied_logits=True, act_quant="fp8_dynamic"),
+    # the FFN block's tail (post_feedforward_layernorm + residual) in the finalize
+    "gemma_block_tail": W.LayerSpec("gemma_tail", 333, 256, 16, 4, 128, "gelu_tanh", "bf16",
+                                    router_mode="gemma", per_expert_scale="uniform", I_dense=192,
+                                    random_gammas=True, block_tail=True),
+    "plain_block_tail": W.LayerSpec("plain_tail", 200, 256, 8, 2, 256, "silu", "bf16", block_tail=True),
+    "fp32_block_tail": W.LayerSpec("fp32_tail", 50, 128, 8, 3, 64, "gelu_tanh", "fp32",
+                                   router_mode="gemma", I_dense=64, random_gammas=True, block_tail=True),
 }
 
 
@@ -194,6 +201,10 @@ DECODE = {
     "h8192": W.LayerSpec("dec_h8192", 1, 8192, 4, 1, 128, "silu", "bf16"),
     "v3_sigmoid_groups": W.LayerSpec("dec_v3", 1, 256, 32, 4, 128, "silu", "bf16", n_shared=1,
                                      I_shared=128, scoring="sigmoid", n_groups=8, topk_groups=2),
+    "gemma_block_tail": W.LayerSpec("dec_gemma_tail", 1, 256, 16, 4, 128, "gelu_tanh", "bf16",
+                                    router_mode="gemma", per_expert_scale="uniform", I_dense=192,
+                                    random_gammas=True, block_tail=True),
+    "plain_block_tail": W.LayerSpec("dec_plain_tail", 1, 256, 8, 2, 512, "silu", "bf16", block_tail=True),
 }
 DECODE_T = {"h8192": (1, 8)}
 
