@@ -82,6 +82,10 @@ SPECS = {
     "deepseek_v3": LayerSpec("deepseek_v3", 8192, 2048, 256, 8, 1408, "silu", "bf16",
                              n_shared=1, I_shared=1408, scoring="sigmoid", n_groups=8,
                              topk_groups=4),
+    # the whole Gemma FFN block: the layer plus post_feedforward_layernorm and the residual add
+    "gemma_block": LayerSpec("gemma_block", 8192, 2816, 128, 8, 704, "gelu_tanh", "bf16",
+                             router_mode="gemma", per_expert_scale="uniform", I_dense=2112,
+                             block_tail=True),
     # FP8 weights and dynamically quantised FP8 activations (W8A8)
     "mixtral_w8a8": LayerSpec("mixtral_w8a8", 4096, 4096, 8, 2, 14336, "silu", "fp8",
                               act_quant="fp8_dynamic"),
@@ -92,7 +96,7 @@ SPECS = {
 # token counts the pages' configurations name for each layer shape
 T_VALUES = {"tiny": [64], "mixtral": [4096], "gemma": [1, 16, 128, 8192],
             "deepseek": [16384], "skewed_fp8": [1, 4096], "deepseek_v3": [1, 16, 8192],
-            "mixtral_w8a8": [4096], "skewed_w8a8": [1, 4096]}
+            "mixtral_w8a8": [4096], "skewed_w8a8": [1, 4096], "gemma_block": [1, 8192]}
 
 
 def _rng(seed, *key):

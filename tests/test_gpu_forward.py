@@ -244,7 +244,7 @@ def test_decode_deterministic_and_workspace_reuse(B):
 FULL = [("tiny", 64), ("mixtral", 1), ("mixtral", 4096), ("gemma", 1), ("gemma", 16), ("gemma", 128),
         ("gemma", 8192), ("deepseek", 16), ("deepseek", 16384), ("skewed_fp8", 1), ("skewed_fp8", 4096),
         ("deepseek_v3", 1), ("deepseek_v3", 16), ("deepseek_v3", 8192),
-        ("mixtral_w8a8", 4096), ("skewed_w8a8", 1), ("skewed_w8a8", 4096)]
+        ("mixtral_w8a8", 4096), ("skewed_w8a8", 1), ("skewed_w8a8", 4096), ("gemma_block", 1), ("gemma_block", 8192)]
 
 
 def _rows(T, n=256):
