@@ -510,6 +510,7 @@ void gemm_mfma_kernel(GemmArgs p) {
     constexpr int AH = NA / 8;   // A instructions per wave for one half of the A tile
     constexpr int BH = NB / 8;   // B instructions per wave for one half of the B tile
     static_assert(AH * 8 == NA && BH * 8 == NB, "DMA parts must split evenly over 4 waves");
+    static_assert(AH + BH <= 32, "one bit per DMA instruction");
     static_assert(4 % WAVES_N == 0 && WAVES_M == 2 * (4 / WAVES_N) && (NA / 2) * A_ROWS_PER_DMA == BM / 2,
                   "each group's wave rows are one half of the A tile (group 0 the lower)");
     // This wave's A instructions: group 1 the lower half of the A tile (group
@@ -531,14 +532,20 @@ void gemm_mfma_kernel(GemmArgs p) {
                      : (uint32_t)(tok * p.lda * EA) + (uint32_t)((((lane % A_CH) ^ lds_swz<A_ROW>(r))) << 4);
     }
     // A half K tile (FP8 x FP8, Kdim % 128 == 64): chunks at or past Kdim load as
-    // zeros.  The global chunk of A instruction i / B instruction i in this lane:
-    const int tail_ch = (p.Kdim % BK) * EA / 16;
-    auto a_chunk = [&](int i) {
-      return (lane % A_CH) ^ lds_swz<A_ROW>((ia0 + i) * A_ROWS_PER_DMA + lane / A_CH);
-    };
-    auto b_chunk = [&](int i) {
-      return (lane % B_CH) ^ lds_swz<B_ROW>(lane / B_CH + 8 * ((((ib0 + i) * B_ROWS_PER_DMA) >> 3) & 1));
-    };
+    // zeros.  Bit i (A instruction i) / AH + i (B instruction i) of past_k: this
+    // lane's global chunk of that instruction lies past Kdim in such a tile.
+    uint32_t past_k = 0;
+    if constexpr (A8) {
+      const int tail_ch = (p.Kdim % BK) * EA / 16;
+#pragma unroll
+      for (int i = 0; i < AH; ++i)
+        if (((lane % A_CH) ^ lds_swz<A_ROW>((ia0 + i) * A_ROWS_PER_DMA + lane / A_CH)) >= tail_ch)
+          past_k |= 1u << i;
+#pragma unroll
+      for (int i = 0; i < BH; ++i)
+        if (((lane % B_CH) ^ lds_swz<B_ROW>(lane / B_CH + 8 * ((((ib0 + i) * B_ROWS_PER_DMA) >> 3) & 1))) >= tail_ch)
+          past_k |= 1u << (AH + i);
+    }
     {
       const int bl_row = lane / B_CH;
 #pragma unroll
@@ -561,7 +568,7 @@ void gemm_mfma_kernel(GemmArgs p) {
       const bool tail = A8 && kt0 + kt == ktail;
 #pragma unroll
       for (int i = 0; i < AH; ++i) {
-        const bool on = live && !(tail && a_chunk(i) >= tail_ch);
+        const bool on = live && !(tail && ((past_k >> i) & 1u));
         dma16(rsA, sA + (ia0 + i) * 1024, on ? a_off[i] : 0x80000000u, live ? (uint32_t)(kt0 + kt) * A_ROW : 0u);
       }
     };
@@ -571,7 +578,7 @@ void gemm_mfma_kernel(GemmArgs p) {
       const bool tail = A8 && kt0 + kt == ktail;
 #pragma unroll
       for (int i = 0; i < BH; ++i) {
-        const bool on = live && !(tail && b_chunk(i) >= tail_ch);
+        const bool on = live && !(tail && ((past_k >> (AH + i)) & 1u));
         dma16(rsB, sB + (ib0 + i) * 1024, on ? b_voff[(((ib0 + i) * B_ROWS_PER_DMA) >> 3) & 1] : 0x80000000u,
               live ? b_soff[i] + (uint32_t)(kt0 + kt) * (uint32_t)B_ROW : 0u);
       }
