@@ -444,6 +444,9 @@ def moe_layer(x, layer, rows=None, logits=None):
     dense = layer.get("dense")
     if dense is not None:
         xe = rmsnorm(x, dense.get("gamma_pre2"), eps)
+        if layer.get("act_quant"):
+            # reading: the normalised expert input is stored (bf16) and quantised as stored
+            xe = round_bf16(xe)
     else:
         xe = x
     moe = moe_combine(xe, w, ids, layer["w13"], layer["w2"], layer["act"], rows,

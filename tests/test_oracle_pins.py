@@ -361,6 +361,15 @@ def test_dynamic_fp8_rows_properties():
     assert np.array_equal(c2, codes) and np.array_equal(s2[nz], scale[nz] * 8)
 
 
+def _torch_fp8_rows(a):
+    """Per-row dynamic FP8 through torch: scale max|row|/448 (1 for zeros), float8_e4m3fn
+    conversion of a / scale, back to float64."""
+    a = torch.as_tensor(a, dtype=torch.float32)
+    s = a.abs().amax(dim=1) / 448.0
+    s = torch.where(s > 0, s, torch.ones_like(s))
+    return (a / s[:, None]).to(torch.float8_e4m3fn).double() * s.double()[:, None]
+
+
 def test_fp8_dynamic_ffn_matches_torch_composition():
     """The W8A8 expert FFN through torch, one library step at a time: per-row scale,
     float8_e4m3fn conversion of x / scale, float64 matmuls, bfloat16 rounding of h,
@@ -371,13 +380,7 @@ def test_fp8_dynamic_ffn_matches_torch_composition():
     w13 = rng.standard_normal((2 * I, H)) / 8
     w2 = rng.standard_normal((H, I)) / 7
 
-    def tq(a):  # torch: per-row dynamic FP8
-        a = torch.as_tensor(a, dtype=torch.float32)
-        s = a.abs().amax(dim=1) / 448.0
-        s = torch.where(s > 0, s, torch.ones_like(s))
-        q = (a / s[:, None]).to(torch.float8_e4m3fn)
-        return q.double() * s.double()[:, None]
-
+    tq = _torch_fp8_rows
     xq = tq(x)
     W13 = torch.from_numpy(w13)
     g, u = xq @ W13[:I].T, xq @ W13[I:].T
@@ -496,6 +499,40 @@ def test_gemma_branch_matches_torch_composition():
     blk = O.moe_layer(x, dict(L, block_tail=True, gamma_post_ff=gff))["out"]
     ref_blk = xt + F.rms_norm(ref, (H,), weight=T_(gff), eps=eps)
     np.testing.assert_allclose(blk, ref_blk.numpy(), rtol=1e-10, atol=1e-11)
+
+
+def test_gemma_w8a8_layer_matches_torch_composition():
+    """FP8 activations with the Gemma branch: the experts' input is pre_norm_2(x) as
+    stored in bf16, quantised per row; h quantised per row after its bf16 rounding; the
+    dense MLP unquantised; post-norms and the sum as in the bf16 layer."""
+    rng = np.random.default_rng(33)
+    T, H, E, K, I, Id = 10, 32, 6, 2, 16, 24
+    eps = 1e-6
+    x = rng.standard_normal((T, H)).astype(np.float32).astype(np.float64)
+    L = _tiny_layer(rng, T, H, E, K, I, act="gelu_tanh")
+    g = {k: rng.uniform(0.5, 1.5, H) for k in ("gamma_pre", "gamma_pre2", "gamma_post1", "gamma_post2")}
+    dw13 = rng.standard_normal((2 * Id, H)) / math.sqrt(H)
+    dw2 = rng.standard_normal((H, Id)) / math.sqrt(Id)
+    L["dense"] = dict(w13=dw13, w2=dw2, **g)
+    L["act_quant"] = "fp8_dynamic"
+    got = O.moe_layer(x, L)
+
+    xt = torch.from_numpy(x)
+    T_ = lambda a: torch.from_numpy(np.asarray(a))
+    D = _brute_dispatch(got["logits"], K, True, L["per_expert_scale"])
+    xe = F.rms_norm(xt, (H,), weight=T_(g["gamma_pre2"]), eps=eps).to(torch.bfloat16).double()
+    xq = _torch_fp8_rows(xe)
+
+    def ffn_q(e):
+        W13 = T_(L["w13"][e])
+        h = F.gelu(xq @ W13[:I].T, approximate="tanh") * (xq @ W13[I:].T)
+        return _torch_fp8_rows(h.to(torch.bfloat16).float()) @ T_(L["w2"][e]).T
+
+    moe = sum(T_(D[:, e:e + 1]) * ffn_q(e) for e in range(E))
+    d = _torch_ffn(F.rms_norm(xt, (H,), weight=T_(g["gamma_pre"]), eps=eps), T_(dw13), T_(dw2), "gelu_tanh")
+    ref = (F.rms_norm(d, (H,), weight=T_(g["gamma_post1"]), eps=eps) +
+           F.rms_norm(moe, (H,), weight=T_(g["gamma_post2"]), eps=eps)).numpy()
+    np.testing.assert_allclose(got["out"], ref, rtol=1e-9, atol=1e-10)
 
 
 def test_row_subset_matches_full():
