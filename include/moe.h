@@ -145,8 +145,8 @@ typedef struct {
   int32_t scoring;       /* moe_scoring (see moe_route) */
   int32_t n_groups;      /* expert groups for group-limited routing: 0 or 1 = none, else 2..64 */
   int32_t topk_groups;   /* groups picked per token when n_groups > 1 */
-  int32_t act_quant;     /* moe_act_quant: MOE_ACT_QUANT_FP8_DYNAMIC needs FP8 weights, bf16 x,
-                            no dense branch and inter <= 16384 (see moe_forward) */
+  int32_t act_quant;     /* moe_act_quant: MOE_ACT_QUANT_FP8_DYNAMIC needs FP8 weights, bf16 x
+                            and inter <= 16384; the dense branch stays bf16 (see moe_forward) */
   int32_t block_tail;    /* 1: also the FFN block's tail, out = x + RMSNorm(out) * gamma_post_ff
                             ([G4] section 1); 0: the layer output alone */
 } moe_layer_desc;
@@ -199,11 +199,11 @@ moe_status moe_forward_workspace_size(const moe_layer_desc* desc, int64_t T, siz
  *            (gated FFN, [MI]; activation SiLU [LC] or GELU-tanh [G4] section 6);
  *            x_e = RMSNorm(x) * gamma_pre2 when the dense branch is present, else x;
  *            FP8 weights: W = decode_e4m3(q) * scale[e, n] ([SG]);
- *            FP8 activations (act_quant, [SG] FP8-Dynamic): the GEMM inputs x_e and
- *            h are each quantised per row first, scale = max|row| / 448 (1 for a
- *            zero row), code = E4M3 nearest-even of value / scale (fp32), h as
- *            stored in bf16; the products run on FP8 x FP8 MFMAs and the row and
- *            channel scales multiply the accumulators;
+ *            FP8 activations (act_quant, [SG] FP8-Dynamic): the routed experts' GEMM
+ *            inputs x_e and h are each quantised per row first, scale = max|row| / 448
+ *            (1 for a zero row), code = E4M3 nearest-even of value / scale (fp32),
+ *            both as stored in bf16; the products run on FP8 x FP8 MFMAs and the row
+ *            and channel scales multiply the accumulators;
  *   moe_t  = sum_j w[t,j] y_{t,j}              (weighted combine, [G4] section 7);
  *   shared experts: moe_t += sum_s FFN_s(x_t) with weight 1 ([LC] shared expert);
  *   dense branch (inter_dense > 0, [G4] section 1):

@@ -168,7 +168,6 @@ moe_status validate_desc(const moe_layer_desc* d) {
   if (d->act_quant) {
     if (d->weight_dtype != MOE_DT_FP8_E4M3 || d->act_dtype != MOE_DT_BF16)
       return fail(MOE_UNSUPPORTED, "FP8 activations need FP8 expert weights and bf16 x");
-    if (d->inter_dense) return fail(MOE_UNSUPPORTED, "FP8 activations with the dense branch");
     if (d->inter > 16384) return fail(MOE_UNSUPPORTED, "FP8 activations need inter <= 16384");
   }
   moe::RouteOpts o;
@@ -205,12 +204,13 @@ moe_status make_plan(const moe_layer_desc& d, const moe_tensors* t, int64_t T, P
   // Without a tensor set (workspace query) size for the case that materialises every row.
   p.mat_r = p.gemma_router && (!t || t->router_scale);
   p.mat_xn1 = p.dense && (!t || t->gamma_pre);
-  p.mat_xn2 = p.dense && (!t || t->gamma_pre2);
+  p.aq = d.act_quant != MOE_ACT_QUANT_NONE;
+  // FP8 activations quantise the normalised expert input as stored: always materialised
+  p.mat_xn2 = p.dense && (!t || t->gamma_pre2 || p.aq);
   const size_t ae = p.f32 ? 4 : 2;  // activation element bytes
   // With the dense branch the MoE sum is RMS-normalised afterwards, which turns
   // its relative error into error at output scale: keep the per-slot rows fp32.
   p.y_f32 = p.f32 || p.dense;
-  p.aq = d.act_quant != MOE_ACT_QUANT_NONE;
   // Split the down GEMM's reduction when its tiles would fill the CUs in few
   // rounds (long reductions over few rows: the Mixtral-style layer); rows are
   // estimated with half a block of padding per expert.
@@ -596,7 +596,8 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
   // 5. grouped gate/up GEMM + gated activation -> h [cap, I]
   //    (FP8 activations: x quantised per token first, its scale a row factor)
   if (p.aq)
-    HIP_TRY(moe::launch_quant_rows_fp8(t->x, T, H, H, nullptr, nullptr, xq, H, xs, st), "x quantisation launch");
+    HIP_TRY(moe::launch_quant_rows_fp8(p.mat_xn2 ? xn2 : t->x, T, H, H, nullptr, nullptr, xq, H, xs, st),
+            "x quantisation launch");
   STAGE(MOE_STAGE_GATE_UP);
   {
     moe::GemmArgs a{};

@@ -1041,14 +1041,15 @@ hipError_t launch_gemm_mfma(const GemmArgs& a, int epi, int belem, int block_m, 
   }
   if (belem == ELEM_FP8X8) {
     // FP8 activations: 8-wave tiles only, K a multiple of 64 (a final half tile is masked)
-    if (a.Kdim % 64 || (epi != EPI_GATED && epi != EPI_SCATTER)) return hipErrorInvalidValue;
-    if (block_m == 256)
-      return epi == EPI_GATED ? run_mfma<256, 256, 4, 2, EPI_GATED, ELEM_FP8X8>(a, s)
-                              : run_mfma<256, 256, 4, 2, EPI_SCATTER, ELEM_FP8X8>(a, s);
-    if (block_m == 128)
-      return epi == EPI_GATED ? run_mfma<128, 512, 2, 4, EPI_GATED, ELEM_FP8X8>(a, s)
-                              : run_mfma<128, 512, 2, 4, EPI_SCATTER, ELEM_FP8X8>(a, s);
-    return hipErrorInvalidValue;
+    if (a.Kdim % 64 || epi == EPI_STORE_F32 || (block_m != 128 && block_m != 256)) return hipErrorInvalidValue;
+    if (block_m == 256) {
+      if (epi == EPI_GATED) return run_mfma<256, 256, 4, 2, EPI_GATED, ELEM_FP8X8>(a, s);
+      if (epi == EPI_SCATTER) return run_mfma<256, 256, 4, 2, EPI_SCATTER, ELEM_FP8X8>(a, s);
+      return run_mfma<256, 256, 4, 2, EPI_SCATTER_F32, ELEM_FP8X8>(a, s);
+    }
+    if (epi == EPI_GATED) return run_mfma<128, 512, 2, 4, EPI_GATED, ELEM_FP8X8>(a, s);
+    if (epi == EPI_SCATTER) return run_mfma<128, 512, 2, 4, EPI_SCATTER, ELEM_FP8X8>(a, s);
+    return run_mfma<128, 512, 2, 4, EPI_SCATTER_F32, ELEM_FP8X8>(a, s);
   }
   if (epi == EPI_GATED)
     return belem == ELEM_FP8 ? run_grouped<EPI_GATED, ELEM_FP8>(a, block_m, s)

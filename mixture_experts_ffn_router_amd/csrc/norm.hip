@@ -37,6 +37,18 @@ __device__ __forceinline__ float block_sum_f32(float v, float* s_red) {
   return t;
 }
 
+__device__ __forceinline__ double block_sum_f64(double v, double* s_red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_sum_f64(v);
+  __syncthreads();
+  if (lane == 0) s_red[wave] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) t += s_red[w];
+  return t;
+}
+
 template <typename TIn>
 __device__ __forceinline__ float ld(const TIn* p, int64_t i);
 template <>
@@ -58,24 +70,27 @@ __global__ __launch_bounds__(NT) void prenorm_kernel(const TX* __restrict__ x, i
                                                      const float* __restrict__ g_pre,
                                                      const float* __restrict__ g_pre2, TX* __restrict__ r_out,
                                                      TX* __restrict__ xn1, TX* __restrict__ xn2) {
-  __shared__ float s_red[NT / 64];
+  // fp64 throughout: a materialised row is then the exactly rounded normalised
+  // value (rounded to fp32, then to the row's type), so any later decision
+  // taken on it (an FP8 code) does not depend on the summation order
+  __shared__ double s_red[NT / 64];
   const int64_t t = blockIdx.x;
   const TX* xr = x + t * H;
-  float ss = 0.f;
+  double ss = 0.0;
   for (int i = threadIdx.x; i < H; i += NT) {
-    float v = ld(xr, i);
+    const double v = ld(xr, i);
     ss += v * v;
   }
-  ss = block_sum_f32(ss, s_red);
-  const float inv = 1.0f / sqrtf(ss / (float)H + eps);
-  const float root = 1.0f / sqrtf((float)H);
-  if (threadIdx.x == 0) inv_rms[t] = inv;
+  ss = block_sum_f64(ss, s_red);
+  const double inv = 1.0 / sqrt(ss / (double)H + (double)eps);
+  const double root = 1.0 / sqrt((double)H);
+  if (threadIdx.x == 0) inv_rms[t] = (float)inv;
   if (!r_out && !xn1 && !xn2) return;
   for (int i = threadIdx.x; i < H; i += NT) {
-    const float n = ld(xr, i) * inv;
-    if (r_out) st(r_out, t * H + i, n * root * (router_scale ? router_scale[i] : 1.f));
-    if (xn1) st(xn1, t * H + i, n * (g_pre ? g_pre[i] : 1.f));
-    if (xn2) st(xn2, t * H + i, n * (g_pre2 ? g_pre2[i] : 1.f));
+    const double n = (double)ld(xr, i) * inv;
+    if (r_out) st(r_out, t * H + i, (float)(n * root * (router_scale ? (double)router_scale[i] : 1.0)));
+    if (xn1) st(xn1, t * H + i, (float)(n * (g_pre ? (double)g_pre[i] : 1.0)));
+    if (xn2) st(xn2, t * H + i, (float)(n * (g_pre2 ? (double)g_pre2[i] : 1.0)));
   }
 }
 

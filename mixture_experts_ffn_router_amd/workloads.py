@@ -91,12 +91,18 @@ SPECS = {
                               act_quant="fp8_dynamic"),
     "skewed_w8a8": LayerSpec("skewed_w8a8", 4096, 2816, 128, 8, 704, "gelu_tanh", "fp8",
                              supplied_logits=True, act_quant="fp8_dynamic"),
+    # the Gemma layer as an FP8-Dynamic checkpoint runs it: FP8 experts with FP8
+    # activations, the dense MLP in bf16
+    "gemma_w8a8": LayerSpec("gemma_w8a8", 8192, 2816, 128, 8, 704, "gelu_tanh", "fp8",
+                            router_mode="gemma", per_expert_scale="uniform", I_dense=2112,
+                            act_quant="fp8_dynamic"),
 }
 
 # token counts the pages' configurations name for each layer shape
 T_VALUES = {"tiny": [64], "mixtral": [4096], "gemma": [1, 16, 128, 8192],
             "deepseek": [16384], "skewed_fp8": [1, 4096], "deepseek_v3": [1, 16, 8192],
-            "mixtral_w8a8": [4096], "skewed_w8a8": [1, 4096], "gemma_block": [1, 8192]}
+            "mixtral_w8a8": [4096], "skewed_w8a8": [1, 4096], "gemma_block": [1, 8192],
+            "gemma_w8a8": [1, 8192]}
 
 
 def _rng(seed, *key):

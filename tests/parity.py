@@ -4,7 +4,13 @@ import torch
 
 # Output tolerances: (max-abs, rel-RMS) for bf16 and fp8-weight layers; fp32 layers
 # are held to 1e-5 relative: max-abs <= 1e-5 * max|ref| and rel-RMS <= 1e-5.
-TOL = {"bf16": (2e-2, 1e-2), "fp8": (5e-2, 3e-2)}
+TOL = {"bf16": (2e-2, 1e-2), "fp8": (5e-2, 3e-2),
+       # FP8 activations with a post-normed MoE branch (Gemma): h's codes follow its bf16
+       # rounding, which the FP8 MFMA's accumulation and the oracle's fp64 take differently
+       # for ~2% of elements (1 ulp); ~1 in 32 of those flips a code, which moves the token's
+       # MoE sum by one E4M3 step of one h element (<= 2^-4 max|h| |w2| w, about 0.02 at the
+       # tested shapes) and the post-norm scales that sum to unit RMS: max-abs 1e-1
+       "fp8_act_postnorm": (1e-1, 3e-2)}
 TOL_F32_REL = 1e-5
 TOPK_W_REL = 1e-6
 

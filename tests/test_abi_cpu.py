@@ -88,7 +88,6 @@ def _ws(desc, T):
     (dict(act_quant=2), B.MOE_INVALID_ARG),
     (dict(block_tail=2), B.MOE_INVALID_ARG),
     (dict(act_quant=1), B.MOE_UNSUPPORTED),                              # bf16 weights
-    (dict(act_quant=1, weight_dtype=B.DT_FP8, inter_dense=64), B.MOE_UNSUPPORTED),
     (dict(act_quant=1, weight_dtype=B.DT_FP8, inter=16448), B.MOE_UNSUPPORTED),
 ])
 def test_bad_descriptors_rejected(kw, status):

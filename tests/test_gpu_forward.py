@@ -41,6 +41,8 @@ def B():
 
 
 def _kind(spec):
+    if spec.act_quant and spec.I_dense:
+        return "fp8_act_postnorm"
     return {"fp32": "fp32", "bf16": "bf16", "fp8": "fp8"}[spec.wdtype]
 
 
@@ -145,6 +147,13 @@ SMALL = {
                               act_quant="fp8_dynamic"),
     "w8a8_three_tokens": W.LayerSpec("w8a8_t3", 3, 128, 8, 2, 128, "gelu_tanh", "fp8",
                                      supplied_logits=True, act_quant="fp8_dynamic"),
+    # FP8 activations with the Gemma branch (expert input normalised, stored, quantised;
+    # fp32 per-slot rows), learned norm weights and the block tail, or unit weights
+    "gemma_w8a8_gammas_tail": W.LayerSpec("gemma_w8a8_g", 333, 256, 16, 4, 192, "gelu_tanh", "fp8",
+                                          router_mode="gemma", per_expert_scale="uniform", I_dense=192,
+                                          random_gammas=True, block_tail=True, act_quant="fp8_dynamic"),
+    "gemma_w8a8_unit_norms": W.LayerSpec("gemma_w8a8_u", 2100, 256, 4, 2, 256, "gelu_tanh", "fp8",
+                                         router_mode="gemma", I_dense=128, act_quant="fp8_dynamic"),
     # the FFN block's tail (post_feedforward_layernorm + residual) in the finalize
     "gemma_block_tail": W.LayerSpec("gemma_tail", 333, 256, 16, 4, 128, "gelu_tanh", "bf16",
                                     router_mode="gemma", per_expert_scale="uniform", I_dense=192,
@@ -244,7 +253,8 @@ def test_decode_deterministic_and_workspace_reuse(B):
 FULL = [("tiny", 64), ("mixtral", 1), ("mixtral", 4096), ("gemma", 1), ("gemma", 16), ("gemma", 128),
         ("gemma", 8192), ("deepseek", 16), ("deepseek", 16384), ("skewed_fp8", 1), ("skewed_fp8", 4096),
         ("deepseek_v3", 1), ("deepseek_v3", 16), ("deepseek_v3", 8192),
-        ("mixtral_w8a8", 4096), ("skewed_w8a8", 1), ("skewed_w8a8", 4096), ("gemma_block", 1), ("gemma_block", 8192)]
+        ("mixtral_w8a8", 4096), ("skewed_w8a8", 1), ("skewed_w8a8", 4096), ("gemma_block", 1), ("gemma_block", 8192),
+        ("gemma_w8a8", 8192)]
 
 
 def _rows(T, n=256):
