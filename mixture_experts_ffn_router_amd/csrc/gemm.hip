@@ -7,7 +7,7 @@
 // expert-major row list; e = the block's expert.  Both operands are
 // K-contiguous ("NT"), which is what the MFMA operand layout wants.
 //
-// bf16 MFMA kernel (v_mfma_f32_32x32x16_bf16), 4 or 8 waves:
+// MFMA kernel (v_mfma_f32_32x32x16_bf16; FP8 x FP8: 32x32x64), 4 or 8 waves:
 //   * BM x BN output tile; every operand tile reaches LDS through buffer loads
 //     that write LDS directly (no staging registers), in K tiles of 64.  8 waves
 //     ping-pong over 2 stages (see pingpong_dma64).  4 waves run a software
@@ -38,6 +38,11 @@
 //   * FP8 B (OCP E4M3 codes, W8A16): B rows are 64 bytes in LDS, widened to bf16
 //     in registers (exact), and the per-output-channel scale is applied in the
 //     epilogue: sum_k x_k (q_kn s_n) = s_n sum_k x_k q_kn.
+//   * FP8 A and B (W8A8, activations quantised per row at run time, the
+//     "FP8-Dynamic" scheme of the sglang PR #24696 page): v_mfma_f32_32x32x64_f8f6f4
+//     on the 8-wave tiles, 128-deep K tiles (128-byte LDS rows, as bf16), one
+//     instruction per half K tile; sum_k (p_tk a_t)(q_kn s_n) = a_t s_n sum_k p_tk q_kn,
+//     so the row scale a_t and the channel scale s_n multiply the accumulator.
 //   * Per-token row scale: an RMSNorm without a learned weight is a per-row
 //     factor, so x_t / rms_t . W = (x_t . W) / rms_t; the epilogue applies it to
 //     the accumulator and the normalised rows are never rounded or stored.
