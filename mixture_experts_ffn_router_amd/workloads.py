@@ -45,7 +45,7 @@ class LayerSpec:
     K: int
     I: int
     act: str                     # "silu" | "gelu_tanh"
-    wdtype: str                  # "fp32" | "bf16" | "fp8"
+    wdtype: str                  # "fp32" | "bf16" | "fp8" | "mxfp4" (decode path only)
     renorm: bool = True
     router_mode: str = "plain"   # "plain" | "gemma"
     per_expert_scale: str = "ones"   # "ones" | "uniform"
@@ -82,6 +82,10 @@ SPECS = {
     "deepseek_v3": LayerSpec("deepseek_v3", 8192, 2048, 256, 8, 1408, "silu", "bf16",
                              n_shared=1, I_shared=1408, scoring="sigmoid", n_groups=8,
                              topk_groups=4),
+    # 4-bit (MXFP4) expert weights for decode bandwidth: the Gemma and Mixtral layers
+    "gemma_mxfp4": LayerSpec("gemma_mxfp4", 1, 2816, 128, 8, 704, "gelu_tanh", "mxfp4",
+                             router_mode="gemma", per_expert_scale="uniform", I_dense=2112),
+    "mixtral_mxfp4": LayerSpec("mixtral_mxfp4", 1, 4096, 8, 2, 14336, "silu", "mxfp4"),
     # the whole Gemma FFN block: the layer plus post_feedforward_layernorm and the residual add
     "gemma_block": LayerSpec("gemma_block", 8192, 2816, 128, 8, 704, "gelu_tanh", "bf16",
                              router_mode="gemma", per_expert_scale="uniform", I_dense=2112,
@@ -102,7 +106,7 @@ SPECS = {
 T_VALUES = {"tiny": [64], "mixtral": [4096], "gemma": [1, 16, 128, 8192],
             "deepseek": [16384], "skewed_fp8": [1, 4096], "deepseek_v3": [1, 16, 8192],
             "mixtral_w8a8": [4096], "skewed_w8a8": [1, 4096], "gemma_block": [1, 8192],
-            "gemma_w8a8": [1, 8192]}
+            "gemma_w8a8": [1, 8192], "gemma_mxfp4": [1, 16], "mixtral_mxfp4": [1]}
 
 
 def _rng(seed, *key):
@@ -143,6 +147,31 @@ def _fp8(w):
     return q.view(torch.uint8), s.to(torch.float32)
 
 
+_E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _mxfp4(w):
+    """MXFP4 quantisation of w [E, N, K] along K in blocks of 32: the block scale is
+    2^(floor(log2(max|block|)) - 2) (2 = the exponent of E2M1's largest power of two),
+    stored as E8M0 (exponent + 127); each element is the nearest E2M1 value of
+    w / scale, ties to the even code, saturating at 6.  Returns (packed codes uint8
+    [E, N, K/2], element 2i in the low nibble; scales uint8 [E, N, K/32])."""
+    E, N, K = w.shape
+    b = w.reshape(E, N, K // 32, 32).astype(np.float64)
+    amax = np.abs(b).max(axis=-1)
+    ex = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
+    ex = np.clip(ex, -127, 127).astype(np.int64)
+    v = np.abs(b) / np.ldexp(1.0, ex)[..., None]
+    v = np.minimum(v, 6.0)
+    hi = np.clip(np.searchsorted(_E2M1_GRID, v, side="left"), 0, 7)
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = v - _E2M1_GRID[lo], _E2M1_GRID[hi] - v
+    idx = np.where((d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0)), hi, lo)
+    codes = (idx | np.where(np.signbit(b), 8, 0)).astype(np.uint8).reshape(E, N, K)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    return torch.from_numpy(packed), torch.from_numpy((ex + 127).astype(np.uint8))
+
+
 def zipf_bias(E, seed=0, alpha=ZIPF_ALPHA, s=ZIPF_S):
     ranks = _rng(seed, _TID["zipf_rank"]).permutation(E) + 1
     return (-alpha * s * np.log(ranks)).astype(np.float32)
@@ -174,6 +203,9 @@ def make_layer(spec: LayerSpec, seed: int = 0, T: Optional[int] = None, x_only=F
     if spec.wdtype == "fp8":
         L["w13"], L["w13_scale"] = _fp8(w13)
         L["w2"], L["w2_scale"] = _fp8(w2)
+    elif spec.wdtype == "mxfp4":
+        L["w13"], L["w13_scale"] = _mxfp4(w13)
+        L["w2"], L["w2_scale"] = _mxfp4(w2)
     else:
         L["w13"], L["w2"] = _store(w13, wd), _store(w2, wd)
         L["w13_scale"] = L["w2_scale"] = None

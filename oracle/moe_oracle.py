@@ -104,6 +104,40 @@ def decode_e4m3fn(codes):
     return np.where((e == 15) & (m == 7), np.nan, val)
 
 
+def decode_e2m1(codes):
+    """Decode FP4 E2M1 codes (low 4 bits) to float64: bit 3 sign, bits 2-1
+    exponent (bias 1), bit 0 mantissa; exponent 0 is subnormal, m * 2^-1;
+    otherwise 2^(e-1) * (1 + m/2).  No infinities or NaN.  Written from the
+    format's definition (OCP microscaling formats, the element type of MXFP4)."""
+    c = np.asarray(codes).astype(np.int64) & 0xF
+    s = (c >> 3) & 1
+    e = (c >> 1) & 3
+    m = c & 1
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, e - 1))
+    return np.where(s == 1, -mag, mag)
+
+
+def decode_e8m0(codes):
+    """Decode E8M0 scale codes: 2^(c - 127), c = 255 is NaN (the MX block scale)."""
+    c = np.asarray(codes).astype(np.int64)
+    return np.where(c == 255, np.nan, np.ldexp(1.0, c - 127))
+
+
+def decode_mxfp4(packed, scales):
+    """MXFP4 weights to float64.  packed [..., K/2] uint8 holds two E2M1 codes per
+    byte, element 2i in the low nibble and 2i+1 in the high nibble; scales
+    [..., K/32] uint8 holds one E8M0 scale per block of 32 consecutive elements
+    along K (readings: the pages name 4-bit expert weights, not a format; MXFP4
+    is the 4-bit format with hardware support on the target, and K, the
+    reduction dimension, is the blocked one, as for the activations' rows)."""
+    packed = np.asarray(packed).astype(np.int64)
+    lo, hi = packed & 0xF, packed >> 4
+    codes = np.stack([lo, hi], axis=-1).reshape(packed.shape[:-1] + (2 * packed.shape[-1],))
+    vals = decode_e2m1(codes)
+    sc = decode_e8m0(scales)
+    return vals * np.repeat(sc, 32, axis=-1)
+
+
 def _e4m3fn_values():
     """The 127 non-negative finite E4M3 values, by code 0..126, ascending."""
     return decode_e4m3fn(np.arange(127, dtype=np.uint8))
@@ -364,7 +398,9 @@ def moe_combine(xe, weights, ids, w13, w2, act, rows=None, w13_scale=None, w2_sc
 
     w13 / w2 are indexable per expert (array [E, 2I, H] / [E, H, I], any real
     dtype holding the exact stored values, or FP8 codes with per-output-channel
-    scales w13_scale [E, 2I] and w2_scale [E, H]: W = decode(q) * s[n])."""
+    scales w13_scale [E, 2I] and w2_scale [E, H]: W = decode(q) * s[n], or MXFP4:
+    packed codes [E, 2I, H/2] / [E, H, I/2] with uint8 E8M0 block scales
+    [E, 2I, H/32] / [E, H, I/32])."""
     xe = _f64(xe)
     weights = _f64(weights)
     ids = np.asarray(ids)
@@ -389,6 +425,8 @@ def moe_combine(xe, weights, ids, w13, w2, act, rows=None, w13_scale=None, w2_sc
 def _expert_weight(w, scale, e):
     if scale is None:
         return _f64(w[e])
+    if np.asarray(scale).dtype == np.uint8:  # MXFP4: packed codes, E8M0 block scales
+        return decode_mxfp4(w[e], scale[e])
     return decode_e4m3fn(w[e]) * _f64(scale[e])[:, None]
 
 

@@ -132,3 +132,10 @@ def test_block_tail_without_residual_is_caught(monkeypatch):
         return r
     monkeypatch.setattr(O, "moe_layer", bad)
     _fails(P.test_gemma_branch_matches_torch_composition)
+
+
+def test_swapped_mxfp4_nibbles_are_caught(monkeypatch):
+    orig = O.decode_mxfp4
+    monkeypatch.setattr(O, "decode_mxfp4",
+                        lambda packed, scales: orig(((np.asarray(packed) & 15) << 4) | (np.asarray(packed) >> 4), scales))
+    _fails(P.test_mxfp4_layer_equals_layer_on_torch_decoded_weights)

@@ -320,6 +320,63 @@ def test_fp8_decode_all_codes_match_torch():
     assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
 
 
+def test_e2m1_and_e8m0_decode_closed_forms():
+    """E2M1 (the MXFP4 element) takes exactly the grid 0, 0.5, 1, 1.5, 2, 3, 4, 6 on
+    codes 0-7, in order, and its negatives on 8-15; E8M0 is 2^(c-127), 255 is NaN."""
+    assert O.decode_e2m1(np.arange(8)).tolist() == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert np.array_equal(O.decode_e2m1(np.arange(8, 16)), -O.decode_e2m1(np.arange(8)))
+    assert np.signbit(O.decode_e2m1(8))
+    sc = O.decode_e8m0(np.array([0, 1, 126, 127, 128, 254, 255]))
+    assert sc[:6].tolist() == [2.0 ** -127, 2.0 ** -126, 0.5, 1.0, 2.0, 2.0 ** 127] and np.isnan(sc[6])
+
+
+def _torch_mxfp4(packed, scales):
+    """MXFP4 decode through torch: the published E2M1 grid as a lookup table, low
+    nibble first, one ldexp per block of 32."""
+    grid = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=torch.float64)
+    p = torch.as_tensor(np.asarray(packed)).long()
+    codes = torch.stack([p & 15, p >> 4], dim=-1).flatten(-2)
+    v = grid[codes & 7] * torch.where(codes >= 8, -1.0, 1.0).double()
+    e = torch.as_tensor(np.asarray(scales)).long() - 127
+    return torch.ldexp(v, e.repeat_interleave(32, dim=-1))
+
+
+def test_mxfp4_layer_equals_layer_on_torch_decoded_weights():
+    rng = np.random.default_rng(34)
+    T, H, E, K, I = 24, 64, 4, 2, 96
+    x = rng.standard_normal((T, H))
+    w13 = (rng.standard_normal((E, 2 * I, H)) / 8).astype(np.float32)
+    w2 = (rng.standard_normal((E, H, I)) / 10).astype(np.float32)
+    q13, s13 = W._mxfp4(w13)
+    q2, s2 = W._mxfp4(w2)
+    wr = rng.standard_normal((E, H))
+    L4 = dict(E=E, K=K, act="silu", renorm=True, w_router=wr, w13=q13.numpy(), w2=q2.numpy(),
+              w13_scale=s13.numpy(), w2_scale=s2.numpy())
+    got = O.moe_layer(x, L4)["out"]
+    d13, d2 = _torch_mxfp4(q13, s13).numpy(), _torch_mxfp4(q2, s2).numpy()
+    ref = O.moe_layer(x, dict(L4, w13=d13, w2=d2, w13_scale=None, w2_scale=None))["out"]
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    # the decoded weights approximate the drawn ones within the format's steps
+    err = np.abs(d13 - w13)
+    scale = np.repeat(O.decode_e8m0(s13.numpy()), 32, axis=-1)
+    assert np.all(err <= np.maximum(0.25 * scale, np.abs(w13) * 0.25) + 1e-12)
+
+
+def test_mxfp4_quantiser_block_scales():
+    """Each block's largest magnitude lands on 4 or 6 (or saturates at 6) after the
+    power-of-two scale; all-zero blocks have zero codes."""
+    rng = np.random.default_rng(35)
+    w = (rng.standard_normal((2, 8, 128)) * rng.uniform(1e-3, 10, (2, 8, 1))).astype(np.float32)
+    w[0, 0, :32] = 0.0
+    q, sc = W._mxfp4(w)
+    d = _torch_mxfp4(q, sc).numpy().reshape(2, 8, 4, 32)
+    sb = O.decode_e8m0(sc.numpy())
+    top = np.abs(d).max(axis=-1) / sb
+    nz = np.abs(w.reshape(2, 8, 4, 32)).max(axis=-1) > 0
+    assert np.all(np.isin(top[nz], [4.0, 6.0]))
+    assert not d[0, 0, 0].any()
+
+
 def test_e4m3_encode_matches_torch_including_ties():
     """Nearest-even E4M3 encoding against torch's float8_e4m3fn conversion: every
     representable value, every midpoint between neighbours (ties), a dense sweep,
