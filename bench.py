@@ -99,9 +99,10 @@ def stage_work(spec, T, counts, path, dense_stage=None):
     dense_stage: decode path only, the stage whose launch runs the dense gate/up."""
     H, E, K, I = spec.H, spec.E, spec.K, spec.I
     S, Id = spec.n_shared, spec.I_dense
-    wb = 1 if spec.wdtype == "fp8" else (4 if spec.wdtype == "fp32" else 2)
+    wb = {"fp8": 1, "fp32": 4, "bf16": 2, "mxfp4": 0.5}[spec.wdtype]
     ab = 4 if spec.wdtype == "fp32" else 2
     sb = 4 if spec.wdtype == "fp8" else 0  # fp32 scale per output channel
+    mx = spec.wdtype == "mxfp4"            # MXFP4: one scale byte per 32 along the reduction
     Kp = K + S
     rows = T * K
     used = int((counts > 0).sum())
@@ -112,8 +113,8 @@ def stage_work(spec, T, counts, path, dense_stage=None):
     fl["down"] = 2 * rows * I * H + 2 * T * S * I * H
     fl["dense_gate_up"] = 2 * T * H * 2 * Id
     fl["dense_down"] = 2 * T * Id * H
-    w_up = used * 2 * I * (H * wb + sb) + S * 2 * I * H * ab
-    w_down = used * H * (I * wb + sb) + S * H * I * ab
+    w_up = int(used * 2 * I * (H * wb + sb + (H // 32 if mx else 0))) + S * 2 * I * H * ab
+    w_down = int(used * H * (I * wb + sb + (I // 32 if mx else 0))) + S * H * I * ab
     by = {}
     if path == "decode":
         # router launch: router logits; gate/up launch: routing + expert gate/up; down
@@ -355,7 +356,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": ("fp8-e4m3 weights and activations (per-row dynamic activation scales)" if spec.act_quant else
-                  {"fp32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 activations"}[spec.wdtype]),
+                  {"fp32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 activations",
+                   "mxfp4": "mxfp4 (e2m1 + e8m0 per 32) weights, bf16 activations"}[spec.wdtype]),
         "data": "synthetic",
         "config": {"workload": f"{spec.name} MoE FFN layer forward", "T": T, "hidden": spec.H,
                    "experts": spec.E, "top_k": spec.K, "inter": spec.I, "act": spec.act,

@@ -18,7 +18,10 @@
  *     a description of the last failure on the calling thread.
  *   - T = 0 is a valid no-op.
  *   - bf16 is stored as uint16_t (the upper half of an IEEE fp32); fp8 weights are
- *     OCP E4M3 ("fn": finite, max 448) codes stored as uint8_t.
+ *     OCP E4M3 ("fn": finite, max 448) codes stored as uint8_t; MXFP4 weights are
+ *     OCP MXFP4: E2M1 codes, two per byte (the even element in the low nibble),
+ *     with one E8M0 scale byte (2^(s-127)) per 32 consecutive elements along the
+ *     reduction dimension.
  *
  * Citations name the web pages that describe each operation:
  *   [G4] "Gemma 4 26B-A4B MoE walkthrough" (yeyulingfeng.com/587419)
@@ -46,7 +49,7 @@ typedef enum {
 } moe_status;
 
 typedef enum { MOE_ACT_SILU = 0, MOE_ACT_GELU_TANH = 1 } moe_act;
-typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1, MOE_DT_FP8_E4M3 = 2 } moe_dtype;
+typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1, MOE_DT_FP8_E4M3 = 2, MOE_DT_MXFP4 = 3 } moe_dtype;
 typedef enum { MOE_ROUTER_PLAIN = 0, MOE_ROUTER_GEMMA = 1 } moe_router_mode;
 /* How the router turns logits into routing probabilities ([LC] routing: a
  * softmax, or in some models a sigmoid). */
@@ -135,7 +138,8 @@ typedef struct {
   int32_t inter;         /* I of every routed expert, multiple of 64 */
   int32_t act;           /* moe_act of the routed / shared experts */
   int32_t act_dtype;     /* MOE_DT_F32 or MOE_DT_BF16: x, out, router / shared / dense weights */
-  int32_t weight_dtype;  /* routed expert weights: F32 (needs act F32), BF16, or FP8_E4M3 (needs BF16) */
+  int32_t weight_dtype;  /* routed expert weights: F32 (needs act F32), BF16, FP8_E4M3 (needs BF16), or
+                            MXFP4 (needs BF16; decode path only, see moe_forward) */
   int32_t renormalize;   /* non-zero: renormalise the top-k weights (see moe_route) */
   int32_t router_mode;   /* moe_router_mode, used when logits are computed */
   int32_t n_shared;      /* always-on shared experts (weight 1, same I), 0..8 */
@@ -163,8 +167,9 @@ typedef struct {
   const float* per_expert_scale;  /* [E], NULL = ones */
   const void* w13;                /* [E, 2I, H]: rows [0,I) gate (w1), rows [I,2I) up (w3) */
   const void* w2;                 /* [E, H, I] down projection */
-  const float* w13_scale;         /* [E, 2I] per-output-channel fp32 scales (FP8 only) */
-  const float* w2_scale;          /* [E, H] (FP8 only) */
+  const float* w13_scale;         /* FP8: [E, 2I] per-output-channel fp32 scales; MXFP4: uint8 E8M0
+                                     block scales [E, 2I, H/32] (one per 32 along H) */
+  const float* w2_scale;          /* FP8: [E, H] fp32; MXFP4: uint8 [E, H, I/32] */
   const void* shared_w13;         /* [n_shared, 2I, H] act_dtype, or NULL when n_shared == 0 */
   const void* shared_w2;          /* [n_shared, H, I] */
   const void* dense_w13;          /* [2*inter_dense, H] act_dtype (gate rows first) */
@@ -199,6 +204,9 @@ moe_status moe_forward_workspace_size(const moe_layer_desc* desc, int64_t T, siz
  *            (gated FFN, [MI]; activation SiLU [LC] or GELU-tanh [G4] section 6);
  *            x_e = RMSNorm(x) * gamma_pre2 when the dense branch is present, else x;
  *            FP8 weights: W = decode_e4m3(q) * scale[e, n] ([SG]);
+ *            MXFP4 weights: W[n, k] = decode_e2m1(q[n, k]) * 2^(s[n, k/32] - 127) ([LC]:
+ *            4-bit experts for decode memory); these run on the decode path only,
+ *            other T return MOE_UNSUPPORTED;
  *            FP8 activations (act_quant, [SG] FP8-Dynamic): the routed experts' GEMM
  *            inputs x_e and h are each quantised per row first, scale = max|row| / 448
  *            (1 for a zero row), code = E4M3 nearest-even of value / scale (fp32),

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
 
 MOE_OK, MOE_INVALID_ARG, MOE_UNSUPPORTED, MOE_WORKSPACE_TOO_SMALL, MOE_HIP_ERROR = range(5)
 ACT = {"silu": 0, "gelu_tanh": 1}
-DT_F32, DT_BF16, DT_FP8 = 0, 1, 2
+DT_F32, DT_BF16, DT_FP8, DT_MXFP4 = 0, 1, 2, 3
 ROUTER_PLAIN, ROUTER_GEMMA = 0, 1
 SCORING = {"softmax": 0, "sigmoid": 1}
 ACT_QUANT = {None: 0, "fp8_dynamic": 1}
@@ -192,7 +192,7 @@ class DeviceLayer:
         f32 = spec.wdtype == "fp32"
         desc = LayerDesc(hidden=spec.H, num_experts=spec.E, top_k=spec.K, inter=spec.I,
                          act=ACT[spec.act], act_dtype=DT_F32 if f32 else DT_BF16,
-                         weight_dtype={"fp32": DT_F32, "bf16": DT_BF16, "fp8": DT_FP8}[spec.wdtype],
+                         weight_dtype={"fp32": DT_F32, "bf16": DT_BF16, "fp8": DT_FP8, "mxfp4": DT_MXFP4}[spec.wdtype],
                          renormalize=int(spec.renorm),
                          router_mode=ROUTER_GEMMA if spec.router_mode == "gemma" else ROUTER_PLAIN,
                          n_shared=spec.n_shared, inter_dense=spec.I_dense, dense_act=ACT[spec.act],

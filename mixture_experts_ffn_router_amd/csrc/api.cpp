@@ -155,10 +155,11 @@ moe_status validate_desc(const moe_layer_desc* d) {
     return fail(MOE_INVALID_ARG, "act_dtype must be F32 or BF16");
   if (d->act_dtype == MOE_DT_F32 && d->weight_dtype != MOE_DT_F32)
     return fail(MOE_UNSUPPORTED, "an fp32 layer needs fp32 expert weights");
-  if (d->act_dtype == MOE_DT_BF16 && d->weight_dtype != MOE_DT_BF16 && d->weight_dtype != MOE_DT_FP8_E4M3)
-    return fail(MOE_UNSUPPORTED, "a bf16 layer needs bf16 or fp8 expert weights");
-  if (d->weight_dtype == MOE_DT_FP8_E4M3 && d->n_shared)
-    return fail(MOE_UNSUPPORTED, "shared experts with fp8 routed experts");
+  if (d->act_dtype == MOE_DT_BF16 && d->weight_dtype != MOE_DT_BF16 && d->weight_dtype != MOE_DT_FP8_E4M3 &&
+      d->weight_dtype != MOE_DT_MXFP4)
+    return fail(MOE_UNSUPPORTED, "a bf16 layer needs bf16, fp8 or mxfp4 expert weights");
+  if ((d->weight_dtype == MOE_DT_FP8_E4M3 || d->weight_dtype == MOE_DT_MXFP4) && d->n_shared)
+    return fail(MOE_UNSUPPORTED, "shared experts with fp8 / mxfp4 routed experts");
   if (d->router_mode != MOE_ROUTER_PLAIN && d->router_mode != MOE_ROUTER_GEMMA)
     return fail(MOE_INVALID_ARG, "unknown router mode %d", d->router_mode);
   if (!(d->eps >= 0.f)) return fail(MOE_INVALID_ARG, "eps must be >= 0");
@@ -272,8 +273,8 @@ moe_status validate_tensors(const moe_layer_desc& d, const moe_tensors* t) {
   if (!t) return fail(MOE_INVALID_ARG, "tensors is NULL");
   if (!t->x || !t->w13 || !t->w2 || !t->out) return fail(MOE_INVALID_ARG, "x, w13, w2 and out are required");
   if (!t->logits && !t->w_router) return fail(MOE_INVALID_ARG, "either logits or w_router is required");
-  if (d.weight_dtype == MOE_DT_FP8_E4M3 && (!t->w13_scale || !t->w2_scale))
-    return fail(MOE_INVALID_ARG, "fp8 weights need w13_scale and w2_scale");
+  if ((d.weight_dtype == MOE_DT_FP8_E4M3 || d.weight_dtype == MOE_DT_MXFP4) && (!t->w13_scale || !t->w2_scale))
+    return fail(MOE_INVALID_ARG, "fp8 / mxfp4 weights need w13_scale and w2_scale");
   if (d.n_shared && (!t->shared_w13 || !t->shared_w2))
     return fail(MOE_INVALID_ARG, "n_shared > 0 needs shared_w13 and shared_w2");
   if (d.inter_dense && (!t->dense_w13 || !t->dense_w2))
@@ -385,6 +386,8 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
   Plan p;
   s = make_plan(d, t, T, p);
   if (s != MOE_OK) return s;
+  if (d.weight_dtype == MOE_DT_MXFP4 && !p.decode)
+    return fail(MOE_UNSUPPORTED, "mxfp4 expert weights serve the decode path only (T <= 16, rows within its LDS staging)");
   if (!workspace || workspace_bytes < p.total)
     return fail(MOE_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, p.total);
   if ((uintptr_t)workspace % ALIGN) return fail(MOE_INVALID_ARG, "workspace must be 256-byte aligned");
@@ -427,8 +430,11 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
     a.pes = t->per_expert_scale;
     a.w13 = t->w13;
     a.w2 = t->w2;
-    a.s13 = t->w13_scale;
-    a.s2 = t->w2_scale;
+    const bool mx = d.weight_dtype == MOE_DT_MXFP4;
+    a.s13 = mx ? nullptr : t->w13_scale;
+    a.s2 = mx ? nullptr : t->w2_scale;
+    a.mx13 = mx ? (const uint8_t*)t->w13_scale : nullptr;
+    a.mx2 = mx ? (const uint8_t*)t->w2_scale : nullptr;
     a.shared_w13 = t->shared_w13;
     a.shared_w2 = t->shared_w2;
     a.dense_w13 = t->dense_w13;
@@ -445,7 +451,7 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
     a.out_f32 = t->out_f32;
     a.topk_w_out = t->topk_w_out;
     a.topk_ids_out = t->topk_ids_out;
-    const bool fp8 = d.weight_dtype == MOE_DT_FP8_E4M3;
+    const int wk = d.weight_dtype == MOE_DT_FP8_E4M3 ? 1 : (d.weight_dtype == MOE_DT_MXFP4 ? 2 : 0);
     STAGE(MOE_STAGE_PRENORM);
     STAGE(MOE_STAGE_ROUTER);
     // router logits
@@ -458,11 +464,11 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
     STAGE(MOE_STAGE_QUANT_X);
     STAGE(MOE_STAGE_GATE_UP);
     // dense gate/up, routing + expert gate/up
-    HIP_TRY(moe::launch_decode_up(a, fp8, st), "decode up launch");
+    HIP_TRY(moe::launch_decode_up(a, wk, st), "decode up launch");
     STAGE(MOE_STAGE_QUANT_H);
     STAGE(MOE_STAGE_DOWN);
     // dense down, expert down + combine
-    HIP_TRY(moe::launch_decode_down(a, fp8, st), "decode down launch");
+    HIP_TRY(moe::launch_decode_down(a, wk, st), "decode down launch");
     STAGE(MOE_STAGE_DENSE_GATE_UP);
     STAGE(MOE_STAGE_DENSE_DOWN);
     STAGE(MOE_STAGE_FINALIZE);

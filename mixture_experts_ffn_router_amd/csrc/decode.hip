@@ -38,12 +38,21 @@
 // Weights are addressed through buffer resources: a row past the end of the
 // tensor (router rows >= E) reads as zero.  FP8 weights are widened to bf16 in
 // registers (exact) and their per-output-channel scale is applied once per
-// expert to the reduced tile.
+// expert to the reduced tile.  MXFP4 weights (4-bit E2M1 codes, one E8M0 scale
+// per 32 along the reduction; llama.cpp lesson 35: 4-bit experts for decode
+// memory) are widened with their block scale by v_cvt_scalef32_pk_bf16_fp4
+// (exact: a power of two times a 4-bit value), half the bytes of FP8.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "route_dev.h"
 
 namespace moe {
+
+// Expert weight kinds of the streaming kernels.
+enum : int { WK_BF16 = 0, WK_FP8 = 1, WK_FP4 = 2 };
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // Macro steps (64 reduction elements each) per load batch (measured: short
 // batches with more resident waves stream bf16 weights best; fp8 prefers longer).
@@ -57,11 +66,58 @@ constexpr int XCH = 8;  // 16-byte chunks per lane of a token row held in regist
 // 8 elements starting at kchunk(m, j, g):
 //   bf16 weights: 64m + 32j + 8g   (each 16-byte load is one MFMA's operand)
 //   fp8 weights:  64m + 16g + 8j   (one 16-byte load holds both MFMAs' operands)
+//   MXFP4:        128(m/2) + 32g + 16(m%2) + 8j
+//                 (one 16-byte load holds a pair of macro steps for a lane group:
+//                 32 elements, exactly one block of the block scale)
 // The assignment of reduction indices to MFMA slots is arbitrary as long as A
-// and B agree; these make every load 16 contiguous bytes.
-template <bool FP8>
+// and B agree; these make every load contiguous.
+template <int WK>
 __device__ __forceinline__ int kchunk(int m, int j, int g) {
-  return FP8 ? 64 * m + 16 * g + 8 * j : 64 * m + 32 * j + 8 * g;
+  if constexpr (WK == WK_FP4) return 128 * (m >> 1) + 32 * g + 16 * (m & 1) + 8 * j;
+  return WK != WK_BF16 ? 64 * m + 16 * g + 8 * j : 64 * m + 32 * j + 8 * g;
+}
+
+// Part idx of parts of the macro steps [lo, hi).  MXFP4 ranges are whole pairs
+// of steps (lo even), so a 16-byte load never straddles two ranges; an odd step
+// count is rounded up to a pair, whose elements past the reduction length the
+// stream zeroes (both steps of a pair hold elements below it).
+template <int WK>
+__device__ __forceinline__ void sub_range(int lo, int hi, int idx, int parts, int& a, int& b) {
+  const int n = hi - lo;
+  if constexpr (WK == WK_FP4) {
+    const int np = (n + 1) / 2;
+    a = lo + 2 * (idx * np / parts);
+    b = lo + 2 * ((idx + 1) * np / parts);
+  } else {
+    a = lo + idx * n / parts;
+    b = lo + (idx + 1) * n / parts;
+  }
+}
+
+// Bytes of n weight elements of kind WK.
+template <int WK>
+__host__ __device__ constexpr int64_t wbytes(int64_t n) {
+  return WK == WK_BF16 ? 2 * n : (WK == WK_FP8 ? n : n / 2);
+}
+
+// E8M0 block scale -> fp32 (2^(c - 127); c = 0 is the subnormal 2^-127)
+__device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
+  return __uint_as_float(c ? c << 23 : 0x00400000u);
+}
+
+// 8 E2M1 codes (element i in bits 4i..4i+3) times scale s -> 8 bf16, in order
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t w, float s) {
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  const bf16x2v p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0);
+  const bf16x2v p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1);
+  const bf16x2v p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2);
+  const bf16x2v p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3);
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, p0);
+  r[1] = __builtin_bit_cast(uint32_t, p1);
+  r[2] = __builtin_bit_cast(uint32_t, p2);
+  r[3] = __builtin_bit_cast(uint32_t, p3);
+  return __builtin_bit_cast(bf16x8, r);
 }
 
 constexpr uint32_t OOB = 0x80000000u;  // a buffer offset past every tensor here: the load returns 0
@@ -74,16 +130,23 @@ __device__ __forceinline__ u32x4 bload(rsrc_t r, uint32_t off) {
 //   ra/aoff: weight tensor and the byte offset of this lane's weight row;
 //   BG = false: B rows in LDS (b_lds = this lane's token row, zero if !bvalid);
 //   BG = true:  B rows in global memory (rb/boff; boff past the end reads zero).
-template <bool FP8, int NR, bool BG, int DU>
+//   MXFP4: rs/soff: the block-scale tensor and the byte offset of this lane's
+//   row of scales (one byte per 32 elements).
+template <int WK, int NR, bool BG, int DU>
 struct Stream {
-  static constexpr int LA = FP8 ? 1 : 2;  // 16-byte A loads per row group per macro step
-  static constexpr int EB = FP8 ? 1 : 2;
+  static_assert(WK != WK_FP4 || DU % 2 == 0, "MXFP4 batches hold whole pairs of steps");
+  static constexpr int LA = WK == WK_BF16 ? 2 : 1;  // A loads per row group per macro step
   rsrc_t ra[NR];
   uint32_t aoff[NR];
+  rsrc_t rs[NR];
+  uint32_t soff[NR];
+  int kmax = 1 << 30;  // MXFP4: the reduction length; a pair that ends past it (K % 128 == 64)
+                       // gives some lane groups elements >= kmax, which take zero A and B
   rsrc_t rb;
   uint32_t boff;
   int g;
   u32x4 av[NR][DU][LA];
+  uint32_t sv[NR][(DU + 1) / 2];  // MXFP4: block scale of each pair of steps
   u32x4 bv[BG ? DU : 1][2];
 
   __device__ __forceinline__ void load(int m, int m1) {
@@ -91,13 +154,27 @@ struct Stream {
     for (int u = 0; u < DU; ++u) {
       const bool live = m + u < m1;
 #pragma unroll
-      for (int r = 0; r < NR; ++r)
+      for (int r = 0; r < NR; ++r) {
+        if constexpr (WK == WK_FP4) {
+          // a pair of steps (m even: batches start on a pair): 32 codes (16 bytes),
+          // one 32-element block, and its scale; the odd step reuses them
+          if (u % 2 == 0) {
+            const int k = kchunk<WK>(m + u, 0, g);
+            av[r][u][0] = bload(ra[r], live ? aoff[r] + (uint32_t)(k / 2) : OOB);
+            sv[r][u / 2] = __builtin_amdgcn_raw_buffer_load_b8(rs[r], (int)(live ? soff[r] + (uint32_t)(k / 32) : OOB), 0, 0);
+          }
+        } else {
 #pragma unroll
-        for (int j = 0; j < LA; ++j)
-          av[r][u][j] = bload(ra[r], live ? aoff[r] + (uint32_t)(kchunk<FP8>(m + u, j, g) * EB) : OOB);
+          for (int j = 0; j < LA; ++j)
+            av[r][u][j] = bload(ra[r], live ? aoff[r] + (uint32_t)wbytes<WK>(kchunk<WK>(m + u, j, g)) : OOB);
+        }
+      }
       if constexpr (BG) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) bv[u][j] = bload(rb, live ? boff + (uint32_t)(kchunk<FP8>(m + u, j, g) * 2) : OOB);
+        for (int j = 0; j < 2; ++j) {
+          const int k = kchunk<WK>(m + u, j, g);
+          bv[u][j] = bload(rb, live && (WK != WK_FP4 || k < kmax) ? boff + (uint32_t)(k * 2) : OOB);
+        }
       }
     }
   }
@@ -113,13 +190,21 @@ struct Stream {
         if constexpr (BG) {
           b = __builtin_bit_cast(bf16x8, bv[u][j]);
         } else {
-          const u32x4 raw = *(const u32x4*)(b_lds + kchunk<FP8>(mu, j, g));
-          b = __builtin_bit_cast(bf16x8, bvalid ? raw : u32x4{0u, 0u, 0u, 0u});
+          const int k = kchunk<WK>(mu, j, g);
+          const bool kin = WK != WK_FP4 || k < kmax;
+          const u32x4 raw = *(const u32x4*)(b_lds + (kin ? k : 0));
+          b = __builtin_bit_cast(bf16x8, bvalid && kin ? raw : u32x4{0u, 0u, 0u, 0u});
         }
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
           bf16x8 a;
-          if constexpr (FP8) {
+          if constexpr (WK == WK_FP4) {
+            // step u of its pair: dwords 2(u % 2) + j; a step past m1 (the second of
+            // a pair that straddles the end) contributes zero weights
+            const u32x4 q = av[r][u & ~1][0];
+            const uint32_t w = m + u < m1 && kchunk<WK>(m + u, j, g) < kmax ? q[2 * (u & 1) + j] : 0u;
+            a = fp4x8_to_bf16x8(w, e8m0_to_f32(sv[r][u / 2]));
+          } else if constexpr (WK == WK_FP8) {
             const u32x4 q = av[r][u][0];
             a = fp8x8_to_bf16x8(j ? q[2] : q[0], j ? q[3] : q[1]);
           } else {
@@ -272,7 +357,7 @@ __device__ void dense_gate_up_tile(const DecodeArgs& a, uint8_t* dsm, int i0) {
   wave_range<PW>(H / 64, wave, m0, m1);
   RowRegs xr;
   if (wave < T) row_load(xr, rx, wave, H, 0, lane);
-  Stream<false, 2, false, DU_BF16> st;
+  Stream<WK_BF16, 2, false, DU_BF16> st;
   st.ra[0] = st.ra[1] = make_rsrc(a.dense_w13, (uint32_t)((int64_t)2 * Id * H * 2));
   st.aoff[0] = (uint32_t)((i0 + col) * H * 2);
   st.aoff[1] = (uint32_t)((Id + i0 + col) * H * 2);
@@ -313,7 +398,7 @@ __global__ __launch_bounds__(PW * 64, 2) void decode_pre_kernel(DecodeArgs a) {
   RowRegs xr;
   if (wave < T) row_load(xr, rx, wave, H, 0, lane);
   const int e0 = blockIdx.x * 16;
-  Stream<false, 1, false, DU_PRE> st;
+  Stream<WK_BF16, 1, false, DU_PRE> st;
   st.ra[0] = make_rsrc(a.w_router, (uint32_t)((int64_t)a.E * H * 2));
   st.aoff[0] = (uint32_t)((e0 + col) * H * 2);  // rows >= E read zero
   st.g = g;
@@ -333,7 +418,7 @@ __global__ __launch_bounds__(PW * 64, 2) void decode_pre_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------- up: dense gate/up, routing + expert gate/up
-template <int VPL, bool FP8>
+template <int VPL, int WK>
 __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) uint8_t dsm[];
   if ((int)blockIdx.x < a.n_dense_groups) {
@@ -412,17 +497,16 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
   }
 
   // 3. (active expert, 16 hidden units) items: a contiguous, balanced range per block
-  constexpr int WB = FP8 ? 1 : 2;
   const int RG = I / 16, n_items = n_act * RG;
   const int it0 = (int)((int64_t)blk * n_items / a.n_up_blocks);
   const int it1 = (int)((int64_t)(blk + 1) * n_items / a.n_up_blocks);
   int m0, m1;
-  wave_range<PW>(H / 64, wave, m0, m1);
+  sub_range<WK>(0, H / 64, wave, PW, m0, m1);
   for (int item = it0; item < it1; ++item) {
     const int u = item / RG, i0 = (item % RG) * 16;
     const int e = s_active[u];
     float sg = 1.f, su = 1.f;  // fp8 per-output-channel scales of the epilogue's row, loaded early
-    if constexpr (FP8) {
+    if constexpr (WK == WK_FP8) {
       if (threadIdx.x < 256) {
         sg = a.s13[(int64_t)e * 2 * I + i0 + (threadIdx.x >> 4)];
         su = a.s13[(int64_t)e * 2 * I + I + i0 + (threadIdx.x >> 4)];
@@ -431,12 +515,18 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
     const int slot_col = col < T ? find_slot(s_ids, Kp, col, e) : -1;
     const bool bvalid = slot_col >= 0;
     const bf16_t* brow = sx + (bvalid ? col : 0) * pitch;
-    const uint8_t* wbase = e < E ? (const uint8_t*)a.w13 + (int64_t)e * 2 * I * H * WB
+    const uint8_t* wbase = e < E ? (const uint8_t*)a.w13 + wbytes<WK>((int64_t)e * 2 * I * H)
                                  : (const uint8_t*)a.shared_w13 + (int64_t)(e - E) * 2 * I * H * 2;
-    Stream<FP8, 2, false, FP8 ? DU_FP8 : DU_BF16> st;
-    st.ra[0] = st.ra[1] = make_rsrc(wbase, (uint32_t)((int64_t)2 * I * H * WB));
-    st.aoff[0] = (uint32_t)((i0 + col) * H * WB);
-    st.aoff[1] = (uint32_t)((I + i0 + col) * H * WB);
+    Stream<WK, 2, false, WK == WK_BF16 ? DU_BF16 : DU_FP8> st;
+    st.ra[0] = st.ra[1] = make_rsrc(wbase, (uint32_t)wbytes<WK>((int64_t)2 * I * H));
+    st.aoff[0] = (uint32_t)wbytes<WK>((int64_t)(i0 + col) * H);
+    st.aoff[1] = (uint32_t)wbytes<WK>((int64_t)(I + i0 + col) * H);
+    if constexpr (WK == WK_FP4) {  // E8M0 scales [E, 2I, H/32]
+      st.kmax = H;
+      st.rs[0] = st.rs[1] = make_rsrc(a.mx13 + (int64_t)e * 2 * I * (H / 32), (uint32_t)(2 * I * (H / 32)));
+      st.soff[0] = (uint32_t)((i0 + col) * (H / 32));
+      st.soff[1] = (uint32_t)((I + i0 + col) * (H / 32));
+    }
     st.g = g;
     f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     st.run(acc, brow, bvalid, m0, m1, false);
@@ -457,7 +547,7 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------- down: dense down, expert down + combine
-template <bool FP8>
+template <int WK>
 __global__ __launch_bounds__(DW3 * 64) void decode_down_kernel(DecodeArgs a) {
   __shared__ float red[DW3 * 4 * 64];
   const int T = a.T, H = a.H, I = a.I, E = a.E, Ep = a.Ep;
@@ -466,7 +556,7 @@ __global__ __launch_bounds__(DW3 * 64) void decode_down_kernel(DecodeArgs a) {
   if ((int)blockIdx.x < a.n_ddown_groups) {
     // dense MLP down projection: 16 output features x T tokens, fp32 out
     const int Id = a.Id, n0 = blockIdx.x * 16;
-    Stream<false, 1, true, DU_BF16> st;
+    Stream<WK_BF16, 1, true, DU_BF16> st;
     st.ra[0] = make_rsrc(a.dense_w2, (uint32_t)((int64_t)H * Id * 2));
     st.aoff[0] = (uint32_t)((n0 + col) * Id * 2);
     st.rb = make_rsrc(a.hd, (uint32_t)(T * Id * 2));
@@ -496,10 +586,11 @@ __global__ __launch_bounds__(DW3 * 64) void decode_down_kernel(DecodeArgs a) {
   const int n_act = a.rinfo[0];
   int e_spec = a.rinfo[1 + us];
   int slot_spec = a.rinfo[1 + Ep + us * 16 + col];
-  const int k0 = part * (I / 64) / P, MS = (part + 1) * (I / 64) / P - k0;  // this part's macro steps
-  const int S = min((DW3 + n_act - 1) / n_act, MS);  // further splits per expert over the waves
+  int k0, k1;  // this part's macro steps
+  sub_range<WK>(0, I / 64, part, P, k0, k1);
+  const int MS = k1 - k0;
+  const int S = max(1, min((DW3 + n_act - 1) / n_act, WK == WK_FP4 ? (MS + 1) / 2 : MS));  // further splits per expert over the waves
   const int n_units = n_act * S;
-  constexpr int WB = FP8 ? 1 : 2;
   const rsrc_t rb = make_rsrc(a.hbuf, (uint32_t)((int64_t)T * a.Kp * I * 2));
   f32x4 tot = {0.f, 0.f, 0.f, 0.f};
   for (int unit = wave; unit < n_units; unit += DW3) {
@@ -507,22 +598,29 @@ __global__ __launch_bounds__(DW3 * 64) void decode_down_kernel(DecodeArgs a) {
     const bool spec = u == us && unit == wave;
     const int e = spec ? e_spec : a.rinfo[1 + u];
     const int slot = spec ? slot_spec : a.rinfo[1 + Ep + u * 16 + col];
-    const uint8_t* wbase = e < E ? (const uint8_t*)a.w2 + (int64_t)e * H * I * WB
+    const uint8_t* wbase = e < E ? (const uint8_t*)a.w2 + wbytes<WK>((int64_t)e * H * I)
                                  : (const uint8_t*)a.shared_w2 + (int64_t)(e - E) * H * I * 2;
-    Stream<FP8, 1, true, FP8 ? DU_FP8 : DU_BF16> st;
-    st.ra[0] = make_rsrc(wbase, (uint32_t)((int64_t)H * I * WB));
-    st.aoff[0] = (uint32_t)((n0 + col) * I * WB);
+    Stream<WK, 1, true, WK == WK_BF16 ? DU_BF16 : DU_FP8> st;
+    st.ra[0] = make_rsrc(wbase, (uint32_t)wbytes<WK>((int64_t)H * I));
+    st.aoff[0] = (uint32_t)wbytes<WK>((int64_t)(n0 + col) * I);
+    if constexpr (WK == WK_FP4) {  // E8M0 scales [E, H, I/32]
+      st.kmax = I;
+      st.rs[0] = make_rsrc(a.mx2 + (int64_t)e * H * (I / 32), (uint32_t)(H * (I / 32)));
+      st.soff[0] = (uint32_t)((n0 + col) * (I / 32));
+    }
     st.rb = rb;
     st.boff = slot >= 0 ? (uint32_t)((int64_t)slot * I * 2) : OOB;
     st.g = g;
     f32x4 sc = {1.f, 1.f, 1.f, 1.f};  // fp8 per-output-channel scales of this lane's rows, loaded early
-    if constexpr (FP8) {
+    if constexpr (WK == WK_FP8) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) sc[v] = a.s2[(int64_t)e * H + n0 + 4 * g + v];
     }
     f32x4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
-    st.run(acc, nullptr, false, k0 + s * MS / S, k0 + (s + 1) * MS / S, false);
-    if constexpr (FP8) {
+    int s0, s1;
+    sub_range<WK>(k0, k1, s, S, s0, s1);
+    st.run(acc, nullptr, false, s0, s1, false);
+    if constexpr (WK == WK_FP8) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) tot[v] += sc[v] * acc[0][v];
     } else {
@@ -570,11 +668,11 @@ hipError_t launch_decode_pre(const DecodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int VPL, bool FP8>
+template <int VPL, int WK>
 static hipError_t up_vpl(const DecodeArgs& a, int nb, int lds, hipStream_t s) {
-  hipError_t e = allow_lds(decode_up_kernel<VPL, FP8>, lds);
+  hipError_t e = allow_lds(decode_up_kernel<VPL, WK>, lds);
   if (e != hipSuccess) return e;
-  decode_up_kernel<VPL, FP8><<<dim3(nb), dim3(PW * 64), lds, s>>>(a);
+  decode_up_kernel<VPL, WK><<<dim3(nb), dim3(PW * 64), lds, s>>>(a);
   return hipGetLastError();
 }
 
@@ -597,7 +695,7 @@ int decode_up_blocks_per_cu(int T, int H, int Kp, int Ep) {
 // a.n_up_blocks holds the number of (expert, 16 hidden units) items on entry;
 // the expert blocks walk them, sized so that they and the dense blocks are
 // resident together.
-hipError_t launch_decode_up(const DecodeArgs& args, bool fp8, hipStream_t s) {
+hipError_t launch_decode_up(const DecodeArgs& args, int wk, hipStream_t s) {
   DecodeArgs a = args;
   const int lds = decode_up_lds_bytes(a.T, a.H, a.Kp, a.Ep);
   const int slots = cu_count() * decode_up_blocks_per_cu(a.T, a.H, a.Kp, a.Ep);
@@ -608,20 +706,18 @@ hipError_t launch_decode_up(const DecodeArgs& args, bool fp8, hipStream_t s) {
   a.n_up_blocks = (a.n_up_blocks + per_block - 1) / per_block;
   const int nb = a.n_dense_groups + a.n_up_blocks;
   const int vpl = a.E <= 64 ? 1 : a.E <= 128 ? 2 : a.E <= 256 ? 4 : 8;
-  if (fp8) {
+  auto go = [&](auto wk_tag) -> hipError_t {
+    constexpr int WK = decltype(wk_tag)::value;
     switch (vpl) {
-      case 1: return up_vpl<1, true>(a, nb, lds, s);
-      case 2: return up_vpl<2, true>(a, nb, lds, s);
-      case 4: return up_vpl<4, true>(a, nb, lds, s);
-      default: return up_vpl<8, true>(a, nb, lds, s);
+      case 1: return up_vpl<1, WK>(a, nb, lds, s);
+      case 2: return up_vpl<2, WK>(a, nb, lds, s);
+      case 4: return up_vpl<4, WK>(a, nb, lds, s);
+      default: return up_vpl<8, WK>(a, nb, lds, s);
     }
-  }
-  switch (vpl) {
-    case 1: return up_vpl<1, false>(a, nb, lds, s);
-    case 2: return up_vpl<2, false>(a, nb, lds, s);
-    case 4: return up_vpl<4, false>(a, nb, lds, s);
-    default: return up_vpl<8, false>(a, nb, lds, s);
-  }
+  };
+  if (wk == WK_FP8) return go(std::integral_constant<int, WK_FP8>{});
+  if (wk == WK_FP4) return go(std::integral_constant<int, WK_FP4>{});
+  return go(std::integral_constant<int, WK_BF16>{});
 }
 
 // Parts per output-feature group of the down kernel: enough blocks for about two
@@ -636,11 +732,12 @@ int decode_down_splits(int T, int H, int I, bool dense) {
   return P < I / 64 ? P : I / 64;
 }
 
-hipError_t launch_decode_down(const DecodeArgs& a, bool fp8, hipStream_t s) {
+hipError_t launch_decode_down(const DecodeArgs& a, int wk, hipStream_t s) {
   if (a.down_splits < 1 || (a.down_splits > 1 && !a.ypart)) return hipErrorInvalidValue;
   const dim3 grid(a.n_ddown_groups + a.H / 16 * a.down_splits), block(DW3 * 64);
-  if (fp8) decode_down_kernel<true><<<grid, block, 0, s>>>(a);
-  else decode_down_kernel<false><<<grid, block, 0, s>>>(a);
+  if (wk == WK_FP8) decode_down_kernel<WK_FP8><<<grid, block, 0, s>>>(a);
+  else if (wk == WK_FP4) decode_down_kernel<WK_FP4><<<grid, block, 0, s>>>(a);
+  else decode_down_kernel<WK_BF16><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -123,6 +123,8 @@ struct DecodeArgs {
   const void* w2;
   const float* s13;
   const float* s2;
+  const uint8_t* mx13;  // MXFP4 experts: E8M0 block scales [E, 2I, H/32] / [E, H, I/32]
+  const uint8_t* mx2;
   const void* shared_w13;
   const void* shared_w2;
   const void* dense_w13;
@@ -146,7 +148,8 @@ int decode_pre_lds_bytes(int T, int H);
 int decode_up_blocks_per_cu(int T, int H, int Kp, int Ep);
 int decode_down_splits(int T, int H, int I, bool dense);
 hipError_t launch_decode_pre(const DecodeArgs& a, hipStream_t s);
-hipError_t launch_decode_up(const DecodeArgs& a, bool fp8, hipStream_t s);
-hipError_t launch_decode_down(const DecodeArgs& a, bool fp8, hipStream_t s);
+// wk: expert weight kind, 0 bf16, 1 FP8 E4M3, 2 MXFP4
+hipError_t launch_decode_up(const DecodeArgs& a, int wk, hipStream_t s);
+hipError_t launch_decode_down(const DecodeArgs& a, int wk, hipStream_t s);
 
 }  // namespace moe

@@ -87,6 +87,9 @@ def _ws(desc, T):
     (dict(num_experts=128, top_k=2, n_groups=128, topk_groups=2), B.MOE_UNSUPPORTED),
     (dict(act_quant=2), B.MOE_INVALID_ARG),
     (dict(block_tail=2), B.MOE_INVALID_ARG),
+    (dict(weight_dtype=B.DT_MXFP4, n_shared=1), B.MOE_UNSUPPORTED),
+    (dict(weight_dtype=B.DT_MXFP4, act_dtype=B.DT_F32), B.MOE_UNSUPPORTED),
+    (dict(weight_dtype=B.DT_MXFP4, act_quant=1), B.MOE_UNSUPPORTED),
     (dict(act_quant=1), B.MOE_UNSUPPORTED),                              # bf16 weights
     (dict(act_quant=1, weight_dtype=B.DT_FP8, inter=16448), B.MOE_UNSUPPORTED),
 ])
@@ -171,3 +174,15 @@ def test_fp8_activation_layers_take_the_grouped_path():
     st0, n0 = _ws(d0, 4096)
     st1, n1 = _ws(d, 4096)
     assert st0 == st1 == B.MOE_OK and n1 > n0 + 4096 * 256
+
+
+def test_mxfp4_layers_run_on_the_decode_path_only():
+    lib = _lib()
+    d = _desc(weight_dtype=B.DT_MXFP4)
+    assert lib.moe_forward_path(C.byref(d), 4) == 1
+    fake = 0x1000  # never dereferenced: the call is refused before any launch
+    ts = B.Tensors(x=fake, w13=fake, w2=fake, out=fake, w_router=fake, w13_scale=fake, w2_scale=fake)
+    st = lib.moe_forward(C.byref(d), C.byref(ts), 64, fake, 1 << 40, None)
+    assert st == B.MOE_UNSUPPORTED and b"decode path" in lib.moe_last_error()
+    ts.w13_scale = None
+    assert lib.moe_forward(C.byref(d), C.byref(ts), 4, fake, 1 << 40, None) == B.MOE_INVALID_ARG

@@ -43,7 +43,8 @@ def B():
 def _kind(spec):
     if spec.act_quant and spec.I_dense:
         return "fp8_act_postnorm"
-    return {"fp32": "fp32", "bf16": "bf16", "fp8": "fp8"}[spec.wdtype]
+    # MXFP4 weights widen exactly to bf16 (a power of two times a 4-bit value): bf16 bounds
+    return {"fp32": "fp32", "bf16": "bf16", "fp8": "fp8", "mxfp4": "bf16"}[spec.wdtype]
 
 
 def run_and_check(B, L, rows=None, check_logits=True):
@@ -214,6 +215,11 @@ DECODE = {
                                     router_mode="gemma", per_expert_scale="uniform", I_dense=192,
                                     random_gammas=True, block_tail=True),
     "plain_block_tail": W.LayerSpec("dec_plain_tail", 1, 256, 8, 2, 512, "silu", "bf16", block_tail=True),
+    # 4-bit (MXFP4) expert weights: E2M1 codes with E8M0 block scales, widened in the kernels
+    "mxfp4_gemma": W.LayerSpec("dec_mxfp4_gemma", 1, 256, 16, 4, 128, "gelu_tanh", "mxfp4",
+                               router_mode="gemma", per_expert_scale="uniform", I_dense=192,
+                               random_gammas=True),
+    "mxfp4_plain": W.LayerSpec("dec_mxfp4", 1, 320, 8, 2, 576, "silu", "mxfp4"),
 }
 DECODE_T = {"h8192": (1, 8)}
 
@@ -254,7 +260,7 @@ FULL = [("tiny", 64), ("mixtral", 1), ("mixtral", 4096), ("gemma", 1), ("gemma",
         ("gemma", 8192), ("deepseek", 16), ("deepseek", 16384), ("skewed_fp8", 1), ("skewed_fp8", 4096),
         ("deepseek_v3", 1), ("deepseek_v3", 16), ("deepseek_v3", 8192),
         ("mixtral_w8a8", 4096), ("skewed_w8a8", 1), ("skewed_w8a8", 4096), ("gemma_block", 1), ("gemma_block", 8192),
-        ("gemma_w8a8", 8192)]
+        ("gemma_w8a8", 8192), ("gemma_mxfp4", 1), ("gemma_mxfp4", 16), ("mixtral_mxfp4", 1)]
 
 
 def _rows(T, n=256):
