@@ -59,6 +59,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int DU_PRE = 6;   // router kernel: few blocks, one batch per wave
 constexpr int DU_BF16 = 2;  // streaming kernels, bf16 weights
 constexpr int DU_FP8 = 6;   // streaming kernels, fp8 weights
+constexpr int DU_FP4 = 4;   // up kernel, MXFP4 weights: 2 pairs per batch, two batches in flight
 constexpr int XCH = 8;  // 16-byte chunks per lane of a token row held in registers (4096 elements)
 
 // Lane l feeds row / token column l & 15 and reduction elements from lane group
@@ -179,7 +180,9 @@ struct Stream {
     }
   }
   // Steps past m1 run with zero weights (their loads fell outside the buffer)
-  // and B re-read from step m1 - 1, so a batch is branch-free.
+  // and B re-read from step m1 - 1, so a batch is branch-free (and every load
+  // of a batch is consumed, which keeps the next batch's loads from waiting
+  // on registers that might still be in flight).
   __device__ __forceinline__ void compute(f32x4 (&acc)[NR], const bf16_t* b_lds, bool bvalid, int m, int m1) {
 #pragma unroll
     for (int u = 0; u < DU; ++u) {
@@ -418,6 +421,72 @@ __global__ __launch_bounds__(PW * 64, 2) void decode_pre_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------- up: dense gate/up, routing + expert gate/up
+// MXFP4 expert gate/up: one wave owns whole (expert, 16 hidden units) items, so
+// the MFMA accumulator holds each item's complete 16 x 16 tiles and the
+// epilogue needs no reduction across waves and no barrier.  A wave's items
+// are one flat sequence of batches (DU_FP4 steps each) streamed through two
+// register sets: the loads of batch b + 1 are in flight while batch b computes.
+__device__ __forceinline__ void up_items_per_wave(const DecodeArgs& a, const int* s_ids, const float* s_w,
+                                                  const int* s_active, const float* fac, const bf16_t* sx,
+                                                  int pitch, int n_items, int gw, int lane) {
+  using S = Stream<WK_FP4, 2, false, DU_FP4>;
+  const int T = a.T, H = a.H, I = a.I, Kp = a.Kp, RG = I / 16;
+  const int g = lane >> 4, col = lane & 15;
+  const int nwv = a.n_up_blocks * PW;
+  const int it0 = (int)((int64_t)gw * n_items / nwv), it1 = (int)((int64_t)(gw + 1) * n_items / nwv);
+  int m0, m1;  // every step of a row: whole pairs, elements past H zeroed by kmax
+  sub_range<WK_FP4>(0, H / 64, 0, 1, m0, m1);
+  const int BPI = (m1 - m0 + DU_FP4 - 1) / DU_FP4;  // batches per item
+  const int NB = (it1 - it0) * BPI;
+  S s0, s1;
+  // batch b >= NB issues loads outside every buffer (no traffic) so that the
+  // loop issues the same loads on every path and each wait covers one batch
+  auto issue = [&](S& st, int b) {
+    const bool live = b < NB;
+    const int bb = live ? b : 0;
+    const int item = it0 + bb / BPI;
+    const int e = s_active[item / RG], i0 = (item % RG) * 16;
+    st.g = g;
+    st.kmax = H;
+    st.ra[0] = st.ra[1] = make_rsrc((const uint8_t*)a.w13 + wbytes<WK_FP4>((int64_t)e * 2 * I * H),
+                                    (uint32_t)wbytes<WK_FP4>((int64_t)2 * I * H));
+    st.aoff[0] = (uint32_t)wbytes<WK_FP4>((int64_t)(i0 + col) * H);
+    st.aoff[1] = (uint32_t)wbytes<WK_FP4>((int64_t)(I + i0 + col) * H);
+    st.rs[0] = st.rs[1] = make_rsrc(a.mx13 + (int64_t)e * 2 * I * (H / 32), (uint32_t)(2 * I * (H / 32)));
+    st.soff[0] = (uint32_t)((i0 + col) * (H / 32));
+    st.soff[1] = (uint32_t)((I + i0 + col) * (H / 32));
+    st.load(live ? m0 + (bb % BPI) * DU_FP4 : m1, m1);
+  };
+  f32x4 acc[2];
+  // batch b: compute; the last batch of an item runs its epilogue.  Tile element
+  // (hidden unit 4g + v, token col) sits in register v of this lane.
+  auto step = [&](S& st, int b) {
+    const int item = it0 + b / BPI, bi = b % BPI;
+    const int e = s_active[item / RG], i0 = (item % RG) * 16;
+    const int slot = col < T ? find_slot(s_ids, Kp, col, e) : -1;
+    if (bi == 0) acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.compute(acc, sx + (slot >= 0 ? col : 0) * pitch, slot >= 0, m0 + bi * DU_FP4, m1);
+    if (bi == BPI - 1 && slot >= 0) {
+      uint32_t packed[2];
+#pragma unroll
+      for (int v = 0; v < 4; v += 2) {
+        const float h0 = apply_act_bf16(a.act, acc[0][v] * fac[col]) * (acc[1][v] * fac[col]) * s_w[slot];
+        const float h1 = apply_act_bf16(a.act, acc[0][v + 1] * fac[col]) * (acc[1][v + 1] * fac[col]) * s_w[slot];
+        packed[v / 2] = (uint32_t)f32_to_bf16(h0) | ((uint32_t)f32_to_bf16(h1) << 16);
+      }
+      *(u32x2*)((bf16_t*)a.hbuf + (int64_t)slot * I + i0 + 4 * g) = u32x2{packed[0], packed[1]};
+    }
+  };
+  if (NB > 0) issue(s0, 0);
+  for (int b = 0; b < NB; b += 2) {
+    issue(s1, b + 1);
+    step(s0, b);
+    if (b + 1 >= NB) break;
+    issue(s0, b + 2);
+    step(s1, b + 1);
+  }
+}
+
 template <int VPL, int WK>
 __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) uint8_t dsm[];
@@ -427,7 +496,9 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
   }
   const int blk = blockIdx.x - a.n_dense_groups;  // expert block
   const int T = a.T, H = a.H, I = a.I, E = a.E, Kp = a.Kp, Ep = a.Ep, pitch = H + 8;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, col = lane & 15;
+  // the wave index is the same on every lane of a wave; saying so keeps the
+  // streams' buffer resources and step ranges in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, g = lane >> 4, col = lane & 15;
   float* red = (float*)dsm;
   int* s_ids = (int*)(dsm + RED_FLOATS * 4);
   float* s_w = (float*)(s_ids + 16 * Kp);
@@ -502,6 +573,15 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
   const int it1 = (int)((int64_t)(blk + 1) * n_items / a.n_up_blocks);
   int m0, m1;
   sub_range<WK>(0, H / 64, wave, PW, m0, m1);
+  // MXFP4 items carry a quarter of the bf16 bytes, so a block-wide reduction
+  // per item costs more than the item's stream: with at least one item per
+  // two waves, each wave takes whole items (every block sees the same n_items)
+  if constexpr (WK == WK_FP4) {
+    if (2 * n_items >= a.n_up_blocks * PW) {
+      up_items_per_wave(a, s_ids, s_w, s_active, fac, sx, pitch, n_items, blk * PW + wave, lane);
+      return;
+    }
+  }
   for (int item = it0; item < it1; ++item) {
     const int u = item / RG, i0 = (item % RG) * 16;
     const int e = s_active[u];
