@@ -59,7 +59,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int DU_PRE = 6;   // router kernel: few blocks, one batch per wave
 constexpr int DU_BF16 = 2;  // streaming kernels, bf16 weights
 constexpr int DU_FP8 = 6;   // streaming kernels, fp8 weights
-constexpr int DU_FP4 = 4;   // up kernel, MXFP4 weights: 2 pairs per batch, two batches in flight
+constexpr int DU_FP4 = 4;   // MXFP4 weights, whole-item streams: 2 pairs per batch, two batches in flight
 constexpr int XCH = 8;  // 16-byte chunks per lane of a token row held in registers (4096 elements)
 
 // Lane l feeds row / token column l & 15 and reduction elements from lane group
@@ -477,12 +477,15 @@ __device__ __forceinline__ void up_items_per_wave(const DecodeArgs& a, const int
       *(u32x2*)((bf16_t*)a.hbuf + (int64_t)slot * I + i0 + 4 * g) = u32x2{packed[0], packed[1]};
     }
   };
+  // sched_barrier: each batch's loads are issued before the other set's MFMAs
   if (NB > 0) issue(s0, 0);
   for (int b = 0; b < NB; b += 2) {
     issue(s1, b + 1);
+    __builtin_amdgcn_sched_barrier(0);
     step(s0, b);
     if (b + 1 >= NB) break;
     issue(s0, b + 2);
+    __builtin_amdgcn_sched_barrier(0);
     step(s1, b + 1);
   }
 }
@@ -626,12 +629,75 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
   }
 }
 
+// MXFP4 expert down projection of one (16 output features, part) block: this
+// wave's units (active expert u, split s) for unit = wave, wave + DW3, ... as one
+// flat sequence of DU_FP4-step batches through two register sets (the next
+// batch in flight while the current one computes), all summed into one 16 x 16
+// accumulator.  The routing summary is staged in LDS first: max_active entries,
+// read without waiting for the active count (entries past it are in bounds and
+// unused), so the first weight loads wait for one round trip and one barrier.
+constexpr int MAX_ACTIVE_FP4 = 512;  // MXFP4 layers have no shared experts and E <= 512
+__device__ __forceinline__ f32x4 down_units_fp4(const DecodeArgs& a, int n_act, int S, int k0, int k1, int n0,
+                                                int wave, int lane) {
+  __shared__ int s_e[MAX_ACTIVE_FP4];
+  __shared__ int s_slot[MAX_ACTIVE_FP4 * 16];
+  using St = Stream<WK_FP4, 1, true, DU_FP4>;
+  const int H = a.H, I = a.I, Ep = a.Ep, g = lane >> 4, col = lane & 15;
+  const int MA = a.max_active;
+  for (int i = threadIdx.x; i < MA; i += DW3 * 64) s_e[i] = a.rinfo[1 + i];
+  for (int i = threadIdx.x; i < MA * 16; i += DW3 * 64) s_slot[i] = a.rinfo[1 + Ep + i];
+  __syncthreads();
+  const int n_units = n_act * S;
+  const int NJ = n_units > wave ? (n_units - wave + DW3 - 1) / DW3 : 0;  // this wave's units
+  const int np = (k1 - k0 + 1) / 2;                                      // pairs of the part
+  const int BPU = (2 * ((np + S - 1) / S) + DU_FP4 - 1) / DU_FP4;        // batches per unit, at most
+  const int NB = NJ * BPU;
+  const rsrc_t rb = make_rsrc(a.hbuf, (uint32_t)((int64_t)a.T * a.Kp * I * 2));
+  St s0, s1;
+  int m_0 = 0, e_0 = 0, m_1 = 0, e_1 = 0;  // each set's first step and end step
+  // batch b >= NB (and steps past a unit's range) load outside every buffer, so
+  // the same loads are issued and consumed on every path
+  auto issue = [&](St& st, int& mb, int& me, int b) {
+    const bool live = b < NB;
+    const int bb = live ? b : 0;
+    const int unit = wave + DW3 * (bb / BPU), bi = bb % BPU;
+    const int u = unit / S, sp = unit % S;
+    const int e = __builtin_amdgcn_readfirstlane(s_e[u]), slot = s_slot[u * 16 + col];
+    int r0, r1;
+    sub_range<WK_FP4>(k0, k1, sp, S, r0, r1);
+    me = r1;
+    mb = live ? min(r0 + bi * DU_FP4, r1) : r1;
+    st.g = g;
+    st.kmax = I;
+    st.ra[0] = make_rsrc((const uint8_t*)a.w2 + wbytes<WK_FP4>((int64_t)e * H * I), (uint32_t)wbytes<WK_FP4>((int64_t)H * I));
+    st.aoff[0] = (uint32_t)wbytes<WK_FP4>((int64_t)(n0 + col) * I);
+    st.rs[0] = make_rsrc(a.mx2 + (int64_t)e * H * (I / 32), (uint32_t)(H * (I / 32)));
+    st.soff[0] = (uint32_t)((n0 + col) * (I / 32));
+    st.rb = rb;
+    st.boff = slot >= 0 ? (uint32_t)((int64_t)slot * I * 2) : OOB;
+    st.load(mb, me);
+  };
+  f32x4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
+  // sched_barrier: each batch's loads are issued before the other set's MFMAs
+  if (NB > 0) issue(s0, m_0, e_0, 0);
+  for (int b = 0; b < NB; b += 2) {
+    issue(s1, m_1, e_1, b + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    s0.compute(acc, nullptr, false, m_0, e_0);
+    if (b + 1 >= NB) break;
+    issue(s0, m_0, e_0, b + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    s1.compute(acc, nullptr, false, m_1, e_1);
+  }
+  return acc[0];
+}
+
 // ---------------------------------------------------------------- down: dense down, expert down + combine
 template <int WK>
 __global__ __launch_bounds__(DW3 * 64) void decode_down_kernel(DecodeArgs a) {
   __shared__ float red[DW3 * 4 * 64];
   const int T = a.T, H = a.H, I = a.I, E = a.E, Ep = a.Ep;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, col = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, g = lane >> 4, col = lane & 15;
 
   if ((int)blockIdx.x < a.n_ddown_groups) {
     // dense MLP down projection: 16 output features x T tokens, fp32 out
@@ -673,7 +739,10 @@ __global__ __launch_bounds__(DW3 * 64) void decode_down_kernel(DecodeArgs a) {
   const int n_units = n_act * S;
   const rsrc_t rb = make_rsrc(a.hbuf, (uint32_t)((int64_t)T * a.Kp * I * 2));
   f32x4 tot = {0.f, 0.f, 0.f, 0.f};
-  for (int unit = wave; unit < n_units; unit += DW3) {
+  if constexpr (WK == WK_FP4) {
+    tot = down_units_fp4(a, n_act, S, k0, k1, n0, wave, lane);
+  }
+  for (int unit = wave; WK != WK_FP4 && unit < n_units; unit += DW3) {
     const int u = unit / S, s = unit % S;
     const bool spec = u == us && unit == wave;
     const int e = spec ? e_spec : a.rinfo[1 + u];
