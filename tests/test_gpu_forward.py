@@ -220,6 +220,9 @@ DECODE = {
                                router_mode="gemma", per_expert_scale="uniform", I_dense=192,
                                random_gammas=True),
     "mxfp4_plain": W.LayerSpec("dec_mxfp4", 1, 320, 8, 2, 576, "silu", "mxfp4"),
+    # enough (expert, 16 hidden units) items at T=16 (8 experts x 256) for the gate/up
+    # kernel's whole-items-per-wave loop, with an odd number of 64-deep steps per row
+    "mxfp4_wide": W.LayerSpec("dec_mxfp4_wide", 1, 320, 8, 2, 4096, "silu", "mxfp4"),
 }
 DECODE_T = {"h8192": (1, 8)}
 
