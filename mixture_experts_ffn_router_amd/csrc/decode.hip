@@ -421,22 +421,26 @@ __global__ __launch_bounds__(PW * 64, 2) void decode_pre_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------- up: dense gate/up, routing + expert gate/up
-// MXFP4 expert gate/up: one wave owns whole (expert, 16 hidden units) items, so
-// the MFMA accumulator holds each item's complete 16 x 16 tiles and the
-// epilogue needs no reduction across waves and no barrier.  A wave's items
-// are one flat sequence of batches (DU_FP4 steps each) streamed through two
-// register sets: the loads of batch b + 1 are in flight while batch b computes.
+// Expert gate/up (bf16 or MXFP4 weights): one wave owns whole (expert, 16
+// hidden units) items, so the MFMA accumulator holds each item's complete
+// 16 x 16 tiles and the epilogue needs no reduction across waves and no
+// barrier.  A wave's items are one flat sequence of batches streamed through
+// two register sets: the loads of batch b + 1 are in flight while batch b
+// computes.
+template <int WK>
 __device__ __forceinline__ void up_items_per_wave(const DecodeArgs& a, const int* s_ids, const float* s_w,
                                                   const int* s_active, const float* fac, const bf16_t* sx,
                                                   int pitch, int n_items, int gw, int lane) {
-  using S = Stream<WK_FP4, 2, false, DU_FP4>;
-  const int T = a.T, H = a.H, I = a.I, Kp = a.Kp, RG = I / 16;
+  static_assert(WK != WK_FP8, "fp8 weights keep the block-wide item loop");
+  constexpr int DU = WK == WK_FP4 ? DU_FP4 : DU_BF16;
+  using S = Stream<WK, 2, false, DU>;
+  const int T = a.T, H = a.H, I = a.I, E = a.E, Kp = a.Kp, RG = I / 16;
   const int g = lane >> 4, col = lane & 15;
   const int nwv = a.n_up_blocks * PW;
   const int it0 = (int)((int64_t)gw * n_items / nwv), it1 = (int)((int64_t)(gw + 1) * n_items / nwv);
-  int m0, m1;  // every step of a row: whole pairs, elements past H zeroed by kmax
-  sub_range<WK_FP4>(0, H / 64, 0, 1, m0, m1);
-  const int BPI = (m1 - m0 + DU_FP4 - 1) / DU_FP4;  // batches per item
+  int m0, m1;  // every step of a row (MXFP4: whole pairs, elements past H zeroed by kmax)
+  sub_range<WK>(0, H / 64, 0, 1, m0, m1);
+  const int BPI = (m1 - m0 + DU - 1) / DU;  // batches per item
   const int NB = (it1 - it0) * BPI;
   S s0, s1;
   // batch b >= NB issues loads outside every buffer (no traffic) so that the
@@ -447,15 +451,19 @@ __device__ __forceinline__ void up_items_per_wave(const DecodeArgs& a, const int
     const int item = it0 + bb / BPI;
     const int e = s_active[item / RG], i0 = (item % RG) * 16;
     st.g = g;
-    st.kmax = H;
-    st.ra[0] = st.ra[1] = make_rsrc((const uint8_t*)a.w13 + wbytes<WK_FP4>((int64_t)e * 2 * I * H),
-                                    (uint32_t)wbytes<WK_FP4>((int64_t)2 * I * H));
-    st.aoff[0] = (uint32_t)wbytes<WK_FP4>((int64_t)(i0 + col) * H);
-    st.aoff[1] = (uint32_t)wbytes<WK_FP4>((int64_t)(I + i0 + col) * H);
-    st.rs[0] = st.rs[1] = make_rsrc(a.mx13 + (int64_t)e * 2 * I * (H / 32), (uint32_t)(2 * I * (H / 32)));
-    st.soff[0] = (uint32_t)((i0 + col) * (H / 32));
-    st.soff[1] = (uint32_t)((I + i0 + col) * (H / 32));
-    st.load(live ? m0 + (bb % BPI) * DU_FP4 : m1, m1);
+    // shared experts (ids E.., bf16 layers only) follow the routed ones
+    const uint8_t* wbase = e < E ? (const uint8_t*)a.w13 + wbytes<WK>((int64_t)e * 2 * I * H)
+                                 : (const uint8_t*)a.shared_w13 + (int64_t)(e - E) * 2 * I * H * 2;
+    st.ra[0] = st.ra[1] = make_rsrc(wbase, (uint32_t)wbytes<WK>((int64_t)2 * I * H));
+    st.aoff[0] = (uint32_t)wbytes<WK>((int64_t)(i0 + col) * H);
+    st.aoff[1] = (uint32_t)wbytes<WK>((int64_t)(I + i0 + col) * H);
+    if constexpr (WK == WK_FP4) {
+      st.kmax = H;
+      st.rs[0] = st.rs[1] = make_rsrc(a.mx13 + (int64_t)e * 2 * I * (H / 32), (uint32_t)(2 * I * (H / 32)));
+      st.soff[0] = (uint32_t)((i0 + col) * (H / 32));
+      st.soff[1] = (uint32_t)((I + i0 + col) * (H / 32));
+    }
+    st.load(live ? m0 + (bb % BPI) * DU : m1, m1);
   };
   f32x4 acc[2];
   // batch b: compute; the last batch of an item runs its epilogue.  Tile element
@@ -465,7 +473,7 @@ __device__ __forceinline__ void up_items_per_wave(const DecodeArgs& a, const int
     const int e = s_active[item / RG], i0 = (item % RG) * 16;
     const int slot = col < T ? find_slot(s_ids, Kp, col, e) : -1;
     if (bi == 0) acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    st.compute(acc, sx + (slot >= 0 ? col : 0) * pitch, slot >= 0, m0 + bi * DU_FP4, m1);
+    st.compute(acc, sx + (slot >= 0 ? col : 0) * pitch, slot >= 0, m0 + bi * DU, m1);
     if (bi == BPI - 1 && slot >= 0) {
       uint32_t packed[2];
 #pragma unroll
@@ -477,16 +485,19 @@ __device__ __forceinline__ void up_items_per_wave(const DecodeArgs& a, const int
       *(u32x2*)((bf16_t*)a.hbuf + (int64_t)slot * I + i0 + 4 * g) = u32x2{packed[0], packed[1]};
     }
   };
-  // sched_barrier: each batch's loads are issued before the other set's MFMAs
-  if (NB > 0) issue(s0, 0);
+  // Two batches ahead: a set is reloaded right after it is consumed, so each
+  // wait covers the older set only (sched_barrier keeps the order).
+  if (NB > 0) {
+    issue(s0, 0);
+    issue(s1, 1);
+  }
   for (int b = 0; b < NB; b += 2) {
-    issue(s1, b + 1);
     __builtin_amdgcn_sched_barrier(0);
     step(s0, b);
-    if (b + 1 >= NB) break;
     issue(s0, b + 2);
     __builtin_amdgcn_sched_barrier(0);
-    step(s1, b + 1);
+    if (b + 1 < NB) step(s1, b + 1);
+    issue(s1, b + 3);
   }
 }
 
@@ -576,12 +587,13 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
   const int it1 = (int)((int64_t)(blk + 1) * n_items / a.n_up_blocks);
   int m0, m1;
   sub_range<WK>(0, H / 64, wave, PW, m0, m1);
-  // MXFP4 items carry a quarter of the bf16 bytes, so a block-wide reduction
-  // per item costs more than the item's stream: with at least one item per
-  // two waves, each wave takes whole items (every block sees the same n_items)
-  if constexpr (WK == WK_FP4) {
-    if (2 * n_items >= a.n_up_blocks * PW) {
-      up_items_per_wave(a, s_ids, s_w, s_active, fac, sx, pitch, n_items, blk * PW + wave, lane);
+  // Whole items per wave when items are plentiful (every block sees the same
+  // n_items): at least one per wave for bf16 weights, one per two waves for
+  // MXFP4, whose items carry a quarter of the bytes, so that a block-wide
+  // reduction per item costs more than the item's stream
+  if constexpr (WK != WK_FP8) {
+    if ((WK == WK_FP4 ? 2 : 1) * n_items >= a.n_up_blocks * PW) {
+      up_items_per_wave<WK>(a, s_ids, s_w, s_active, fac, sx, pitch, n_items, blk * PW + wave, lane);
       return;
     }
   }

@@ -223,6 +223,8 @@ DECODE = {
     # enough (expert, 16 hidden units) items at T=16 (8 experts x 256) for the gate/up
     # kernel's whole-items-per-wave loop, with an odd number of 64-deep steps per row
     "mxfp4_wide": W.LayerSpec("dec_mxfp4_wide", 1, 320, 8, 2, 4096, "silu", "mxfp4"),
+    # the same loop with bf16 weights (one item per wave needed: 8 experts x 512 at T=16)
+    "wide_bf16": W.LayerSpec("dec_wide", 1, 320, 8, 2, 8192, "silu", "bf16"),
 }
 DECODE_T = {"h8192": (1, 8)}
 
