@@ -452,10 +452,10 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
     a.topk_w_out = t->topk_w_out;
     a.topk_ids_out = t->topk_ids_out;
     const int wk = d.weight_dtype == MOE_DT_FP8_E4M3 ? 1 : (d.weight_dtype == MOE_DT_MXFP4 ? 2 : 0);
-    // the MXFP4 down kernel stages the routing summary in a 512-entry LDS table;
-    // E <= 512 and no shared experts keep max_active within it
-    if (mx && (a.max_active > 512 || p.Ep != d.num_experts))
-      return fail(MOE_UNSUPPORTED, "mxfp4 decode: %d active experts exceed the routing table", a.max_active);
+    // the bf16 / MXFP4 down kernel stages the routing summary in a 520-entry LDS
+    // table; E <= 512 and at most 8 shared experts keep max_active within it
+    if (wk != 1 && a.max_active > 520)
+      return fail(MOE_UNSUPPORTED, "decode: %d active experts exceed the routing table", a.max_active);
     STAGE(MOE_STAGE_PRENORM);
     STAGE(MOE_STAGE_ROUTER);
     // router logits

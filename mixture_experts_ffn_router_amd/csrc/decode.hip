@@ -641,28 +641,48 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
   }
 }
 
-// MXFP4 expert down projection of one (16 output features, part) block: this
-// wave's units (active expert u, split s) for unit = wave, wave + DW3, ... as one
-// flat sequence of DU_FP4-step batches through two register sets (the next
-// batch in flight while the current one computes), all summed into one 16 x 16
-// accumulator.  The routing summary is staged in LDS first: max_active entries,
-// read without waiting for the active count (entries past it are in bounds and
-// unused), so the first weight loads wait for one round trip and one barrier.
-constexpr int MAX_ACTIVE_FP4 = 512;  // MXFP4 layers have no shared experts and E <= 512
-__device__ __forceinline__ f32x4 down_units_fp4(const DecodeArgs& a, int n_act, int S, int k0, int k1, int n0,
-                                                int wave, int lane) {
-  __shared__ int s_e[MAX_ACTIVE_FP4];
-  __shared__ int s_slot[MAX_ACTIVE_FP4 * 16];
-  using St = Stream<WK_FP4, 1, true, DU_FP4>;
-  const int H = a.H, I = a.I, Ep = a.Ep, g = lane >> 4, col = lane & 15;
+// Expert down projection (bf16 or MXFP4 weights) of one (16 output features,
+// part) block: this wave's units (active expert u, split s) for unit = wave,
+// wave + DW3, ... as one flat sequence of batches through two register sets
+// (the next batch in flight while the current one computes), all summed into
+// one 16 x 16 accumulator (the routing weight is already in h').  The routing
+// summary is staged in LDS first: max_active entries, read without waiting for
+// the active count (entries past it are in bounds and unused), so the first
+// weight loads wait for one round trip and one barrier.
+constexpr int MAX_ACTIVE_DOWN = 520;  // E <= 512 routed + 8 shared experts
+template <int WK>
+__device__ __forceinline__ f32x4 down_units(const DecodeArgs& a, int n_act, int S, int k0, int k1, int n0,
+                                            int wave, int lane) {
+  static_assert(WK != WK_FP8, "fp8 weights scale each unit's tile by its channel scales");
+  __shared__ int s_e[MAX_ACTIVE_DOWN];
+  __shared__ int s_slot[MAX_ACTIVE_DOWN * 16];
+  constexpr int DU = WK == WK_FP4 ? DU_FP4 : DU_BF16;
+  using St = Stream<WK, 1, true, DU>;
+  const int H = a.H, I = a.I, E = a.E, Ep = a.Ep, g = lane >> 4, col = lane & 15;
   const int MA = a.max_active;
-  for (int i = threadIdx.x; i < MA; i += DW3 * 64) s_e[i] = a.rinfo[1 + i];
-  for (int i = threadIdx.x; i < MA * 16; i += DW3 * 64) s_slot[i] = a.rinfo[1 + Ep + i];
+  {  // four loads in flight per thread before their stores (one round trip up to 2048 slots)
+    constexpr int NT = DW3 * 64;
+    for (int i = threadIdx.x; i < MA; i += NT) s_e[i] = a.rinfo[1 + i];
+    for (int base = 0; base < MA * 16; base += 4 * NT) {
+      int v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = base + threadIdx.x + j * NT;
+        v[j] = i < MA * 16 ? a.rinfo[1 + Ep + i] : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = base + threadIdx.x + j * NT;
+        if (i < MA * 16) s_slot[i] = v[j];
+      }
+    }
+  }
   __syncthreads();
   const int n_units = n_act * S;
   const int NJ = n_units > wave ? (n_units - wave + DW3 - 1) / DW3 : 0;  // this wave's units
-  const int np = (k1 - k0 + 1) / 2;                                      // pairs of the part
-  const int BPU = (2 * ((np + S - 1) / S) + DU_FP4 - 1) / DU_FP4;        // batches per unit, at most
+  // steps per unit, at most (MXFP4: whole pairs)
+  const int spu = WK == WK_FP4 ? 2 * (((k1 - k0 + 1) / 2 + S - 1) / S) : (k1 - k0 + S - 1) / S;
+  const int BPU = (spu + DU - 1) / DU;  // batches per unit, at most
   const int NB = NJ * BPU;
   const rsrc_t rb = make_rsrc(a.hbuf, (uint32_t)((int64_t)a.T * a.Kp * I * 2));
   St s0, s1;
@@ -676,15 +696,20 @@ __device__ __forceinline__ f32x4 down_units_fp4(const DecodeArgs& a, int n_act, 
     const int u = unit / S, sp = unit % S;
     const int e = __builtin_amdgcn_readfirstlane(s_e[u]), slot = s_slot[u * 16 + col];
     int r0, r1;
-    sub_range<WK_FP4>(k0, k1, sp, S, r0, r1);
+    sub_range<WK>(k0, k1, sp, S, r0, r1);
     me = r1;
-    mb = live ? min(r0 + bi * DU_FP4, r1) : r1;
+    mb = live ? min(r0 + bi * DU, r1) : r1;
     st.g = g;
-    st.kmax = I;
-    st.ra[0] = make_rsrc((const uint8_t*)a.w2 + wbytes<WK_FP4>((int64_t)e * H * I), (uint32_t)wbytes<WK_FP4>((int64_t)H * I));
-    st.aoff[0] = (uint32_t)wbytes<WK_FP4>((int64_t)(n0 + col) * I);
-    st.rs[0] = make_rsrc(a.mx2 + (int64_t)e * H * (I / 32), (uint32_t)(H * (I / 32)));
-    st.soff[0] = (uint32_t)((n0 + col) * (I / 32));
+    // shared experts (ids E.., bf16 layers only) follow the routed ones
+    const uint8_t* wbase = e < E ? (const uint8_t*)a.w2 + wbytes<WK>((int64_t)e * H * I)
+                                 : (const uint8_t*)a.shared_w2 + (int64_t)(e - E) * H * I * 2;
+    st.ra[0] = make_rsrc(wbase, (uint32_t)wbytes<WK>((int64_t)H * I));
+    st.aoff[0] = (uint32_t)wbytes<WK>((int64_t)(n0 + col) * I);
+    if constexpr (WK == WK_FP4) {
+      st.kmax = I;
+      st.rs[0] = make_rsrc(a.mx2 + (int64_t)e * H * (I / 32), (uint32_t)(H * (I / 32)));
+      st.soff[0] = (uint32_t)((n0 + col) * (I / 32));
+    }
     st.rb = rb;
     st.boff = slot >= 0 ? (uint32_t)((int64_t)slot * I * 2) : OOB;
     st.load(mb, me);
@@ -751,10 +776,13 @@ __global__ __launch_bounds__(DW3 * 64) void decode_down_kernel(DecodeArgs a) {
   const int n_units = n_act * S;
   const rsrc_t rb = make_rsrc(a.hbuf, (uint32_t)((int64_t)T * a.Kp * I * 2));
   f32x4 tot = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (WK == WK_FP4) {
-    tot = down_units_fp4(a, n_act, S, k0, k1, n0, wave, lane);
+  // bf16 / MXFP4 with more units than waves: staged routing summary and a
+  // two-deep stream over each wave's units (n_units is the same in every wave)
+  const bool staged = WK != WK_FP8 && n_units > DW3;
+  if constexpr (WK != WK_FP8) {
+    if (staged) tot = down_units<WK>(a, n_act, S, k0, k1, n0, wave, lane);
   }
-  for (int unit = wave; WK != WK_FP4 && unit < n_units; unit += DW3) {
+  for (int unit = wave; !staged && unit < n_units; unit += DW3) {
     const int u = unit / S, s = unit % S;
     const bool spec = u == us && unit == wave;
     const int e = spec ? e_spec : a.rinfo[1 + u];
