@@ -244,7 +244,7 @@ def cpu_baseline(L, seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py runs on one GPU: the layer has no multi-GPU path here (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
