@@ -139,3 +139,22 @@ def test_swapped_mxfp4_nibbles_are_caught(monkeypatch):
     monkeypatch.setattr(O, "decode_mxfp4",
                         lambda packed, scales: orig(((np.asarray(packed) & 15) << 4) | (np.asarray(packed) >> 4), scales))
     _fails(P.test_mxfp4_layer_equals_layer_on_torch_decoded_weights)
+
+
+def test_e8m0_bias_off_by_one_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "decode_e8m0", lambda c: np.where(np.asarray(c).astype(np.int64) == 255, np.nan,
+                                                             np.ldexp(1.0, np.asarray(c).astype(np.int64) - 126)))
+    _fails(P.test_e2m1_and_e8m0_decode_closed_forms)
+    _fails(P.test_mxfp4_layer_equals_layer_on_torch_decoded_weights)
+
+
+def test_mxfp4_scale_blocks_of_16_are_caught(monkeypatch):
+    def bad(packed, scales):
+        packed = np.asarray(packed).astype(np.int64)
+        codes = np.stack([packed & 0xF, packed >> 4], axis=-1).reshape(packed.shape[:-1] + (2 * packed.shape[-1],))
+        sc = O.decode_e8m0(scales)
+        sc = np.repeat(sc, 16, axis=-1)                      # blocks of 16 ...
+        sc = np.concatenate([sc, sc], axis=-1)[..., :codes.shape[-1]]  # ... padded to the row length
+        return O.decode_e2m1(codes) * sc
+    monkeypatch.setattr(O, "decode_mxfp4", bad)
+    _fails(P.test_mxfp4_layer_equals_layer_on_torch_decoded_weights)
