@@ -225,8 +225,12 @@ DECODE = {
     "mxfp4_wide": W.LayerSpec("dec_mxfp4_wide", 1, 320, 8, 2, 4096, "silu", "mxfp4"),
     # the same loop with bf16 weights (one item per wave needed: 8 experts x 512 at T=16)
     "wide_bf16": W.LayerSpec("dec_wide", 1, 320, 8, 2, 8192, "silu", "bf16"),
+    # the most experts and picks: at T=16 most of 512 experts are active, which
+    # fills the down kernel's staged routing table
+    "e512_k64_bf16": W.LayerSpec("dec_e512_k64", 1, 128, 512, 64, 64, "silu", "bf16"),
+    "e512_k64_mxfp4": W.LayerSpec("dec_e512_k64_mx", 1, 128, 512, 64, 64, "silu", "mxfp4"),
 }
-DECODE_T = {"h8192": (1, 8)}
+DECODE_T = {"h8192": (1, 8), "e512_k64_bf16": (16,), "e512_k64_mxfp4": (16,)}
 
 
 @pytest.mark.parametrize("name,T", [(n, t) for n in DECODE for t in DECODE_T.get(n, (1, 5, 16))],
