@@ -122,6 +122,7 @@ SMALL = {
     # aligned (E=6: the router's direct-store epilogue), and a dense gate/up wide
     # enough for ragged 8-wave tiles (2112 = 16.5 x 128 output columns)
     "bf16_e512": W.LayerSpec("bf16_e512", 200, 128, 512, 8, 64, "silu", "bf16"),
+    "bf16_e512_k64": W.LayerSpec("bf16_e512_k64", 100, 128, 512, 64, 64, "silu", "bf16"),
     "bf16_h8192": W.LayerSpec("bf16_h8192", 300, 8192, 4, 2, 128, "silu", "bf16"),
     "bf16_k_equals_e": W.LayerSpec("bf16_keqe", 100, 256, 4, 4, 128, "gelu_tanh", "bf16",
                                    per_expert_scale="uniform"),
