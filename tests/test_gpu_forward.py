@@ -123,6 +123,8 @@ SMALL = {
     # enough for ragged 8-wave tiles (2112 = 16.5 x 128 output columns)
     "bf16_e512": W.LayerSpec("bf16_e512", 200, 128, 512, 8, 64, "silu", "bf16"),
     "bf16_e512_k64": W.LayerSpec("bf16_e512_k64", 100, 128, 512, 64, 64, "silu", "bf16"),
+    "w8a8_e512_k64": W.LayerSpec("w8a8_e512_k64", 100, 128, 512, 64, 64, "silu", "fp8",
+                                 act_quant="fp8_dynamic"),
     "bf16_h8192": W.LayerSpec("bf16_h8192", 300, 8192, 4, 2, 128, "silu", "bf16"),
     "bf16_k_equals_e": W.LayerSpec("bf16_keqe", 100, 256, 4, 4, 128, "gelu_tanh", "bf16",
                                    per_expert_scale="uniform"),
@@ -230,6 +232,9 @@ DECODE = {
     # fills the down kernel's staged routing table
     "e512_k64_bf16": W.LayerSpec("dec_e512_k64", 1, 128, 512, 64, 64, "silu", "bf16"),
     "e512_k64_mxfp4": W.LayerSpec("dec_e512_k64_mx", 1, 128, 512, 64, 64, "silu", "mxfp4"),
+    "mxfp4_gemma_tail": W.LayerSpec("dec_mxfp4_tail", 1, 256, 16, 4, 128, "gelu_tanh", "mxfp4",
+                                    router_mode="gemma", per_expert_scale="uniform", I_dense=192,
+                                    random_gammas=True, block_tail=True),
 }
 DECODE_T = {"h8192": (1, 8), "e512_k64_bf16": (16,), "e512_k64_mxfp4": (16,)}
 
