@@ -360,7 +360,7 @@ def permutation(ids, E):
 # Expert FFN ("MOE Inference" gated FFN; Gemma 4 walkthrough §6)
 # ----------------------------------------------------------------------------
 
-def gated_ffn(xrows, w13, w2, act, act_quant=None):
+def gated_ffn(xrows, w13, w2, act, act_quant=None, h_fp8=None):
     """(Act(x w1) * (x w3)) w2 for a block of rows.
 
     w13 has shape [2I, H]: rows [0, I) are the gate projection w1, rows
@@ -369,7 +369,12 @@ def gated_ffn(xrows, w13, w2, act, act_quant=None):
 
     act_quant="fp8_dynamic": each projection's input rows are quantised as in
     quantize_rows_fp8 first: x before gate/up, and h, as stored (rounded to
-    bf16), before the down projection."""
+    bf16), before the down projection.  h_fp8 = (codes [n, I] uint8, scales
+    [n] float32), when given, are the quantised h rows to project instead of
+    this function's own quantisation of h: the codes are integers that
+    floating point decides, so parity checks them as it checks top-k ids, on
+    the other side's own h, and takes them as given for the rest of the layer
+    (as routing parity takes the logits)."""
     xrows = _f64(xrows)
     w13 = _f64(w13)
     I = w13.shape[0] // 2
@@ -381,12 +386,18 @@ def gated_ffn(xrows, w13, w2, act, act_quant=None):
     u = xrows @ w13[I:].T
     h = activation(act)(g) * u
     if act_quant == "fp8_dynamic":
-        h = fp8_roundtrip_rows(round_bf16(h))
+        if h_fp8 is None:
+            h = fp8_roundtrip_rows(round_bf16(h))
+        else:
+            codes, scales = h_fp8
+            h = decode_e4m3fn(codes) * np.asarray(scales, dtype=np.float32).astype(np.float64)[:, None]
+    elif h_fp8 is not None:
+        raise ValueError("h_fp8 needs act_quant='fp8_dynamic'")
     return h @ _f64(w2).T
 
 
 def moe_combine(xe, weights, ids, w13, w2, act, rows=None, w13_scale=None, w2_scale=None,
-                act_quant=None):
+                act_quant=None, h_fp8=None):
     """Sparse MoE output for the selected rows: out_t = sum_j w[t,j] * FFN_{ids[t,j]}(xe_t).
 
     Only the selected experts are evaluated (llama.cpp lesson 35: mul_mat_id
@@ -400,7 +411,11 @@ def moe_combine(xe, weights, ids, w13, w2, act, rows=None, w13_scale=None, w2_sc
     dtype holding the exact stored values, or FP8 codes with per-output-channel
     scales w13_scale [E, 2I] and w2_scale [E, H]: W = decode(q) * s[n], or MXFP4:
     packed codes [E, 2I, H/2] / [E, H, I/2] with uint8 E8M0 block scales
-    [E, 2I, H/32] / [E, H, I/32])."""
+    [E, 2I, H/32] / [E, H, I/32]).
+
+    h_fp8 = (codes [T, k, I] uint8, scales [T, k] float32): quantised expert
+    intermediates per (token, slot) to use instead of the oracle's own (see
+    gated_ffn); FP8 activations only."""
     xe = _f64(xe)
     weights = _f64(weights)
     ids = np.asarray(ids)
@@ -415,7 +430,8 @@ def moe_combine(xe, weights, ids, w13, w2, act, rows=None, w13_scale=None, w2_sc
             continue
         W13 = _expert_weight(w13, w13_scale, e)
         W2 = _expert_weight(w2, w2_scale, e)
-        y[ri, ji] = gated_ffn(xe[rows[ri]], W13, W2, act, act_quant)
+        hq = None if h_fp8 is None else (h_fp8[0][rows[ri], ji], h_fp8[1][rows[ri], ji])
+        y[ri, ji] = gated_ffn(xe[rows[ri]], W13, W2, act, act_quant, hq)
     out = np.zeros((len(rows), H))
     for j in range(k):  # slot order
         out += weights[rows, j][:, None] * y[:, j]
@@ -434,7 +450,7 @@ def _expert_weight(w, scale, e):
 # The whole layer
 # ----------------------------------------------------------------------------
 
-def moe_layer(x, layer, rows=None, logits=None):
+def moe_layer(x, layer, rows=None, logits=None, h_fp8=None):
     """The MoE FFN layer forward for token rows `rows` (all when None).
 
     `layer` is a dict with:
@@ -464,6 +480,10 @@ def moe_layer(x, layer, rows=None, logits=None):
     outside the FFN layer (reading) unless block_tail asks for them:
       out = x + post_feedforward_layernorm(out).
 
+    h_fp8 (FP8 activations only): quantised expert intermediates (codes
+    [T, K, I] uint8, scales [T, K] float32) taken as given, like `logits`; see
+    gated_ffn.
+
     Returns dict(out [len(rows),H], logits [T,E], weights [T,K], ids [T,K],
     counts [E], offsets [E+1], order [T*K])."""
     x = _f64(x)
@@ -488,7 +508,7 @@ def moe_layer(x, layer, rows=None, logits=None):
     else:
         xe = x
     moe = moe_combine(xe, w, ids, layer["w13"], layer["w2"], layer["act"], rows,
-                      layer.get("w13_scale"), layer.get("w2_scale"), layer.get("act_quant"))
+                      layer.get("w13_scale"), layer.get("w2_scale"), layer.get("act_quant"), h_fp8)
     shared = layer.get("shared")
     if shared is not None:
         sw13, sw2 = shared

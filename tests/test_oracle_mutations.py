@@ -7,9 +7,9 @@ from oracle import moe_oracle as O
 import tests.test_oracle_pins as P
 
 
-def _swapped_gate_up(xrows, w13, w2, act, act_quant=None):
+def _swapped_gate_up(xrows, w13, w2, act, act_quant=None, h_fp8=None):
     I = w13.shape[0] // 2
-    return O.__dict__["_orig_gated_ffn"](xrows, np.concatenate([w13[I:], w13[:I]]), w2, act, act_quant)
+    return O.__dict__["_orig_gated_ffn"](xrows, np.concatenate([w13[I:], w13[:I]]), w2, act, act_quant, h_fp8)
 
 
 def _fails(fn, *a, **k):

@@ -592,6 +592,52 @@ def test_gemma_w8a8_layer_matches_torch_composition():
     np.testing.assert_allclose(got["out"], ref, rtol=1e-9, atol=1e-10)
 
 
+def test_fp8_h_codes_taken_as_given():
+    """h_fp8: the down projection of given E4M3 codes and row scales (decoded by
+    torch's float8_e4m3fn), per (token, slot); with the codes the oracle itself
+    would pick, the layer is unchanged."""
+    rng = np.random.default_rng(34)
+    T, H, E, K, I, Id = 9, 32, 6, 2, 16, 24
+    x = rng.standard_normal((T, H)).astype(np.float32).astype(np.float64)
+    L = _tiny_layer(rng, T, H, E, K, I, act="gelu_tanh")
+    L["dense"] = dict(w13=rng.standard_normal((2 * Id, H)) / math.sqrt(H),
+                      w2=rng.standard_normal((H, Id)) / math.sqrt(Id))
+    L["act_quant"] = "fp8_dynamic"
+    own = O.moe_layer(x, L)
+    ids = own["ids"]
+    # the codes the oracle picks, rebuilt through torch: x quantised as stored, then h
+    xe = torch.from_numpy(O.rmsnorm(x)).to(torch.bfloat16).double()
+    xq = _torch_fp8_rows(xe)
+    codes = np.zeros((T, K, I), np.uint8)
+    scales = np.zeros((T, K), np.float32)
+    for t in range(T):
+        for j in range(K):
+            W13 = torch.from_numpy(L["w13"][ids[t, j]])
+            h = F.gelu(xq[t:t + 1] @ W13[:I].T, approximate="tanh") * (xq[t:t + 1] @ W13[I:].T)
+            hb = h.to(torch.bfloat16).float()
+            sc = torch.clamp(hb.abs().amax(), min=0) / 448.0
+            sc = sc if sc > 0 else torch.ones(())
+            q = (hb / sc).to(torch.float8_e4m3fn)
+            codes[t, j] = q.view(torch.uint8).numpy()[0]
+            scales[t, j] = sc.item()
+    same = O.moe_layer(x, L, h_fp8=(codes, scales))
+    np.testing.assert_allclose(same["out"], own["out"], rtol=1e-12, atol=1e-13)
+    # other codes change the output by exactly their own down projection
+    c2 = codes.copy()
+    c2[4, 1, 7] ^= 0x01  # one mantissa step
+    other = O.moe_layer(x, L, h_fp8=(c2, scales))
+    dq = (torch.tensor([c2[4, 1, 7]], dtype=torch.uint8).view(torch.float8_e4m3fn).double() -
+          torch.tensor([codes[4, 1, 7]], dtype=torch.uint8).view(torch.float8_e4m3fn).double()).item()
+    dmoe = own["weights"][4, 1] * dq * float(scales[4, 1]) * L["w2"][ids[4, 1]][:, 7]
+    moe_own = O.moe_combine(O.round_bf16(O.rmsnorm(x)), own["weights"], ids, L["w13"], L["w2"], "gelu_tanh",
+                            act_quant="fp8_dynamic")
+    d = O.gated_ffn(O.rmsnorm(x), L["dense"]["w13"], L["dense"]["w2"], "gelu_tanh")
+    want = O.rmsnorm(d) + O.rmsnorm(moe_own + np.eye(T)[4][:, None] * dmoe[None, :])
+    np.testing.assert_allclose(other["out"], want, rtol=1e-11, atol=1e-12)
+    with pytest.raises(ValueError):
+        O.gated_ffn(x, L["w13"][0], L["w2"][0], "silu", h_fp8=(codes[:, 0], scales[:, 0]))
+
+
 def test_row_subset_matches_full():
     rng = np.random.default_rng(15)
     T, H, E, K, I = 40, 16, 8, 2, 8
