@@ -6,10 +6,12 @@
  *   - All tensors are dense, row-major, contiguous device pointers (HIP device
  *     memory the caller owns).  The library allocates no device memory and keeps
  *     no data between calls; calls on different streams are independent.  The
- *     one thing it keeps: moe_forward creates, on first need per host thread and
- *     device, a second stream (default priority, non-blocking) and two events,
- *     held until the process ends; a layer's dense branch runs on that stream,
- *     ordered with the caller's stream by those events (see moe_forward).
+ *     one thing it keeps: moe_forward creates, on first need per caller stream,
+ *     host thread and device (up to 16 caller streams per thread), a second
+ *     stream (default priority, non-blocking) and two events, held until the
+ *     process ends; a layer's dense branch runs on that stream, ordered with the
+ *     caller's stream by those events (see moe_forward).  Every return after the
+ *     fork, errors included, first makes the caller's stream wait for it.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work
  *     is enqueued asynchronously on it; the call returns once it is enqueued.
  *   - Arguments are validated on the host before anything is launched.  A bad
@@ -108,7 +110,8 @@ int64_t moe_permute_capacity(int64_t T, int32_t K, int32_t E, int32_t block_m);
 /*
  * moe_permute - the dispatch permutation map: (token, slot) pairs regrouped
  * expert-major without copying any token data ([G4] sections 6-7: dispatch
- * builds a permutation map that the grouped GEMM reads indirectly).
+ * builds a permutation map that the grouped GEMM reads indirectly; section 7
+ * walks the token -> (expert, row) map both ways).
  *
  * Flat slot f = t*K + j refers to topk_ids[t, j].  Expert e's segment is
  * sorted_slots[offsets[e] .. offsets[e] + counts[e]) and lists its flat slots
@@ -116,19 +119,28 @@ int64_t moe_permute_capacity(int64_t T, int32_t K, int32_t E, int32_t block_m);
  * -1 up to a multiple of block_m, so offsets[e+1] - offsets[e] =
  * ceil(counts[e] / block_m) * block_m and offsets[E] is the padded total.
  * block_expert[b] = expert owning rows [b*block_m, (b+1)*block_m) for
- * b < offsets[E] / block_m.  Entries past offsets[E] are left untouched.
+ * b < offsets[E] / block_m.  slot_row is the inverse map: slot_row[f] = the
+ * padded row r with sorted_slots[r] == f.  Entries of sorted_slots and
+ * block_expert past the padded total are left untouched.
+ *
+ * Work: a histogram per chunk of 4096 slots, one scan over the experts, and a
+ * stable scatter: every id is read twice, however many experts there are.
  *
  *   topk_ids      [T, K] int32, each in [0, E).
  *   counts        [E] int32 out.          offsets [E+1] int32 out.
  *   sorted_slots  [moe_permute_capacity(T,K,E,block_m)] int32 out.
  *   block_expert  [capacity / block_m] int32 out.
+ *   num_padded    [1] int32 out (= offsets[E]), or NULL.
+ *   slot_row      [T*K] int32 out (also holds per-chunk counts while the call's
+ *                 work runs on `stream`; may be NULL only when T == 0).
  * Limits: block_m a power of two in [16, 256]; 1 <= K <= 64; 1 <= E <= 1024;
  * T*K < 2^31.  Expert ids outside [0, E) are a precondition violation: those
- * slots are dropped from every segment (the counts then sum to less than T*K).
+ * slots are dropped from every segment (the counts then sum to less than T*K)
+ * and their slot_row entries are -1.
  */
 moe_status moe_permute(const int32_t* topk_ids, int64_t T, int32_t K, int32_t E, int32_t block_m,
                        int32_t* counts, int32_t* offsets, int32_t* sorted_slots,
-                       int32_t* block_expert, void* stream);
+                       int32_t* block_expert, int32_t* num_padded, int32_t* slot_row, void* stream);
 
 /* Layer description (host memory, read during the call only). */
 typedef struct {
@@ -256,6 +268,32 @@ int32_t moe_forward_path(const moe_layer_desc* desc, int64_t T);
  * -1 for an invalid descriptor, a layer without the dense branch, or a T that
  * takes the grouped path.  For measurement (bytes per stage). */
 int32_t moe_decode_dense_gate_up_stage(const moe_layer_desc* desc, int64_t T);
+
+/* Where one moe_forward call keeps its intermediates in the workspace, for
+ * inspection (tests, debugging): byte offsets into the workspace, -1 for a
+ * buffer the call does not have.  Contents are those the call left once its
+ * work on the stream has completed, until the workspace is used again.  The
+ * grouped path only (path == MOE_PATH_DECODE: every offset is -1).
+ *   topk_w, topk_ids  [T, slots_per_token] fp32 / int32 (shared experts appended
+ *                     as ids E.., weight 1)
+ *   counts [E+S], offsets [E+S+1], sorted_slots [capacity], block_expert
+ *   [capacity / block_m], slot_row [T * slots_per_token]  (as moe_permute)
+ *   inv_rms           [T] fp32, 1/sqrt(mean(x^2) + eps) (router or dense branch present)
+ *   x_expert          [T, H] act dtype: the normalised expert input, where stored
+ *   h                 [capacity, I] act dtype: the gated intermediate per padded row
+ *   y                 [T * slots_per_token * y_parts, H] (fp32 when y_f32, else act
+ *                     dtype): row (slot * y_parts + part) holds the routing-weighted
+ *                     expert output of flat slot `slot`, summed over the parts
+ *   x_codes [T, H] u8, x_scales [T] fp32, h_codes [capacity, I] u8,
+ *   h_scales [capacity] fp32: FP8 activations (E4M3 codes, per-row scales) */
+typedef struct {
+  int32_t path, block_m, slots_per_token, y_parts, y_f32;
+  int64_t capacity;
+  int64_t topk_w, topk_ids, counts, offsets, sorted_slots, block_expert, slot_row, inv_rms, x_expert, h, y,
+      x_codes, x_scales, h_codes, h_scales;
+} moe_workspace_layout;
+moe_status moe_forward_workspace_layout(const moe_layer_desc* desc, const moe_tensors* tensors, int64_t T,
+                                        moe_workspace_layout* layout);
 
 /* Stages of moe_forward, in launch order (indices into the event array below). */
 typedef enum {

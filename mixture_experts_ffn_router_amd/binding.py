@@ -51,9 +51,16 @@ class Tensors(C.Structure):
         "gamma_post_ff")]
 
 
+class WorkspaceLayout(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("path", "block_m", "slots_per_token", "y_parts", "y_f32")] + \
+               [(n, C.c_int64) for n in ("capacity", "topk_w", "topk_ids", "counts", "offsets", "sorted_slots",
+                                         "block_expert", "slot_row", "inv_rms", "x_expert", "h", "y", "x_codes",
+                                         "x_scales", "h_codes", "h_scales")]
+
+
 EXPORTS = ["moe_status_string", "moe_last_error", "moe_route", "moe_permute_capacity", "moe_permute",
            "moe_forward_workspace_size", "moe_forward", "moe_forward_profiled", "moe_forward_path",
-           "moe_decode_dense_gate_up_stage"]
+           "moe_decode_dense_gate_up_stage", "moe_forward_workspace_layout"]
 PATHS = {0: "grouped", 1: "decode"}
 STAGES = ["prenorm", "router", "route", "permute", "quant_x", "gate_up", "quant_h", "down", "dense_gate_up",
           "dense_down", "finalize"]
@@ -82,7 +89,7 @@ def load(path: str = LIB_PATH):
     lib.moe_permute_capacity.argtypes = [C.c_int64, C.c_int32, C.c_int32, C.c_int32]
     lib.moe_permute.restype = C.c_int
     lib.moe_permute.argtypes = [C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
-                                C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
+                                C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
     lib.moe_forward_workspace_size.restype = C.c_int
     lib.moe_forward_workspace_size.argtypes = [C.POINTER(LayerDesc), C.c_int64, C.POINTER(C.c_size_t)]
     lib.moe_forward.restype = C.c_int
@@ -93,6 +100,9 @@ def load(path: str = LIB_PATH):
                                          C.c_size_t, C.c_void_p, C.POINTER(C.c_void_p)]
     lib.moe_forward_path.restype = C.c_int32
     lib.moe_forward_path.argtypes = [C.POINTER(LayerDesc), C.c_int64]
+    lib.moe_forward_workspace_layout.restype = C.c_int
+    lib.moe_forward_workspace_layout.argtypes = [C.POINTER(LayerDesc), C.POINTER(Tensors), C.c_int64,
+                                                 C.POINTER(WorkspaceLayout)]
     lib.moe_decode_dense_gate_up_stage.restype = C.c_int32
     lib.moe_decode_dense_gate_up_stage.argtypes = [C.POINTER(LayerDesc), C.c_int64]
     _lib = lib
@@ -154,7 +164,8 @@ def permute_capacity(T, k, E, block_m):
 
 
 def permute(topk_ids: torch.Tensor, num_experts: int, block_m: int = 64):
-    """moe_permute: dict(counts [E], offsets [E+1], sorted_slots [cap], block_expert [cap/block_m])."""
+    """moe_permute: dict(counts [E], offsets [E+1], sorted_slots [cap], block_expert [cap/block_m],
+    num_padded [1], slot_row [T*k])."""
     lib = load()
     T, k = topk_ids.shape
     _dev(topk_ids, "topk_ids", torch.int32)
@@ -166,10 +177,14 @@ def permute(topk_ids: torch.Tensor, num_experts: int, block_m: int = 64):
     offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
     sorted_slots = torch.full((max(cap, 1),), -7, dtype=torch.int32, device=dev)
     block_expert = torch.full((max(cap // block_m, 1),), -7, dtype=torch.int32, device=dev)
+    num_padded = torch.full((1,), -7, dtype=torch.int32, device=dev)
+    slot_row = torch.full((max(T * k, 1),), -7, dtype=torch.int32, device=dev)
     _check(lib.moe_permute(_ptr(topk_ids), T, k, num_experts, block_m, _ptr(counts), _ptr(offsets),
-                           _ptr(sorted_slots), _ptr(block_expert), _stream()))
+                           _ptr(sorted_slots), _ptr(block_expert), _ptr(num_padded), _ptr(slot_row),
+                           _stream()))
     return dict(counts=counts, offsets=offsets, sorted_slots=sorted_slots[:cap],
-                block_expert=block_expert[:cap // block_m], capacity=cap)
+                block_expert=block_expert[:cap // block_m], num_padded=num_padded,
+                slot_row=slot_row[:T * k], capacity=cap)
 
 
 # ----------------------------------------------------------------------------- moe_forward
@@ -233,11 +248,13 @@ class DeviceLayer:
 
     def forward(self, x: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = "layer",
                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                want_routing: bool = False, events=None):
+                want_routing: bool = False, events=None, want_intermediates: bool = False):
         """moe_forward.  Returns out [T,H]; with want_routing also a dict of the
         logits, topk_w, topk_ids and out_f32 (the output before its final rounding).
         events: optional list of len(STAGES)+1 recorded torch.cuda.Event objects; the
-        library records them between its stages (moe_forward_profiled)."""
+        library records them between its stages (moe_forward_profiled).
+        want_intermediates (with want_routing): the dict also holds "ws", views of
+        the call's intermediates in its workspace (moe_forward_workspace_layout)."""
         lib = load()
         t = self.t
         x = t["x"] if x is None else x
@@ -275,6 +292,41 @@ class DeviceLayer:
             arr = (C.c_void_p * len(events))(*[e._as_parameter_.value for e in events])
             _check(lib.moe_forward_profiled(C.byref(self.desc), C.byref(ts), T, _ptr(workspace),
                                             workspace.numel(), _stream(), arr))
+        if want_intermediates:
+            extra["ws"] = self._intermediates(ts, T, workspace)
         if want_routing:
             return out, extra
         return out
+
+    def _intermediates(self, ts, T, workspace):
+        lay = WorkspaceLayout()
+        _check(load().moe_forward_workspace_layout(C.byref(self.desc), C.byref(ts), T, C.byref(lay)))
+        d = self.desc
+        kp, cap, H, I = lay.slots_per_token, lay.capacity, d.hidden, d.inter
+        act = self.act_dtype
+        ydt = torch.float32 if lay.y_f32 else act
+
+        def view(off, dtype, shape):
+            if off < 0:
+                return None
+            n = 1
+            for v in shape:
+                n *= v
+            nb = n * torch.empty((), dtype=dtype).element_size()
+            return workspace[off:off + nb].view(dtype).view(*shape)
+
+        return dict(
+            path=PATHS[lay.path], block_m=lay.block_m, slots_per_token=kp, y_parts=lay.y_parts,
+            y_f32=bool(lay.y_f32), capacity=cap,
+            topk_w=view(lay.topk_w, torch.float32, (T, kp)), topk_ids=view(lay.topk_ids, torch.int32, (T, kp)),
+            counts=view(lay.counts, torch.int32, (d.num_experts + d.n_shared,)),
+            offsets=view(lay.offsets, torch.int32, (d.num_experts + d.n_shared + 1,)),
+            sorted_slots=view(lay.sorted_slots, torch.int32, (cap,)),
+            block_expert=view(lay.block_expert, torch.int32, (cap // max(lay.block_m, 1),)),
+            slot_row=view(lay.slot_row, torch.int32, (T * kp,)),
+            inv_rms=view(lay.inv_rms, torch.float32, (T,)),
+            x_expert=view(lay.x_expert, act, (T, H)),
+            h=view(lay.h, act, (cap, I)),
+            y=view(lay.y, ydt, (T * kp * lay.y_parts, H)),
+            x_codes=view(lay.x_codes, torch.uint8, (T, H)), x_scales=view(lay.x_scales, torch.float32, (T,)),
+            h_codes=view(lay.h_codes, torch.uint8, (cap, I)), h_scales=view(lay.h_scales, torch.float32, (cap,)))

@@ -37,30 +37,59 @@ moe_status hip_fail(hipError_t e, const char* what) {
     if (_e != hipSuccess) return hip_fail(_e, what); \
   } while (0)
 
-// A second stream per host thread and device, created on first use and kept
-// until the process ends: the dense MLP branch of a layer runs on it, between a
-// fork event recorded on the caller's stream after the input norms and a join
-// event the caller's stream waits for before the finalize, so it fills the CUs
-// that routing, permutation and the tails of the grouped GEMMs leave idle.
-// Default priority, non-blocking, ordered only by those events.
+// A second stream per caller stream, host thread and device, created on first
+// use and kept until the process ends: the dense MLP branch of a layer runs on
+// it, between a fork event recorded on the caller's stream after the input norms
+// and a join event the caller's stream waits for before the finalize, so it fills
+// the CUs that routing, permutation and the tails of the grouped GEMMs leave
+// idle.  Default priority, non-blocking, ordered only by those events.  Keyed by
+// the caller's stream so that layers forwarded on different streams never meet
+// on a shared side stream; past SIDE_MAX caller streams on a thread the dense
+// branch runs on the caller's stream itself.
 struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
-  bool tried = false, ok = false;
 };
-SideStream* side_stream() {
+constexpr int SIDE_MAX = 16;
+SideStream* side_stream(hipStream_t caller) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  thread_local SideStream per_device[64];
-  SideStream& x = per_device[dev];
-  if (!x.tried) {
-    x.tried = true;
-    x.ok = hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) == hipSuccess &&
-           hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) == hipSuccess &&
-           hipEventCreateWithFlags(&x.join, hipEventDisableTiming) == hipSuccess;
-  }
-  return x.ok ? &x : nullptr;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  struct Entry {
+    int dev;
+    hipStream_t caller;
+    bool ok;
+    SideStream side;
+  };
+  thread_local Entry table[SIDE_MAX];
+  thread_local int used = 0;
+  for (int i = 0; i < used; ++i)
+    if (table[i].dev == dev && table[i].caller == caller) return table[i].ok ? &table[i].side : nullptr;
+  if (used == SIDE_MAX) return nullptr;
+  Entry& x = table[used++];
+  x.dev = dev;
+  x.caller = caller;
+  x.ok = hipStreamCreateWithFlags(&x.side.s, hipStreamNonBlocking) == hipSuccess &&
+         hipEventCreateWithFlags(&x.side.fork, hipEventDisableTiming) == hipSuccess &&
+         hipEventCreateWithFlags(&x.side.join, hipEventDisableTiming) == hipSuccess;
+  return x.ok ? &x.side : nullptr;
 }
+
+// Once the dense branch is forked, every way out of the call (errors included)
+// makes the caller's stream wait for the side stream, so no work of this call
+// outlives it on the side stream (or stays unjoined in a stream capture).
+struct SideJoin {
+  SideStream* side = nullptr;
+  hipStream_t st = nullptr;
+  bool armed = false;
+  hipError_t join() {
+    if (!armed) return hipSuccess;
+    armed = false;
+    hipError_t e = hipEventRecord(side->join, side->s);
+    hipError_t w = hipStreamWaitEvent(st, side->join, 0);
+    return e != hipSuccess ? e : w;
+  }
+  ~SideJoin() { join(); }
+};
 
 constexpr size_t ALIGN = 256;
 size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
@@ -107,6 +136,7 @@ struct Plan {
   bool y_f32;                    // per-slot expert outputs kept in fp32
   bool aq;                       // FP8 activations: x and h quantised per row
   size_t o_xq, o_xs, o_hq, o_hs;  // their codes and scales
+  size_t o_slotrow;  // inverse map of the permutation (slot -> padded row)
   size_t o_logits, o_w, o_ids, o_counts, o_offsets, o_sorted, o_bexp, o_rms, o_r, o_xn1, o_xn2, o_h, o_y,
       o_dh, o_dout, total;
   size_t o_rinfo, o_ypart;  // decode path only
@@ -216,6 +246,10 @@ moe_status make_plan(const moe_layer_desc& d, const moe_tensors* t, int64_t T, P
   // rounds (long reductions over few rows: the Mixtral-style layer); rows are
   // estimated with half a block of padding per expert.
   p.ks = p.f32 ? 1 : moe::gemm_scatter_k_splits(slots + (int64_t)p.Ep * (p.bm / 2), p.bm, d.hidden, d.inter);
+  // The per-slot rows are sized for the most parts this row block allows, not for
+  // the parts this T picks (which can fall as T grows): the reported workspace size
+  // must not decrease with T.
+  const int ks_room = p.f32 ? 1 : moe::gemm_scatter_k_splits_max(p.bm, d.inter);
   const size_t H = d.hidden;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -230,12 +264,13 @@ moe_status make_plan(const moe_layer_desc& d, const moe_tensors* t, int64_t T, P
   p.o_offsets = take((size_t)(p.Ep + 1) * 4);
   p.o_sorted = take((size_t)p.cap * 4);
   p.o_bexp = take((size_t)(p.cap / p.bm) * 4);
+  p.o_slotrow = take((size_t)slots * 4);
   p.o_rms = take(p.need_prenorm ? (size_t)T * 4 : 0);
   p.o_r = take(p.mat_r ? (size_t)T * H * ae : 0);
   p.o_xn1 = take(p.mat_xn1 ? (size_t)T * H * ae : 0);
   p.o_xn2 = take(p.mat_xn2 ? (size_t)T * H * ae : 0);
   p.o_h = take((size_t)p.cap * d.inter * ae);
-  p.o_y = take((size_t)slots * p.ks * H * (p.y_f32 ? 4 : ae));
+  p.o_y = take((size_t)slots * ks_room * H * (p.y_f32 ? 4 : ae));
   p.o_dh = take(p.dense ? (size_t)T * d.inter_dense * ae : 0);
   p.o_dout = take(p.dense ? (size_t)T * H * 4 : 0);
   p.o_xq = take(p.aq ? (size_t)T * H : 0);
@@ -332,7 +367,7 @@ MOE_API int64_t moe_permute_capacity(int64_t T, int32_t K, int32_t E, int32_t bl
 
 MOE_API moe_status moe_permute(const int32_t* topk_ids, int64_t T, int32_t K, int32_t E, int32_t block_m,
                                int32_t* counts, int32_t* offsets, int32_t* sorted_slots, int32_t* block_expert,
-                               void* stream) {
+                               int32_t* num_padded, int32_t* slot_row, void* stream) {
   g_err[0] = 0;
   if (T < 0) return fail(MOE_INVALID_ARG, "T < 0");
   if (K < 1 || K > 64) return fail(MOE_INVALID_ARG, "K %d outside [1, 64]", K);
@@ -340,10 +375,10 @@ MOE_API moe_status moe_permute(const int32_t* topk_ids, int64_t T, int32_t K, in
   const int l2 = log2_exact(block_m);
   if (l2 < 4 || block_m > 256) return fail(MOE_INVALID_ARG, "block_m %d must be a power of two in [16, 256]", block_m);
   if (T * K >= ((int64_t)1 << 31)) return fail(MOE_UNSUPPORTED, "T*K >= 2^31");
-  if (!counts || !offsets || !sorted_slots || !block_expert || (T > 0 && !topk_ids))
+  if (!counts || !offsets || !sorted_slots || !block_expert || (T > 0 && (!topk_ids || !slot_row)))
     return fail(MOE_INVALID_ARG, "null output pointer");
-  HIP_TRY(moe::launch_permute(topk_ids, T * K, E, l2, counts, offsets, sorted_slots, block_expert,
-                              (hipStream_t)stream),
+  HIP_TRY(moe::launch_permute(topk_ids, T * K, E, l2, counts, offsets, sorted_slots, block_expert, num_padded,
+                              slot_row, (hipStream_t)stream),
           "permute launch");
   return MOE_OK;
 }
@@ -370,6 +405,43 @@ MOE_API moe_status moe_forward_workspace_size(const moe_layer_desc* desc, int64_
   s = make_plan(*desc, nullptr, T, p);
   if (s != MOE_OK) return s;
   *bytes = p.total;
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_forward_workspace_layout(const moe_layer_desc* desc, const moe_tensors* t, int64_t T,
+                                                moe_workspace_layout* out) {
+  g_err[0] = 0;
+  moe_status s = validate_desc(desc);
+  if (s != MOE_OK) return s;
+  if ((s = validate_tensors(*desc, t)) != MOE_OK) return s;
+  if (T < 1) return fail(MOE_INVALID_ARG, "T must be >= 1");
+  if (!out) return fail(MOE_INVALID_ARG, "layout is NULL");
+  Plan p;
+  if ((s = make_plan(*desc, t, T, p)) != MOE_OK) return s;
+  moe_workspace_layout L;
+  L.path = p.decode ? MOE_PATH_DECODE : MOE_PATH_GROUPED;
+  L.block_m = p.bm;
+  L.slots_per_token = p.Kp;
+  L.y_parts = p.ks;
+  L.y_f32 = p.y_f32;
+  L.capacity = p.cap;
+  auto off = [&](bool has, size_t o) { return (!p.decode && has) ? (int64_t)o : (int64_t)-1; };
+  L.topk_w = off(true, p.o_w);
+  L.topk_ids = off(true, p.o_ids);
+  L.counts = off(true, p.o_counts);
+  L.offsets = off(true, p.o_offsets);
+  L.sorted_slots = off(true, p.o_sorted);
+  L.block_expert = off(true, p.o_bexp);
+  L.slot_row = off(true, p.o_slotrow);
+  L.inv_rms = off(p.need_prenorm, p.o_rms);
+  L.x_expert = off(p.mat_xn2, p.o_xn2);
+  L.h = off(true, p.o_h);
+  L.y = off(true, p.o_y);
+  L.x_codes = off(p.aq, p.o_xq);
+  L.x_scales = off(p.aq, p.o_xs);
+  L.h_codes = off(p.aq, p.o_hq);
+  L.h_scales = off(p.aq, p.o_hs);
+  *out = L;
   return MOE_OK;
 }
 
@@ -545,7 +617,8 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
     return MOE_OK;
   };
   // Overlap the dense branch with the MoE path unless stages are being timed.
-  SideStream* side = p.dense && !events ? side_stream() : nullptr;
+  SideStream* side = p.dense && !events ? side_stream(st) : nullptr;
+  SideJoin side_join;
 
   STAGE(MOE_STAGE_PRENORM);
   // 1. input norms (Gemma router preprocessing, pre_feedforward_layernorm / _2):
@@ -557,9 +630,11 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
   if (side) {
     HIP_TRY(hipEventRecord(side->fork, st), "fork event");
     HIP_TRY(hipStreamWaitEvent(side->s, side->fork, 0), "fork wait");
+    side_join.side = side;
+    side_join.st = st;
+    side_join.armed = true;
     s = dense_branch(side->s, false);
     if (s != MOE_OK) return s;
-    HIP_TRY(hipEventRecord(side->join, side->s), "join event");
   }
 
   STAGE(MOE_STAGE_ROUTER);
@@ -599,7 +674,8 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
 
   STAGE(MOE_STAGE_PERMUTE);
   // 4. permutation map
-  HIP_TRY(moe::launch_permute(ids, T * p.Kp, p.Ep, log2_exact(p.bm), counts, offsets, sorted, bexp, st),
+  HIP_TRY(moe::launch_permute(ids, T * p.Kp, p.Ep, log2_exact(p.bm), counts, offsets, sorted, bexp, nullptr,
+                              (int32_t*)(ws + p.o_slotrow), st),
           "permute launch");
 
   STAGE(MOE_STAGE_QUANT_X);
@@ -679,7 +755,7 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
   } else {
     STAGE(MOE_STAGE_DENSE_DOWN);
   }
-  if (side) HIP_TRY(hipStreamWaitEvent(st, side->join, 0), "join wait");
+  HIP_TRY(side_join.join(), "join of the dense branch");
   STAGE(MOE_STAGE_FINALIZE);
   // 8. per-token combine in slot order (+ Gemma post-norms and branch sum)
   HIP_TRY(moe::launch_finalize(y, p.y_f32 ? moe::ELEM_F32 : act_elem, p.Kp * p.ks, dout, t->gamma_post1, t->gamma_post2, d.eps, t->out, act_elem,

@@ -865,18 +865,6 @@ static hipError_t up_vpl(const DecodeArgs& a, int nb, int lds, hipStream_t s) {
   return hipGetLastError();
 }
 
-static int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 int decode_up_blocks_per_cu(int T, int H, int Kp, int Ep) {
   return decode_up_lds_bytes(T, H, Kp, Ep) * 2 <= 160 * 1024 ? 2 : 1;
 }
@@ -887,7 +875,7 @@ int decode_up_blocks_per_cu(int T, int H, int Kp, int Ep) {
 hipError_t launch_decode_up(const DecodeArgs& args, int wk, hipStream_t s) {
   DecodeArgs a = args;
   const int lds = decode_up_lds_bytes(a.T, a.H, a.Kp, a.Ep);
-  const int slots = cu_count() * decode_up_blocks_per_cu(a.T, a.H, a.Kp, a.Ep);
+  const int slots = device_cu_count() * decode_up_blocks_per_cu(a.T, a.H, a.Kp, a.Ep);
   const int room = slots - a.n_dense_groups > slots / 2 ? slots - a.n_dense_groups : slots / 2;
   // as few blocks as keep the item count per block at its minimum, so that every
   // block gets the same number of items when all experts the bound allows are active
@@ -916,7 +904,7 @@ hipError_t launch_decode_up(const DecodeArgs& args, int wk, hipStream_t s) {
 int decode_down_splits(int T, int H, int I, bool dense) {
   if (!dense && T < 4) return 1;
   const int ng = H / 16;
-  int P = (2 * cu_count() + ng - 1) / ng;
+  int P = (2 * device_cu_count() + ng - 1) / ng;
   P = P < 1 ? 1 : (P > 4 ? 4 : P);
   return P < I / 64 ? P : I / 64;
 }

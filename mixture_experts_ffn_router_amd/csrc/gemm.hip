@@ -48,6 +48,7 @@
 //     the accumulator and the normalised rows are never rounded or stored.
 //
 // fp32 kernel (the fp32 layer): plain LDS-tiled FMA, 64x64 tile, same epilogues.
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -932,16 +933,20 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
 }
 
 // ------------------------------------------------------------------ dispatch
-static int device_cu_count() {
-  static int cached[64] = {0};
+// Host-side caches below are atomics: several host threads may launch at once
+// (each computes the same value; whichever store lands first is kept).
+int device_cu_count() {
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (!v) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
+    v = n;
   }
-  return cached[dev];
+  return v;
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI, int BELEM>
@@ -953,10 +958,12 @@ static hipError_t run_mfma(const GemmArgs& a, hipStream_t s) {
   const int64_t tiles = mb_cap * nb * a.k_splits;  // upper bound; the kernel counts the real ones
   if (tiles <= 0) return hipSuccess;
   auto kern = gemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, EPI, BELEM>;
-  static int per_cu = 0;  // resident blocks per CU for this instantiation
+  static std::atomic<int> per_cu_cache{0};  // resident blocks per CU for this instantiation
+  int per_cu = per_cu_cache.load(std::memory_order_relaxed);
   if (!per_cu) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, THREADS, 0) != hipSuccess || n <= 0) n = 1;
+    per_cu_cache.store(n, std::memory_order_relaxed);
     per_cu = n;
   }
   const int64_t resident = (int64_t)device_cu_count() * per_cu;
@@ -1014,6 +1021,13 @@ int gemm_scatter_k_splits(int64_t rows, int block_m, int N, int Kdim) {
     }
   }
   return best;
+}
+
+int gemm_scatter_k_splits_max(int block_m, int Kdim) {
+  if (block_m != 256) return 1;
+  int ks = 1;
+  while (ks < 4 && (Kdim / 64) / (ks + 1) >= 32) ++ks;
+  return ks;
 }
 
 // Reduction parts for a store GEMM over identity rows (the router): enough tiles

@@ -24,9 +24,14 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int K, const Rout
                         float* w_out, int32_t* ids_out, int out_stride, int n_shared, hipStream_t s,
                         int nparts = 1, int64_t part_stride = 0, float* sum_out = nullptr);
 
+// slot_row [n] is required (it also holds the per-chunk counts between the
+// launches); num_padded may be NULL.  E <= 1024.
 hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int bm_log2, int32_t* counts,
-                          int32_t* offsets, int32_t* sorted_slots, int32_t* block_expert,
-                          hipStream_t s);
+                          int32_t* offsets, int32_t* sorted_slots, int32_t* block_expert, int32_t* num_padded,
+                          int32_t* slot_row, hipStream_t s);
+
+// Compute units of the current device (256 when it cannot be queried).
+int device_cu_count();
 
 enum GemmEpi { EPI_GATED = 0, EPI_SCATTER = 1, EPI_STORE_F32 = 2, EPI_SCATTER_F32 = 3 };
 // B element type; ELEM_FP8X8: A and B both FP8 (E4M3), the per-row A scale in row_scale
@@ -72,6 +77,9 @@ hipError_t launch_gemm_mfma(const GemmArgs& a, int epi, int belem, int block_m, 
 // Reduction parts for a grouped scatter GEMM of about `rows` rows: the count in
 // 1..4 that wastes least of the last round of tiles on this device's CUs.
 int gemm_scatter_k_splits(int64_t rows, int block_m, int N, int Kdim);
+// The most parts gemm_scatter_k_splits returns for this row block and reduction
+// length, whatever the rows (non-decreasing in block_m).
+int gemm_scatter_k_splits_max(int block_m, int Kdim);
 int gemm_store_k_splits(int64_t M, int N, int Kdim);
 // fp32 A and B (the fp32 layer).  block_m = 64.
 hipError_t launch_gemm_f32(const GemmArgs& a, int epi, hipStream_t s);

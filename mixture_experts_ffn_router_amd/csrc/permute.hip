@@ -3,129 +3,241 @@
 // ("Gemma 4 26B-A4B MoE walkthrough" sections 6-7: dispatch builds a
 // permutation map that the grouped GEMM reads indirectly; no token moves).
 //
-// Two launches, one workgroup (16 waves) per expert in each:
-//   count:   expert e counts the slots whose id is e;
-//   scatter: expert e sums the padded sizes of experts < e to find its segment,
-//            then walks the ids in order, 4096 slots per step (the next step's
-//            ids loaded while this one is ranked), and compacts the matching
-//            flat slot indices.  A thread owns 4 consecutive slots;
-//            its rank inside the step is an exclusive prefix of per-thread
-//            match counts (0..4), taken from three ballots (one per bit of the
-//            count) and per-wave totals in LDS, so the order is deterministic
-//            and stable without atomics.  Pads get -1 and block_expert gets e.
+// Histogram, prefix scan, stable scatter; every id is read twice in all, so the
+// cost is O(T*K + E) however many experts there are.  The ids are cut into
+// chunks of CHUNK consecutive flat slots, one 1024-thread block per chunk.
+//   hist:    block b counts its chunk's ids per expert in LDS and stores the E
+//            counts in slot_row[b*CHUNK .. b*CHUNK + E) (the chunk's own part of
+//            that output, free until the scatter writes it); a ragged last chunk,
+//            whose part may be shorter than E, stores them in counts[] instead.
+//   scan:    one block, a thread per expert: turns the full chunks' counts into
+//            exclusive prefixes over the chunks (in place), adds the last
+//            chunk's to get counts[e], scans the padded sizes over the experts
+//            into offsets[], and writes block_expert[] and the -1 pads.
+//   scatter: block b ranks each id among the equal ids before it in its chunk
+//            (a wave's equal ids are found with one ballot per bit of the id;
+//            waves are ordered through per-wave counts in LDS, so no atomics
+//            decide any order), reads its chunk's prefixes into LDS before any
+//            of its slot_row entries is overwritten, and writes
+//            sorted_slots[pos] = f and slot_row[f] = pos with
+//            pos = offsets[e] + (equal ids in earlier chunks) + rank.
+// Only block b reads or writes slot_row[b*CHUNK, (b+1)*CHUNK) between the
+// launches' boundaries, so the reuse is race-free.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-constexpr int PERM_THREADS = 1024;
-constexpr int PERM_STEP = PERM_THREADS * 4;
+namespace {
+constexpr int PT = 1024;             // threads per block
+constexpr int PW = PT / 64;          // waves per block
+constexpr int ROUNDS = 4;            // ids per thread per chunk
+constexpr int CHUNK = PT * ROUNDS;   // flat slots per chunk (>= the largest E, 1024)
 
-__device__ __forceinline__ int block_sum_i32(int v, int* s_red) {
+__device__ __forceinline__ int chunk_id(const int32_t* __restrict__ ids, int64_t n, int64_t f, int E) {
+  if (f >= n) return -1;
+  const int e = ids[f];
+  return (e >= 0 && e < E) ? e : -1;  // ids outside [0, E) belong to no segment
+}
+
+// Block-wide exclusive scan of one int per thread (1024 threads); returns the
+// thread's exclusive prefix, *total the sum.
+__device__ __forceinline__ int block_excl_scan(int v, int* s_w, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // wave all-reduce on the u32 pattern (values are small non-negative ints)
-  v = (int)wave_allreduce_u32((uint32_t)v, [](uint32_t a, uint32_t b) { return a + b; }, 0u);
-  if (lane == 0) s_red[wave] = v;
-  __syncthreads();
-  int tot = 0;
-  for (int w = 0; w < PERM_THREADS / 64; ++w) tot += s_red[w];
-  __syncthreads();
-  return tot;
-}
-
-// ids f0 .. f0+3 (-1 past n, not read); one 16-byte load when the ids are
-// 16-byte aligned and all four exist.
-__device__ __forceinline__ int4 load_ids4(const int32_t* __restrict__ ids, int64_t n, int64_t f0, bool vec) {
-  if (vec && f0 + 3 < n) return *(const int4*)(ids + f0);
-  int4 r;
-  r.x = f0 < n ? ids[f0] : -1;
-  r.y = f0 + 1 < n ? ids[f0 + 1] : -1;
-  r.z = f0 + 2 < n ? ids[f0 + 2] : -1;
-  r.w = f0 + 3 < n ? ids[f0 + 3] : -1;
-  return r;
-}
-__device__ __forceinline__ uint32_t match4(int4 v, int e) {
-  return (uint32_t)(v.x == e) | ((uint32_t)(v.y == e) << 1) | ((uint32_t)(v.z == e) << 2) | ((uint32_t)(v.w == e) << 3);
-}
-
-__global__ __launch_bounds__(PERM_THREADS) void permute_count_kernel(const int32_t* __restrict__ ids,
-                                                                     int64_t n, int32_t* __restrict__ counts,
-                                                                     bool vec) {
-  __shared__ int s_red[PERM_THREADS / 64];
-  const int e = blockIdx.x;
-  int c = 0;
-  // the next step's ids are loaded before this step's are counted
-  int64_t f = (int64_t)threadIdx.x * 4;
-  int4 cur = load_ids4(ids, n, f, vec);
-  for (; f < n; f += PERM_STEP) {
-    const int4 nxt = load_ids4(ids, n, f + PERM_STEP, vec);
-    c += __popc(match4(cur, e));
-    cur = nxt;
-  }
-  c = block_sum_i32(c, s_red);
-  if (threadIdx.x == 0) counts[e] = c;
-}
-
-__global__ __launch_bounds__(PERM_THREADS) void permute_scatter_kernel(
-    const int32_t* __restrict__ ids, int64_t n, int E, int bm_log2, const int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slots, int32_t* __restrict__ block_expert,
-    bool vec) {
-  __shared__ int s_red[PERM_THREADS / 64];
-  __shared__ int s_wtot[PERM_THREADS / 64];
-  const int e = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int bm = 1 << bm_log2;
-  auto padded_size = [&](int c) { return ((c + bm - 1) >> bm_log2) << bm_log2; };
-
-  int part = 0;
-  for (int j = tid; j < e; j += PERM_THREADS) part += padded_size(counts[j]);
-  const int start = block_sum_i32(part, s_red);
-  const int cnt = counts[e];
-  const int padded = padded_size(cnt);
-  if (tid == 0) {
-    offsets[e] = start;
-    if (e == E - 1) offsets[E] = start + padded;
-  }
-
-  const uint64_t lt = (1ull << lane) - 1ull;
-  int running = 0;
-  int4 cur = load_ids4(ids, n, (int64_t)tid * 4, vec);
-  for (int64_t base = 0; base < n; base += PERM_STEP) {
-    const int64_t f0 = base + (int64_t)tid * 4;
-    const int4 nxt = load_ids4(ids, n, f0 + PERM_STEP, vec);  // next step, in flight meanwhile
-    const uint32_t bits = match4(cur, e);
-    cur = nxt;
-    const int c = __popc(bits);
-    const uint64_t b0 = __ballot(c & 1), b1 = __ballot(c & 2), b2 = __ballot(c & 4);
-    const int wprefix = __popcll(b0 & lt) + 2 * __popcll(b1 & lt) + 4 * __popcll(b2 & lt);
-    if (lane == 0) s_wtot[wave] = __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
-    __syncthreads();
-    int wbase = 0, btot = 0;
-    for (int w = 0; w < PERM_THREADS / 64; ++w) {
-      int x = s_wtot[w];
-      wbase += (w < wave) ? x : 0;
-      btot += x;
-    }
-    int pos = start + running + wbase + wprefix;
+  // inclusive scan inside the wave with shuffles (log steps)
+  int incl = v;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if ((bits >> q) & 1u) sorted_slots[pos++] = (int32_t)(f0 + q);
-    running += btot;
-    __syncthreads();
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
   }
-  for (int i = cnt + tid; i < padded; i += PERM_THREADS) sorted_slots[start + i] = -1;
-  for (int b = tid; b < (padded >> bm_log2); b += PERM_THREADS) block_expert[(start >> bm_log2) + b] = e;
+  if (lane == 63) s_w[wave] = incl;
+  __syncthreads();
+  int wbase = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < PW; ++w) {
+    const int x = s_w[w];
+    wbase += w < wave ? x : 0;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return wbase + incl - v;
 }
+}  // namespace
+
+__global__ __launch_bounds__(PT) void permute_hist_kernel(const int32_t* __restrict__ ids, int64_t n, int E,
+                                                          int32_t* __restrict__ slot_row,
+                                                          int32_t* __restrict__ counts) {
+  extern __shared__ int s_hist[];  // [E]
+  const int b = blockIdx.x, tid = threadIdx.x;
+  for (int e = tid; e < E; e += PT) s_hist[e] = 0;
+  __syncthreads();
+  const int64_t f0 = (int64_t)b * CHUNK;
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int e = chunk_id(ids, n, f0 + r * PT + tid, E);
+    if (e >= 0) atomicAdd(&s_hist[e], 1);  // a sum: the order of the adds does not matter
+  }
+  __syncthreads();
+  const bool full = f0 + CHUNK <= n;
+  int32_t* dst = full ? slot_row + f0 : counts;
+  for (int e = tid; e < E; e += PT) dst[e] = s_hist[e];
+}
+
+__global__ __launch_bounds__(PT) void permute_scan_kernel(int64_t n, int E, int bm_log2,
+                                                          int32_t* __restrict__ slot_row,
+                                                          int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ sorted_slots,
+                                                          int32_t* __restrict__ block_expert,
+                                                          int32_t* __restrict__ num_padded) {
+  __shared__ int s_w[PW];
+  __shared__ int s_off[1025];
+  __shared__ int s_cnt[1024];
+  const int tid = threadIdx.x;
+  const int64_t nfull = n / CHUNK;
+  const bool tail = n % CHUNK != 0;
+  const int bm = 1 << bm_log2;
+  int cnt = 0;
+  if (tid < E) {
+    // exclusive prefix over the full chunks, in place; four loads in flight
+    int32_t* p = slot_row + tid;
+    int64_t c = 0;
+    for (; c + 4 <= nfull; c += 4) {
+      const int v0 = p[(c + 0) * CHUNK], v1 = p[(c + 1) * CHUNK], v2 = p[(c + 2) * CHUNK], v3 = p[(c + 3) * CHUNK];
+      p[(c + 0) * CHUNK] = cnt;
+      p[(c + 1) * CHUNK] = cnt + v0;
+      p[(c + 2) * CHUNK] = cnt + v0 + v1;
+      p[(c + 3) * CHUNK] = cnt + v0 + v1 + v2;
+      cnt += v0 + v1 + v2 + v3;
+    }
+    for (; c < nfull; ++c) {
+      const int v = p[c * CHUNK];
+      p[c * CHUNK] = cnt;
+      cnt += v;
+    }
+    if (tail) cnt += counts[tid];
+    counts[tid] = cnt;
+  }
+  const int padded = ((cnt + bm - 1) >> bm_log2) << bm_log2;
+  int total = 0;
+  const int start = block_excl_scan(tid < E ? padded : 0, s_w, &total);
+  if (tid < E) {
+    offsets[tid] = start;
+    s_off[tid] = start;
+    s_cnt[tid] = cnt;
+  }
+  if (tid == 0) {
+    offsets[E] = total;
+    s_off[E] = total;
+    if (num_padded) *num_padded = total;
+  }
+  __syncthreads();
+  // row block j belongs to the last expert whose segment starts at or before it
+  // (empty experts start where the next one does); its rows past the expert's
+  // count are pads
+  const int nblk = total >> bm_log2;
+  for (int j = tid; j < nblk; j += PT) {
+    const int row = j << bm_log2;
+    int lo = 0, hi = E - 1;  // s_off[lo] <= row < s_off[E]
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[mid] <= row) lo = mid;
+      else hi = mid - 1;
+    }
+    block_expert[j] = lo;
+    const int pad0 = s_off[lo] + s_cnt[lo];
+    for (int r = row > pad0 ? row : pad0; r < row + bm; ++r) sorted_slots[r] = -1;
+  }
+}
+
+__global__ __launch_bounds__(PT) void permute_scatter_kernel(const int32_t* __restrict__ ids, int64_t n, int E,
+                                                             const int32_t* __restrict__ counts,
+                                                             const int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ sorted_slots,
+                                                             int32_t* __restrict__ slot_row) {
+  extern __shared__ int s_dyn[];
+  int* s_base = s_dyn;                        // [E] offsets[e] + equal ids before the current round
+  uint16_t* s_wcnt = (uint16_t*)(s_dyn + E);  // [PW][E] per-wave counts of the current round (<= 64)
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t f0 = (int64_t)b * CHUNK;
+  const bool full = f0 + CHUNK <= n;
+  int e_r[ROUNDS];
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) e_r[r] = chunk_id(ids, n, f0 + r * PT + tid, E);
+  if (full) {
+    for (int e = tid; e < E; e += PT) s_base[e] = offsets[e] + slot_row[f0 + e];
+  } else {
+    // the ragged last chunk: equal ids in earlier chunks = counts[e] - this chunk's
+    for (int e = tid; e < E; e += PT) s_base[e] = offsets[e] + counts[e];
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r)
+      if (e_r[r] >= 0) atomicSub(&s_base[e_r[r]], 1);  // a count: the order does not matter
+  }
+  const uint64_t lt = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int e = e_r[r];
+    // lanes of this wave holding the same id: one ballot per bit of the id (and
+    // one for validity, so invalid lanes form their own group)
+    uint64_t same = __ballot(e >= 0);
+    if (e < 0) same = ~same;
+#pragma unroll
+    for (int bit = 0; bit < 10; ++bit) {
+      const bool v = (e >> bit) & 1;
+      const uint64_t bal = __ballot(v);
+      same &= v ? bal : ~bal;
+    }
+    for (int i = tid; i < PW * E; i += PT) s_wcnt[i] = 0;
+    __syncthreads();  // zeroed; also: the previous round's reads of s_base are done
+    const bool leader = (same & lt) == 0;
+    if (e >= 0 && leader) s_wcnt[wave * E + e] = (uint16_t)__popcll(same);
+    __syncthreads();
+    if (e >= 0) {
+      int pos = s_base[e] + __popcll(same & lt);
+      for (int w = 0; w < wave; ++w) pos += s_wcnt[w * E + e];
+      const int64_t f = f0 + r * PT + tid;
+      sorted_slots[pos] = (int32_t)f;
+      e_r[r] = pos;  // written to slot_row below, once every base read is done
+    } else {
+      e_r[r] = -1;
+    }
+    __syncthreads();
+    for (int x = tid; x < E; x += PT) {
+      int s = 0;
+      for (int w = 0; w < PW; ++w) s += s_wcnt[w * E + x];
+      s_base[x] += s;
+    }
+    __syncthreads();  // the sums above have read s_wcnt before the next round clears it
+  }
+  // every base of this chunk has been read (from slot_row for a full chunk)
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int64_t f = f0 + r * PT + tid;
+    if (f < n) slot_row[f] = e_r[r];
+  }
+}
+
+int permute_chunk() { return CHUNK; }
 
 hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int bm_log2, int32_t* counts,
-                          int32_t* offsets, int32_t* sorted_slots, int32_t* block_expert,
-                          hipStream_t s) {
-  const bool vec = ((uintptr_t)ids & 15) == 0;
-  permute_count_kernel<<<E, PERM_THREADS, 0, s>>>(ids, n, counts, vec);
+                          int32_t* offsets, int32_t* sorted_slots, int32_t* block_expert, int32_t* num_padded,
+                          int32_t* slot_row, hipStream_t s) {
+  if (E < 1 || E > 1024) return hipErrorInvalidValue;
+  const int64_t nchunks = (n + CHUNK - 1) / CHUNK;
+  if (nchunks > 0) {
+    permute_hist_kernel<<<(unsigned)nchunks, PT, E * sizeof(int), s>>>(ids, n, E, slot_row, counts);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  permute_scan_kernel<<<1, PT, 0, s>>>(n, E, bm_log2, slot_row, counts, offsets, sorted_slots, block_expert,
+                                       num_padded);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  permute_scatter_kernel<<<E, PERM_THREADS, 0, s>>>(ids, n, E, bm_log2, counts, offsets, sorted_slots,
-                                                    block_expert, vec);
+  if (err != hipSuccess || nchunks == 0) return err;
+  permute_scatter_kernel<<<(unsigned)nchunks, PT, (size_t)E * sizeof(int) + (size_t)PW * E * sizeof(uint16_t), s>>>(
+      ids, n, E, counts, offsets, sorted_slots, slot_row);
   return hipGetLastError();
 }
 

@@ -110,6 +110,27 @@ def test_workspace_size_grows_with_T_and_covers_buffers():
     assert n2 >= 4096 * 2 * 256 * 2
 
 
+@pytest.mark.parametrize("shape", [
+    dict(hidden=4096, num_experts=8, top_k=2, inter=14336),                      # Mixtral-style
+    dict(hidden=2048, num_experts=64, top_k=6, inter=1408, n_shared=2),          # DeepSeek-style
+    dict(hidden=2816, num_experts=128, top_k=8, inter=704, inter_dense=2112),    # Gemma-style
+    dict(hidden=256, num_experts=2, top_k=1, inter=4096),                        # long down reduction
+])
+def test_workspace_size_never_decreases_with_T(shape):
+    """A workspace sized for the largest T serves every smaller T: the reported
+    size is non-decreasing over every T up to 20000 or the largest supported T
+    (row-block changes and the down GEMM's reduction parts included)."""
+    d = _desc(**shape)
+    prev = 0
+    for T in range(0, 20001):
+        st, n = _ws(d, T)
+        if st == B.MOE_UNSUPPORTED and T > 4096:  # an activation buffer would pass 2 GiB
+            break
+        assert st == B.MOE_OK
+        assert n >= prev, f"workspace size falls from {prev} to {n} at T = {T}"
+        prev = n
+
+
 def test_forward_rejects_missing_tensors_and_small_workspace():
     lib = _lib()
     d = _desc()
@@ -150,10 +171,12 @@ def test_route_and_permute_validation():
     assert lib.moe_route(None, 0, 8, 5, 1, 1, 4, 2, None, None, None, None) == B.MOE_INVALID_ARG
     assert lib.moe_route(None, 0, 8, 4, 1, 1, 4, 2, None, None, None, None) == B.MOE_OK
     assert lib.moe_route(None, 0, 8, 2, 1, 0, 1, 0, None, None, None, None) == B.MOE_OK  # 1 group = none
-    assert lib.moe_permute(fake, 4, 2, 8, 48, fake, fake, fake, fake, None) == B.MOE_INVALID_ARG
-    assert lib.moe_permute(fake, 4, 2, 8, 512, fake, fake, fake, fake, None) == B.MOE_INVALID_ARG
-    assert lib.moe_permute(fake, 4, 0, 8, 64, fake, fake, fake, fake, None) == B.MOE_INVALID_ARG
-    assert lib.moe_permute(fake, 4, 2, 8, 64, None, fake, fake, fake, None) == B.MOE_INVALID_ARG
+    assert lib.moe_permute(fake, 4, 2, 8, 48, fake, fake, fake, fake, None, fake, None) == B.MOE_INVALID_ARG
+    assert lib.moe_permute(fake, 4, 2, 8, 512, fake, fake, fake, fake, None, fake, None) == B.MOE_INVALID_ARG
+    assert lib.moe_permute(fake, 4, 0, 8, 64, fake, fake, fake, fake, None, fake, None) == B.MOE_INVALID_ARG
+    assert lib.moe_permute(fake, 4, 2, 8, 64, None, fake, fake, fake, None, fake, None) == B.MOE_INVALID_ARG
+    # slot_row (the inverse map) is required for T > 0; num_padded is optional
+    assert lib.moe_permute(fake, 4, 2, 8, 64, fake, fake, fake, fake, fake, None, None) == B.MOE_INVALID_ARG
 
 
 def test_permute_capacity():

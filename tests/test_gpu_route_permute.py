@@ -122,10 +122,22 @@ def _check_permute(B, ids, E, bm):
         assert (ss[off[e] + c[e]:off[e + 1]] == -1).all()
         assert (be[off[e] // bm:off[e + 1] // bm] == e).all()
     assert off[E] <= res["capacity"]
+    assert int(res["num_padded"].item()) == off[E]
+    # inverse map: the oracle's compact position of each slot, moved to its padded segment
+    inv = np.empty(T * K, dtype=np.int64)
+    inv[order] = np.arange(T * K)
+    flat = ids.reshape(-1)
+    want = inv - offsets[flat] + off[flat]
+    assert np.array_equal(res["slot_row"].cpu().numpy(), want)
+    assert np.array_equal(ss[want], np.arange(T * K))
 
 
 @pytest.mark.parametrize("T,K,E", [(1, 1, 1), (1, 8, 128), (16, 8, 128), (128, 8, 128), (4096, 2, 8),
-                                   (1000, 6, 66), (333, 3, 1024), (8192, 8, 128), (5, 2, 700)])
+                                   (1000, 6, 66), (333, 3, 1024), (8192, 8, 128), (5, 2, 700),
+                                   # whole 4096-slot chunks only, and one slot past them
+                                   (512, 8, 128), (1025, 8, 256),
+                                   # many chunks with many experts: 16384 x 64 slots over 512 experts
+                                   (16384, 64, 512), (16384, 6, 1024)])
 @pytest.mark.parametrize("bm", [16, 64, 256])
 def test_permute_matches_oracle(B, T, K, E, bm):
     rng = np.random.default_rng(T + K + E)
