@@ -37,6 +37,7 @@ METRIC = "MoE layer tokens/s; prefill TFLOP/s % MFMA peak; decode GB/s % HBM pea
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA (the FP8-activation layers' contraction)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+PEAK_F32_TFLOPS = 157.3    # MI355X fp32 vector FMA
 MALL_BYTES = 256 << 20
 
 
@@ -134,7 +135,10 @@ def stage_work(spec, T, counts, path, dense_stage=None):
     else:
         by["router"] = z * (E * H * ab + T * H * ab + T * E * 4)
         by["gate_up"] = w_up + T * H * ab + rows * I * ab
-        by["down"] = w_down + rows * I * ab + (rows + T * S) * H * ab
+        # down + weighted combine: reads h, writes each token's combined row once (the
+        # per-slot rows the library keeps in between are its own design, not counted)
+        ob = 4 if Id else ab  # the MoE sum is fp32 when a post-norm follows
+        by["down"] = w_down + rows * I * ab + T * H * ob
         if spec.act_quant:
             # the GEMMs read 1-byte codes; the quantisations read bf16 rows and write
             # codes and one fp32 scale per row
@@ -144,8 +148,27 @@ def stage_work(spec, T, counts, path, dense_stage=None):
             by["quant_h"] = rows * I * ab + rows * I + rows * 4
         by["dense_gate_up"] = 2 * Id * H * ab + T * H * ab + T * Id * ab
         by["dense_down"] = H * Id * ab + T * Id * ab + T * H * 4
-        by["finalize"] = T * Kp * H * (4 if Id else ab) + T * H * ab
+        # combined MoE rows (+ the dense branch's rows) in, the layer output out
+        by["finalize"] = T * H * ob + (T * H * 4 if Id else 0) + T * H * ab
     return fl, by
+
+
+# Which roofline a workload is rated against (the configurations' own split): the
+# decode-sized token counts (T <= 128) by the bytes the dominant kernel must move,
+# against HBM; the prefill-sized ones by its FLOP, against the MFMA peak of the
+# contraction's dtype (FP8 x FP8 for layers with FP8 activations, else bf16); the
+# fp32 layer runs on the vector ALUs (fp32 FMA, 157.3 TFLOP/s).
+DECODE_MAX_T = 128
+
+
+def roofline_class(spec, T, dom):
+    if spec.wdtype == "fp32":
+        return "alu", PEAK_F32_TFLOPS
+    if T <= DECODE_MAX_T:
+        return "hbm", PEAK_HBM_GBS
+    if spec.act_quant and dom in ("gate_up", "down"):
+        return "mfma", PEAK_FP8_TFLOPS
+    return "mfma", PEAK_BF16_TFLOPS
 
 
 def launched_stages(spec, path, dense_stage, raw_ms, marker_ms):
@@ -324,22 +347,20 @@ def main():
     cand = [s for s in ("gate_up", "down", "dense_gate_up", "dense_down", "router") if fl[s] > 0]
     dom = max(cand, key=lambda s: stage_ms[s])
     dom_s = stage_ms[dom] / 1e3
-    intensity = fl[dom] / max(by[dom], 1)
-    # ridge point of MI355X: 2500e12 / 8e12 = 312 FLOP/byte (bf16); fp8: 625
-    peak_mfma = PEAK_FP8_TFLOPS if spec.act_quant and dom in ("gate_up", "down") else PEAK_BF16_TFLOPS
-    if intensity >= peak_mfma / PEAK_HBM_GBS * 1e3:
+    bound, peak = roofline_class(spec, T, dom)
+    if bound != "hbm":
         achieved = fl[dom] / dom_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_mfma, "unit": "TFLOP/s",
-                "frac": round(achieved / peak_mfma, 4), "traffic": None}
+        roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None}
     else:
         achieved = by[dom] / dom_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": peak, "unit": "GB/s",
+                "frac": round(achieved / peak, 4), "traffic": None}
     wl = f"{spec.name}_T{T}"
     traffic = stored_traffic(wl, dom, path)
     roof["traffic"] = traffic
     roof.update({"kernel": dom, "kernel_ms": round(stage_ms[dom], 5),
-                 "algorithmic_per_launch": fl[dom] if roof["bound"] == "mfma" else by[dom],
+                 "algorithmic_per_launch": fl[dom] if roof["bound"] != "hbm" else by[dom],
                  "algorithmic_bytes_per_launch": by[dom],
                  "traffic_over_algorithmic": round(traffic / by[dom], 3) if traffic else None,
                  "event_marker_ms": round(marker_ms, 5), "kernel_source_digest": source_digest(path)})

@@ -63,3 +63,32 @@ def test_decode_bytes_mxfp4_half_a_byte_and_a_scale_per_32():
     w16 = 8 * 3 * H * I * 2
     # only the expert weights differ between the two layers
     assert sum(by16.values()) - sum(by4.values()) == pytest.approx(w16 - w4, abs=1)
+
+
+def test_rooflines_follow_the_configurations_split():
+    """Prefill-sized token counts are rated by FLOP against the MFMA peak of the
+    contraction's dtype, decode-sized ones (T <= 128) by bytes against HBM."""
+    S = W.SPECS
+    assert bench.roofline_class(S["mixtral"], 4096, "gate_up") == ("mfma", 2500.0)
+    assert bench.roofline_class(S["gemma"], 8192, "gate_up") == ("mfma", 2500.0)
+    assert bench.roofline_class(S["deepseek_v3"], 8192, "gate_up") == ("mfma", 2500.0)
+    assert bench.roofline_class(S["gemma_w8a8"], 8192, "down") == ("mfma", 5000.0)
+    assert bench.roofline_class(S["mixtral_w8a8"], 4096, "gate_up") == ("mfma", 5000.0)
+    # the dense MLP of an FP8-activation layer stays bf16
+    assert bench.roofline_class(S["gemma_w8a8"], 8192, "dense_gate_up") == ("mfma", 2500.0)
+    for T in (1, 16, 128):
+        assert bench.roofline_class(S["gemma"], T, "gate_up") == ("hbm", 8000.0)
+    assert bench.roofline_class(S["skewed_w8a8"], 1, "gate_up") == ("hbm", 8000.0)
+    assert bench.roofline_class(S["tiny"], 64, "gate_up")[0] == "alu"
+
+
+def test_combine_bytes_are_the_combined_rows():
+    """The down GEMM with its weighted combine reads h and writes one combined row
+    per token; the per-slot rows a design keeps in between are not algorithmic."""
+    s = W.SPECS["gemma"]
+    T = 8192
+    counts = np.full(s.E, T * s.K // s.E)
+    _, by = bench.stage_work(s, T, counts, "grouped")
+    H, I, E, K = 2816, 704, 128, 8
+    assert by["down"] == E * H * I * 2 + T * K * I * 2 + T * H * 4
+    assert by["finalize"] == T * H * 4 + T * H * 4 + T * H * 2
