@@ -255,6 +255,27 @@ moe_status moe_forward_workspace_size(const moe_layer_desc* desc, int64_t T, siz
 moe_status moe_forward(const moe_layer_desc* desc, const moe_tensors* tensors, int64_t T,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * moe_forward_noalloc - moe_forward (same operation, results, arguments and
+ * errors) for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  It takes no
+ * workspace: the library's own static device scratch of
+ * MOE_NOALLOC_SCRATCH_BYTES serves as one (each GPU the library runs on holds
+ * its copy until the process ends), and the call allocates nothing and creates
+ * no stream or event (the dense branch runs on `stream`).  The first call on a
+ * device looks up that device's scratch address once.
+ *
+ * A call whose layout needs more than MOE_NOALLOC_SCRATCH_BYTES returns
+ * MOE_WORKSPACE_TOO_SMALL before launching anything (the decode path and
+ * moderate token counts fit; large prefill batches need moe_forward with a
+ * workspace).  Every call on one GPU shares that GPU's scratch: calls that
+ * overlap on one GPU (on different streams, or from several threads without
+ * stream ordering) race and give undefined results.  The scratch keeps the
+ * last call's contents; nothing in it needs to start at zero.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_forward_noalloc(const moe_layer_desc* desc, const moe_tensors* tensors, int64_t T, void* stream);
+
 /* Execution path moe_forward takes for T tokens ([LC] lesson 35: a decode
  * token touches only its experts' weights, so the layer is bound by reading
  * them).  Returns MOE_PATH_GROUPED, MOE_PATH_DECODE, or -1 for an invalid

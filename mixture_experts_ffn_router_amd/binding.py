@@ -60,7 +60,8 @@ class WorkspaceLayout(C.Structure):
 
 EXPORTS = ["moe_status_string", "moe_last_error", "moe_route", "moe_permute_capacity", "moe_permute",
            "moe_forward_workspace_size", "moe_forward", "moe_forward_profiled", "moe_forward_path",
-           "moe_decode_dense_gate_up_stage", "moe_forward_workspace_layout"]
+           "moe_decode_dense_gate_up_stage", "moe_forward_workspace_layout", "moe_forward_noalloc"]
+NOALLOC_SCRATCH_BYTES = 64 << 20
 PATHS = {0: "grouped", 1: "decode"}
 STAGES = ["prenorm", "router", "route", "permute", "quant_x", "gate_up", "quant_h", "down", "dense_gate_up",
           "dense_down", "finalize"]
@@ -100,6 +101,8 @@ def load(path: str = LIB_PATH):
                                          C.c_size_t, C.c_void_p, C.POINTER(C.c_void_p)]
     lib.moe_forward_path.restype = C.c_int32
     lib.moe_forward_path.argtypes = [C.POINTER(LayerDesc), C.c_int64]
+    lib.moe_forward_noalloc.restype = C.c_int
+    lib.moe_forward_noalloc.argtypes = [C.POINTER(LayerDesc), C.POINTER(Tensors), C.c_int64, C.c_void_p]
     lib.moe_forward_workspace_layout.restype = C.c_int
     lib.moe_forward_workspace_layout.argtypes = [C.POINTER(LayerDesc), C.POINTER(Tensors), C.c_int64,
                                                  C.POINTER(WorkspaceLayout)]
@@ -248,13 +251,15 @@ class DeviceLayer:
 
     def forward(self, x: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = "layer",
                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                want_routing: bool = False, events=None, want_intermediates: bool = False):
+                want_routing: bool = False, events=None, want_intermediates: bool = False,
+                noalloc: bool = False):
         """moe_forward.  Returns out [T,H]; with want_routing also a dict of the
         logits, topk_w, topk_ids and out_f32 (the output before its final rounding).
         events: optional list of len(STAGES)+1 recorded torch.cuda.Event objects; the
         library records them between its stages (moe_forward_profiled).
         want_intermediates (with want_routing): the dict also holds "ws", views of
-        the call's intermediates in its workspace (moe_forward_workspace_layout)."""
+        the call's intermediates in its workspace (moe_forward_workspace_layout).
+        noalloc: call moe_forward_noalloc (the library's static scratch, no workspace)."""
         lib = load()
         t = self.t
         x = t["x"] if x is None else x
@@ -267,9 +272,13 @@ class DeviceLayer:
         if out is None:
             out = torch.empty(T, H, dtype=self.act_dtype, device=x.device)
         _dev(out, "out", self.act_dtype, (T, H))
-        ws_bytes = self.workspace_size(T)
-        if workspace is None or workspace.numel() < ws_bytes:
-            workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+        if noalloc:
+            if events is not None or want_intermediates:
+                raise ValueError("the no-allocation entry point takes no events and keeps no workspace")
+        else:
+            ws_bytes = self.workspace_size(T)
+            if workspace is None or workspace.numel() < ws_bytes:
+                workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
         extra = {}
         if want_routing:
             extra = dict(logits=torch.empty(T, E, dtype=torch.float32, device=x.device),
@@ -283,7 +292,9 @@ class DeviceLayer:
                          "w_router", "router_scale", "per_expert_scale", "w13", "w2", "w13_scale",
                          "w2_scale", "shared_w13", "shared_w2", "dense_w13", "dense_w2", "gamma_pre",
                          "gamma_pre2", "gamma_post1", "gamma_post2", "gamma_post_ff")})
-        if events is None:
+        if noalloc:
+            _check(lib.moe_forward_noalloc(C.byref(self.desc), C.byref(ts), T, _stream()))
+        elif events is None:
             _check(lib.moe_forward(C.byref(self.desc), C.byref(ts), T, _ptr(workspace), workspace.numel(),
                                    _stream()))
         else:

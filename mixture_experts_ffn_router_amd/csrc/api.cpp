@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstring>
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "kernels.h"
@@ -140,6 +141,7 @@ struct Plan {
   size_t o_logits, o_w, o_ids, o_counts, o_offsets, o_sorted, o_bexp, o_rms, o_r, o_xn1, o_xn2, o_h, o_y,
       o_dh, o_dout, total;
   size_t o_rinfo, o_ypart;  // decode path only
+  size_t path_total;        // bytes the path this call takes lays out (total: the larger of the two)
   int down_splits;
 };
 
@@ -289,6 +291,7 @@ moe_status make_plan(const moe_layer_desc& d, const moe_tensors* t, int64_t T, P
   }
   // The decode path lays out its own (smaller) buffers over the same workspace;
   // the size reported stays that of the grouped path, so it grows with T.
+  p.path_total = p.total;
   p.decode = use_decode(d, T);
   if (p.decode) {
     o = 0;
@@ -299,6 +302,7 @@ moe_status make_plan(const moe_layer_desc& d, const moe_tensors* t, int64_t T, P
     p.o_dout = take(p.dense ? (size_t)T * H * 4 : 0);
     p.down_splits = moe::decode_down_splits((int)T, d.hidden, d.inter, p.dense);
     p.o_ypart = take(p.dense || p.down_splits > 1 || d.block_tail ? (size_t)T * p.down_splits * H * 4 : 0);
+    p.path_total = o;
     if (o > p.total) p.total = o;
   }
   return MOE_OK;
@@ -445,8 +449,11 @@ MOE_API moe_status moe_forward_workspace_layout(const moe_layer_desc* desc, cons
   return MOE_OK;
 }
 
+// noalloc: the workspace is the library's static scratch, sized for the path this
+// call takes, and the dense branch runs on the caller's stream (no side stream or
+// events are created).
 static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t, int64_t T, void* workspace,
-                               size_t workspace_bytes, void* stream, void* const* events) {
+                               size_t workspace_bytes, void* stream, void* const* events, bool noalloc = false) {
   g_err[0] = 0;
   moe_status s = validate_desc(desc);
   if (s != MOE_OK) return s;
@@ -460,8 +467,9 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
   if (s != MOE_OK) return s;
   if (d.weight_dtype == MOE_DT_MXFP4 && !p.decode)
     return fail(MOE_UNSUPPORTED, "mxfp4 expert weights serve the decode path only (T <= 16, rows within its LDS staging)");
-  if (!workspace || workspace_bytes < p.total)
-    return fail(MOE_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, p.total);
+  const size_t need = noalloc ? p.path_total : p.total;
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, need);
   if ((uintptr_t)workspace % ALIGN) return fail(MOE_INVALID_ARG, "workspace must be 256-byte aligned");
 
   hipStream_t st = (hipStream_t)stream;
@@ -617,7 +625,7 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
     return MOE_OK;
   };
   // Overlap the dense branch with the MoE path unless stages are being timed.
-  SideStream* side = p.dense && !events ? side_stream(st) : nullptr;
+  SideStream* side = p.dense && !events && !noalloc ? side_stream(st) : nullptr;
   SideJoin side_join;
 
   STAGE(MOE_STAGE_PRENORM);
@@ -772,6 +780,51 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
 MOE_API moe_status moe_forward(const moe_layer_desc* desc, const moe_tensors* t, int64_t T, void* workspace,
                                size_t workspace_bytes, void* stream) {
   return forward_impl(desc, t, T, workspace, workspace_bytes, stream, nullptr);
+}
+
+// ---- moe_forward for callers that cannot allocate: the workspace is a static
+// device array of MOE_NOALLOC_SCRATCH_BYTES, one copy per GPU, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, never device
+// memory: its device address is looked up once per device with
+// hipGetSymbolAddress and only that address is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+static moe_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(MOE_UNSUPPORTED, "device index %d >= 64", dev);
+  static std::mutex mu;
+  static void* addr[64] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || (uintptr_t)ptr % ALIGN) return fail(MOE_HIP_ERROR, "static scratch at an unusable address");
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_forward_noalloc(const moe_layer_desc* desc, const moe_tensors* t, int64_t T, void* stream) {
+  g_err[0] = 0;
+  moe_status s = validate_desc(desc);
+  if (s != MOE_OK) return s;
+  if ((s = validate_tensors(*desc, t)) != MOE_OK) return s;
+  if (T < 0) return fail(MOE_INVALID_ARG, "T < 0");
+  if (T == 0) return MOE_OK;
+  Plan p;
+  if ((s = make_plan(*desc, t, T, p)) != MOE_OK) return s;
+  if (p.path_total > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_WORKSPACE_TOO_SMALL,
+                "T = %lld needs %zu bytes of scratch; the static scratch holds %zu (call moe_forward with a "
+                "workspace instead)",
+                (long long)T, p.path_total, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((s = scratch_address(&ws)) != MOE_OK) return s;
+  return forward_impl(desc, t, T, ws, MOE_NOALLOC_SCRATCH_BYTES, stream, nullptr, true);
 }
 
 MOE_API moe_status moe_forward_profiled(const moe_layer_desc* desc, const moe_tensors* t, int64_t T,

@@ -157,6 +157,21 @@ def test_forward_rejects_missing_tensors_and_small_workspace():
     assert lib.moe_forward(C.byref(d), C.byref(ts), 0, None, 0, None) == B.MOE_OK
 
 
+def test_noalloc_refuses_large_layouts_before_any_launch():
+    """The no-allocation entry point checks its static scratch's size on the host:
+    a layout beyond it is refused with MOE_WORKSPACE_TOO_SMALL, nothing touched."""
+    lib = _lib()
+    d = _desc(hidden=4096, num_experts=8, top_k=2, inter=14336)
+    st, need = _ws(d, 4096)
+    assert st == B.MOE_OK and need > B.NOALLOC_SCRATCH_BYTES
+    fake = 0x1000
+    ts = B.Tensors(x=fake, w_router=fake, w13=fake, w2=fake, out=fake)
+    assert lib.moe_forward_noalloc(C.byref(d), C.byref(ts), 4096, None) == B.MOE_WORKSPACE_TOO_SMALL
+    assert b"static scratch" in lib.moe_last_error()
+    assert lib.moe_forward_noalloc(C.byref(d), C.byref(ts), 0, None) == B.MOE_OK  # T = 0: a no-op
+    assert lib.moe_forward_noalloc(C.byref(d), None, 16, None) == B.MOE_INVALID_ARG
+
+
 def test_route_and_permute_validation():
     lib = _lib()
     fake = 0x1000

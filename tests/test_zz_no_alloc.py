@@ -1,0 +1,80 @@
+"""moe_forward_noalloc: the entry point for callers that cannot allocate.
+
+It runs the same kernels as moe_forward on the library's static device scratch
+instead of a caller workspace, with the dense branch on the caller's stream.
+Its output must equal moe_forward's bit for bit (the kernels are deterministic),
+on two calls in a row, the second with fewer tokens, so the second call runs on
+scratch the first one left dirty; a call that needs more scratch than there is
+is refused before anything is launched."""
+import ctypes as C
+
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_ffn_router_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mixture_experts_ffn_router_amd import binding
+    binding.load()
+    return binding
+
+
+CASES = {
+    # grouped path with the Gemma dense branch (which moe_forward runs on its side stream)
+    "gemma_grouped": (W.LayerSpec("na_gemma", 333, 256, 16, 4, 128, "gelu_tanh", "bf16", router_mode="gemma",
+                                  per_expert_scale="uniform", I_dense=192, random_gammas=True), 101),
+    # FP8 activations: quantisation buffers in the scratch
+    "w8a8_grouped": (W.LayerSpec("na_w8a8", 300, 256, 16, 4, 192, "gelu_tanh", "fp8", supplied_logits=True,
+                                 act_quant="fp8_dynamic"), 77),
+    # shared experts without renormalisation
+    "shared_grouped": (W.LayerSpec("na_shared", 200, 256, 8, 3, 128, "silu", "bf16", renorm=False, n_shared=2,
+                                   I_shared=128), 37),
+    # 256-row blocks with the down reduction split in parts
+    "ksplit_grouped": (W.LayerSpec("na_ksplit", 2048, 256, 2, 1, 4096, "silu", "bf16"), 1500),
+    # decode path (its own smaller layout in the scratch), with the block tail
+    "gemma_decode": (W.LayerSpec("na_dec", 16, 256, 16, 4, 128, "gelu_tanh", "bf16", router_mode="gemma",
+                                 per_expert_scale="uniform", I_dense=192, random_gammas=True, block_tail=True), 3),
+    # the full-size Gemma-style layer at decode sizes
+    "gemma_full_decode": (W.SPECS["gemma"].with_T(16), 1),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_noalloc_equals_forward_on_two_calls(B, name):
+    spec, t2 = CASES[name]
+    print(f"[noalloc] {name} T={spec.T} then T={t2}", flush=True)
+    L = W.make_layer(spec, seed=3)
+    dl = B.DeviceLayer.from_generated(L)
+    x = dl.t["x"]
+    for T in (spec.T, t2):
+        xs = x[:T].contiguous()
+        lg = None if dl.t["logits"] is None else dl.t["logits"][:T].contiguous()
+        ref, rr = dl.forward(x=xs, logits=lg, want_routing=True)
+        got, rg = dl.forward(x=xs, logits=lg, want_routing=True, noalloc=True)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), f"{name} T={T}: output differs from moe_forward"
+        assert torch.equal(rg["out_f32"], rr["out_f32"])
+        assert torch.equal(rg["topk_ids"], rr["topk_ids"]) and torch.equal(rg["topk_w"], rr["topk_w"])
+
+
+def test_noalloc_refuses_layouts_beyond_its_scratch(B):
+    L = W.make_layer(W.LayerSpec("na_big", 4096, 1024, 8, 2, 4096, "silu", "bf16"), seed=1)
+    dl = B.DeviceLayer.from_generated(L)
+    assert dl.workspace_size(4096) > B.NOALLOC_SCRATCH_BYTES
+    out = torch.full((4096, 1024), 7, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(B.MoEError) as e:
+        dl.forward(out=out, noalloc=True)
+    assert e.value.status == B.MOE_WORKSPACE_TOO_SMALL
+    torch.cuda.synchronize()
+    assert (out == 7).all(), "a refused call launched work"
+    # a smaller batch of the same layer fits
+    ref = dl.forward(x=dl.t["x"][:64].contiguous())
+    got = dl.forward(x=dl.t["x"][:64].contiguous(), noalloc=True)
+    assert torch.equal(got, ref)
