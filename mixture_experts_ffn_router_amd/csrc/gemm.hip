@@ -10,7 +10,8 @@
 // MFMA kernel (v_mfma_f32_32x32x16_bf16; FP8 x FP8: 32x32x64), 4 or 8 waves:
 //   * BM x BN output tile; every operand tile reaches LDS through buffer loads
 //     that write LDS directly (no staging registers), in K tiles of 64.  8 waves
-//     ping-pong over 2 stages (see pingpong_dma64).  4 waves run a software
+//     ping-pong over 2 A stages and (where LDS holds them) 3 B stages, so the
+//     weight tiles stream two K tiles ahead (see pingpong_dma64).  4 waves run a software
 //     pipeline over up to 4 stages: tiles kt+1 .. kt+NS-1 are in flight while
 //     tile kt computes, and the waits are explicit vmcnt counts, so only the
 //     oldest tile is waited for.  Buffer resources bound each operand, so a load
@@ -181,6 +182,12 @@ void gemm_mfma_kernel(GemmArgs p) {
                 "stage must split into 1 KiB DMA instructions over the waves");
   static_assert(!GATED || ((BN / 2) % B_ROWS_PER_DMA == 0), "DMA groups must not straddle gate/up");
   static_assert(NS * STAGE <= 160 * 1024, "LDS");
+  // 8 waves: two A stages and, where LDS holds them, three B stages, so the
+  // weight tile of K tile t+2 streams in while tile t computes (weights come
+  // from HBM, whose latency under load outlasts the two phases a two-stage
+  // ring leaves them); else two B stages.
+  constexpr int NBS = PP ? ((2 * A_BYTES + 3 * B_BYTES <= 160 * 1024) ? 3 : 2) : 0;
+  constexpr int LDS_MAIN = PP ? 2 * A_BYTES + NBS * B_BYTES : NS * STAGE;
   constexpr int NCOLS = GATED ? BN / 2 : BN;  // output columns per block
   constexpr int OESZ = (GATED || EPI == EPI_SCATTER) ? 2 : 4;  // output element bytes
   constexpr int EROWB = NCOLS * OESZ + 4 * OESZ;  // staged output row (padded)
@@ -190,7 +197,7 @@ void gemm_mfma_kernel(GemmArgs p) {
   // store directly)
   constexpr int EPI_LDS = (EPI == EPI_GATED || EPI == EPI_SCATTER_F32) ? 0 : PROWS * EROWB + PROWS * 4;
   static_assert(WAVES_M % EPASS == 0 && EPI_LDS <= 160 * 1024, "epilogue passes of whole wave rows");
-  constexpr int SMEM = NS * STAGE > EPI_LDS ? NS * STAGE : EPI_LDS;
+  constexpr int SMEM = LDS_MAIN > EPI_LDS ? LDS_MAIN : EPI_LDS;
   constexpr int THREADS = 64 * WAVES_M * WAVES_N;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
 
@@ -278,9 +285,7 @@ void gemm_mfma_kernel(GemmArgs p) {
     u32x8 b[TN];
   };
   using Frags = std::conditional_t<A8, Frags8, FragsW>;
-  auto load_frags = [&](int buf, int s, Frags& f) {
-    const uint8_t* sa = smem + buf * STAGE;
-    const uint8_t* sb = sa + A_BYTES;
+  auto load_frags_ab = [&](const uint8_t* sa, const uint8_t* sb, int s, Frags& f) {
     if constexpr (A8) {
       const int c = 4 * s + 2 * hsel;
 #pragma unroll
@@ -315,6 +320,9 @@ void gemm_mfma_kernel(GemmArgs p) {
       f.b[j] = *(const u32x4*)(sb + b_row_off[j] + ((c ^ swb) << 4));
     }
     }
+  };
+  auto load_frags = [&](int buf, int s, Frags& f) {
+    load_frags_ab(smem + buf * STAGE, smem + buf * STAGE + A_BYTES, s, f);
   };
   auto mfmas = [&](const Frags& f) {
     if constexpr (A8) {
@@ -567,9 +575,12 @@ void gemm_mfma_kernel(GemmArgs p) {
         b_soff[i] = (uint32_t)((int64_t)brow * p.Kdim * EB);
       }
     }
-    // this wave's A part / B part of tile kt into stage buf (past the end: zero fill)
+    // this wave's A part / B part of tile kt into A stage abuf / B stage bbuf (past
+    // the end: zero fill).  LDS: A stages [0, 2 A_BYTES), then the B stages.
+    auto a_stage = [&](int buf) { return smem + buf * A_BYTES; };
+    auto b_stage = [&](int buf) { return smem + 2 * A_BYTES + buf * B_BYTES; };
     auto issue_a = [&](int kt, int buf) {
-      uint8_t* sA = smem + buf * STAGE;
+      uint8_t* sA = a_stage(buf);
       const bool live = kt < nk;
       const bool tail = A8 && kt0 + kt == ktail;
 #pragma unroll
@@ -579,7 +590,7 @@ void gemm_mfma_kernel(GemmArgs p) {
       }
     };
     auto issue_b = [&](int kt, int buf) {
-      uint8_t* sB = smem + buf * STAGE + A_BYTES;
+      uint8_t* sB = b_stage(buf);
       const bool live = kt < nk;
       const bool tail = A8 && kt0 + kt == ktail;
 #pragma unroll
@@ -589,35 +600,52 @@ void gemm_mfma_kernel(GemmArgs p) {
               live ? b_soff[i] + (uint32_t)(kt0 + kt) * (uint32_t)B_ROW : 0u);
       }
     };
+    // With three B stages the B tile of K tile t+2 is issued during tile t (its
+    // stage held tile t-1, read for the last time in phase 4t-1), and the waits
+    // leave this wave's BW loads of it in flight; near the end, where it is not
+    // issued, they wait for everything.
+    constexpr int BAHEAD = NBS - 1;        // B tiles issued ahead of the one computing
+    constexpr int BW = NBS == 3 ? BH : 0;  // this wave's B loads left in flight at a wait
     Frags f[2];
     issue_a(0, 0);
     issue_b(0, 0);
+    const bool b1 = NBS == 3 && nk > 1;
+    if (b1) issue_b(1, 1);
     if (grp == 1) {
       issue_a(1, 1);
-      wait_vmcnt<AH>();  // this wave's parts of tile 0
+      if (b1) wait_vmcnt<AH + BW>();  // this wave's parts of tile 0
+      else wait_vmcnt<AH>();
     } else {
-      wait_vmcnt<0>();
+      if (b1) wait_vmcnt<BW>();
+      else wait_vmcnt<0>();
     }
     phase_barrier();
     if (grp == 1) phase_barrier();
     constexpr int SPH = A8 ? 1 : BK / (FP8 ? 32 : 16) / 2;  // sub-steps per half tile
+    int bs = 0;  // B stage of tile t (t % NBS)
     for (int t = 0; t < nk; ++t) {
       const int st = t & 1;
+      const int bnext = bs + BAHEAD >= NBS ? bs + BAHEAD - NBS : bs + BAHEAD;  // B stage of tile t + BAHEAD
+      const bool bfar = t + BAHEAD < nk;  // B of tile t + BAHEAD is issued this tile
+      const uint8_t* sa = a_stage(st);
+      const uint8_t* sb = b_stage(bs);
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         // memory phase: fragment reads first, so they do not queue behind the
         // DMA's LDS writes
         if constexpr (LIVE) {
 #pragma unroll
-          for (int q = 0; q < SPH; ++q) load_frags(st, SPH * hh + q, f[q]);
+          for (int q = 0; q < SPH; ++q) load_frags_ab(sa, sb, SPH * hh + q, f[q]);
         }
-        if (hh == 0 && t + 1 < nk) {
-          if (grp == 0) issue_a(t + 1, st ^ 1);  // group 1's rows of tile t+1
-          issue_b(t + 1, st ^ 1);                // this group's half of the B rows
+        if (hh == 0) {
+          if (grp == 0 && t + 1 < nk) issue_a(t + 1, st ^ 1);  // group 1's rows of tile t+1
+          if (bfar) issue_b(t + BAHEAD, bnext);                 // this group's half of the B rows
         }
         wait_lgkmcnt0();
         if (hh == 1 && grp == 1) {
-          wait_vmcnt<0>();                     // own parts of tile t+1 have landed
+          // own parts of tile t+1 have landed
+          if (NBS == 3 && bfar) wait_vmcnt<BW>();
+          else wait_vmcnt<0>();
           if (t + 2 < nk) issue_a(t + 2, st);  // group 0's rows of tile t: read for the last time in phase 4t+2
         }
         phase_barrier();
@@ -626,9 +654,13 @@ void gemm_mfma_kernel(GemmArgs p) {
 #pragma unroll
           for (int q = 0; q < SPH; ++q) mfmas(f[q]);
         }
-        if (hh == 1 && grp == 0) wait_vmcnt<0>();  // own parts of tile t+1 have landed
+        if (hh == 1 && grp == 0) {  // own parts of tile t+1 have landed
+          if (NBS == 3 && bfar) wait_vmcnt<BW>();
+          else wait_vmcnt<0>();
+        }
         phase_barrier();
       }
+      bs = bs + 1 == NBS ? 0 : bs + 1;
     }
     if (grp == 0) phase_barrier();  // same barrier count in both groups
   };
