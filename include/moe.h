@@ -59,6 +59,13 @@ typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_scoring;
 /* Activation quantisation of the routed experts' GEMM inputs ([SG]: the
  * "FP8-Dynamic" checkpoints quantise activations at run time, per token). */
 typedef enum { MOE_ACT_QUANT_NONE = 0, MOE_ACT_QUANT_FP8_DYNAMIC = 1 } moe_act_quant;
+/* The weighted combine ([G4] section 7: a weighted scatter-add of the expert
+ * outputs into their tokens' rows).  SLOT_ORDER: each (token, slot) row is
+ * stored and a token's rows are summed in slot order: deterministic, bit for
+ * bit.  ATOMIC: the down GEMM adds each weighted row (every part of a split
+ * reduction) into its token's fp32 row with float atomics: less memory
+ * traffic, but the summation order, and so the last bits, vary between runs. */
+typedef enum { MOE_COMBINE_SLOT_ORDER = 0, MOE_COMBINE_ATOMIC = 1 } moe_combine;
 
 /* Human-readable name of a status code (static storage). */
 const char* moe_status_string(moe_status s);
@@ -165,6 +172,8 @@ typedef struct {
                             and inter <= 16384; the dense branch stays bf16 (see moe_forward) */
   int32_t block_tail;    /* 1: also the FFN block's tail, out = x + RMSNorm(out) * gamma_post_ff
                             ([G4] section 1); 0: the layer output alone */
+  int32_t combine;       /* moe_combine, grouped bf16 path: how a token's weighted expert outputs
+                            are summed (the decode path sums in its accumulators either way) */
 } moe_layer_desc;
 
 /* Tensors of one forward call (device pointers unless noted).  The matrix
@@ -304,7 +313,9 @@ int32_t moe_decode_dense_gate_up_stage(const moe_layer_desc* desc, int64_t T);
  *   h                 [capacity, I] act dtype: the gated intermediate per padded row
  *   y                 [T * slots_per_token * y_parts, H] (fp32 when y_f32, else act
  *                     dtype): row (slot * y_parts + part) holds the routing-weighted
- *                     expert output of flat slot `slot`, summed over the parts
+ *                     expert output of flat slot `slot`, summed over the parts;
+ *                     with the atomic combine y_parts is 0 and y is [T, H] fp32,
+ *                     each token's combined MoE row
  *   x_codes [T, H] u8, x_scales [T] fp32, h_codes [capacity, I] u8,
  *   h_scales [capacity] fp32: FP8 activations (E4M3 codes, per-row scales) */
 typedef struct {

@@ -40,7 +40,9 @@ class LayerDesc(C.Structure):
                 ("weight_dtype", C.c_int32), ("renormalize", C.c_int32), ("router_mode", C.c_int32),
                 ("n_shared", C.c_int32), ("inter_dense", C.c_int32), ("dense_act", C.c_int32),
                 ("eps", C.c_float), ("scoring", C.c_int32), ("n_groups", C.c_int32),
-                ("topk_groups", C.c_int32), ("act_quant", C.c_int32), ("block_tail", C.c_int32)]
+                ("topk_groups", C.c_int32), ("act_quant", C.c_int32), ("block_tail", C.c_int32),
+                ("combine", C.c_int32)]
+COMBINE = {"slot_order": 0, "atomic": 1}
 
 
 class Tensors(C.Structure):
@@ -204,8 +206,9 @@ class DeviceLayer:
         return torch.float32 if self.desc.act_dtype == DT_F32 else torch.bfloat16
 
     @classmethod
-    def from_generated(cls, L: dict, device="cuda", eps: float = 1e-6):
-        """Build from a workloads.make_layer() dict (CPU tensors in storage dtypes)."""
+    def from_generated(cls, L: dict, device="cuda", eps: float = 1e-6, combine: str = "slot_order"):
+        """Build from a workloads.make_layer() dict (CPU tensors in storage dtypes).
+        combine: "slot_order" (deterministic) or "atomic" (moe_combine)."""
         spec = L["spec"]
         f32 = spec.wdtype == "fp32"
         desc = LayerDesc(hidden=spec.H, num_experts=spec.E, top_k=spec.K, inter=spec.I,
@@ -216,7 +219,7 @@ class DeviceLayer:
                          n_shared=spec.n_shared, inter_dense=spec.I_dense, dense_act=ACT[spec.act],
                          eps=eps, scoring=SCORING[spec.scoring], n_groups=spec.n_groups,
                          topk_groups=spec.topk_groups, act_quant=ACT_QUANT[spec.act_quant],
-                         block_tail=int(spec.block_tail))
+                         block_tail=int(spec.block_tail), combine=COMBINE[combine])
 
         def d(t):
             return None if t is None else t.to(device, non_blocking=False).contiguous()
@@ -338,6 +341,6 @@ class DeviceLayer:
             inv_rms=view(lay.inv_rms, torch.float32, (T,)),
             x_expert=view(lay.x_expert, act, (T, H)),
             h=view(lay.h, act, (cap, I)),
-            y=view(lay.y, ydt, (T * kp * lay.y_parts, H)),
+            y=view(lay.y, ydt, (T, H) if lay.y_parts == 0 else (T * kp * lay.y_parts, H)),
             x_codes=view(lay.x_codes, torch.uint8, (T, H)), x_scales=view(lay.x_scales, torch.float32, (T,)),
             h_codes=view(lay.h_codes, torch.uint8, (cap, I)), h_scales=view(lay.h_scales, torch.float32, (cap,)))

@@ -135,6 +135,7 @@ struct Plan {
   bool need_logits, need_prenorm, gemma_router, dense;
   bool mat_r, mat_xn1, mat_xn2;  // normalised rows that must be materialised (learned weight present)
   bool y_f32;                    // per-slot expert outputs kept in fp32
+  bool atomic;                   // atomic combine: y is one fp32 row per token
   bool aq;                       // FP8 activations: x and h quantised per row
   size_t o_xq, o_xs, o_hq, o_hs;  // their codes and scales
   size_t o_slotrow;  // inverse map of the permutation (slot -> padded row)
@@ -196,6 +197,10 @@ moe_status validate_desc(const moe_layer_desc* d) {
     return fail(MOE_INVALID_ARG, "unknown router mode %d", d->router_mode);
   if (!(d->eps >= 0.f)) return fail(MOE_INVALID_ARG, "eps must be >= 0");
   if (d->block_tail != 0 && d->block_tail != 1) return fail(MOE_INVALID_ARG, "block_tail must be 0 or 1");
+  if (d->combine != MOE_COMBINE_SLOT_ORDER && d->combine != MOE_COMBINE_ATOMIC)
+    return fail(MOE_INVALID_ARG, "unknown combine %d", d->combine);
+  if (d->combine == MOE_COMBINE_ATOMIC && d->act_dtype == MOE_DT_F32)
+    return fail(MOE_UNSUPPORTED, "the atomic combine serves bf16 layers");
   if (d->act_quant != MOE_ACT_QUANT_NONE && d->act_quant != MOE_ACT_QUANT_FP8_DYNAMIC)
     return fail(MOE_INVALID_ARG, "unknown act_quant %d", d->act_quant);
   if (d->act_quant) {
@@ -244,6 +249,7 @@ moe_status make_plan(const moe_layer_desc& d, const moe_tensors* t, int64_t T, P
   // With the dense branch the MoE sum is RMS-normalised afterwards, which turns
   // its relative error into error at output scale: keep the per-slot rows fp32.
   p.y_f32 = p.f32 || p.dense;
+  p.atomic = d.combine == MOE_COMBINE_ATOMIC;
   // Split the down GEMM's reduction when its tiles would fill the CUs in few
   // rounds (long reductions over few rows: the Mixtral-style layer); rows are
   // estimated with half a block of padding per expert.
@@ -272,7 +278,7 @@ moe_status make_plan(const moe_layer_desc& d, const moe_tensors* t, int64_t T, P
   p.o_xn1 = take(p.mat_xn1 ? (size_t)T * H * ae : 0);
   p.o_xn2 = take(p.mat_xn2 ? (size_t)T * H * ae : 0);
   p.o_h = take((size_t)p.cap * d.inter * ae);
-  p.o_y = take((size_t)slots * ks_room * H * (p.y_f32 ? 4 : ae));
+  p.o_y = take(p.atomic ? (size_t)T * H * 4 : (size_t)slots * ks_room * H * (p.y_f32 ? 4 : ae));
   p.o_dh = take(p.dense ? (size_t)T * d.inter_dense * ae : 0);
   p.o_dout = take(p.dense ? (size_t)T * H * 4 : 0);
   p.o_xq = take(p.aq ? (size_t)T * H : 0);
@@ -426,8 +432,8 @@ MOE_API moe_status moe_forward_workspace_layout(const moe_layer_desc* desc, cons
   L.path = p.decode ? MOE_PATH_DECODE : MOE_PATH_GROUPED;
   L.block_m = p.bm;
   L.slots_per_token = p.Kp;
-  L.y_parts = p.ks;
-  L.y_f32 = p.y_f32;
+  L.y_parts = p.atomic ? 0 : p.ks;
+  L.y_f32 = p.y_f32 || p.atomic;
   L.capacity = p.cap;
   auto off = [&](bool has, size_t o) { return (!p.decode && has) ? (int64_t)o : (int64_t)-1; };
   L.topk_w = off(true, p.o_w);
@@ -729,6 +735,7 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
     HIP_TRY(moe::launch_quant_rows_fp8(h, p.cap, I, I, sorted, offsets + p.Ep, hq, I, hs, st),
             "h quantisation launch");
   STAGE(MOE_STAGE_DOWN);
+  if (p.atomic) HIP_TRY(moe::launch_zero(y, (size_t)T * H * 4, st), "zero fill launch");
   {
     moe::GemmArgs a{};
     a.A = p.aq ? (const void*)hq : h;
@@ -752,8 +759,10 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
     a.c_rows = sorted;
     a.row_weight = w;
     a.k_splits = p.ks;
-    HIP_TRY(gemm(a, (p.y_f32 && !p.f32) ? moe::EPI_SCATTER_F32 : moe::EPI_SCATTER, b_elem, p.bm),
-            "down gemm launch");
+    a.row_div = p.Kp;  // atomic combine: a slot's token
+    const int epi = p.atomic ? moe::EPI_SCATTER_ATOMIC
+                             : ((p.y_f32 && !p.f32) ? moe::EPI_SCATTER_F32 : moe::EPI_SCATTER);
+    HIP_TRY(gemm(a, epi, b_elem, p.bm), "down gemm launch");
   }
   STAGE(MOE_STAGE_DENSE_GATE_UP);
   // 7. parallel dense MLP (Gemma), here when it did not run on the side stream
@@ -766,7 +775,8 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
   HIP_TRY(side_join.join(), "join of the dense branch");
   STAGE(MOE_STAGE_FINALIZE);
   // 8. per-token combine in slot order (+ Gemma post-norms and branch sum)
-  HIP_TRY(moe::launch_finalize(y, p.y_f32 ? moe::ELEM_F32 : act_elem, p.Kp * p.ks, dout, t->gamma_post1, t->gamma_post2, d.eps, t->out, act_elem,
+  HIP_TRY(moe::launch_finalize(y, p.y_f32 || p.atomic ? moe::ELEM_F32 : act_elem, p.atomic ? 1 : p.Kp * p.ks, dout,
+                               t->gamma_post1, t->gamma_post2, d.eps, t->out, act_elem,
                                t->out_f32, T, H, st, d.block_tail ? t->x : nullptr, t->gamma_post_ff),
           "finalize launch");
   // 9. optional copies of the routing result

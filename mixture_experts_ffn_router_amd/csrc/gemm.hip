@@ -36,6 +36,9 @@
 //     per-token sum happens in the finalize kernel in slot order.  The bf16
 //     scatter and the fp32 store epilogues stage the tile in LDS and copy whole
 //     rows out with 16-byte stores on consecutive lanes.
+//   * Atomic scatter epilogue (the weighted scatter-add combine): the staged
+//     rows are added into their token's fp32 row with float atomics, every
+//     reduction part into the same row; the sum order then varies between runs.
 //   * FP8 B (OCP E4M3 codes, W8A16): B rows are 64 bytes in LDS, widened to bf16
 //     in registers (exact), and the per-output-channel scale is applied in the
 //     epilogue: sum_k x_k (q_kn s_n) = s_n sum_k x_k q_kn.
@@ -688,7 +691,7 @@ void gemm_mfma_kernel(GemmArgs p) {
       }
       rs = p.row_scale[tok];
     }
-    if constexpr (EPI == EPI_SCATTER || EPI == EPI_SCATTER_F32) {
+    if constexpr (EPI == EPI_SCATTER || EPI == EPI_SCATTER_F32 || EPI == EPI_SCATTER_ATOMIC) {
       const int slot = p.c_rows[grow];
       rs *= (slot >= 0 && p.row_weight) ? p.row_weight[slot] : 1.f;  // (x the A row's scale, if any)
     } else if constexpr (EPI == EPI_STORE_F32) {
@@ -722,6 +725,9 @@ void gemm_mfma_kernel(GemmArgs p) {
     else if constexpr (EPI == EPI_SCATTER || EPI == EPI_SCATTER_F32) {
       const int slot = p.c_rows[grow];
       return slot < 0 ? -1 : (int64_t)slot * KS + ks;  // the part's row of this slot
+    } else if constexpr (EPI == EPI_SCATTER_ATOMIC) {
+      const int slot = p.c_rows[grow];
+      return slot < 0 ? -1 : (int64_t)(slot / p.row_div);  // the slot's token: every part adds to it
     } else {
       return (int64_t)ks * p.M + grow;  // part ks's plane of [KS, M, ldc]
     }
@@ -733,7 +739,7 @@ void gemm_mfma_kernel(GemmArgs p) {
   // (E columns).  The gated and fp32 scatter epilogues store directly (8 / 16
   // bytes per lane, 16 / 32 contiguous bytes per row): staging them measured
   // no faster.
-  bool staged = EPI == EPI_SCATTER || EPI == EPI_STORE_F32;
+  bool staged = EPI == EPI_SCATTER || EPI == EPI_STORE_F32 || EPI == EPI_SCATTER_ATOMIC;
   if constexpr (EPI == EPI_STORE_F32 && !PP)
     staged = (p.N % CPL) == 0 && (p.ldc % CPL) == 0 && (((uintptr_t)p.C & 15) == 0);
   if (staged) {
@@ -777,13 +783,26 @@ void gemm_mfma_kernel(GemmArgs p) {
       int32_t* s_orow = (int32_t*)(smem + PROWS * EROWB);
       for (int r = tid; r < PROWS; r += THREADS) s_orow[r] = (int32_t)out_row(m0 + pass * PROWS + r);
       __syncthreads();
-      constexpr int CHR = NCOLS * OESZ / 16;  // 16-byte chunks per row
-      for (int idx = tid; idx < PROWS * CHR; idx += THREADS) {
-        const int r = idx / CHR, c = idx - r * CHR;
-        const int col = n0 + c * CPL;
-        const int32_t orow = s_orow[r];
-        if (orow < 0 || col >= p.N) continue;
-        *(uint4*)((uint8_t*)p.C + ((int64_t)orow * p.ldc + col) * OESZ) = *(const uint4*)(smem + r * EROWB + c * 16);
+      if constexpr (EPI == EPI_SCATTER_ATOMIC) {
+        // weighted rows added into their token's fp32 row: one element per lane,
+        // consecutive lanes on consecutive columns (an instruction covers 256
+        // contiguous bytes of one row)
+        for (int idx = tid; idx < PROWS * NCOLS; idx += THREADS) {
+          const int r = idx / NCOLS, c = idx - r * NCOLS;
+          const int col = n0 + c;
+          const int32_t orow = s_orow[r];
+          if (orow < 0 || col >= p.N) continue;
+          unsafeAtomicAdd((float*)p.C + (int64_t)orow * p.ldc + col, *(const float*)(smem + r * EROWB + c * 4));
+        }
+      } else {
+        constexpr int CHR = NCOLS * OESZ / 16;  // 16-byte chunks per row
+        for (int idx = tid; idx < PROWS * CHR; idx += THREADS) {
+          const int r = idx / CHR, c = idx - r * CHR;
+          const int col = n0 + c * CPL;
+          const int32_t orow = s_orow[r];
+          if (orow < 0 || col >= p.N) continue;
+          *(uint4*)((uint8_t*)p.C + ((int64_t)orow * p.ldc + col) * OESZ) = *(const uint4*)(smem + r * EROWB + c * 16);
+        }
       }
     }
   } else if constexpr (GATED) {
@@ -1096,10 +1115,12 @@ hipError_t launch_gemm_mfma(const GemmArgs& a, int epi, int belem, int block_m, 
     if (block_m == 256) {
       if (epi == EPI_GATED) return run_mfma<256, 256, 4, 2, EPI_GATED, ELEM_FP8X8>(a, s);
       if (epi == EPI_SCATTER) return run_mfma<256, 256, 4, 2, EPI_SCATTER, ELEM_FP8X8>(a, s);
+      if (epi == EPI_SCATTER_ATOMIC) return run_mfma<256, 256, 4, 2, EPI_SCATTER_ATOMIC, ELEM_FP8X8>(a, s);
       return run_mfma<256, 256, 4, 2, EPI_SCATTER_F32, ELEM_FP8X8>(a, s);
     }
     if (epi == EPI_GATED) return run_mfma<128, 512, 2, 4, EPI_GATED, ELEM_FP8X8>(a, s);
     if (epi == EPI_SCATTER) return run_mfma<128, 512, 2, 4, EPI_SCATTER, ELEM_FP8X8>(a, s);
+    if (epi == EPI_SCATTER_ATOMIC) return run_mfma<128, 512, 2, 4, EPI_SCATTER_ATOMIC, ELEM_FP8X8>(a, s);
     return run_mfma<128, 512, 2, 4, EPI_SCATTER_F32, ELEM_FP8X8>(a, s);
   }
   if (epi == EPI_GATED)
@@ -1108,6 +1129,9 @@ hipError_t launch_gemm_mfma(const GemmArgs& a, int epi, int belem, int block_m, 
   if (epi == EPI_SCATTER_F32)
     return belem == ELEM_FP8 ? run_grouped<EPI_SCATTER_F32, ELEM_FP8>(a, block_m, s)
                              : run_grouped<EPI_SCATTER_F32, ELEM_BF16>(a, block_m, s);
+  if (epi == EPI_SCATTER_ATOMIC)
+    return belem == ELEM_FP8 ? run_grouped<EPI_SCATTER_ATOMIC, ELEM_FP8>(a, block_m, s)
+                             : run_grouped<EPI_SCATTER_ATOMIC, ELEM_BF16>(a, block_m, s);
   return belem == ELEM_FP8 ? run_grouped<EPI_SCATTER, ELEM_FP8>(a, block_m, s)
                            : run_grouped<EPI_SCATTER, ELEM_BF16>(a, block_m, s);
 }

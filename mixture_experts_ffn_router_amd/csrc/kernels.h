@@ -33,7 +33,9 @@ hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int bm_log2, int
 // Compute units of the current device (256 when it cannot be queried).
 int device_cu_count();
 
-enum GemmEpi { EPI_GATED = 0, EPI_SCATTER = 1, EPI_STORE_F32 = 2, EPI_SCATTER_F32 = 3 };
+// EPI_SCATTER_ATOMIC: fp32 atomic add of each weighted row into row c_rows[r] / row_div
+// of C (the slot's token), every reduction part into the same row.
+enum GemmEpi { EPI_GATED = 0, EPI_SCATTER = 1, EPI_STORE_F32 = 2, EPI_SCATTER_F32 = 3, EPI_SCATTER_ATOMIC = 4 };
 // B element type; ELEM_FP8X8: A and B both FP8 (E4M3), the per-row A scale in row_scale
 enum GemmElem { ELEM_F32 = 0, ELEM_BF16 = 1, ELEM_FP8 = 2, ELEM_FP8X8 = 3 };
 
@@ -105,6 +107,9 @@ hipError_t launch_finalize(const void* ybuf, int yelem, int Kp, const float* den
                            const float* gamma_post1, const float* gamma_post2, float eps, void* out,
                            int oelem, float* out_f32, int64_t T, int H, hipStream_t s,
                            const void* resid = nullptr, const float* gamma_post_ff = nullptr);
+
+// bytes of zeros at p (16-byte aligned, a multiple of 16)
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
 hipError_t launch_gather_topk(const float* w_in, const int32_t* ids_in, int in_stride, int K, int64_t T,
                               float* w_out, int32_t* ids_out, hipStream_t s);

@@ -282,4 +282,21 @@ hipError_t launch_gather_topk(const float* w_in, const int32_t* ids_in, int in_s
   return hipGetLastError();
 }
 
+// Zero fill (the atomic combine's fp32 sums start from zero): 16 bytes per lane,
+// a grid-stride loop over a few blocks per CU.
+__global__ __launch_bounds__(256) void zero_kernel(uint4* __restrict__ p, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return hipSuccess;
+  if (bytes % 16 || ((uintptr_t)p & 15)) return hipErrorInvalidValue;
+  const int64_t n16 = (int64_t)(bytes / 16);
+  int64_t blocks = (n16 + 255) / 256;
+  if (blocks > 4 * 256) blocks = 4 * 256;
+  zero_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>((uint4*)p, n16);
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -22,7 +22,8 @@
 //            sorted_slots[pos] = f and slot_row[f] = pos with
 //            pos = offsets[e] + (equal ids in earlier chunks) + rank.
 // Only block b reads or writes slot_row[b*CHUNK, (b+1)*CHUNK) between the
-// launches' boundaries, so the reuse is race-free.
+// launches' boundaries, so the reuse is race-free.  Up to 16384 slots with few
+// experts, one block takes the three steps in one launch instead.
 #include "common.h"
 #include "kernels.h"
 
@@ -38,6 +39,21 @@ __device__ __forceinline__ int chunk_id(const int32_t* __restrict__ ids, int64_t
   if (f >= n) return -1;
   const int e = ids[f];
   return (e >= 0 && e < E) ? e : -1;  // ids outside [0, E) belong to no segment
+}
+
+// Lanes of this wave holding the same id as this lane: one ballot per bit of
+// the id (ids < 1024) and one for validity, so invalid lanes (-1) form their
+// own group.
+__device__ __forceinline__ uint64_t wave_match(int e) {
+  uint64_t same = __ballot(e >= 0);
+  if (e < 0) same = ~same;
+#pragma unroll
+  for (int bit = 0; bit < 10; ++bit) {
+    const bool v = (e >> bit) & 1;
+    const uint64_t bal = __ballot(v);
+    same &= v ? bal : ~bal;
+  }
+  return same;
 }
 
 // Block-wide exclusive scan of one int per thread (1024 threads); returns the
@@ -74,10 +90,15 @@ __global__ __launch_bounds__(PT) void permute_hist_kernel(const int32_t* __restr
   for (int e = tid; e < E; e += PT) s_hist[e] = 0;
   __syncthreads();
   const int64_t f0 = (int64_t)b * CHUNK;
+  int e_r[ROUNDS];  // every id load in flight before the first is used
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) e_r[r] = chunk_id(ids, n, f0 + r * PT + tid, E);
+  const uint64_t lt = (1ull << (tid & 63)) - 1ull;
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {
-    const int e = chunk_id(ids, n, f0 + r * PT + tid, E);
-    if (e >= 0) atomicAdd(&s_hist[e], 1);  // a sum: the order of the adds does not matter
+    // one add per distinct id of the wave (a sum: the order of the adds does not matter)
+    const uint64_t same = wave_match(e_r[r]);
+    if (e_r[r] >= 0 && (same & lt) == 0) atomicAdd(&s_hist[e_r[r]], __popcll(same));
   }
   __syncthreads();
   const bool full = f0 + CHUNK <= n;
@@ -172,24 +193,18 @@ __global__ __launch_bounds__(PT) void permute_scatter_kernel(const int32_t* __re
     // the ragged last chunk: equal ids in earlier chunks = counts[e] - this chunk's
     for (int e = tid; e < E; e += PT) s_base[e] = offsets[e] + counts[e];
     __syncthreads();
+    const uint64_t lt0 = (1ull << lane) - 1ull;
 #pragma unroll
-    for (int r = 0; r < ROUNDS; ++r)
-      if (e_r[r] >= 0) atomicSub(&s_base[e_r[r]], 1);  // a count: the order does not matter
+    for (int r = 0; r < ROUNDS; ++r) {  // a count: the order does not matter
+      const uint64_t same = wave_match(e_r[r]);
+      if (e_r[r] >= 0 && (same & lt0) == 0) atomicSub(&s_base[e_r[r]], __popcll(same));
+    }
   }
   const uint64_t lt = (1ull << lane) - 1ull;
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {
     const int e = e_r[r];
-    // lanes of this wave holding the same id: one ballot per bit of the id (and
-    // one for validity, so invalid lanes form their own group)
-    uint64_t same = __ballot(e >= 0);
-    if (e < 0) same = ~same;
-#pragma unroll
-    for (int bit = 0; bit < 10; ++bit) {
-      const bool v = (e >> bit) & 1;
-      const uint64_t bal = __ballot(v);
-      same &= v ? bal : ~bal;
-    }
+    const uint64_t same = wave_match(e);
     for (int i = tid; i < PW * E; i += PT) s_wcnt[i] = 0;
     __syncthreads();  // zeroed; also: the previous round's reads of s_base are done
     const bool leader = (same & lt) == 0;
@@ -220,12 +235,108 @@ __global__ __launch_bounds__(PT) void permute_scatter_kernel(const int32_t* __re
   }
 }
 
-int permute_chunk() { return CHUNK; }
+// Up to SMALL_N slots with few experts: the three steps in one block and one
+// launch (the launches cost more than the work), in two passes over the ids
+// held in registers.  Pass 1 ranks each id inside its wave and records every
+// (round, wave)'s count per expert in an LDS table; one thread per expert turns
+// its column into exclusive prefixes (round-major, then wave) and its count;
+// pass 2 places each id at offsets[e] + its (round, wave) prefix + its rank.
+// Round r covers slots [1024 r, 1024 (r + 1)), thread tid slot 1024 r + tid.
+constexpr int SMALL_ROUNDS = 16;
+constexpr int64_t SMALL_N = (int64_t)SMALL_ROUNDS * PT;  // 16384
+constexpr int SMALL_TABLE = 32768;                       // uint16 table entries: rounds x waves x E
+
+__global__ __launch_bounds__(PT) void permute_small_kernel(const int32_t* __restrict__ ids, int64_t n, int E,
+                                                           int bm_log2, int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ sorted_slots,
+                                                           int32_t* __restrict__ block_expert,
+                                                           int32_t* __restrict__ num_padded,
+                                                           int32_t* __restrict__ slot_row) {
+  __shared__ uint16_t s_tab[SMALL_TABLE];  // [round][wave][E]: counts, then exclusive prefixes
+  __shared__ int s_off[1025];
+  __shared__ int s_cnt[1024];
+  __shared__ int s_w[PW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bm = 1 << bm_log2;
+  const int rounds = (int)((n + PT - 1) / PT);
+  const int ncell = rounds * PW * E;
+  int e_r[SMALL_ROUNDS];  // every id of the call, all loads in flight at once
+#pragma unroll
+  for (int r = 0; r < SMALL_ROUNDS; ++r) e_r[r] = chunk_id(ids, n, (int64_t)r * PT + tid, E);
+  for (int i = tid; i < ncell; i += PT) s_tab[i] = 0;
+  __syncthreads();
+  const uint64_t lt = (1ull << lane) - 1ull;
+  int rank[SMALL_ROUNDS];
+#pragma unroll
+  for (int r = 0; r < SMALL_ROUNDS; ++r) {
+    rank[r] = 0;
+    if (r < rounds) {  // uniform
+      const uint64_t same = wave_match(e_r[r]);
+      rank[r] = __popcll(same & lt);
+      if (e_r[r] >= 0 && rank[r] == 0) s_tab[(r * PW + wave) * E + e_r[r]] = (uint16_t)__popcll(same);
+    }
+  }
+  __syncthreads();
+  int cnt = 0;
+  if (tid < E) {
+    for (int c = 0; c < rounds * PW; ++c) {
+      const int v = s_tab[c * E + tid];
+      s_tab[c * E + tid] = (uint16_t)cnt;  // < 16384: fits
+      cnt += v;
+    }
+  }
+  const int padded = ((cnt + bm - 1) >> bm_log2) << bm_log2;
+  int total = 0;
+  const int start = block_excl_scan(tid < E ? padded : 0, s_w, &total);
+  if (tid < E) {
+    counts[tid] = cnt;
+    offsets[tid] = start;
+    s_off[tid] = start;
+    s_cnt[tid] = cnt;
+  }
+  if (tid == 0) {
+    offsets[E] = total;
+    s_off[E] = total;
+    if (num_padded) *num_padded = total;
+  }
+  __syncthreads();
+  const int nblk = total >> bm_log2;
+  for (int j = tid; j < nblk; j += PT) {
+    const int row = j << bm_log2;
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[mid] <= row) lo = mid;
+      else hi = mid - 1;
+    }
+    block_expert[j] = lo;
+    const int pad0 = s_off[lo] + s_cnt[lo];
+    for (int q = row > pad0 ? row : pad0; q < row + bm; ++q) sorted_slots[q] = -1;
+  }
+#pragma unroll
+  for (int r = 0; r < SMALL_ROUNDS; ++r) {
+    const int64_t f = (int64_t)r * PT + tid;
+    if (r < rounds && f < n) {
+      int pos = -1;
+      if (e_r[r] >= 0) {
+        pos = s_off[e_r[r]] + s_tab[(r * PW + wave) * E + e_r[r]] + rank[r];
+        sorted_slots[pos] = (int32_t)f;
+      }
+      slot_row[f] = pos;
+    }
+  }
+}
 
 hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int bm_log2, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_slots, int32_t* block_expert, int32_t* num_padded,
                           int32_t* slot_row, hipStream_t s) {
   if (E < 1 || E > 1024) return hipErrorInvalidValue;
+  if (n <= SMALL_N && ((n + PT - 1) / PT) * PW * E <= SMALL_TABLE) {
+    permute_small_kernel<<<1, PT, 0, s>>>(ids, n, E, bm_log2, counts, offsets, sorted_slots, block_expert,
+                                          num_padded, slot_row);
+    return hipGetLastError();
+  }
   const int64_t nchunks = (n + CHUNK - 1) / CHUNK;
   if (nchunks > 0) {
     permute_hist_kernel<<<(unsigned)nchunks, PT, E * sizeof(int), s>>>(ids, n, E, slot_row, counts);

@@ -115,22 +115,28 @@ def staged_fp8_act_check(L, r, rows, ref):
     assert np.array_equal(hs_gpu, hs), "h scales"
     # down projection and routing weight of each slot, on the GPU's h codes
     yp = ws["y_parts"]
-    y_rows = torch.from_numpy((slot[:, None] * yp + np.arange(yp)[None, :]).reshape(-1)).cuda().long()
-    y_parts = to64(ws["y"][y_rows].float()).reshape(len(slot), yp, H)
-    y_gpu = y_parts.sum(axis=1)
+    if yp:
+        y_rows = torch.from_numpy((slot[:, None] * yp + np.arange(yp)[None, :]).reshape(-1)).cuda().long()
+        y_parts = to64(ws["y"][y_rows].float()).reshape(len(slot), yp, H)
+        y_gpu = y_parts.sum(axis=1)
     hdq = O.decode_e4m3fn(hc) * hs.astype(np.float64)[:, None]
-    y_ref = np.empty_like(y_gpu)
-    ymag = np.empty_like(y_gpu)
+    y_ref = np.empty((len(slot), H))
+    ymag = np.empty((len(slot), H))
     for e in np.unique(exp_of):
         n = np.nonzero(exp_of == e)[0]
         W2 = O._expert_weight(layer["w2"], layer.get("w2_scale"), e)
         wn = ref["weights"][tok[n], sl[n]][:, None]
         y_ref[n] = wn * (hdq[n] @ W2.T)
         ymag[n] = np.abs(wn) * (np.abs(hdq[n]) @ np.abs(W2).T)
+    if not yp:
+        # the atomic combine keeps one fp32 row per token: compare the slots' sums
+        K_ = len(slot) // len(rows)
+        y_ref, ymag = y_ref.reshape(len(rows), K_, H).sum(1), ymag.reshape(len(rows), K_, H).sum(1)
+        y_gpu = to64(ws["y"][torch.from_numpy(rows).cuda().long()])
     ma, rr, mx = errors(y_gpu, y_ref)
     # stored in bf16 without a dense branch: one rounding of each part's row (at
     # most half a step of the stored part each)
-    ystep = _bf16_ulp(y_parts).sum(axis=1) / 2 if not ws["y_f32"] else 0.0
+    ystep = _bf16_ulp(y_parts).sum(axis=1) / 2 if yp and not ws["y_f32"] else 0.0
     yover = np.maximum(np.abs(y_gpu - y_ref) - ystep, 0) / np.maximum(ymag, 1e-300)
     print(f"  down: max-abs {ma:.3e} (max {mx:.3f}) rel-RMS {rr:.3e}; beyond storage rounding at most "
           f"{yover.max():.3e} of the accumulation magnitude", flush=True)
@@ -146,9 +152,9 @@ def staged_fp8_act_check(L, r, rows, ref):
                        h_fp8=(codes, scales))
 
 
-def run_and_check(B, L, rows=None, check_logits=True):
+def run_and_check(B, L, rows=None, check_logits=True, combine="slot_order"):
     spec = L["spec"]
-    dl = B.DeviceLayer.from_generated(L)
+    dl = B.DeviceLayer.from_generated(L, combine=combine)
     staged = bool(spec.act_quant)
     out, r = dl.forward(want_routing=True, want_intermediates=staged)
     torch.cuda.synchronize()
@@ -286,6 +292,18 @@ def test_small_layers_every_element(B, name):
     run_and_check(B, L)
 
 
+ATOMIC = ["bf16_ragged_bm64", "bf16_bm256_down_split", "gemma_small", "gemma_dense_bm256", "deepseek_small",
+          "fp8_small", "fp8_small_bm256", "w8a8_small", "gemma_w8a8_gammas_tail", "bf16_e512_k64", "gemma_block_tail"]
+
+
+@pytest.mark.parametrize("name", ATOMIC)
+def test_atomic_combine_every_element(B, name):
+    """The weighted combine as fp32 atomic adds (moe_combine ATOMIC): the same
+    layer, another summation order, held to the same bounds."""
+    L = W.make_layer(SMALL[name], seed=11)
+    run_and_check(B, L, combine="atomic")
+
+
 def test_one_token(B):
     L = W.make_layer(SMALL["gemma_small"].with_T(1), seed=12)
     run_and_check(B, L)
@@ -402,6 +420,15 @@ def _rows(T, n=256):
 def test_full_size_configs(B, name, T):
     L = W.make_layer(W.SPECS[name].with_T(T), seed=0)
     run_and_check(B, L, rows=_rows(T))
+
+
+FULL_ATOMIC = [("mixtral", 4096), ("gemma", 8192), ("deepseek", 16384), ("gemma_w8a8", 8192)]
+
+
+@pytest.mark.parametrize("name,T", FULL_ATOMIC, ids=[f"{n}-T{t}" for n, t in FULL_ATOMIC])
+def test_full_size_atomic_combine(B, name, T):
+    L = W.make_layer(W.SPECS[name].with_T(T), seed=0)
+    run_and_check(B, L, rows=_rows(T), combine="atomic")
 
 
 @pytest.mark.parametrize("name,T", [("w8a8_small", 300), ("gemma_small", 333), ("gemma_small", 4)],

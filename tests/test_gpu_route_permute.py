@@ -134,8 +134,11 @@ def _check_permute(B, ids, E, bm):
 
 @pytest.mark.parametrize("T,K,E", [(1, 1, 1), (1, 8, 128), (16, 8, 128), (128, 8, 128), (4096, 2, 8),
                                    (1000, 6, 66), (333, 3, 1024), (8192, 8, 128), (5, 2, 700),
-                                   # whole 4096-slot chunks only, and one slot past them
-                                   (512, 8, 128), (1025, 8, 256),
+                                   # the one-block path at its limit (16384 slots)
+                                   (2048, 8, 128), (4096, 4, 1024),
+                                   # the chunked path: whole 4096-slot chunks only, and a few
+                                   # slots past them
+                                   (4096, 8, 128), (4097, 4, 256),
                                    # many chunks with many experts: 16384 x 64 slots over 512 experts
                                    (16384, 64, 512), (16384, 6, 1024)])
 @pytest.mark.parametrize("bm", [16, 64, 256])
