@@ -327,22 +327,18 @@ __device__ void stage_token(RowRegs& r, bool preloaded, rsrc_t rx, int t, int H,
   if (lane == 0) fac[t] = xform ? 1.f : f;
 }
 
-__device__ __forceinline__ int find_slot(const int* s_ids, int Kp, int t, int e) {
-  for (int k = 0; k < Kp; ++k)
-    if (s_ids[t * Kp + k] == e) return t * Kp + k;
-  return -1;
-}
-
 constexpr int PW = 8;                          // waves per block of the pre and up kernels
 constexpr int DW3 = 8;                         // waves per block of the down kernel
 constexpr int RED_FLOATS = PW * 2 * 4 * 64;    // partial tiles of up to two row groups
 
 __host__ __device__ __forceinline__ int stage_bytes(int T, int H) { return (T * (H + 8) * 2 + 15) / 16 * 16; }
 // up kernel: partial tiles, slot ids and weights, expert flags and list, active
-// count, per-token factors; then the staged rows
-__host__ __device__ __forceinline__ int up_small_bytes(int Kp, int Ep) {
-  return (RED_FLOATS * 4 + (32 * Kp + 2 * Ep + 1 + 16) * 4 + 15) / 16 * 16;
+// count, per-token factors, the slot of each (active expert, token) as int16
+// (max_active x 16); then the staged rows
+__host__ __device__ __forceinline__ int up_small_bytes(int Kp, int Ep, int max_active) {
+  return (RED_FLOATS * 4 + (32 * Kp + 2 * Ep + 1 + 16) * 4 + max_active * 16 * 2 + 15) / 16 * 16;
 }
+__host__ __device__ __forceinline__ int up_max_active(int T, int Kp, int Ep) { return T * Kp < Ep ? T * Kp : Ep; }
 
 // Dense MLP gate/up for 16 hidden units.  It needs no routing: run by the up
 // kernel's leading blocks (their weights stream while the expert blocks route)
@@ -428,7 +424,7 @@ __global__ __launch_bounds__(PW * 64, 2) void decode_pre_kernel(DecodeArgs a) {
 // two register sets: the loads of batch b + 1 are in flight while batch b
 // computes.
 template <int WK>
-__device__ __forceinline__ void up_items_per_wave(const DecodeArgs& a, const int* s_ids, const float* s_w,
+__device__ __forceinline__ void up_items_per_wave(const DecodeArgs& a, const int16_t* s_slot, const float* s_w,
                                                   const int* s_active, const float* fac, const bf16_t* sx,
                                                   int pitch, int n_items, int gw, int lane) {
   static_assert(WK != WK_FP8, "fp8 weights keep the block-wide item loop");
@@ -470,8 +466,8 @@ __device__ __forceinline__ void up_items_per_wave(const DecodeArgs& a, const int
   // (hidden unit 4g + v, token col) sits in register v of this lane.
   auto step = [&](S& st, int b) {
     const int item = it0 + b / BPI, bi = b % BPI;
-    const int e = s_active[item / RG], i0 = (item % RG) * 16;
-    const int slot = col < T ? find_slot(s_ids, Kp, col, e) : -1;
+    const int i0 = (item % RG) * 16;
+    const int slot = col < T ? s_slot[(item / RG) * 16 + col] : -1;
     if (bi == 0) acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
     st.compute(acc, sx + (slot >= 0 ? col : 0) * pitch, slot >= 0, m0 + bi * DU, m1);
     if (bi == BPI - 1 && slot >= 0) {
@@ -520,7 +516,8 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
   int* s_active = s_flag + Ep;
   int* s_nact = s_active + Ep;
   float* fac = (float*)(s_nact + 1);
-  bf16_t* sx = (bf16_t*)(dsm + up_small_bytes(Kp, Ep));
+  int16_t* s_slot = (int16_t*)(fac + 16);  // [max_active][16]: slot of (active expert, token), -1: none
+  bf16_t* sx = (bf16_t*)(dsm + up_small_bytes(Kp, Ep, a.max_active));
   const rsrc_t rx = make_rsrc(a.x, (uint32_t)(T * H * 2));
 
   // 1. token rows and logits in flight together, then the routing of the T
@@ -552,34 +549,43 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
   __syncthreads();
   for (int i = threadIdx.x; i < T * Kp; i += PW * 64) s_flag[s_ids[i]] = 1;
   __syncthreads();
-  if (wave == 0) {  // ascending list of the experts with at least one slot
+  if (wave == 0) {  // ascending list of the experts with at least one slot, and each one's place in it
     int base = 0;
     for (int j = 0; j < Ep; j += 64) {
       const int e = j + lane;
       const bool f = e < Ep && s_flag[e];
       const uint64_t mask = __ballot(f);
-      if (f) s_active[base + __popcll(mask & ((1ull << lane) - 1ull))] = e;
+      if (f) {
+        const int u = base + __popcll(mask & ((1ull << lane) - 1ull));
+        s_active[u] = e;
+        s_flag[e] = u;
+      }
       base += __popcll(mask);
     }
     if (lane == 0) *s_nact = base;
   }
   __syncthreads();
   const int n_act = *s_nact;
+  // slot of each (active expert, token): one write per slot through the experts' places
+  for (int i = threadIdx.x; i < n_act * 16; i += PW * 64) s_slot[i] = -1;
+  __syncthreads();
+  for (int i = threadIdx.x; i < T * Kp; i += PW * 64) s_slot[s_flag[s_ids[i]] * 16 + i / Kp] = (int16_t)i;
+  __syncthreads();
 
-  // 2. the first expert block publishes the routing for the down kernel and the caller
-  if (blk == 0) {
+  // 2. the first expert block publishes the routing for the down kernel and the
+  //    caller once its own items are issued (stores then never sit in front of
+  //    the weight loads' waits)
+  auto publish = [&]() {
+    if (blk != 0) return;
     if (threadIdx.x == 0) a.rinfo[0] = n_act;
     for (int i = threadIdx.x; i < n_act; i += PW * 64) a.rinfo[1 + i] = s_active[i];
-    for (int i = threadIdx.x; i < n_act * 16; i += PW * 64) {
-      const int t = i & 15;
-      a.rinfo[1 + Ep + i] = t < T ? find_slot(s_ids, Kp, t, s_active[i >> 4]) : -1;
-    }
+    for (int i = threadIdx.x; i < n_act * 16; i += PW * 64) a.rinfo[1 + Ep + i] = s_slot[i];
     for (int i = threadIdx.x; i < T * a.K; i += PW * 64) {
       const int t = i / a.K, k = i % a.K;
       if (a.topk_w_out) a.topk_w_out[i] = s_w[t * Kp + k];
       if (a.topk_ids_out) a.topk_ids_out[i] = s_ids[t * Kp + k];
     }
-  }
+  };
 
   // 3. (active expert, 16 hidden units) items: a contiguous, balanced range per block
   const int RG = I / 16, n_items = n_act * RG;
@@ -593,7 +599,8 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
   // reduction per item costs more than the item's stream
   if constexpr (WK != WK_FP8) {
     if ((WK == WK_FP4 ? 2 : 1) * n_items >= a.n_up_blocks * PW) {
-      up_items_per_wave<WK>(a, s_ids, s_w, s_active, fac, sx, pitch, n_items, blk * PW + wave, lane);
+      up_items_per_wave<WK>(a, s_slot, s_w, s_active, fac, sx, pitch, n_items, blk * PW + wave, lane);
+      publish();
       return;
     }
   }
@@ -607,7 +614,7 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
         su = a.s13[(int64_t)e * 2 * I + I + i0 + (threadIdx.x >> 4)];
       }
     }
-    const int slot_col = col < T ? find_slot(s_ids, Kp, col, e) : -1;
+    const int slot_col = col < T ? s_slot[u * 16 + col] : -1;
     const bool bvalid = slot_col >= 0;
     const bf16_t* brow = sx + (bvalid ? col : 0) * pitch;
     const uint8_t* wbase = e < E ? (const uint8_t*)a.w13 + wbytes<WK>((int64_t)e * 2 * I * H)
@@ -629,7 +636,7 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
     __syncthreads();
     if (threadIdx.x < 256) {
       const int rho = threadIdx.x >> 4, t = threadIdx.x & 15;
-      const int slot = t < T ? find_slot(s_ids, Kp, t, e) : -1;
+      const int slot = t < T ? s_slot[u * 16 + t] : -1;
       if (slot >= 0) {
         const float gv = reduced<PW, 2>(red, 0, rho, t) * fac[t] * sg;
         const float uv = reduced<PW, 2>(red, 1, rho, t) * fac[t] * su;
@@ -639,6 +646,7 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
     }
     __syncthreads();  // red is rewritten by the next item
   }
+  publish();
 }
 
 // Expert down projection (bf16 or MXFP4 weights) of one (16 output features,
@@ -837,7 +845,7 @@ __global__ __launch_bounds__(DW3 * 64) void decode_down_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------- launches
 int decode_up_lds_bytes(int T, int H, int Kp, int Ep) {
   // expert blocks; the dense gate/up blocks need stage_bytes + (RED_FLOATS + 16) * 4, which is less
-  return up_small_bytes(Kp, Ep) + stage_bytes(T, H);
+  return up_small_bytes(Kp, Ep, up_max_active(T, Kp, Ep)) + stage_bytes(T, H);
 }
 int decode_pre_lds_bytes(int T, int H) { return stage_bytes(T, H) + (RED_FLOATS + 16) * 4; }
 

@@ -4,11 +4,13 @@
 // llama.cpp MoE lesson: sigmoid scoring and expert groups.
 //
 // One wavefront per token.  Lane l holds the logits of experts l, l+64, ...
-// Selection runs K rounds of a wave-wide arg-max on the key (value desc,
-// index asc): a DPP max over the order-preserving uint32 image of the value,
-// then a DPP min over the indices of the lanes that hold that maximum.  The
-// selected logit is recovered exactly from its key, so every lane computes the
-// same exp(z - max) for it; slot k's result ends up in lane k.
+// Selection works on the order-preserving uint32 image of each logit (the key;
+// value descending, index ascending on ties): a radix select finds the K-th
+// largest key from ballot counts, one bit per step, the keys above it and the
+// lowest-index keys equal to it are the selection, and each selected value's
+// slot is its number of selected predecessors in (key desc, index asc) order,
+// again from ballots.  The selected logit is recovered exactly from its key;
+// slot k's result ends up in lane k.
 //
 // Renormalised weights are computed as exp(z_k - m) / sum_{selected} exp(z_j - m):
 // the full softmax denominator cancels exactly (the page's own derivation of

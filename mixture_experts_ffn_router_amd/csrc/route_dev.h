@@ -91,31 +91,65 @@ __device__ __forceinline__ void route_logits(const TokenLogits<VPL>& zl, int E, 
     s_all = wave_sum_f64(s);
   }
 
-  uint32_t taken = 0;  // bit j: this lane's value j already selected
-  double my_e = 0.0;
-  int my_id = 0;
-  double denom = 0.0;
-  for (int k = 0; k < K; ++k) {
-    uint32_t bk = 0, bi = 0xFFFFFFFFu;
+  // Top-k by radix select on the keys: tau = the K-th largest key, found bit by
+  // bit from the top (a bit stays set while at least K keys are >= the prefix);
+  // every key above tau is selected, and of the keys equal to tau the lowest
+  // indices (index = lane + 64 j: all j = 0 before j = 1, ...) fill the rest.
+  // Counts come from ballots, so each step is a few scalar instructions.
+  uint32_t tau = 0;
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      if (!((taken >> j) & 1u) && key[j] > bk) {  // j ascending: lowest index wins ties
-        bk = key[j];
-        bi = (uint32_t)(lane + 64 * j);
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = tau | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) cnt += __popcll(__ballot(key[j] >= c));
+    if (cnt >= K) tau = c;
+  }
+  const uint64_t lt = (1ull << lane) - 1ull;
+  int need = K;  // keys equal to tau still to take
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) need -= __popcll(__ballot(key[j] > tau));
+  uint32_t sel = 0;  // bit j: this lane's value j is selected
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const uint64_t eq = __ballot(key[j] == tau);
+    if (key[j] > tau || (key[j] == tau && __popcll(eq & lt) < need)) sel |= 1u << j;
+    const int here = __popcll(eq);
+    need -= here < need ? here : need;
+  }
+  // Slot order: a selected value's slot is the number of selected values with a
+  // larger key, or an equal key and a lower index; the lane of that slot takes
+  // its index and key.
+  int my_id = 0;
+  uint32_t my_key = 0;
+#pragma unroll
+  for (int j2 = 0; j2 < VPL; ++j2) {
+    uint64_t m2 = __ballot((sel >> j2) & 1u);
+    while (m2) {
+      const int l2 = __builtin_ctzll(m2);
+      m2 &= m2 - 1;
+      const uint32_t k2 = (uint32_t)__builtin_amdgcn_readlane((int)key[j2], l2);
+      const int idx2 = l2 + 64 * j2;
+      int r = 0;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        const bool sj = (sel >> j) & 1u;
+        r += __popcll(__ballot(sj && (key[j] > k2 || (key[j] == k2 && lane + 64 * j < idx2))));
+      }
+      if (lane == r) {
+        my_id = idx2;
+        my_key = k2;
       }
     }
-    const uint32_t gk = wave_max_u32(bk);
-    const uint32_t gi = wave_min_u32(bk == gk ? bi : 0xFFFFFFFFu);
-    if ((int)(gi & 63u) == lane) taken |= 1u << (gi >> 6);
-    const float zk = f32_from_order_key(gk);
-    // softmax: fp32 exp(z - max); sigmoid: 1 / (1 + exp(-z)) in fp64
-    const double e = sigmoid ? 1.0 / (1.0 + exp(-(double)zk)) : (double)expf(zk - m);
-    denom += e;  // slot order
-    if (lane == k) {
-      my_e = e;
-      my_id = (int)gi;
-    }
   }
+  // softmax: fp32 exp(z - max); sigmoid: 1 / (1 + exp(-z)) in fp64; the sum of the
+  // selected terms in fp64
+  double my_e = 0.0;
+  if (lane < K) {
+    const float zk = f32_from_order_key(my_key);
+    my_e = sigmoid ? 1.0 / (1.0 + exp(-(double)zk)) : (double)expf(zk - m);
+  }
+  const double denom = wave_sum_f64(my_e);
   w_slot = 0.f;
   id_slot = 0;
   if (lane < K) {
