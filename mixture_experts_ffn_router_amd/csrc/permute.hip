@@ -22,7 +22,7 @@
 //            sorted_slots[pos] = f and slot_row[f] = pos with
 //            pos = offsets[e] + (equal ids in earlier chunks) + rank.
 // Only block b reads or writes slot_row[b*CHUNK, (b+1)*CHUNK) between the
-// launches' boundaries, so the reuse is race-free.  Up to 16384 slots with few
+// launches' boundaries, so the reuse is race-free.  Up to 8192 slots with few
 // experts, one block takes the three steps in one launch instead.
 #include "common.h"
 #include "kernels.h"
@@ -41,14 +41,16 @@ __device__ __forceinline__ int chunk_id(const int32_t* __restrict__ ids, int64_t
   return (e >= 0 && e < E) ? e : -1;  // ids outside [0, E) belong to no segment
 }
 
+// Bits of an id in [0, E): ceil(log2(E)), 0 for E = 1.
+__device__ __forceinline__ int id_bits(int E) { return E <= 1 ? 0 : 32 - __clz(E - 1); }
+
 // Lanes of this wave holding the same id as this lane: one ballot per bit of
-// the id (ids < 1024) and one for validity, so invalid lanes (-1) form their
-// own group.
-__device__ __forceinline__ uint64_t wave_match(int e) {
+// the id (nbits = id_bits(E)) and one for validity, so invalid lanes (-1) form
+// their own group.
+__device__ __forceinline__ uint64_t wave_match(int e, int nbits) {
   uint64_t same = __ballot(e >= 0);
   if (e < 0) same = ~same;
-#pragma unroll
-  for (int bit = 0; bit < 10; ++bit) {
+  for (int bit = 0; bit < nbits; ++bit) {
     const bool v = (e >> bit) & 1;
     const uint64_t bal = __ballot(v);
     same &= v ? bal : ~bal;
@@ -80,6 +82,22 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_w, int* total) {
   *total = tot;
   return wbase + incl - v;
 }
+
+// block_expert and pads from the padded segment offsets s_off[0..E] and counts
+// s_cnt[E] in LDS: wave w takes experts w, w + PW, ...; its lanes write the
+// expert's row blocks and pad rows (sorted_slots = -1) coalesced.  An empty
+// expert owns no block.
+__device__ __forceinline__ void write_blocks(int E, int bm_log2, const int* s_off, const int* s_cnt,
+                                             int32_t* __restrict__ block_expert,
+                                             int32_t* __restrict__ sorted_slots, bool pads) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int e = wave; e < E; e += PW) {
+    const int o0 = s_off[e], o1 = s_off[e + 1];
+    for (int j = (o0 >> bm_log2) + lane; j < (o1 >> bm_log2); j += 64) block_expert[j] = e;
+    if (pads)
+      for (int q = o0 + s_cnt[e] + lane; q < o1; q += 64) sorted_slots[q] = -1;
+  }
+}
 }  // namespace
 
 __global__ __launch_bounds__(PT) void permute_hist_kernel(const int32_t* __restrict__ ids, int64_t n, int E,
@@ -94,10 +112,11 @@ __global__ __launch_bounds__(PT) void permute_hist_kernel(const int32_t* __restr
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) e_r[r] = chunk_id(ids, n, f0 + r * PT + tid, E);
   const uint64_t lt = (1ull << (tid & 63)) - 1ull;
+  const int nbits = id_bits(E);
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {
     // one add per distinct id of the wave (a sum: the order of the adds does not matter)
-    const uint64_t same = wave_match(e_r[r]);
+    const uint64_t same = wave_match(e_r[r], nbits);
     if (e_r[r] >= 0 && (same & lt) == 0) atomicAdd(&s_hist[e_r[r]], __popcll(same));
   }
   __syncthreads();
@@ -155,22 +174,7 @@ __global__ __launch_bounds__(PT) void permute_scan_kernel(int64_t n, int E, int 
     if (num_padded) *num_padded = total;
   }
   __syncthreads();
-  // row block j belongs to the last expert whose segment starts at or before it
-  // (empty experts start where the next one does); its rows past the expert's
-  // count are pads
-  const int nblk = total >> bm_log2;
-  for (int j = tid; j < nblk; j += PT) {
-    const int row = j << bm_log2;
-    int lo = 0, hi = E - 1;  // s_off[lo] <= row < s_off[E]
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_off[mid] <= row) lo = mid;
-      else hi = mid - 1;
-    }
-    block_expert[j] = lo;
-    const int pad0 = s_off[lo] + s_cnt[lo];
-    for (int r = row > pad0 ? row : pad0; r < row + bm; ++r) sorted_slots[r] = -1;
-  }
+  write_blocks(E, bm_log2, s_off, s_cnt, block_expert, sorted_slots, true);
 }
 
 __global__ __launch_bounds__(PT) void permute_scatter_kernel(const int32_t* __restrict__ ids, int64_t n, int E,
@@ -184,6 +188,7 @@ __global__ __launch_bounds__(PT) void permute_scatter_kernel(const int32_t* __re
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t f0 = (int64_t)b * CHUNK;
   const bool full = f0 + CHUNK <= n;
+  const int nbits = id_bits(E);
   int e_r[ROUNDS];
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) e_r[r] = chunk_id(ids, n, f0 + r * PT + tid, E);
@@ -196,7 +201,7 @@ __global__ __launch_bounds__(PT) void permute_scatter_kernel(const int32_t* __re
     const uint64_t lt0 = (1ull << lane) - 1ull;
 #pragma unroll
     for (int r = 0; r < ROUNDS; ++r) {  // a count: the order does not matter
-      const uint64_t same = wave_match(e_r[r]);
+      const uint64_t same = wave_match(e_r[r], nbits);
       if (e_r[r] >= 0 && (same & lt0) == 0) atomicSub(&s_base[e_r[r]], __popcll(same));
     }
   }
@@ -204,7 +209,7 @@ __global__ __launch_bounds__(PT) void permute_scatter_kernel(const int32_t* __re
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {
     const int e = e_r[r];
-    const uint64_t same = wave_match(e);
+    const uint64_t same = wave_match(e, nbits);
     for (int i = tid; i < PW * E; i += PT) s_wcnt[i] = 0;
     __syncthreads();  // zeroed; also: the previous round's reads of s_base are done
     const bool leader = (same & lt) == 0;
@@ -238,13 +243,20 @@ __global__ __launch_bounds__(PT) void permute_scatter_kernel(const int32_t* __re
 // Up to SMALL_N slots with few experts: the three steps in one block and one
 // launch (the launches cost more than the work), in two passes over the ids
 // held in registers.  Pass 1 ranks each id inside its wave and records every
-// (round, wave)'s count per expert in an LDS table; one thread per expert turns
-// its column into exclusive prefixes (round-major, then wave) and its count;
-// pass 2 places each id at offsets[e] + its (round, wave) prefix + its rank.
+// (round, wave)'s count per expert in an LDS table; parallel prefix steps turn
+// the table into exclusive prefixes in (round, wave) order per expert; pass 2
+// places each id at offsets[e] + its (round, wave) prefix + its rank.  When the
+// padded rows fit in LDS, sorted_slots is assembled there (pads pre-filled) and
+// written out in order: one CU's scattered stores to L2 would cost more.
 // Round r covers slots [1024 r, 1024 (r + 1)), thread tid slot 1024 r + tid.
-constexpr int SMALL_ROUNDS = 16;
-constexpr int64_t SMALL_N = (int64_t)SMALL_ROUNDS * PT;  // 16384
+// Measured on MI355X: one launch costs about 7 us plus 0.5-1 us per 1024 slots
+// (one CU's ballots), the three launches 12-16 us whatever the size; the one
+// block wins up to about 8192 slots.
+constexpr int SMALL_ROUNDS = 8;
+constexpr int64_t SMALL_N = (int64_t)SMALL_ROUNDS * PT;  // 8192
 constexpr int SMALL_TABLE = 32768;                       // uint16 table entries: rounds x waves x E
+constexpr int SMALL_STAGE = 36864;                       // ints of LDS: table + round prefixes, then rows
+static_assert(SMALL_TABLE / 2 + SMALL_TABLE / PW <= SMALL_STAGE, "LDS plan");
 
 __global__ __launch_bounds__(PT) void permute_small_kernel(const int32_t* __restrict__ ids, int64_t n, int E,
                                                            int bm_log2, int32_t* __restrict__ counts,
@@ -253,7 +265,9 @@ __global__ __launch_bounds__(PT) void permute_small_kernel(const int32_t* __rest
                                                            int32_t* __restrict__ block_expert,
                                                            int32_t* __restrict__ num_padded,
                                                            int32_t* __restrict__ slot_row) {
-  __shared__ uint16_t s_tab[SMALL_TABLE];  // [round][wave][E]: counts, then exclusive prefixes
+  __shared__ __align__(16) int s_big[SMALL_STAGE];
+  uint16_t* s_tab = reinterpret_cast<uint16_t*>(s_big);  // [round][wave][E]: counts, then exclusive prefixes
+  int* s_rpre = s_big + SMALL_TABLE / 2;                   // [round][E]: round totals, then their prefixes
   __shared__ int s_off[1025];
   __shared__ int s_cnt[1024];
   __shared__ int s_w[PW];
@@ -261,34 +275,68 @@ __global__ __launch_bounds__(PT) void permute_small_kernel(const int32_t* __rest
   const int bm = 1 << bm_log2;
   const int rounds = (int)((n + PT - 1) / PT);
   const int ncell = rounds * PW * E;
+  const int nbits = id_bits(E);
   int e_r[SMALL_ROUNDS];  // every id of the call, all loads in flight at once
 #pragma unroll
   for (int r = 0; r < SMALL_ROUNDS; ++r) e_r[r] = chunk_id(ids, n, (int64_t)r * PT + tid, E);
-  for (int i = tid; i < ncell; i += PT) s_tab[i] = 0;
+  for (int i = tid; i < (ncell + 7) / 8; i += PT) reinterpret_cast<int4*>(s_big)[i] = make_int4(0, 0, 0, 0);
   __syncthreads();
   const uint64_t lt = (1ull << lane) - 1ull;
-  int rank[SMALL_ROUNDS];
+  int pos[SMALL_ROUNDS];  // rank inside the (round, wave), then the row
 #pragma unroll
   for (int r = 0; r < SMALL_ROUNDS; ++r) {
-    rank[r] = 0;
+    pos[r] = 0;
     if (r < rounds) {  // uniform
-      const uint64_t same = wave_match(e_r[r]);
-      rank[r] = __popcll(same & lt);
-      if (e_r[r] >= 0 && rank[r] == 0) s_tab[(r * PW + wave) * E + e_r[r]] = (uint16_t)__popcll(same);
+      const uint64_t same = wave_match(e_r[r], nbits);
+      pos[r] = __popcll(same & lt);
+      if (e_r[r] >= 0 && pos[r] == 0) s_tab[(r * PW + wave) * E + e_r[r]] = (uint16_t)__popcll(same);
     }
   }
   __syncthreads();
-  int cnt = 0;
-  if (tid < E) {
-    for (int c = 0; c < rounds * PW; ++c) {
-      const int v = s_tab[c * E + tid];
-      s_tab[c * E + tid] = (uint16_t)cnt;  // < 16384: fits
-      cnt += v;
+  // (1) each round's total per expert
+  const int nre = rounds * E;
+  for (int i = tid; i < nre; i += PT) {  // (round r, expert e) = (i / E, i % E)
+    const int r = i / E, e = i - r * E;
+    int tot = 0;
+#pragma unroll
+    for (int w = 0; w < PW; ++w) tot += s_tab[(r * PW + w) * E + e];
+    s_rpre[i] = tot;
+  }
+  __syncthreads();
+  // (2) exclusive prefixes over the rounds: a group of R = 2^lgR >= rounds lanes
+  // per expert scans with shuffles; the group's last lane holds the count
+  const int lgR = rounds <= 1 ? 0 : 32 - __clz(rounds - 1);
+  const int nit = E << lgR;
+  for (int base = 0; base < nit; base += PT) {  // uniform trip count: every lane shuffles
+    const int i = base + tid;
+    const int e = i >> lgR, r = i & ((1 << lgR) - 1);
+    const bool ok = i < nit && r < rounds;
+    const int v = ok ? s_rpre[r * E + e] : 0;
+    int incl = v;
+    for (int d = 1; d < (1 << lgR); d <<= 1) {
+      const int o = __shfl_up(incl, d, 64);
+      if (r >= d) incl += o;
+    }
+    if (ok) s_rpre[r * E + e] = incl - v;
+    if (i < nit && r == (1 << lgR) - 1) s_cnt[e] = incl;
+  }
+  __syncthreads();
+  // (3) exclusive prefixes over the waves inside each round
+  for (int i = tid; i < nre; i += PT) {
+    const int r = i / E, e = i - r * E;
+    int run = s_rpre[i];
+#pragma unroll
+    for (int w = 0; w < PW; ++w) {
+      const int c = (r * PW + w) * E + e;
+      const int v = s_tab[c];
+      s_tab[c] = (uint16_t)run;  // < SMALL_N: fits
+      run += v;
     }
   }
+  const int cnt = tid < E ? (rounds ? s_cnt[tid] : 0) : 0;
   const int padded = ((cnt + bm - 1) >> bm_log2) << bm_log2;
   int total = 0;
-  const int start = block_excl_scan(tid < E ? padded : 0, s_w, &total);
+  const int start = block_excl_scan(tid < E ? padded : 0, s_w, &total);  // also orders step (3)
   if (tid < E) {
     counts[tid] = cnt;
     offsets[tid] = start;
@@ -301,30 +349,29 @@ __global__ __launch_bounds__(PT) void permute_small_kernel(const int32_t* __rest
     if (num_padded) *num_padded = total;
   }
   __syncthreads();
-  const int nblk = total >> bm_log2;
-  for (int j = tid; j < nblk; j += PT) {
-    const int row = j << bm_log2;
-    int lo = 0, hi = E - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_off[mid] <= row) lo = mid;
-      else hi = mid - 1;
-    }
-    block_expert[j] = lo;
-    const int pad0 = s_off[lo] + s_cnt[lo];
-    for (int q = row > pad0 ? row : pad0; q < row + bm; ++q) sorted_slots[q] = -1;
+#pragma unroll
+  for (int r = 0; r < SMALL_ROUNDS; ++r)
+    pos[r] = (r < rounds && e_r[r] >= 0) ? s_off[e_r[r]] + s_tab[(r * PW + wave) * E + e_r[r]] + pos[r] : -1;
+  const bool staged = total <= SMALL_STAGE;  // uniform
+  write_blocks(E, bm_log2, s_off, s_cnt, block_expert, sorted_slots, !staged);
+  if (staged) {
+    __syncthreads();  // every table read above is done
+    for (int i = tid; i < total; i += PT) s_big[i] = -1;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < SMALL_ROUNDS; ++r)
+      if (pos[r] >= 0) s_big[pos[r]] = r * PT + tid;
+    __syncthreads();
+    for (int i = tid; i < total; i += PT) sorted_slots[i] = s_big[i];
+  } else {
+#pragma unroll
+    for (int r = 0; r < SMALL_ROUNDS; ++r)
+      if (pos[r] >= 0) sorted_slots[pos[r]] = r * PT + tid;
   }
 #pragma unroll
   for (int r = 0; r < SMALL_ROUNDS; ++r) {
     const int64_t f = (int64_t)r * PT + tid;
-    if (r < rounds && f < n) {
-      int pos = -1;
-      if (e_r[r] >= 0) {
-        pos = s_off[e_r[r]] + s_tab[(r * PW + wave) * E + e_r[r]] + rank[r];
-        sorted_slots[pos] = (int32_t)f;
-      }
-      slot_row[f] = pos;
-    }
+    if (r < rounds && f < n) slot_row[f] = pos[r];
   }
 }
 

@@ -134,8 +134,9 @@ def _check_permute(B, ids, E, bm):
 
 @pytest.mark.parametrize("T,K,E", [(1, 1, 1), (1, 8, 128), (16, 8, 128), (128, 8, 128), (4096, 2, 8),
                                    (1000, 6, 66), (333, 3, 1024), (8192, 8, 128), (5, 2, 700),
-                                   # the one-block path at its limit (16384 slots)
-                                   (2048, 8, 128), (4096, 4, 1024),
+                                   # the one-block path at its limits (8192 slots; its table full
+                                   # at 2048 x 4 over 256 experts), then just past them
+                                   (1024, 8, 128), (2048, 4, 256), (2048, 8, 128), (4096, 4, 1024),
                                    # the chunked path: whole 4096-slot chunks only, and a few
                                    # slots past them
                                    (4096, 8, 128), (4097, 4, 256),
