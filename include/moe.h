@@ -251,11 +251,14 @@ moe_status moe_forward_workspace_size(const moe_layer_desc* desc, int64_t T, siz
  * grouped GEMMs; moe_forward_profiled keeps it on `stream`.
  *
  * Two execution paths compute this same operation (moe_forward_path tells which
- * one a call takes; layers with FP8 activations always take the grouped path).  The grouped path permutes the routed rows and runs grouped
+ * one a call takes).  The grouped path permutes the routed rows and runs grouped
  * GEMMs.  The decode path (T <= 16 bf16 tokens) streams each selected expert's
  * weights once and applies them to all tokens together; it folds the routing
- * weight into the gated intermediate before its bf16 rounding and sums the
- * expert outputs of a token in fp32 before the single output rounding.
+ * weight into the gated intermediate before its bf16 rounding (with FP8
+ * activations: into the slot's h scale, after the quantisation of the
+ * unweighted h) and sums the expert outputs of a token in fp32 before the
+ * single output rounding.  Its FP8 activation codes equal the grouped path's;
+ * its products take the codes widened to bf16 (exact) on bf16 MFMAs.
  *
  * workspace: device memory of at least moe_forward_workspace_size() bytes,
  * 256-byte aligned, owned by the caller; contents on entry do not matter and
@@ -302,8 +305,11 @@ int32_t moe_decode_dense_gate_up_stage(const moe_layer_desc* desc, int64_t T);
 /* Where one moe_forward call keeps its intermediates in the workspace, for
  * inspection (tests, debugging): byte offsets into the workspace, -1 for a
  * buffer the call does not have.  Contents are those the call left once its
- * work on the stream has completed, until the workspace is used again.  The
- * grouped path only (path == MOE_PATH_DECODE: every offset is -1).
+ * work on the stream has completed, until the workspace is used again.  On the
+ * decode path (path == MOE_PATH_DECODE) only h, as [T * slots_per_token, I] rows
+ * in slot order (capacity = T * slots_per_token), and with FP8 activations
+ * x_codes, x_scales, h_codes and h_scales (per slot row) are given; every other
+ * offset is -1 and y_parts is 0.
  *   topk_w, topk_ids  [T, slots_per_token] fp32 / int32 (shared experts appended
  *                     as ids E.., weight 1)
  *   counts [E+S], offsets [E+S+1], sorted_slots [capacity], block_expert

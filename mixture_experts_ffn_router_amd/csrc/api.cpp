@@ -122,9 +122,10 @@ int choose_block_m(const moe_layer_desc& d, int64_t T) {
 }
 
 // Decode path: at most 16 bf16 tokens (one MFMA tile of token columns) whose
-// rows fit the decode kernels' LDS staging.
+// rows fit the decode kernels' LDS staging (FP8 activations included: FP8
+// weights, which have no shared experts).
 bool use_decode(const moe_layer_desc& d, int64_t T) {
-  if (d.act_dtype != MOE_DT_BF16 || d.act_quant || T < 1 || T > 16) return false;
+  if (d.act_dtype != MOE_DT_BF16 || T < 1 || T > 16) return false;
   const int lds_max = 160 * 1024;
   return moe::decode_up_lds_bytes((int)T, d.hidden, d.top_k + d.n_shared, d.num_experts + d.n_shared) <= lds_max &&
          moe::decode_pre_lds_bytes((int)T, d.hidden) <= lds_max;
@@ -145,7 +146,7 @@ struct Plan {
   size_t o_slotrow;  // inverse map of the permutation (slot -> padded row)
   size_t o_logits, o_w, o_ids, o_counts, o_offsets, o_sorted, o_bexp, o_rms, o_r, o_xn1, o_xn2, o_h, o_y,
       o_dh, o_dout, total;
-  size_t o_rinfo, o_ypart;  // decode path only
+  size_t o_rinfo, o_ypart, o_slotw;  // decode path only (o_slotw: FP8 activations)
   size_t path_total;        // bytes the path this call takes lays out (total: the larger of the two)
   int down_splits;
 };
@@ -312,6 +313,12 @@ moe_status make_plan(const moe_layer_desc& d, const moe_tensors* t, int64_t T, P
     p.o_dout = take(p.dense ? (size_t)T * H * 4 : 0);
     p.down_splits = moe::decode_down_splits((int)T, d.hidden, d.inter, p.dense);
     p.o_ypart = take(p.dense || p.down_splits > 1 || d.block_tail ? (size_t)T * p.down_splits * H * 4 : 0);
+    // FP8 activations: x codes and scales, h codes and scales per slot, slot weights
+    p.o_xq = take(p.aq ? (size_t)T * H : 0);
+    p.o_xs = take(p.aq ? (size_t)T * 4 : 0);
+    p.o_hq = take(p.aq ? (size_t)slots * d.inter : 0);
+    p.o_hs = take(p.aq ? (size_t)slots * 4 : 0);
+    p.o_slotw = take(p.aq ? (size_t)slots * 4 : 0);
     p.path_total = o;
     if (o > p.total) p.total = o;
   }
@@ -440,6 +447,23 @@ MOE_API moe_status moe_forward_workspace_layout(const moe_layer_desc* desc, cons
   L.y_f32 = p.y_f32 || p.atomic;
   L.capacity = p.cap;
   auto off = [&](bool has, size_t o) { return (!p.decode && has) ? (int64_t)o : (int64_t)-1; };
+  if (p.decode) {
+    // the decode path's h rows are per slot (row t * slots_per_token + k); with FP8
+    // activations also the codes and scales it takes
+    L.y_parts = 0;
+    L.y_f32 = 0;
+    L.capacity = T * p.Kp;
+    auto doff = [&](bool has, size_t o) { return has ? (int64_t)o : (int64_t)-1; };
+    L.topk_w = L.topk_ids = L.counts = L.offsets = L.sorted_slots = L.block_expert = L.slot_row = -1;
+    L.inv_rms = L.x_expert = L.y = -1;
+    L.h = doff(true, p.o_h);
+    L.x_codes = doff(p.aq, p.o_xq);
+    L.x_scales = doff(p.aq, p.o_xs);
+    L.h_codes = doff(p.aq, p.o_hq);
+    L.h_scales = doff(p.aq, p.o_hs);
+    *out = L;
+    return MOE_OK;
+  }
   L.topk_w = off(true, p.o_w);
   L.topk_ids = off(true, p.o_ids);
   L.counts = off(true, p.o_counts);
@@ -541,6 +565,14 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
     a.out_f32 = t->out_f32;
     a.topk_w_out = t->topk_w_out;
     a.topk_ids_out = t->topk_ids_out;
+    a.aq = p.aq;
+    if (p.aq) {
+      a.xcodes = ws + p.o_xq;
+      a.xscales = (float*)(ws + p.o_xs);
+      a.hcodes = ws + p.o_hq;
+      a.hscales = (float*)(ws + p.o_hs);
+      a.slot_w = (float*)(ws + p.o_slotw);
+    }
     const int wk = d.weight_dtype == MOE_DT_FP8_E4M3 ? 1 : (d.weight_dtype == MOE_DT_MXFP4 ? 2 : 0);
     // the bf16 / MXFP4 down kernel stages the routing summary in a 520-entry LDS
     // table; E <= 512 and at most 8 shared experts keep max_active within it
@@ -560,6 +592,11 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
     // dense gate/up, routing + expert gate/up
     HIP_TRY(moe::launch_decode_up(a, wk, st), "decode up launch");
     STAGE(MOE_STAGE_QUANT_H);
+    // FP8 activations: the h row of every slot quantised (all T * Kp rows are written)
+    if (p.aq)
+      HIP_TRY(moe::launch_quant_rows_fp8(a.hbuf, T * p.Kp, d.inter, d.inter, nullptr, nullptr, (uint8_t*)a.hcodes,
+                                         d.inter, (float*)a.hscales, st),
+              "decode h quantisation launch");
     STAGE(MOE_STAGE_DOWN);
     // dense down, expert down + combine
     HIP_TRY(moe::launch_decode_down(a, wk, st), "decode down launch");

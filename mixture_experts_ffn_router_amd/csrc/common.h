@@ -143,6 +143,42 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// Dynamic per-row FP8 quantisation pieces (the "FP8-Dynamic" scheme named on
+// the sglang PR #24696 page): a row's scale is its largest magnitude / 448 (1 for
+// an all-zero row) and a code is the E4M3 nearest-even of value / scale, with an
+// IEEE fp32 division and v_cvt_pk_fp8_f32 (round to nearest even, saturating at
+// 448), so a code depends on the fp32 values alone.
+__device__ __forceinline__ float absmax8(uint4 x) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  float m = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    m = fmaxf(m, fabsf(__uint_as_float(w[q] << 16)));
+    m = fmaxf(m, fabsf(__uint_as_float(w[q] & 0xFFFF0000u)));
+  }
+  return m;
+}
+
+// codes of the 8 bf16 values in x at scale s, in order (two dwords of 4 codes)
+__device__ __forceinline__ uint2 codes8(uint4 x, float s) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint32_t out[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float f0 = __uint_as_float(w[2 * h] << 16) / s, f1 = __uint_as_float(w[2 * h] & 0xFFFF0000u) / s;
+    const float f2 = __uint_as_float(w[2 * h + 1] << 16) / s, f3 = __uint_as_float(w[2 * h + 1] & 0xFFFF0000u) / s;
+    int p = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
+    p = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, p, true);
+    out[h] = (uint32_t)p;
+  }
+  return make_uint2(out[0], out[1]);
+}
+
+__device__ __forceinline__ float scale_of(float amax) {
+  const float s = amax / 448.0f;
+  return s > 0.f ? s : 1.f;
+}
+
 // Buffer resource over [base, base + bytes): loads past the end return 0.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 

@@ -133,9 +133,12 @@ __device__ __forceinline__ u32x4 bload(rsrc_t r, uint32_t off) {
 //   BG = true:  B rows in global memory (rb/boff; boff past the end reads zero).
 //   MXFP4: rs/soff: the block-scale tensor and the byte offset of this lane's
 //   row of scales (one byte per 32 elements).
-template <int WK, int NR, bool BG, int DU>
+//   BQ: B rows in global memory are FP8 codes (boff in bytes), widened to bf16
+//   (exact); with fp8 weights one 16-byte load holds both MFMAs' B operands.
+template <int WK, int NR, bool BG, int DU, bool BQ = false>
 struct Stream {
   static_assert(WK != WK_FP4 || DU % 2 == 0, "MXFP4 batches hold whole pairs of steps");
+  static_assert(!BQ || (BG && WK == WK_FP8), "B codes go with fp8 weights and B rows in global memory");
   static constexpr int LA = WK == WK_BF16 ? 2 : 1;  // A loads per row group per macro step
   rsrc_t ra[NR];
   uint32_t aoff[NR];
@@ -170,7 +173,9 @@ struct Stream {
             av[r][u][j] = bload(ra[r], live ? aoff[r] + (uint32_t)wbytes<WK>(kchunk<WK>(m + u, j, g)) : OOB);
         }
       }
-      if constexpr (BG) {
+      if constexpr (BQ) {
+        bv[u][0] = bload(rb, live ? boff + (uint32_t)kchunk<WK>(m + u, 0, g) : OOB);
+      } else if constexpr (BG) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int k = kchunk<WK>(m + u, j, g);
@@ -190,7 +195,10 @@ struct Stream {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         bf16x8 b;
-        if constexpr (BG) {
+        if constexpr (BQ) {
+          const u32x4 q = bv[u][0];
+          b = fp8x8_to_bf16x8(j ? q[2] : q[0], j ? q[3] : q[1]);
+        } else if constexpr (BG) {
           b = __builtin_bit_cast(bf16x8, bv[u][j]);
         } else {
           const int k = kchunk<WK>(mu, j, g);
@@ -280,31 +288,55 @@ __device__ __forceinline__ float sumsq8(u32x4 q) {
   return s;
 }
 
+__device__ __forceinline__ double sumsq8_f64(u32x4 q) {
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const double lo = __uint_as_float(q[i] << 16), hi = __uint_as_float(q[i] & 0xFFFF0000u);
+    s += lo * lo + hi * hi;
+  }
+  return s;
+}
+
 // Stage token t (one wave).  With norm, f = c / sqrt(mean(x_t^2) + eps):
 //   vec given: s[t][k] = bf16(x[t][k] * f * vec[k]), fac[t] = 1
 //              (a learned per-dimension weight has to be applied before the dot product);
 //   otherwise: s[t] = x[t] unchanged, fac[t] = f, applied in fp32 to the dot products
 //              (a norm without a weight is a per-token factor: x_t / rms_t . w = (x_t . w) / rms_t).
 // Without norm the row is copied and fac[t] = 1.  r holds pass 0 when preloaded.
+// quant (FP8 activations, c = 1): the row the grouped path stores is formed first
+// (a normalised row in fp64 throughout, rounded to fp32 and then bf16, so that it
+// is the exactly rounded value and its codes do not depend on summation order),
+// then replaced by its codes at the row's scale, widened to bf16 (exact), and
+// fac[t] = the scale.
 __device__ void stage_token(RowRegs& r, bool preloaded, rsrc_t rx, int t, int H, bool norm, float eps, float c,
-                            const float* __restrict__ vec, bf16_t* s, int pitch, float* fac, int lane) {
+                            const float* __restrict__ vec, bf16_t* s, int pitch, float* fac, int lane,
+                            bool quant = false) {
   const int npass = (H + XCH * 512 - 1) / (XCH * 512);
   bf16_t* sr = s + t * pitch;
-  const bool xform = norm && vec;
+  const bool xform = norm && (vec || quant);
   float ss = 0.f;
+  double ssd = 0.0;
   for (int p = 0; p < npass; ++p) {
     if (p > 0 || !preloaded) row_load(r, rx, t, H, p, lane);
 #pragma unroll
     for (int ch = 0; ch < XCH; ++ch) {
       const int k = (p * XCH + ch) * 512 + lane * 8;
       if (k < H) {
-        if (norm) ss += sumsq8(r.q[ch]);
+        if (norm) {
+          if (quant) ssd += sumsq8_f64(r.q[ch]);
+          else ss += sumsq8(r.q[ch]);
+        }
         if (!xform) *(u32x4*)(sr + k) = r.q[ch];
       }
     }
   }
   float f = 1.f;
-  if (norm) f = c / sqrtf(wave_sum_f32(ss) / (float)H + eps);
+  double fd = 1.0;
+  if (norm) {
+    if (quant) fd = 1.0 / sqrt(wave_sum_f64(ssd) / (double)H + (double)eps);
+    else f = c / sqrtf(wave_sum_f32(ss) / (float)H + eps);
+  }
   if (xform) {
     for (int p = 0; p < npass; ++p) {
       if (npass > 1) row_load(r, rx, t, H, p, lane);  // one pass: the row is still in registers
@@ -315,14 +347,37 @@ __device__ void stage_token(RowRegs& r, bool preloaded, rsrc_t rx, int t, int H,
           u32x4 o;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float lo = __uint_as_float(r.q[ch][i] << 16) * f * vec[k + 2 * i];
-            const float hi = __uint_as_float(r.q[ch][i] & 0xFFFF0000u) * f * vec[k + 2 * i + 1];
+            const float xl = __uint_as_float(r.q[ch][i] << 16), xh = __uint_as_float(r.q[ch][i] & 0xFFFF0000u);
+            float lo, hi;
+            if (quant) {
+              lo = (float)((double)xl * fd * (vec ? (double)vec[k + 2 * i] : 1.0));
+              hi = (float)((double)xh * fd * (vec ? (double)vec[k + 2 * i + 1] : 1.0));
+            } else {
+              lo = xl * f * vec[k + 2 * i];
+              hi = xh * f * vec[k + 2 * i + 1];
+            }
             o[i] = pack_bf16x2(lo, hi);
           }
           *(u32x4*)(sr + k) = o;
         }
       }
     }
+  }
+  if (quant) {
+    // this lane reads back exactly the chunks it wrote above
+    float m = 0.f;
+    for (int k = lane * 8; k < H; k += 512) {
+      const u32x4 v = *(const u32x4*)(sr + k);
+      m = fmaxf(m, absmax8(make_uint4(v[0], v[1], v[2], v[3])));
+    }
+    const float sc = scale_of(wave_max_f32(m));
+    for (int k = lane * 8; k < H; k += 512) {
+      const u32x4 v = *(const u32x4*)(sr + k);
+      const uint2 q = codes8(make_uint4(v[0], v[1], v[2], v[3]), sc);
+      *(bf16x8*)(sr + k) = fp8x8_to_bf16x8(q.x, q.y);
+    }
+    if (lane == 0) fac[t] = sc;
+    return;
   }
   if (lane == 0) fac[t] = xform ? 1.f : f;
 }
@@ -544,8 +599,10 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
     }
   }
   // expert input rows: pre_feedforward_layernorm_2(x) with the dense branch, x otherwise
-  if (t0 < T) stage_token(xr0, true, rx, t0, H, a.dense != 0, a.eps, 1.f, a.dense ? a.g_pre2 : nullptr, sx, pitch, fac, lane);
-  if (t1 < T) stage_token(xr1, true, rx, t1, H, a.dense != 0, a.eps, 1.f, a.dense ? a.g_pre2 : nullptr, sx, pitch, fac, lane);
+  if (t0 < T)
+    stage_token(xr0, true, rx, t0, H, a.dense != 0, a.eps, 1.f, a.dense ? a.g_pre2 : nullptr, sx, pitch, fac, lane, a.aq != 0);
+  if (t1 < T)
+    stage_token(xr1, true, rx, t1, H, a.dense != 0, a.eps, 1.f, a.dense ? a.g_pre2 : nullptr, sx, pitch, fac, lane, a.aq != 0);
   __syncthreads();
   for (int i = threadIdx.x; i < T * Kp; i += PW * 64) s_flag[s_ids[i]] = 1;
   __syncthreads();
@@ -584,6 +641,17 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
       const int t = i / a.K, k = i % a.K;
       if (a.topk_w_out) a.topk_w_out[i] = s_w[t * Kp + k];
       if (a.topk_ids_out) a.topk_ids_out[i] = s_ids[t * Kp + k];
+    }
+    if (a.aq) {
+      for (int i = threadIdx.x; i < T * Kp; i += PW * 64) a.slot_w[i] = s_w[i];
+      for (int i = threadIdx.x; i < T; i += PW * 64) a.xscales[i] = fac[i];
+      // the staged codes (bf16 values of E4M3 codes, so re-encoding them is exact)
+      for (int i = threadIdx.x; i < T * (H / 8); i += PW * 64) {
+        const int t = i / (H / 8), k = (i % (H / 8)) * 8;
+        const u32x4 v = *(const u32x4*)(sx + t * pitch + k);
+        const uint2 q = codes8(make_uint4(v[0], v[1], v[2], v[3]), 1.f);
+        *(uint2*)(a.xcodes + (int64_t)t * H + k) = q;
+      }
     }
   };
 
@@ -640,7 +708,8 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
       if (slot >= 0) {
         const float gv = reduced<PW, 2>(red, 0, rho, t) * fac[t] * sg;
         const float uv = reduced<PW, 2>(red, 1, rho, t) * fac[t] * su;
-        const float h = apply_act_bf16(a.act, gv) * uv * s_w[slot];
+        // FP8 activations: h is quantised as stored, before the routing weight
+        const float h = apply_act_bf16(a.act, gv) * uv * (a.aq ? 1.f : s_w[slot]);
         ((bf16_t*)a.hbuf)[(int64_t)slot * I + i0 + rho] = f32_to_bf16(h);
       }
     }
@@ -797,29 +866,41 @@ __global__ __launch_bounds__(DW3 * 64) void decode_down_kernel(DecodeArgs a) {
     const int slot = spec ? slot_spec : a.rinfo[1 + Ep + u * 16 + col];
     const uint8_t* wbase = e < E ? (const uint8_t*)a.w2 + wbytes<WK>((int64_t)e * H * I)
                                  : (const uint8_t*)a.shared_w2 + (int64_t)(e - E) * H * I * 2;
-    Stream<WK, 1, true, WK == WK_BF16 ? DU_BF16 : DU_FP8> st;
-    st.ra[0] = make_rsrc(wbase, (uint32_t)wbytes<WK>((int64_t)H * I));
-    st.aoff[0] = (uint32_t)wbytes<WK>((int64_t)(n0 + col) * I);
-    if constexpr (WK == WK_FP4) {  // E8M0 scales [E, H, I/32]
-      st.kmax = I;
-      st.rs[0] = make_rsrc(a.mx2 + (int64_t)e * H * (I / 32), (uint32_t)(H * (I / 32)));
-      st.soff[0] = (uint32_t)((n0 + col) * (I / 32));
-    }
-    st.rb = rb;
-    st.boff = slot >= 0 ? (uint32_t)((int64_t)slot * I * 2) : OOB;
-    st.g = g;
+    auto prep = [&](auto& st, rsrc_t rbx, uint32_t bo) {
+      st.ra[0] = make_rsrc(wbase, (uint32_t)wbytes<WK>((int64_t)H * I));
+      st.aoff[0] = (uint32_t)wbytes<WK>((int64_t)(n0 + col) * I);
+      if constexpr (WK == WK_FP4) {  // E8M0 scales [E, H, I/32]
+        st.kmax = I;
+        st.rs[0] = make_rsrc(a.mx2 + (int64_t)e * H * (I / 32), (uint32_t)(H * (I / 32)));
+        st.soff[0] = (uint32_t)((n0 + col) * (I / 32));
+      }
+      st.rb = rbx;
+      st.boff = bo;
+      st.g = g;
+    };
     f32x4 sc = {1.f, 1.f, 1.f, 1.f};  // fp8 per-output-channel scales of this lane's rows, loaded early
+    float cf = 1.f;                    // FP8 activations: this lane's slot's h scale times its routing weight
     if constexpr (WK == WK_FP8) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) sc[v] = a.s2[(int64_t)e * H + n0 + 4 * g + v];
+      if (a.aq) cf = slot >= 0 ? a.hscales[slot] * a.slot_w[slot] : 0.f;
     }
     f32x4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
     int s0, s1;
     sub_range<WK>(k0, k1, s, S, s0, s1);
-    st.run(acc, nullptr, false, s0, s1, false);
+    if (WK == WK_FP8 && a.aq) {
+      // B: the slot's h codes (the h scale is in cf)
+      Stream<WK, 1, true, DU_FP8, WK == WK_FP8> st;
+      prep(st, make_rsrc(a.hcodes, (uint32_t)((int64_t)T * a.Kp * I)), slot >= 0 ? (uint32_t)((int64_t)slot * I) : OOB);
+      st.run(acc, nullptr, false, s0, s1, false);
+    } else {
+      Stream<WK, 1, true, WK == WK_BF16 ? DU_BF16 : DU_FP8> st;
+      prep(st, rb, slot >= 0 ? (uint32_t)((int64_t)slot * I * 2) : OOB);
+      st.run(acc, nullptr, false, s0, s1, false);
+    }
     if constexpr (WK == WK_FP8) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) tot[v] += sc[v] * acc[0][v];
+      for (int v = 0; v < 4; ++v) tot[v] += sc[v] * acc[0][v] * cf;
     } else {
       tot += acc[0];
     }

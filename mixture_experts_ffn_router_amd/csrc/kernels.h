@@ -154,6 +154,17 @@ struct DecodeArgs {
   float* out_f32;
   float* topk_w_out;
   int32_t* topk_ids_out;
+  // FP8 activations (FP8 expert weights, expert inputs quantised per row): the up
+  // kernel stages the codes of each token's expert input (scale = max / 448)
+  // widened to bf16 and stores h unweighted; launch_quant_rows_fp8 turns h into
+  // hcodes / hscales; the down kernel takes the codes and applies each slot's
+  // scale and routing weight to its expert's partial tile.
+  int aq;
+  uint8_t* xcodes;      // [T, H] x codes and [T] scales, written by the first expert block
+  float* xscales;
+  const uint8_t* hcodes;  // [T * Kp, I]
+  const float* hscales;   // [T * Kp]
+  float* slot_w;        // [T * Kp] routing weight of each slot, written by the first expert block
 };
 
 int decode_up_lds_bytes(int T, int H, int Kp, int Ep);

@@ -19,37 +19,6 @@ namespace {
 constexpr int QT = 256;
 constexpr int QMAXV = 8;  // 16-byte loads per lane
 
-__device__ __forceinline__ float absmax8(uint4 x) {
-  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-  float m = 0.f;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    m = fmaxf(m, fabsf(__uint_as_float(w[q] << 16)));
-    m = fmaxf(m, fabsf(__uint_as_float(w[q] & 0xFFFF0000u)));
-  }
-  return m;
-}
-
-// codes of the 8 bf16 values in x at scale s, in order (two dwords of 4 codes)
-__device__ __forceinline__ uint2 codes8(uint4 x, float s) {
-  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-  uint32_t out[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const float f0 = __uint_as_float(w[2 * h] << 16) / s, f1 = __uint_as_float(w[2 * h] & 0xFFFF0000u) / s;
-    const float f2 = __uint_as_float(w[2 * h + 1] << 16) / s, f3 = __uint_as_float(w[2 * h + 1] & 0xFFFF0000u) / s;
-    int p = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
-    p = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, p, true);
-    out[h] = (uint32_t)p;
-  }
-  return make_uint2(out[0], out[1]);
-}
-
-__device__ __forceinline__ float scale_of(float amax) {
-  const float s = amax / 448.0f;
-  return s > 0.f ? s : 1.f;
-}
-
 // Rows handled by NTH threads each (64: a wavefront; QT: the block).  Returns
 // false for rows that need no work (past the count, or padding set to zeros).
 template <int NTH>

@@ -202,10 +202,10 @@ def test_permute_capacity():
     assert lib.moe_permute_capacity(-1, 2, 8, 64) == -1
 
 
-def test_fp8_activation_layers_take_the_grouped_path():
+def test_fp8_activation_layers_take_the_decode_path_up_to_16_tokens():
     lib = _lib()
     d = _desc(act_quant=1, weight_dtype=B.DT_FP8)
-    assert [lib.moe_forward_path(C.byref(d), t) for t in (1, 4, 16, 4096)] == [0, 0, 0, 0]
+    assert [lib.moe_forward_path(C.byref(d), t) for t in (1, 4, 16, 17, 4096)] == [1, 1, 1, 0, 0]
     d0 = _desc(weight_dtype=B.DT_FP8)
     assert lib.moe_forward_path(C.byref(d0), 4) == 1
     # the workspace holds the codes and scales of x and h as well

@@ -60,18 +60,27 @@ def staged_fp8_act_check(L, r, rows, ref):
     against the oracle (x's exactly, h within one bf16 step: the FP8 MFMA
     accumulates differently from float64, which moves h's rounding now and then),
     and the rest of the layer is checked on the GPU's codes, as routing parity
-    takes the GPU's logits.  Returns the oracle on the GPU's h codes."""
+    takes the GPU's logits.  Returns the oracle on the GPU's h codes.
+
+    The decode path keeps neither the normalised expert input nor per-slot down
+    rows (its down kernel sums a token's slots in the accumulator): its x codes
+    are checked against the oracle's own normalised input, its h rows are per
+    slot, and its down projection is covered by the layer check on its h codes."""
     spec, ws, layer = L["spec"], r["ws"], W.oracle_layer(L)
     T, H, I, K = L["T"], spec.H, spec.I, spec.K
     x = to64(L["x"])
     rows = np.arange(T) if rows is None else np.asarray(rows)
-    assert ws["path"] == "grouped" and ws["slots_per_token"] == K
+    decode = ws["path"] == "decode"
+    assert ws["path"] in ("grouped", "decode") and ws["slots_per_token"] == K
     # x: the expert input as stored, then its codes and scales
     if spec.I_dense:
-        xe = to64(ws["x_expert"])
         g2 = layer["dense"].get("gamma_pre2")
-        assert np.array_equal(xe, O.round_bf16(O.rmsnorm(x, g2, layer.get("eps", O.RMS_EPS)))), \
-            "stored expert input differs from the oracle's"
+        xe_ref = O.round_bf16(O.rmsnorm(x, g2, layer.get("eps", O.RMS_EPS)))
+        if decode:
+            xe = xe_ref
+        else:
+            xe = to64(ws["x_expert"])
+            assert np.array_equal(xe, xe_ref), "stored expert input differs from the oracle's"
     else:
         xe = x
     xc, xs = O.quantize_rows_fp8(xe)
@@ -80,7 +89,7 @@ def staged_fp8_act_check(L, r, rows, ref):
     # h of the checked tokens' slots, at their padded rows
     ids = ref["ids"]
     slot = (rows[:, None] * K + np.arange(K)[None, :]).reshape(-1)
-    prow = ws["slot_row"].cpu().numpy()[slot]
+    prow = slot if decode else ws["slot_row"].cpu().numpy()[slot]
     h_gpu = to64(ws["h"][torch.from_numpy(prow).cuda().long()])
     hc_gpu = ws["h_codes"][torch.from_numpy(prow).cuda().long()].cpu().numpy()
     hs_gpu = ws["h_scales"][torch.from_numpy(prow).cuda().long()].cpu().numpy()
@@ -115,6 +124,8 @@ def staged_fp8_act_check(L, r, rows, ref):
     assert np.array_equal(hs_gpu, hs), "h scales"
     # down projection and routing weight of each slot, on the GPU's h codes
     yp = ws["y_parts"]
+    if decode:
+        return _layer_on_codes(L, r, rows, x, layer, hc, hs, moved)
     if yp:
         y_rows = torch.from_numpy((slot[:, None] * yp + np.arange(yp)[None, :]).reshape(-1)).cuda().long()
         y_parts = to64(ws["y"][y_rows].float()).reshape(len(slot), yp, H)
@@ -141,7 +152,12 @@ def staged_fp8_act_check(L, r, rows, ref):
     print(f"  down: max-abs {ma:.3e} (max {mx:.3f}) rel-RMS {rr:.3e}; beyond storage rounding at most "
           f"{yover.max():.3e} of the accumulation magnitude", flush=True)
     assert (yover <= 2.0 ** -12).all(), "down projection off by more than its storage and accumulation rounding"
-    # the whole layer on the GPU's h codes
+    return _layer_on_codes(L, r, rows, x, layer, hc, hs, moved)
+
+
+def _layer_on_codes(L, r, rows, x, layer, hc, hs, moved):
+    """The oracle's layer on the GPU's h codes (rows: the checked tokens)."""
+    T, I, K = L["T"], L["spec"].I, L["spec"].K
     codes = np.zeros((T, K, I), np.uint8)
     scales = np.ones((T, K), np.float32)
     codes[rows] = hc.reshape(len(rows), K, I)
@@ -365,6 +381,18 @@ DECODE = {
     "mxfp4_gemma_tail": W.LayerSpec("dec_mxfp4_tail", 1, 256, 16, 4, 128, "gelu_tanh", "mxfp4",
                                     router_mode="gemma", per_expert_scale="uniform", I_dense=192,
                                     random_gammas=True, block_tail=True),
+    # FP8 activations: x quantised in the staging of the gate/up kernel, h by the
+    # row quantisation between gate/up and down; computed and supplied logits, a
+    # row of 320 (two staging passes), the Gemma branch with learned and with unit
+    # norm weights (the expert input normalised and quantised as stored)
+    "w8a8_plain": W.LayerSpec("dec_w8a8", 1, 256, 16, 4, 192, "gelu_tanh", "fp8", act_quant="fp8_dynamic"),
+    "w8a8_supplied_h320": W.LayerSpec("dec_w8a8_h320", 1, 320, 8, 2, 256, "silu", "fp8", supplied_logits=True,
+                                      per_expert_scale="uniform", act_quant="fp8_dynamic"),
+    "gemma_w8a8_gammas_tail": W.LayerSpec("dec_gemma_w8a8", 1, 256, 16, 4, 128, "gelu_tanh", "fp8",
+                                          router_mode="gemma", per_expert_scale="uniform", I_dense=192,
+                                          random_gammas=True, block_tail=True, act_quant="fp8_dynamic"),
+    "gemma_w8a8_unit_norms": W.LayerSpec("dec_gemma_w8a8_u", 1, 256, 8, 2, 256, "gelu_tanh", "fp8",
+                                         router_mode="gemma", I_dense=128, act_quant="fp8_dynamic"),
 }
 DECODE_T = {"h8192": (1, 8), "e512_k64_bf16": (16,), "e512_k64_mxfp4": (16,)}
 
@@ -404,7 +432,7 @@ def test_decode_deterministic_and_workspace_reuse(B):
 FULL = [("tiny", 64), ("mixtral", 1), ("mixtral", 4096), ("gemma", 1), ("gemma", 16), ("gemma", 128),
         ("gemma", 8192), ("deepseek", 16), ("deepseek", 16384), ("skewed_fp8", 1), ("skewed_fp8", 4096),
         ("deepseek_v3", 1), ("deepseek_v3", 16), ("deepseek_v3", 8192),
-        ("mixtral_w8a8", 4096), ("skewed_w8a8", 1), ("skewed_w8a8", 4096), ("gemma_block", 1), ("gemma_block", 8192),
+        ("mixtral_w8a8", 1), ("mixtral_w8a8", 4096), ("skewed_w8a8", 1), ("skewed_w8a8", 16), ("skewed_w8a8", 4096), ("gemma_block", 1), ("gemma_block", 8192),
         ("gemma_w8a8", 8192), ("gemma_mxfp4", 1), ("gemma_mxfp4", 16), ("mixtral_mxfp4", 1)]
 
 
