@@ -128,6 +128,12 @@ def stage_work(spec, T, counts, path, dense_stage=None):
         by["router"] = z * (E * H * ab + T * E * 4 + T * H * ab)
         by["gate_up"] = w_up + T * H * ab + T * Kp * I * ab
         by["down"] = w_down + T * Kp * I * ab + T * H * (4 if Id else ab) + (H * Id * ab + T * Id * ab + T * H * 4 if Id else 0)
+        if spec.act_quant:
+            # the gate/up launch also writes x's codes and scales; the h rows are
+            # quantised between the launches; the down launch reads 1-byte codes
+            by["gate_up"] += T * H + T * 4
+            by["quant_h"] = T * Kp * I * ab + T * Kp * I + T * Kp * 4
+            by["down"] -= T * Kp * I * (ab - 1)
         if Id:
             fl[dense_stage] += dgu_fl
             by[dense_stage] += dgu_by
@@ -177,7 +183,7 @@ def launched_stages(spec, path, dense_stage, raw_ms, marker_ms):
     their event record)."""
     supplied, dense = spec.supplied_logits, spec.I_dense > 0
     if path == "decode":
-        st = {"gate_up", "down"}
+        st = {"gate_up", "down"} | ({"quant_h"} if spec.act_quant else set())
         if not supplied or (dense and dense_stage == "router"):
             st.add("router")
         # finalize: with the dense branch, or when the down kernel splits its
