@@ -574,9 +574,9 @@ static moe_status forward_impl(const moe_layer_desc* desc, const moe_tensors* t,
       a.slot_w = (float*)(ws + p.o_slotw);
     }
     const int wk = d.weight_dtype == MOE_DT_FP8_E4M3 ? 1 : (d.weight_dtype == MOE_DT_MXFP4 ? 2 : 0);
-    // the bf16 / MXFP4 down kernel stages the routing summary in a 520-entry LDS
-    // table; E <= 512 and at most 8 shared experts keep max_active within it
-    if (wk != 1 && a.max_active > 520)
+    // the down kernel stages the routing summary in a 520-entry LDS table; E <= 512
+    // and at most 8 shared experts keep max_active within it
+    if (a.max_active > 520)
       return fail(MOE_UNSUPPORTED, "decode: %d active experts exceed the routing table", a.max_active);
     STAGE(MOE_STAGE_PRENORM);
     STAGE(MOE_STAGE_ROUTER);

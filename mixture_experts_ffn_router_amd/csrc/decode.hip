@@ -60,6 +60,7 @@ constexpr int DU_PRE = 6;   // router kernel: few blocks, one batch per wave
 constexpr int DU_BF16 = 2;  // streaming kernels, bf16 weights
 constexpr int DU_FP8 = 6;   // streaming kernels, fp8 weights
 constexpr int DU_FP4 = 4;   // MXFP4 weights, whole-item streams: 2 pairs per batch, two batches in flight
+constexpr int DU_FP8W = 4;  // fp8 weights, whole-item streams: the bytes of a bf16 batch
 constexpr int XCH = 8;  // 16-byte chunks per lane of a token row held in registers (4096 elements)
 
 // Lane l feeds row / token column l & 15 and reduction elements from lane group
@@ -472,7 +473,7 @@ __global__ __launch_bounds__(PW * 64, 2) void decode_pre_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------- up: dense gate/up, routing + expert gate/up
-// Expert gate/up (bf16 or MXFP4 weights): one wave owns whole (expert, 16
+// Expert gate/up (bf16, fp8 or MXFP4 weights): one wave owns whole (expert, 16
 // hidden units) items, so the MFMA accumulator holds each item's complete
 // 16 x 16 tiles and the epilogue needs no reduction across waves and no
 // barrier.  A wave's items are one flat sequence of batches streamed through
@@ -482,8 +483,7 @@ template <int WK>
 __device__ __forceinline__ void up_items_per_wave(const DecodeArgs& a, const int16_t* s_slot, const float* s_w,
                                                   const int* s_active, const float* fac, const bf16_t* sx,
                                                   int pitch, int n_items, int gw, int lane) {
-  static_assert(WK != WK_FP8, "fp8 weights keep the block-wide item loop");
-  constexpr int DU = WK == WK_FP4 ? DU_FP4 : DU_BF16;
+  constexpr int DU = WK == WK_FP4 ? DU_FP4 : (WK == WK_FP8 ? DU_FP8W : DU_BF16);
   using S = Stream<WK, 2, false, DU>;
   const int T = a.T, H = a.H, I = a.I, E = a.E, Kp = a.Kp, RG = I / 16;
   const int g = lane >> 4, col = lane & 15;
@@ -494,13 +494,24 @@ __device__ __forceinline__ void up_items_per_wave(const DecodeArgs& a, const int
   const int BPI = (m1 - m0 + DU - 1) / DU;  // batches per item
   const int NB = (it1 - it0) * BPI;
   S s0, s1;
+  // fp8 weights: the per-output-channel scales of each set's item (gate and up
+  // rows of hidden units i0 + 4g .. + 3), loaded with every batch of the item
+  f32x4 sg0 = {1.f, 1.f, 1.f, 1.f}, su0 = sg0, sg1 = sg0, su1 = sg0;
   // batch b >= NB issues loads outside every buffer (no traffic) so that the
   // loop issues the same loads on every path and each wait covers one batch
-  auto issue = [&](S& st, int b) {
+  auto issue = [&](S& st, f32x4& sg, f32x4& su, int b) {
     const bool live = b < NB;
     const int bb = live ? b : 0;
     const int item = it0 + bb / BPI;
     const int e = s_active[item / RG], i0 = (item % RG) * 16;
+    if constexpr (WK == WK_FP8) {
+      const float* sp = a.s13 + (live ? (int64_t)e * 2 * I + i0 + 4 * g : 0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        sg[v] = sp[v];
+        su[v] = sp[(live ? I : 0) + v];
+      }
+    }
     st.g = g;
     // shared experts (ids E.., bf16 layers only) follow the routed ones
     const uint8_t* wbase = e < E ? (const uint8_t*)a.w13 + wbytes<WK>((int64_t)e * 2 * I * H)
@@ -519,7 +530,7 @@ __device__ __forceinline__ void up_items_per_wave(const DecodeArgs& a, const int
   f32x4 acc[2];
   // batch b: compute; the last batch of an item runs its epilogue.  Tile element
   // (hidden unit 4g + v, token col) sits in register v of this lane.
-  auto step = [&](S& st, int b) {
+  auto step = [&](S& st, const f32x4& sg, const f32x4& su, int b) {
     const int item = it0 + b / BPI, bi = b % BPI;
     const int i0 = (item % RG) * 16;
     const int slot = col < T ? s_slot[(item / RG) * 16 + col] : -1;
@@ -527,11 +538,23 @@ __device__ __forceinline__ void up_items_per_wave(const DecodeArgs& a, const int
     st.compute(acc, sx + (slot >= 0 ? col : 0) * pitch, slot >= 0, m0 + bi * DU, m1);
     if (bi == BPI - 1 && slot >= 0) {
       uint32_t packed[2];
+      if constexpr (WK == WK_FP8) {
+        // FP8 activations: h is quantised as stored, before the routing weight
+        const float w = a.aq ? 1.f : s_w[slot];
 #pragma unroll
-      for (int v = 0; v < 4; v += 2) {
-        const float h0 = apply_act_bf16(a.act, acc[0][v] * fac[col]) * (acc[1][v] * fac[col]) * s_w[slot];
-        const float h1 = apply_act_bf16(a.act, acc[0][v + 1] * fac[col]) * (acc[1][v + 1] * fac[col]) * s_w[slot];
-        packed[v / 2] = (uint32_t)f32_to_bf16(h0) | ((uint32_t)f32_to_bf16(h1) << 16);
+        for (int v = 0; v < 4; v += 2) {
+          const float h0 = apply_act_bf16(a.act, acc[0][v] * fac[col] * sg[v]) * (acc[1][v] * fac[col] * su[v]) * w;
+          const float h1 =
+              apply_act_bf16(a.act, acc[0][v + 1] * fac[col] * sg[v + 1]) * (acc[1][v + 1] * fac[col] * su[v + 1]) * w;
+          packed[v / 2] = (uint32_t)f32_to_bf16(h0) | ((uint32_t)f32_to_bf16(h1) << 16);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; v += 2) {
+          const float h0 = apply_act_bf16(a.act, acc[0][v] * fac[col]) * (acc[1][v] * fac[col]) * s_w[slot];
+          const float h1 = apply_act_bf16(a.act, acc[0][v + 1] * fac[col]) * (acc[1][v + 1] * fac[col]) * s_w[slot];
+          packed[v / 2] = (uint32_t)f32_to_bf16(h0) | ((uint32_t)f32_to_bf16(h1) << 16);
+        }
       }
       *(u32x2*)((bf16_t*)a.hbuf + (int64_t)slot * I + i0 + 4 * g) = u32x2{packed[0], packed[1]};
     }
@@ -539,16 +562,16 @@ __device__ __forceinline__ void up_items_per_wave(const DecodeArgs& a, const int
   // Two batches ahead: a set is reloaded right after it is consumed, so each
   // wait covers the older set only (sched_barrier keeps the order).
   if (NB > 0) {
-    issue(s0, 0);
-    issue(s1, 1);
+    issue(s0, sg0, su0, 0);
+    issue(s1, sg1, su1, 1);
   }
   for (int b = 0; b < NB; b += 2) {
     __builtin_amdgcn_sched_barrier(0);
-    step(s0, b);
-    issue(s0, b + 2);
+    step(s0, sg0, su0, b);
+    issue(s0, sg0, su0, b + 2);
     __builtin_amdgcn_sched_barrier(0);
-    if (b + 1 < NB) step(s1, b + 1);
-    issue(s1, b + 3);
+    if (b + 1 < NB) step(s1, sg1, su1, b + 1);
+    issue(s1, sg1, su1, b + 3);
   }
 }
 
@@ -662,15 +685,13 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
   int m0, m1;
   sub_range<WK>(0, H / 64, wave, PW, m0, m1);
   // Whole items per wave when items are plentiful (every block sees the same
-  // n_items): at least one per wave for bf16 weights, one per two waves for
-  // MXFP4, whose items carry a quarter of the bytes, so that a block-wide
+  // n_items): at least one per wave for bf16 and fp8 weights, one per two waves
+  // for MXFP4, whose items carry a quarter of the bytes, so that a block-wide
   // reduction per item costs more than the item's stream
-  if constexpr (WK != WK_FP8) {
-    if ((WK == WK_FP4 ? 2 : 1) * n_items >= a.n_up_blocks * PW) {
-      up_items_per_wave<WK>(a, s_slot, s_w, s_active, fac, sx, pitch, n_items, blk * PW + wave, lane);
-      publish();
-      return;
-    }
+  if ((WK == WK_FP4 ? 2 : 1) * n_items >= a.n_up_blocks * PW) {
+    up_items_per_wave<WK>(a, s_slot, s_w, s_active, fac, sx, pitch, n_items, blk * PW + wave, lane);
+    publish();
+    return;
   }
   for (int item = it0; item < it1; ++item) {
     const int u = item / RG, i0 = (item % RG) * 16;
@@ -718,7 +739,7 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
   publish();
 }
 
-// Expert down projection (bf16 or MXFP4 weights) of one (16 output features,
+// Expert down projection (bf16, fp8 or MXFP4 weights) of one (16 output features,
 // part) block: this wave's units (active expert u, split s) for unit = wave,
 // wave + DW3, ... as one flat sequence of batches through two register sets
 // (the next batch in flight while the current one computes), all summed into
@@ -727,14 +748,18 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
 // the active count (entries past it are in bounds and unused), so the first
 // weight loads wait for one round trip and one barrier.
 constexpr int MAX_ACTIVE_DOWN = 520;  // E <= 512 routed + 8 shared experts
-template <int WK>
+// fp8 weights: each unit's tile is summed in an accumulator of its own, then
+// scaled by its expert's channel scales (and, BQ: B are the slots' h codes, by
+// the slot's h scale times routing weight) and added.
+// s_e [MAX_ACTIVE_DOWN], s_slot [MAX_ACTIVE_DOWN * 16]: the kernel's LDS table.
+template <int WK, bool BQ>
 __device__ __forceinline__ f32x4 down_units(const DecodeArgs& a, int n_act, int S, int k0, int k1, int n0,
-                                            int wave, int lane) {
-  static_assert(WK != WK_FP8, "fp8 weights scale each unit's tile by its channel scales");
-  __shared__ int s_e[MAX_ACTIVE_DOWN];
-  __shared__ int s_slot[MAX_ACTIVE_DOWN * 16];
-  constexpr int DU = WK == WK_FP4 ? DU_FP4 : DU_BF16;
-  using St = Stream<WK, 1, true, DU>;
+                                            int wave, int lane, int* s_e, int* s_slot) {
+  static_assert(!BQ || WK == WK_FP8, "h codes go with fp8 weights");
+  // fp8 weights with bf16 h rows: two steps per batch (their B loads take twice
+  // the registers of the codes' loads), which keeps two blocks per CU
+  constexpr int DU = WK == WK_FP4 ? DU_FP4 : (WK == WK_FP8 ? (BQ ? DU_FP8W : 2) : DU_BF16);
+  using St = Stream<WK, 1, true, DU, BQ>;
   const int H = a.H, I = a.I, E = a.E, Ep = a.Ep, g = lane >> 4, col = lane & 15;
   const int MA = a.max_active;
   {  // four loads in flight per thread before their stores (one round trip up to 2048 slots)
@@ -761,12 +786,15 @@ __device__ __forceinline__ f32x4 down_units(const DecodeArgs& a, int n_act, int 
   const int spu = WK == WK_FP4 ? 2 * (((k1 - k0 + 1) / 2 + S - 1) / S) : (k1 - k0 + S - 1) / S;
   const int BPU = (spu + DU - 1) / DU;  // batches per unit, at most
   const int NB = NJ * BPU;
-  const rsrc_t rb = make_rsrc(a.hbuf, (uint32_t)((int64_t)a.T * a.Kp * I * 2));
+  const rsrc_t rb = BQ ? make_rsrc(a.hcodes, (uint32_t)((int64_t)a.T * a.Kp * I))
+                      : make_rsrc(a.hbuf, (uint32_t)((int64_t)a.T * a.Kp * I * 2));
   St s0, s1;
   int m_0 = 0, e_0 = 0, m_1 = 0, e_1 = 0;  // each set's first step and end step
+  f32x4 sc0 = {1.f, 1.f, 1.f, 1.f}, sc1 = sc0;  // fp8: each set's unit's channel scales (rows n0 + 4g ..)
+  float cf0 = 1.f, cf1 = 1.f;                   // BQ: each set's unit's slot h scale x routing weight
   // batch b >= NB (and steps past a unit's range) load outside every buffer, so
   // the same loads are issued and consumed on every path
-  auto issue = [&](St& st, int& mb, int& me, int b) {
+  auto issue = [&](St& st, int& mb, int& me, f32x4& sc, float& cf, int b) {
     const bool live = b < NB;
     const int bb = live ? b : 0;
     const int unit = wave + DW3 * (bb / BPU), bi = bb % BPU;
@@ -788,28 +816,49 @@ __device__ __forceinline__ f32x4 down_units(const DecodeArgs& a, int n_act, int 
       st.soff[0] = (uint32_t)((n0 + col) * (I / 32));
     }
     st.rb = rb;
-    st.boff = slot >= 0 ? (uint32_t)((int64_t)slot * I * 2) : OOB;
+    st.boff = slot >= 0 ? (uint32_t)((int64_t)slot * I * (BQ ? 1 : 2)) : OOB;
+    if constexpr (WK == WK_FP8) {
+      const float* sp = a.s2 + (live ? (int64_t)e * H + n0 + 4 * g : 0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sc[v] = sp[v];
+      if constexpr (BQ) cf = (live && slot >= 0) ? a.hscales[slot] * a.slot_w[slot] : 0.f;
+    }
     st.load(mb, me);
   };
-  f32x4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
+  f32x4 acc[1] = {{0.f, 0.f, 0.f, 0.f}}, uacc[1] = {{0.f, 0.f, 0.f, 0.f}};
+  auto comp = [&](St& st, int mb, int me, const f32x4& sc, float cf, int b) {
+    if constexpr (WK == WK_FP8) {
+      const int bi = b % BPU;
+      if (bi == 0) uacc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      st.compute(uacc, nullptr, false, mb, me);
+      if (bi == BPU - 1) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[0][v] += sc[v] * uacc[0][v] * cf;
+      }
+    } else {
+      st.compute(acc, nullptr, false, mb, me);
+    }
+  };
   // sched_barrier: each batch's loads are issued before the other set's MFMAs
-  if (NB > 0) issue(s0, m_0, e_0, 0);
+  if (NB > 0) issue(s0, m_0, e_0, sc0, cf0, 0);
   for (int b = 0; b < NB; b += 2) {
-    issue(s1, m_1, e_1, b + 1);
+    issue(s1, m_1, e_1, sc1, cf1, b + 1);
     __builtin_amdgcn_sched_barrier(0);
-    s0.compute(acc, nullptr, false, m_0, e_0);
+    comp(s0, m_0, e_0, sc0, cf0, b);
     if (b + 1 >= NB) break;
-    issue(s0, m_0, e_0, b + 2);
+    issue(s0, m_0, e_0, sc0, cf0, b + 2);
     __builtin_amdgcn_sched_barrier(0);
-    s1.compute(acc, nullptr, false, m_1, e_1);
+    comp(s1, m_1, e_1, sc1, cf1, b + 1);
   }
   return acc[0];
 }
 
 // ---------------------------------------------------------------- down: dense down, expert down + combine
 template <int WK>
-__global__ __launch_bounds__(DW3 * 64) void decode_down_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(DW3 * 64, 4) void decode_down_kernel(DecodeArgs a) {
   __shared__ float red[DW3 * 4 * 64];
+  __shared__ int s_e[MAX_ACTIVE_DOWN];          // staged routing summary (down_units)
+  __shared__ int s_slot[MAX_ACTIVE_DOWN * 16];
   const int T = a.T, H = a.H, I = a.I, E = a.E, Ep = a.Ep;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, g = lane >> 4, col = lane & 15;
 
@@ -853,11 +902,12 @@ __global__ __launch_bounds__(DW3 * 64) void decode_down_kernel(DecodeArgs a) {
   const int n_units = n_act * S;
   const rsrc_t rb = make_rsrc(a.hbuf, (uint32_t)((int64_t)T * a.Kp * I * 2));
   f32x4 tot = {0.f, 0.f, 0.f, 0.f};
-  // bf16 / MXFP4 with more units than waves: staged routing summary and a
-  // two-deep stream over each wave's units (n_units is the same in every wave)
-  const bool staged = WK != WK_FP8 && n_units > DW3;
-  if constexpr (WK != WK_FP8) {
-    if (staged) tot = down_units<WK>(a, n_act, S, k0, k1, n0, wave, lane);
+  // more units than waves: staged routing summary and a two-deep stream over
+  // each wave's units (n_units is the same in every wave)
+  const bool staged = n_units > DW3;
+  if (staged) {
+    if (WK == WK_FP8 && a.aq) tot = down_units<WK, WK == WK_FP8>(a, n_act, S, k0, k1, n0, wave, lane, s_e, s_slot);
+    else tot = down_units<WK, false>(a, n_act, S, k0, k1, n0, wave, lane, s_e, s_slot);
   }
   for (int unit = wave; !staged && unit < n_units; unit += DW3) {
     const int u = unit / S, s = unit % S;
