@@ -393,8 +393,14 @@ DECODE = {
                                           random_gammas=True, block_tail=True, act_quant="fp8_dynamic"),
     "gemma_w8a8_unit_norms": W.LayerSpec("dec_gemma_w8a8_u", 1, 256, 8, 2, 256, "gelu_tanh", "fp8",
                                          router_mode="gemma", I_dense=128, act_quant="fp8_dynamic"),
+    # fp8 weights on the whole-items-per-wave gate/up stream (8 experts x 512 items at
+    # T=16: one item per wave or more) and the staged down stream, with bf16 h rows and
+    # with FP8 activations (h codes)
+    "wide_fp8": W.LayerSpec("dec_wide_fp8", 1, 320, 8, 2, 8192, "silu", "fp8", supplied_logits=True),
+    "wide_w8a8": W.LayerSpec("dec_wide_w8a8", 1, 320, 8, 2, 8192, "gelu_tanh", "fp8", act_quant="fp8_dynamic"),
 }
-DECODE_T = {"h8192": (1, 8), "e512_k64_bf16": (16,), "e512_k64_mxfp4": (16,)}
+DECODE_T = {"h8192": (1, 8), "e512_k64_bf16": (16,), "e512_k64_mxfp4": (16,), "wide_fp8": (8, 16),
+            "wide_w8a8": (8, 16)}
 
 
 @pytest.mark.parametrize("name,T", [(n, t) for n in DECODE for t in DECODE_T.get(n, (1, 5, 16))],
