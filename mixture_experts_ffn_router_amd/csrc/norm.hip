@@ -18,6 +18,8 @@
 //         post_feedforward_layernorm and the residual add of section 1)
 // The per-slot rows were already multiplied by their routing weights; out is
 // rounded once, at the end.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -121,8 +123,11 @@ __device__ __forceinline__ void st8(float* p, const float* v) {
   *(float4*)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-// One block per token; thread g owns elements [8g, 8g + 8) (+ NT*8 strides).
-template <typename TY, typename TO>
+// One block per token; thread g owns elements [8g, 8g + 8) (+ NT*8 strides), G
+// groups of them (H <= NT * 8 * G).  The dense branch's and the residual's rows
+// are loaded first, so their loads are in flight with the slot rows' (one round
+// trip per block, not three); the residual stays raw until it is used.
+template <typename TY, typename TO, int G>
 __global__ __launch_bounds__(NT) void finalize_kernel(const TY* __restrict__ ybuf, int Kp,
                                                       const float* __restrict__ dense_out,
                                                       const float* __restrict__ g1, const float* __restrict__ g2,
@@ -131,9 +136,23 @@ __global__ __launch_bounds__(NT) void finalize_kernel(const TY* __restrict__ ybu
                                                       const TO* __restrict__ resid,
                                                       const float* __restrict__ gff) {
   __shared__ float s_red[NT / 64];
-  constexpr int G = 4;  // H <= NT * 8 * G
+  constexpr bool RB = std::is_same<TO, bf16_t>::value;  // residual rows in bf16 (else fp32)
   const int64_t t = blockIdx.x;
   const int ng = H / 8;
+  float d[G][8];
+  uint4 rr[G][RB ? 1 : 2];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int idx = threadIdx.x + g * NT;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) d[g][q] = 0.f;
+    if (dense_out && idx < ng) ld8(dense_out + t * H + idx * 8, d[g]);
+    if (tail && idx < ng) {
+      const uint4* rp = (const uint4*)(resid + t * H + idx * 8);
+      rr[g][0] = rp[0];
+      if constexpr (!RB) rr[g][RB ? 0 : 1] = rp[1];
+    }
+  }
   float m[G][8];
 #pragma unroll
   for (int g = 0; g < G; ++g)
@@ -163,15 +182,11 @@ __global__ __launch_bounds__(NT) void finalize_kernel(const TY* __restrict__ ybu
 #pragma unroll
       for (int q = 0; q < 8; ++q) o[g][q] = m[g][q];
   } else {
-    float d[G][8];
     float ssm = 0.f, ssd = 0.f;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int idx = threadIdx.x + g * NT;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) d[g][q] = 0.f;
       if (idx < ng) {
-        ld8(dense_out + t * H + idx * 8, d[g]);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           ssm += m[g][q] * m[g][q];
@@ -206,7 +221,23 @@ __global__ __launch_bounds__(NT) void finalize_kernel(const TY* __restrict__ ybu
       const int idx = threadIdx.x + g * NT;
       if (idx < ng) {
         float r[8];
-        ld8(resid + t * H + idx * 8, r);
+        if constexpr (RB) {
+          const uint32_t w[4] = {rr[g][0].x, rr[g][0].y, rr[g][0].z, rr[g][0].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            r[2 * i] = __uint_as_float(w[i] << 16);
+            r[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+          }
+        } else {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint4 u = rr[g][RB ? 0 : h];
+            r[4 * h] = __uint_as_float(u.x);
+            r[4 * h + 1] = __uint_as_float(u.y);
+            r[4 * h + 2] = __uint_as_float(u.z);
+            r[4 * h + 3] = __uint_as_float(u.w);
+          }
+        }
 #pragma unroll
         for (int q = 0; q < 8; ++q) o[g][q] = r[q] + o[g][q] * io * (gff ? gff[idx * 8 + q] : 1.f);
       }
@@ -256,21 +287,27 @@ hipError_t launch_finalize(const void* ybuf, int yelem, int Kp, const float* den
   if (H > NT * 32 || H % 8) return hipErrorInvalidValue;
   const bool tail = resid != nullptr;
   dim3 g((unsigned)T), b(NT);
-  if (yelem == ELEM_F32 && oelem == ELEM_F32)
-    finalize_kernel<float, float><<<g, b, 0, s>>>((const float*)ybuf, Kp, dense_out, gamma_post1,
-                                                  gamma_post2, eps, (float*)out, out_f32, H, tail,
-                                                  (const float*)resid, gamma_post_ff);
-  else if (yelem == ELEM_BF16 && oelem == ELEM_BF16)
-    finalize_kernel<bf16_t, bf16_t><<<g, b, 0, s>>>((const bf16_t*)ybuf, Kp, dense_out, gamma_post1,
-                                                    gamma_post2, eps, (bf16_t*)out, out_f32, H, tail,
-                                                    (const bf16_t*)resid, gamma_post_ff);
-  else if (yelem == ELEM_F32 && oelem == ELEM_BF16)
-    finalize_kernel<float, bf16_t><<<g, b, 0, s>>>((const float*)ybuf, Kp, dense_out, gamma_post1,
-                                                   gamma_post2, eps, (bf16_t*)out, out_f32, H, tail,
-                                                   (const bf16_t*)resid, gamma_post_ff);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  // rows up to 4096 elements: two groups of 8 per thread (fewer registers)
+  auto go = [&](auto g_tag) -> hipError_t {
+    constexpr int G = decltype(g_tag)::value;
+    if (yelem == ELEM_F32 && oelem == ELEM_F32)
+      finalize_kernel<float, float, G><<<g, b, 0, s>>>((const float*)ybuf, Kp, dense_out, gamma_post1,
+                                                       gamma_post2, eps, (float*)out, out_f32, H, tail,
+                                                       (const float*)resid, gamma_post_ff);
+    else if (yelem == ELEM_BF16 && oelem == ELEM_BF16)
+      finalize_kernel<bf16_t, bf16_t, G><<<g, b, 0, s>>>((const bf16_t*)ybuf, Kp, dense_out, gamma_post1,
+                                                         gamma_post2, eps, (bf16_t*)out, out_f32, H, tail,
+                                                         (const bf16_t*)resid, gamma_post_ff);
+    else if (yelem == ELEM_F32 && oelem == ELEM_BF16)
+      finalize_kernel<float, bf16_t, G><<<g, b, 0, s>>>((const float*)ybuf, Kp, dense_out, gamma_post1,
+                                                        gamma_post2, eps, (bf16_t*)out, out_f32, H, tail,
+                                                        (const bf16_t*)resid, gamma_post_ff);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  };
+  if (H <= NT * 8 * 2) return go(std::integral_constant<int, 2>{});
+  return go(std::integral_constant<int, 4>{});
 }
 
 hipError_t launch_gather_topk(const float* w_in, const int32_t* ids_in, int in_stride, int K, int64_t T,
