@@ -599,20 +599,28 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
   const rsrc_t rx = make_rsrc(a.x, (uint32_t)(T * H * 2));
 
   // 1. token rows and logits in flight together, then the routing of the T
-  //    tokens (every block computes the same routing); wave w takes tokens w
-  //    and w + PW
-  const int t0 = wave, t1 = wave + PW;
+  //    tokens (every block computes the same routing).  Up to PW / 2 tokens, wave
+  //    w routes token w while wave PW / 2 + w stages its row; more tokens, wave w
+  //    routes and stages tokens w and w + PW.
+  const bool split = T <= PW / 2;
+  const int rt0 = wave, rt1 = split ? T : wave + PW;                 // tokens this wave routes (< T)
+  const int st0 = split ? wave - PW / 2 : wave, st1 = split ? T : wave + PW;  // and stages (0 <= t < T)
   RowRegs xr0, xr1;
-  if (t0 < T) row_load(xr0, rx, t0, H, 0, lane);
-  if (t1 < T) row_load(xr1, rx, t1, H, 0, lane);
+  if (st0 >= 0 && st0 < T) row_load(xr0, rx, st0, H, 0, lane);
+  if (st1 < T) row_load(xr1, rx, st1, H, 0, lane);
   TokenLogits<VPL> z0, z1;
-  if (t0 < T) z0 = load_logits<VPL>(a.z + t0 * E, E, lane);
-  if (t1 < T) z1 = load_logits<VPL>(a.z + t1 * E, E, lane);
-  for (int i = threadIdx.x; i < Ep; i += PW * 64) s_flag[i] = 0;
-  for (int t = t0; t < T && t <= t1; t += PW) {
+  if (rt0 < T) z0 = load_logits<VPL>(a.z + rt0 * E, E, lane);
+  if (rt1 < T) z1 = load_logits<VPL>(a.z + rt1 * E, E, lane);
+  // one token (its Kp slots pick distinct experts: the top-k picks, then the
+  // shared ids E..): wave 0 ranks them into the ascending active list right
+  // after routing, one barrier in all
+  const bool one = T == 1 && Kp <= 64;
+  if (!one)
+    for (int i = threadIdx.x; i < Ep; i += PW * 64) s_flag[i] = 0;
+  for (int t = rt0; t < T && t <= rt1; t += PW) {
     float w;
     int id;
-    route_logits<VPL>(t == t0 ? z0 : z1, E, a.K, a.route, a.pes, lane, w, id);
+    route_logits<VPL>(t == rt0 ? z0 : z1, E, a.K, a.route, a.pes, lane, w, id);
     if (lane < a.K) {
       s_ids[t * Kp + lane] = id;
       s_w[t * Kp + lane] = w;
@@ -621,36 +629,52 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
       s_w[t * Kp + lane] = 1.f;
     }
   }
-  // expert input rows: pre_feedforward_layernorm_2(x) with the dense branch, x otherwise
-  if (t0 < T)
-    stage_token(xr0, true, rx, t0, H, a.dense != 0, a.eps, 1.f, a.dense ? a.g_pre2 : nullptr, sx, pitch, fac, lane, a.aq != 0);
-  if (t1 < T)
-    stage_token(xr1, true, rx, t1, H, a.dense != 0, a.eps, 1.f, a.dense ? a.g_pre2 : nullptr, sx, pitch, fac, lane, a.aq != 0);
-  __syncthreads();
-  for (int i = threadIdx.x; i < T * Kp; i += PW * 64) s_flag[s_ids[i]] = 1;
-  __syncthreads();
-  if (wave == 0) {  // ascending list of the experts with at least one slot, and each one's place in it
-    int base = 0;
-    for (int j = 0; j < Ep; j += 64) {
-      const int e = j + lane;
-      const bool f = e < Ep && s_flag[e];
-      const uint64_t mask = __ballot(f);
-      if (f) {
-        const int u = base + __popcll(mask & ((1ull << lane) - 1ull));
-        s_active[u] = e;
-        s_flag[e] = u;
-      }
-      base += __popcll(mask);
+  if (one && wave == 0) {
+    const int id = lane < Kp ? s_ids[lane] : 0x7fffffff;
+    int rank = 0;
+    for (int j = 0; j < Kp; ++j) rank += __shfl(id, j, 64) < id ? 1 : 0;
+    if (lane < Kp) {
+      s_active[rank] = id;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) s_slot[rank * 16 + c] = (int16_t)(c == 0 ? lane : -1);
     }
-    if (lane == 0) *s_nact = base;
+    if (lane == 0) *s_nact = Kp;
   }
+  // expert input rows: pre_feedforward_layernorm_2(x) with the dense branch, x otherwise
+  if (st0 >= 0 && st0 < T)
+    stage_token(xr0, true, rx, st0, H, a.dense != 0, a.eps, 1.f, a.dense ? a.g_pre2 : nullptr, sx, pitch, fac, lane,
+                a.aq != 0);
+  if (st1 < T)
+    stage_token(xr1, true, rx, st1, H, a.dense != 0, a.eps, 1.f, a.dense ? a.g_pre2 : nullptr, sx, pitch, fac, lane,
+                a.aq != 0);
   __syncthreads();
+  if (!one) {
+    for (int i = threadIdx.x; i < T * Kp; i += PW * 64) s_flag[s_ids[i]] = 1;
+    __syncthreads();
+    if (wave == 0) {  // ascending list of the experts with at least one slot, and each one's place in it
+      int base = 0;
+      for (int j = 0; j < Ep; j += 64) {
+        const int e = j + lane;
+        const bool f = e < Ep && s_flag[e];
+        const uint64_t mask = __ballot(f);
+        if (f) {
+          const int u = base + __popcll(mask & ((1ull << lane) - 1ull));
+          s_active[u] = e;
+          s_flag[e] = u;
+        }
+        base += __popcll(mask);
+      }
+      if (lane == 0) *s_nact = base;
+    }
+    __syncthreads();
+    const int na = *s_nact;
+    // slot of each (active expert, token): one write per slot through the experts' places
+    for (int i = threadIdx.x; i < na * 16; i += PW * 64) s_slot[i] = -1;
+    __syncthreads();
+    for (int i = threadIdx.x; i < T * Kp; i += PW * 64) s_slot[s_flag[s_ids[i]] * 16 + i / Kp] = (int16_t)i;
+    __syncthreads();
+  }
   const int n_act = *s_nact;
-  // slot of each (active expert, token): one write per slot through the experts' places
-  for (int i = threadIdx.x; i < n_act * 16; i += PW * 64) s_slot[i] = -1;
-  __syncthreads();
-  for (int i = threadIdx.x; i < T * Kp; i += PW * 64) s_slot[s_flag[s_ids[i]] * 16 + i / Kp] = (int16_t)i;
-  __syncthreads();
 
   // 2. the first expert block publishes the routing for the down kernel and the
   //    caller once its own items are issued (stores then never sit in front of
