@@ -609,8 +609,8 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
   if (st0 >= 0 && st0 < T) row_load(xr0, rx, st0, H, 0, lane);
   if (st1 < T) row_load(xr1, rx, st1, H, 0, lane);
   TokenLogits<VPL> z0, z1;
-  if (rt0 < T) z0 = load_logits<VPL>(a.z + rt0 * E, E, lane);
-  if (rt1 < T) z1 = load_logits<VPL>(a.z + rt1 * E, E, lane);
+  if (rt0 < T) z0 = load_logits<VPL>(a.z + rt0 * E, E, lane, a.pes);
+  if (rt1 < T) z1 = load_logits<VPL>(a.z + rt1 * E, E, lane, a.pes);
   // one token (its Kp slots pick distinct experts: the top-k picks, then the
   // shared ids E..): wave 0 ranks them into the ascending active list right
   // after routing, one barrier in all

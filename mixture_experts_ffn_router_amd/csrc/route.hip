@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // uniform per wave
   // the logits of token t: partial sums of the router GEMM's reduction parts, in part order
-  TokenLogits<VPL> z = load_logits<VPL>(logits + t * (int64_t)E, E, lane);
+  TokenLogits<VPL> z = load_logits<VPL>(logits + t * (int64_t)E, E, lane, pes);
   for (int q = 1; q < nparts; ++q) {
     const TokenLogits<VPL> zq = load_logits<VPL>(logits + q * part_stride + t * (int64_t)E, E, lane);
 #pragma unroll

@@ -12,16 +12,24 @@ namespace moe {
 // and expert id.  z points at the token's E logits; load_logits / route_logits
 // split the load from the arithmetic so a caller can issue several tokens'
 // loads at once.
-// The logits a lane holds: experts lane, lane + 64, ... (0 past E).
+// The logits a lane holds: experts lane, lane + 64, ... (0 past E), and, when
+// the layer has per-expert scales, those experts' scales (loaded with the
+// logits, so no load waits on the selection).
 template <int VPL>
 struct TokenLogits {
   float v[VPL];
+  float p[VPL];
 };
 template <int VPL>
-__device__ __forceinline__ TokenLogits<VPL> load_logits(const float* __restrict__ z, int E, int lane) {
+__device__ __forceinline__ TokenLogits<VPL> load_logits(const float* __restrict__ z, int E, int lane,
+                                                        const float* __restrict__ pes = nullptr) {
   TokenLogits<VPL> r;
 #pragma unroll
-  for (int j = 0; j < VPL; ++j) r.v[j] = lane + 64 * j < E ? z[lane + 64 * j] : 0.f;
+  for (int j = 0; j < VPL; ++j) {
+    const int idx = lane + 64 * j;
+    r.v[j] = idx < E ? z[idx] : 0.f;
+    r.p[j] = (pes && idx < E) ? pes[idx] : 1.f;
+  }
   return r;
 }
 
@@ -60,6 +68,8 @@ __device__ __forceinline__ void mask_groups(uint32_t (&key)[VPL], int E, int G, 
   }
 }
 
+// pes: the layer's per-expert scales (NULL: none); zl.p must hold them (load_logits
+// with the same pes).
 template <int VPL>
 __device__ __forceinline__ void route_logits(const TokenLogits<VPL>& zl, int E, int K, const RouteOpts& o,
                                              const float* __restrict__ pes, int lane, float& w_slot,
@@ -150,12 +160,21 @@ __device__ __forceinline__ void route_logits(const TokenLogits<VPL>& zl, int E, 
     my_e = sigmoid ? 1.0 / (1.0 + exp(-(double)zk)) : (double)expf(zk - m);
   }
   const double denom = wave_sum_f64(my_e);
+  // the scale of this slot's expert, from the lane that loaded it
+  float my_p = 1.f;
+  if (pes) {
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const float pj = __shfl(zl.p[j], my_id & 63, 64);
+      if ((my_id >> 6) == j) my_p = pj;
+    }
+  }
   w_slot = 0.f;
   id_slot = 0;
   if (lane < K) {
     const double d = o.renorm ? (denom > 0.0 ? denom : 1.0) : s_all;
     double w = my_e / d;
-    if (pes) w *= (double)pes[my_id];
+    if (pes) w *= (double)my_p;
     w_slot = (float)w;
     id_slot = my_id;
   }
