@@ -214,6 +214,32 @@ def test_fp8_activation_layers_take_the_decode_path_up_to_16_tokens():
     assert st0 == st1 == B.MOE_OK and n1 > n0 + 4096 * 256
 
 
+def test_decode_layout_exposes_h_and_the_fp8_activation_codes():
+    """On the decode path the layout query gives h per slot row and, with FP8
+    activations, the codes and scales of x and h, all inside the workspace the
+    size query reports; the grouped path's buffers are -1."""
+    lib = _lib()
+    fake = 0x1000  # never dereferenced: the query launches nothing
+    ts = B.Tensors(x=fake, w13=fake, w2=fake, out=fake, w_router=fake, w13_scale=fake, w2_scale=fake)
+    for aq in (0, 1):
+        d = _desc(act_quant=aq, weight_dtype=B.DT_FP8, top_k=2, num_experts=8, hidden=256, inter=512)
+        T = 5
+        lay = B.WorkspaceLayout()
+        assert lib.moe_forward_workspace_layout(C.byref(d), C.byref(ts), T, C.byref(lay)) == B.MOE_OK
+        _, total = _ws(d, T)
+        assert lay.path == 1 and lay.slots_per_token == 2 and lay.capacity == T * 2 and lay.y_parts == 0
+        assert lay.topk_w == lay.sorted_slots == lay.slot_row == lay.y == lay.x_expert == -1
+        assert 0 <= lay.h and lay.h + T * 2 * 512 * 2 <= total
+        bufs = [(lay.x_codes, T * 256), (lay.x_scales, T * 4), (lay.h_codes, T * 2 * 512), (lay.h_scales, T * 2 * 4)]
+        if aq:
+            for off, n in bufs:
+                assert off >= 0 and off % 256 == 0 and off + n <= total
+            ends = sorted((off, off + n) for off, n in bufs + [(lay.h, T * 2 * 512 * 2)])
+            assert all(a[1] <= b[0] for a, b in zip(ends, ends[1:])), "buffers overlap"
+        else:
+            assert all(off == -1 for off, _ in bufs)
+
+
 def test_mxfp4_layers_run_on_the_decode_path_only():
     lib = _lib()
     d = _desc(weight_dtype=B.DT_MXFP4)
