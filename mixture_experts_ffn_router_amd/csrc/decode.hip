@@ -611,10 +611,10 @@ __global__ __launch_bounds__(PW * 64, 4) void decode_up_kernel(DecodeArgs a) {
   TokenLogits<VPL> z0, z1;
   if (rt0 < T) z0 = load_logits<VPL>(a.z + rt0 * E, E, lane, a.pes);
   if (rt1 < T) z1 = load_logits<VPL>(a.z + rt1 * E, E, lane, a.pes);
-  // one token (its Kp slots pick distinct experts: the top-k picks, then the
-  // shared ids E..): wave 0 ranks them into the ascending active list right
+  // one token (its Kp <= 64 slots pick distinct experts: the top-k picks, then
+  // the shared ids E..): wave 0 ranks them into the ascending active list right
   // after routing, one barrier in all
-  const bool one = T == 1 && Kp <= 64;
+  const bool one = T == 1;
   if (!one)
     for (int i = threadIdx.x; i < Ep; i += PW * 64) s_flag[i] = 0;
   for (int t = rt0; t < T && t <= rt1; t += PW) {

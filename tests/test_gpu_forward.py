@@ -396,10 +396,14 @@ DECODE = {
     # fp8 weights on the whole-items-per-wave gate/up stream (8 experts x 512 items at
     # T=16: one item per wave or more) and the staged down stream, with bf16 h rows and
     # with FP8 activations (h codes)
+    # the most slots a token can have (top-62 plus two shared experts: 64, the
+    # routing wave's own active list at one token, shared ids included)
+    "k62_shared2_bf16": W.LayerSpec("dec_k62_sh2", 1, 128, 128, 62, 64, "silu", "bf16", n_shared=2, I_shared=64),
     "wide_fp8": W.LayerSpec("dec_wide_fp8", 1, 320, 8, 2, 8192, "silu", "fp8", supplied_logits=True),
     "wide_w8a8": W.LayerSpec("dec_wide_w8a8", 1, 320, 8, 2, 8192, "gelu_tanh", "fp8", act_quant="fp8_dynamic"),
 }
-DECODE_T = {"h8192": (1, 8), "e512_k64_bf16": (16,), "e512_k64_mxfp4": (16,), "wide_fp8": (8, 16),
+DECODE_T = {"h8192": (1, 8), "e512_k64_bf16": (1, 16), "e512_k64_mxfp4": (1, 16), "k62_shared2_bf16": (1, 2),
+            "wide_fp8": (8, 16),
             "wide_w8a8": (8, 16)}
 
 
