@@ -43,6 +43,13 @@ CASES = {
                                  per_expert_scale="uniform", I_dense=192, random_gammas=True, block_tail=True), 3),
     # the full-size Gemma-style layer at decode sizes
     "gemma_full_decode": (W.SPECS["gemma"].with_T(16), 1),
+    # decode path with FP8 activations: x and h codes, their scales and the slot
+    # weights in the scratch, left dirty by the first call for the second
+    "gemma_w8a8_decode": (W.LayerSpec("na_dec_w8a8", 16, 256, 16, 4, 128, "gelu_tanh", "fp8",
+                                      router_mode="gemma", per_expert_scale="uniform", I_dense=192,
+                                      random_gammas=True, block_tail=True, act_quant="fp8_dynamic"), 5),
+    # decode path with 4-bit expert weights
+    "mxfp4_decode": (W.LayerSpec("na_dec_mx", 16, 320, 8, 2, 576, "silu", "mxfp4"), 2),
 }
 
 
