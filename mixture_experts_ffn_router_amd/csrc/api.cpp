@@ -311,7 +311,8 @@ moe_status make_plan(const moe_layer_desc& d, const moe_tensors* t, int64_t T, P
     p.o_h = take((size_t)slots * d.inter * 2);
     p.o_dh = take(p.dense ? (size_t)T * d.inter_dense * 2 : 0);
     p.o_dout = take(p.dense ? (size_t)T * H * 4 : 0);
-    p.down_splits = moe::decode_down_splits((int)T, d.hidden, d.inter, p.dense);
+    const int wbits = d.weight_dtype == MOE_DT_FP8_E4M3 ? 8 : (d.weight_dtype == MOE_DT_MXFP4 ? 4 : 16);
+    p.down_splits = moe::decode_down_splits((int)T, d.hidden, d.inter, p.dense, p.Kp, wbits);
     p.o_ypart = take(p.dense || p.down_splits > 1 || d.block_tail ? (size_t)T * p.down_splits * H * 4 : 0);
     // FP8 activations: x codes and scales, h codes and scales per slot, slot weights
     p.o_xq = take(p.aq ? (size_t)T * H : 0);

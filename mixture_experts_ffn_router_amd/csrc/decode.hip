@@ -877,6 +877,23 @@ __device__ __forceinline__ f32x4 down_units(const DecodeArgs& a, int n_act, int 
   return acc[0];
 }
 
+// Splits per expert of the staged down stream, searched from s_min up (one
+// candidate per lane, so s_min .. s_min + 63): the split whose busiest wave
+// (units dealt round-robin over DW3 waves) has the fewest batches of DU steps,
+// ties to the fewer units.  The same in every wave of every block.
+template <int WK>
+__device__ __forceinline__ int staged_splits(int n_act, int MS, int s_min, int DU, int lane) {
+  const int steps = WK == WK_FP4 ? (MS + 1) / 2 : MS;  // MXFP4: pairs of steps
+  const int S = s_min + lane;
+  uint32_t key = 0xFFFFFFFFu;
+  if (S <= steps) {
+    const int spu = WK == WK_FP4 ? 2 * ((steps + S - 1) / S) : (steps + S - 1) / S;
+    const int cost = (n_act * S + DW3 - 1) / DW3 * ((spu + DU - 1) / DU);
+    key = (uint32_t)cost << 6 | (uint32_t)lane;
+  }
+  return s_min + (int)(wave_min_u32(key) & 63u);
+}
+
 // ---------------------------------------------------------------- down: dense down, expert down + combine
 template <int WK>
 __global__ __launch_bounds__(DW3 * 64, 4) void decode_down_kernel(DecodeArgs a) {
@@ -922,7 +939,13 @@ __global__ __launch_bounds__(DW3 * 64, 4) void decode_down_kernel(DecodeArgs a) 
   int k0, k1;  // this part's macro steps
   sub_range<WK>(0, I / 64, part, P, k0, k1);
   const int MS = k1 - k0;
-  const int S = max(1, min((DW3 + n_act - 1) / n_act, WK == WK_FP4 ? (MS + 1) / 2 : MS));  // further splits per expert over the waves
+  // further splits per expert over the waves: at least enough units for every wave
+  int S = max(1, min((DW3 + n_act - 1) / n_act, WK == WK_FP4 ? (MS + 1) / 2 : MS));
+  // More units than waves take the staged stream, whose units are dealt to the
+  // waves in turn: there the split is chosen to give the busiest wave the fewest
+  // batches (9 experts as 9 units on 8 waves: 2 whole units on one wave)
+  if (n_act * S > DW3)
+    S = staged_splits<WK>(n_act, MS, S, WK == WK_FP4 ? DU_FP4 : (WK == WK_FP8 ? (a.aq ? DU_FP8W : 2) : DU_BF16), lane);
   const int n_units = n_act * S;
   const rsrc_t rb = make_rsrc(a.hbuf, (uint32_t)((int64_t)T * a.Kp * I * 2));
   f32x4 tot = {0.f, 0.f, 0.f, 0.f};
@@ -1061,12 +1084,17 @@ hipError_t launch_decode_up(const DecodeArgs& args, int wk, hipStream_t s) {
 }
 
 // Parts per output-feature group of the down kernel: enough blocks for about two
-// per CU, when a finalize runs anyway (dense branch) or the call has 4+ tokens
-// (a finalize launch then costs less than the idle CUs); at most one per 64-deep
-// step of the reduction.
-int decode_down_splits(int T, int H, int I, bool dense) {
-  if (!dense && T < 4) return 1;
+// per CU, when a finalize runs anyway (dense branch), when the call has 4+ tokens,
+// or when the feature groups leave CUs idle while each streams a long range
+// (at most T * Kp experts' 16 rows of I weights of wbits bits: 256 KB or more);
+// a finalize launch then costs less than the idle CUs.  At most one part per
+// 64-deep step of the reduction.
+int decode_down_splits(int T, int H, int I, bool dense, int Kp, int wbits) {
   const int ng = H / 16;
+  if (!dense && T < 4) {
+    const int64_t block_bytes = (int64_t)T * Kp * 16 * I * wbits / 8;
+    if (ng >= device_cu_count() || block_bytes < (256 << 10)) return 1;
+  }
   int P = (2 * device_cu_count() + ng - 1) / ng;
   P = P < 1 ? 1 : (P > 4 ? 4 : P);
   return P < I / 64 ? P : I / 64;

@@ -170,7 +170,7 @@ struct DecodeArgs {
 int decode_up_lds_bytes(int T, int H, int Kp, int Ep);
 int decode_pre_lds_bytes(int T, int H);
 int decode_up_blocks_per_cu(int T, int H, int Kp, int Ep);
-int decode_down_splits(int T, int H, int I, bool dense);
+int decode_down_splits(int T, int H, int I, bool dense, int Kp, int wbits);
 hipError_t launch_decode_pre(const DecodeArgs& a, hipStream_t s);
 // wk: expert weight kind, 0 bf16, 1 FP8 E4M3, 2 MXFP4
 hipError_t launch_decode_up(const DecodeArgs& a, int wk, hipStream_t s);

@@ -105,15 +105,22 @@ __device__ __forceinline__ void route_logits(const TokenLogits<VPL>& zl, int E, 
   // bit from the top (a bit stays set while at least K keys are >= the prefix);
   // every key above tau is selected, and of the keys equal to tau the lowest
   // indices (index = lane + 64 j: all j = 0 before j = 1, ...) fill the rest.
-  // Counts come from ballots, so each step is a few scalar instructions.
+  // Counts come from ballots, so each step is a few scalar instructions.  Once
+  // exactly K keys are >= the prefix they are the K largest, and the rest of the
+  // bits cannot change the selection (below, every key above tau is taken and
+  // the keys equal to it complete K), so the search stops there: after about
+  // log2(E) informative bits when the top keys are distinct, all 32 with a tie
+  // at the K-th place.
   uint32_t tau = 0;
-#pragma unroll
   for (int b = 31; b >= 0; --b) {
     const uint32_t c = tau | (1u << b);
     int cnt = 0;
 #pragma unroll
     for (int j = 0; j < VPL; ++j) cnt += __popcll(__ballot(key[j] >= c));
-    if (cnt >= K) tau = c;
+    if (cnt >= K) {
+      tau = c;
+      if (cnt == K) break;
+    }
   }
   const uint64_t lt = (1ull << lane) - 1ull;
   int need = K;  // keys equal to tau still to take
