@@ -115,6 +115,12 @@ def test_workspace_size_grows_with_T_and_covers_buffers():
     dict(hidden=2048, num_experts=64, top_k=6, inter=1408, n_shared=2),          # DeepSeek-style
     dict(hidden=2816, num_experts=128, top_k=8, inter=704, inter_dense=2112),    # Gemma-style
     dict(hidden=256, num_experts=2, top_k=1, inter=4096),                        # long down reduction
+    # DeepSeek-V3 routing shape: below 4 tokens its decode down kernel splits the
+    # reduction into parts (128 feature groups, long per-block streams)
+    dict(hidden=2048, num_experts=256, top_k=8, inter=1408, n_shared=1, scoring=1, n_groups=8,
+         topk_groups=4),
+    # FP8 weights and activations: the decode layout (codes and scales) up to 16 tokens
+    dict(hidden=2816, num_experts=128, top_k=8, inter=704, weight_dtype=B.DT_FP8, act_quant=1),
 ])
 def test_workspace_size_never_decreases_with_T(shape):
     """A workspace sized for the largest T serves every smaller T: the reported
