@@ -71,11 +71,13 @@ STAGES = ["prenorm", "router", "route", "permute", "quant_x", "gate_up", "quant_
 _lib = None
 
 
-def load(path: str = LIB_PATH):
-    """Load the library (once).  Raises if it is missing: there is no fallback."""
+def load(path: Optional[str] = None):
+    """Load the library (once; `path` defaults to LIB_PATH, read at call time).
+    Raises if it is missing: there is no fallback."""
     global _lib
     if _lib is not None:
         return _lib
+    path = LIB_PATH if path is None else path
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with "
                           f"`python -m mixture_experts_ffn_router_amd.build`")

@@ -256,3 +256,23 @@ def test_mxfp4_layers_run_on_the_decode_path_only():
     assert st == B.MOE_UNSUPPORTED and b"decode path" in lib.moe_last_error()
     ts.w13_scale = None
     assert lib.moe_forward(C.byref(d), C.byref(ts), 4, fake, 1 << 40, None) == B.MOE_INVALID_ARG
+
+
+def test_every_entry_point_raises_without_the_library(monkeypatch, tmp_path):
+    """No fallback: with the library missing, the loader and the calls that go
+    through it raise instead of computing anything another way."""
+    missing = str(tmp_path / "libmoe_mi355x.so")
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", missing)
+    with pytest.raises(ImportError, match="is missing"):
+        B.load()
+    with pytest.raises(ImportError, match="is missing"):
+        B.permute_capacity(16, 2, 8, 64)
+    d = B.LayerDesc(hidden=256, num_experts=8, top_k=2, inter=512, act=0, act_dtype=B.DT_BF16,
+                    weight_dtype=B.DT_BF16, renormalize=1, eps=1e-6)
+    layer = B.DeviceLayer.__new__(B.DeviceLayer)
+    layer.desc = d
+    with pytest.raises(ImportError, match="is missing"):
+        layer.path(16)
+    with pytest.raises(ImportError, match="is missing"):
+        layer.workspace_size(16)
