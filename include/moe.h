@@ -210,6 +210,10 @@ typedef struct {
 /*
  * Bytes of workspace moe_forward needs for T tokens (*bytes set on MOE_OK).
  * Non-decreasing in T: a workspace sized for T serves every smaller T.
+ * MOE_UNSUPPORTED when one of the layout's buffers would pass 2 GiB (the kernels
+ * address them with 32-bit offsets): from some T on, and then for every larger
+ * T; from T = 0 for layers whose row padding alone (up to block_m - 1 rows per
+ * expert, times inter) passes it.
  */
 moe_status moe_forward_workspace_size(const moe_layer_desc* desc, int64_t T, size_t* bytes);
 

@@ -224,6 +224,35 @@ moe::RouteOpts layer_route_opts(const moe_layer_desc& d) {
   return o;
 }
 
+// The decode path's buffers for T tokens (offsets into the workspace, set in p,
+// and the parts of its down kernel); returns the bytes they span.  Needs p's
+// Kp, Ep, need_logits, dense and aq.
+size_t decode_layout(const moe_layer_desc& d, int64_t T, Plan& p) {
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t r = o;
+    o = align_up(o + bytes);
+    return r;
+  };
+  const size_t H = d.hidden;
+  const int64_t slots = T * p.Kp;
+  p.o_logits = take(p.need_logits ? (size_t)T * d.num_experts * 4 : 0);
+  p.o_rinfo = take((size_t)(1 + 17 * p.Ep) * 4);
+  p.o_h = take((size_t)slots * d.inter * 2);
+  p.o_dh = take(p.dense ? (size_t)T * d.inter_dense * 2 : 0);
+  p.o_dout = take(p.dense ? (size_t)T * H * 4 : 0);
+  const int wbits = d.weight_dtype == MOE_DT_FP8_E4M3 ? 8 : (d.weight_dtype == MOE_DT_MXFP4 ? 4 : 16);
+  p.down_splits = moe::decode_down_splits((int)T, d.hidden, d.inter, p.dense, p.Kp, wbits);
+  p.o_ypart = take(p.dense || p.down_splits > 1 || d.block_tail ? (size_t)T * p.down_splits * H * 4 : 0);
+  // FP8 activations: x codes and scales, h codes and scales per slot, slot weights
+  p.o_xq = take(p.aq ? (size_t)T * H : 0);
+  p.o_xs = take(p.aq ? (size_t)T * 4 : 0);
+  p.o_hq = take(p.aq ? (size_t)slots * d.inter : 0);
+  p.o_hs = take(p.aq ? (size_t)slots * 4 : 0);
+  p.o_slotw = take(p.aq ? (size_t)slots * 4 : 0);
+  return o;
+}
+
 moe_status make_plan(const moe_layer_desc& d, const moe_tensors* t, int64_t T, Plan& p) {
   p.f32 = d.act_dtype == MOE_DT_F32;
   p.Kp = d.top_k + d.n_shared;
@@ -235,8 +264,15 @@ moe_status make_plan(const moe_layer_desc& d, const moe_tensors* t, int64_t T, P
   // Every GEMM operand is addressed through a buffer resource with 32-bit offsets.
   const int64_t lim = (int64_t)1 << 31;
   const int64_t wb = d.weight_dtype == MOE_DT_FP8_E4M3 ? 1 : (d.weight_dtype == MOE_DT_F32 ? 4 : 2);
-  if (T * d.hidden * 4 >= lim || p.cap * d.inter * 4 >= lim || T * (int64_t)d.inter_dense * 4 >= lim)
+  if (T * d.hidden * 4 >= lim || T * (int64_t)d.inter_dense * 4 >= lim)
     return fail(MOE_UNSUPPORTED, "T = %lld too large: an activation buffer would exceed 2 GiB", (long long)T);
+  // The padding alone (up to block_m - 1 rows per expert) can pass the limit for
+  // layers with very many wide experts, at any T.
+  if (p.cap * d.inter * 4 >= lim)
+    return fail(MOE_UNSUPPORTED,
+                "T = %lld too large for this layer: the expert intermediate of %lld padded rows x inter %d "
+                "would exceed 2 GiB",
+                (long long)T, (long long)p.cap, d.inter);
   if ((int64_t)2 * d.inter * d.hidden * wb >= lim || (int64_t)2 * d.inter_dense * d.hidden * 4 >= lim ||
       (int64_t)d.num_experts * d.hidden * 4 >= lim)
     return fail(MOE_UNSUPPORTED, "one expert's weights exceed 2 GiB");
@@ -300,28 +336,24 @@ moe_status make_plan(const moe_layer_desc& d, const moe_tensors* t, int64_t T, P
     const size_t h_bytes = (size_t)p.cap * d.inter * ae;
     while (p.ks_r > 1 && (size_t)p.ks_r * T * d.num_experts * 4 > h_bytes) --p.ks_r;
   }
-  // The decode path lays out its own (smaller) buffers over the same workspace;
-  // the size reported stays that of the grouped path, so it grows with T.
+  // The decode path lays out its own buffers over the same workspace.  The size
+  // reported covers both layouts, and past the decode range still the largest
+  // decode layout: for small layers the decode path's fp32 partial rows can
+  // outweigh the grouped path's buffers, and the size must not fall where a call
+  // leaves the decode path.
   p.path_total = p.total;
   p.decode = use_decode(d, T);
   if (p.decode) {
-    o = 0;
-    p.o_logits = take(p.need_logits ? (size_t)T * d.num_experts * 4 : 0);
-    p.o_rinfo = take((size_t)(1 + 17 * p.Ep) * 4);
-    p.o_h = take((size_t)slots * d.inter * 2);
-    p.o_dh = take(p.dense ? (size_t)T * d.inter_dense * 2 : 0);
-    p.o_dout = take(p.dense ? (size_t)T * H * 4 : 0);
-    const int wbits = d.weight_dtype == MOE_DT_FP8_E4M3 ? 8 : (d.weight_dtype == MOE_DT_MXFP4 ? 4 : 16);
-    p.down_splits = moe::decode_down_splits((int)T, d.hidden, d.inter, p.dense, p.Kp, wbits);
-    p.o_ypart = take(p.dense || p.down_splits > 1 || d.block_tail ? (size_t)T * p.down_splits * H * 4 : 0);
-    // FP8 activations: x codes and scales, h codes and scales per slot, slot weights
-    p.o_xq = take(p.aq ? (size_t)T * H : 0);
-    p.o_xs = take(p.aq ? (size_t)T * 4 : 0);
-    p.o_hq = take(p.aq ? (size_t)slots * d.inter : 0);
-    p.o_hs = take(p.aq ? (size_t)slots * 4 : 0);
-    p.o_slotw = take(p.aq ? (size_t)slots * 4 : 0);
-    p.path_total = o;
-    if (o > p.total) p.total = o;
+    p.path_total = decode_layout(d, T, p);
+    if (p.path_total > p.total) p.total = p.path_total;
+  } else {
+    int64_t td = std::min<int64_t>(T, 16);  // decode-eligible T form a prefix: LDS needs grow with T
+    while (td >= 1 && !use_decode(d, td)) --td;
+    if (td >= 1) {
+      Plan q = p;
+      const size_t bytes = decode_layout(d, td, q);
+      if (bytes > p.total) p.total = bytes;
+    }
   }
   return MOE_OK;
 }

@@ -276,3 +276,68 @@ def test_every_entry_point_raises_without_the_library(monkeypatch, tmp_path):
         layer.path(16)
     with pytest.raises(ImportError, match="is missing"):
         layer.workspace_size(16)
+
+
+
+def _valid_desc(draw):
+    """A random descriptor inside the header's limits (every rule of moe.h)."""
+    from hypothesis import strategies as st
+    wd = draw(st.sampled_from([B.DT_BF16, B.DT_FP8, B.DT_MXFP4, B.DT_F32]))
+    f32 = wd == B.DT_F32
+    n_shared = 0 if wd in (B.DT_FP8, B.DT_MXFP4) else draw(st.integers(0, 8))
+    E = draw(st.integers(1, 512))
+    K = draw(st.integers(1, min(E, 64 - n_shared)))
+    kw = dict(hidden=64 * draw(st.integers(1, 128)), num_experts=E, top_k=K, inter=64 * draw(st.integers(1, 256)),
+              act=draw(st.integers(0, 1)), act_dtype=B.DT_F32 if f32 else B.DT_BF16, weight_dtype=wd,
+              renormalize=draw(st.integers(0, 1)), router_mode=draw(st.integers(0, 1)), n_shared=n_shared,
+              inter_dense=64 * draw(st.integers(0, 64)), dense_act=draw(st.integers(0, 1)),
+              scoring=draw(st.integers(0, 1)), block_tail=draw(st.integers(0, 1)),
+              combine=0 if f32 else draw(st.integers(0, 1)),
+              act_quant=1 if wd == B.DT_FP8 and draw(st.booleans()) else 0)
+    groups = [g for g in range(2, 65) if E % g == 0]
+    if groups and draw(st.booleans()):
+        G = draw(st.sampled_from(groups))
+        kg_min = -(-K // (E // G))  # the picked groups must hold at least K experts
+        kw.update(n_groups=G, topk_groups=draw(st.integers(kg_min, G)))
+    return _desc(**kw)
+
+
+def test_workspace_size_never_decreases_for_random_layers():
+    """The size contract (non-decreasing in T, so a workspace sized for the
+    largest T serves every smaller one) over random layers inside every limit the
+    header states: each T up to 300 (the decode range and the row-block changes
+    of small batches), then T growing by an eighth up to 2^17.  A layer whose
+    buffers would pass 2 GiB is refused from some T on (from T = 0 when the row
+    padding of very many wide experts alone passes it), and then for every larger
+    T.  Every size also holds the gated intermediate of all T * (top_k +
+    n_shared) rows."""
+    hyp = pytest.importorskip("hypothesis")
+    from hypothesis import strategies as st
+    Ts = list(range(0, 301))
+    while Ts[-1] < 1 << 17:
+        Ts.append(Ts[-1] + max(1, Ts[-1] // 8))
+
+    seen = []
+
+    @hyp.settings(max_examples=400, deadline=None, derandomize=True)
+    @hyp.given(st.composite(_valid_desc)())
+    def run(d):
+        seen.append((d.num_experts, d.hidden, d.inter, d.weight_dtype))
+        prev, refused = 0, None
+        ae = 4 if d.act_dtype == B.DT_F32 else 2
+        for T in Ts:
+            st_, n = _ws(d, T)
+            if refused is not None:
+                assert st_ == B.MOE_UNSUPPORTED, f"T = {T} accepted after T = {refused} was refused"
+                continue
+            if st_ == B.MOE_UNSUPPORTED:  # from T = 0 on when the padding alone passes the limit
+                assert b"would exceed 2 GiB" in _lib().moe_last_error(), _lib().moe_last_error()
+                refused = T
+                continue
+            assert st_ == B.MOE_OK, _lib().moe_last_error()
+            assert n >= prev, f"workspace size falls from {prev} to {n} at T = {T}"
+            assert n >= T * (d.top_k + d.n_shared) * d.inter * ae
+            prev = n
+
+    run()
+    assert len(set(seen)) >= 100, len(set(seen))
