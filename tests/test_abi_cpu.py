@@ -323,6 +323,9 @@ def test_workspace_size_never_decreases_for_random_layers():
     @hyp.given(st.composite(_valid_desc)())
     def run(d):
         seen.append((d.num_experts, d.hidden, d.inter, d.weight_dtype))
+        # the T that take the decode path form a prefix of 1..16 (its LDS needs grow with T)
+        paths = [_lib().moe_forward_path(C.byref(d), T) for T in range(1, 18)]
+        assert paths == sorted(paths, reverse=True) and paths[-1] == 0, paths
         prev, refused = 0, None
         ae = 4 if d.act_dtype == B.DT_F32 else 2
         for T in Ts:
