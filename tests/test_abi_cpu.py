@@ -344,3 +344,66 @@ def test_workspace_size_never_decreases_for_random_layers():
 
     run()
     assert len(set(seen)) >= 100, len(set(seen))
+
+
+def _layout_extents(d, lay, T):
+    """(name, offset, bytes) of every buffer the layout query reports, with the
+    shapes moe.h gives for them."""
+    Kp, Ep = d.top_k + d.n_shared, d.num_experts + d.n_shared
+    H, I, cap = d.hidden, d.inter, lay.capacity
+    ae = 4 if d.act_dtype == B.DT_F32 else 2
+    if lay.path == 1:  # decode: h per slot row, FP8 activation codes and scales
+        bufs = [("h", lay.h, T * Kp * I * 2), ("x_codes", lay.x_codes, T * H), ("x_scales", lay.x_scales, T * 4),
+                ("h_codes", lay.h_codes, T * Kp * I), ("h_scales", lay.h_scales, T * Kp * 4)]
+    else:
+        y_bytes = T * H * 4 if lay.y_parts == 0 else T * Kp * lay.y_parts * H * (4 if lay.y_f32 else ae)
+        bufs = [("topk_w", lay.topk_w, T * Kp * 4), ("topk_ids", lay.topk_ids, T * Kp * 4),
+                ("counts", lay.counts, Ep * 4), ("offsets", lay.offsets, (Ep + 1) * 4),
+                ("sorted_slots", lay.sorted_slots, cap * 4), ("block_expert", lay.block_expert, cap // lay.block_m * 4),
+                ("slot_row", lay.slot_row, T * Kp * 4), ("inv_rms", lay.inv_rms, T * 4),
+                ("x_expert", lay.x_expert, T * H * ae), ("h", lay.h, cap * I * ae), ("y", lay.y, y_bytes),
+                ("x_codes", lay.x_codes, T * H), ("x_scales", lay.x_scales, T * 4),
+                ("h_codes", lay.h_codes, cap * I), ("h_scales", lay.h_scales, cap * 4)]
+    return [b for b in bufs if b[1] != -1]
+
+
+def test_workspace_layout_fits_the_reported_size_for_random_layers():
+    """For random layers and token counts, every buffer the layout query reports
+    (at the shape the header gives it) is 256-byte aligned, lies inside the
+    workspace the size query asks for, and overlaps no other; the grouped path's
+    capacity is the padded total moe_permute_capacity gives, and the decode path
+    keeps one h row per slot."""
+    hyp = pytest.importorskip("hypothesis")
+    from hypothesis import strategies as st
+    lib = _lib()
+    fake = 0x1000  # never dereferenced: the queries launch nothing
+    seen = []
+
+    @hyp.settings(max_examples=300, deadline=None, derandomize=True)
+    @hyp.given(st.composite(_valid_desc)(), st.sampled_from([1, 2, 5, 16, 17, 64, 129, 300, 1000, 4099]))
+    def run(d, T):
+        ts = B.Tensors(x=fake, w13=fake, w2=fake, out=fake, w_router=fake, w13_scale=fake, w2_scale=fake,
+                       shared_w13=fake if d.n_shared else None, shared_w2=fake if d.n_shared else None,
+                       dense_w13=fake if d.inter_dense else None, dense_w2=fake if d.inter_dense else None)
+        st_, total = _ws(d, T)
+        if st_ == B.MOE_UNSUPPORTED:
+            return
+        assert st_ == B.MOE_OK
+        lay = B.WorkspaceLayout()
+        assert lib.moe_forward_workspace_layout(C.byref(d), C.byref(ts), T, C.byref(lay)) == B.MOE_OK
+        assert lay.path == lib.moe_forward_path(C.byref(d), T)
+        Kp = d.top_k + d.n_shared
+        if lay.path == 1:
+            assert lay.capacity == T * Kp
+        else:
+            assert lay.capacity == lib.moe_permute_capacity(T, Kp, d.num_experts + d.n_shared, lay.block_m)
+        bufs = _layout_extents(d, lay, T)
+        for name, off, n in bufs:
+            assert off % 256 == 0 and 0 <= off and off + n <= total, (name, off, n, total)
+        ends = sorted((off, off + n, name) for name, off, n in bufs if n)
+        for a, b in zip(ends, ends[1:]):
+            assert a[1] <= b[0], f"{a[2]} and {b[2]} overlap"
+        seen.append((lay.path, T))
+
+    run()
+    assert {p for p, _ in seen} == {0, 1} and len(seen) >= 200, len(seen)
