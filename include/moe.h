@@ -149,7 +149,12 @@ moe_status moe_permute(const int32_t* topk_ids, int64_t T, int32_t K, int32_t E,
                        int32_t* counts, int32_t* offsets, int32_t* sorted_slots,
                        int32_t* block_expert, int32_t* num_padded, int32_t* slot_row, void* stream);
 
-/* Layer description (host memory, read during the call only). */
+/* Layer description (host memory, read during the call only).  Besides the
+ * per-field rules below, the kernels address each operand with 32-bit byte
+ * offsets: one routed expert's w13 (2 * inter * hidden elements, counted at 1
+ * byte for fp8, 2 for bf16 and MXFP4, 4 for fp32), the dense w13 (2 *
+ * inter_dense * hidden * 4 bytes) and the router (num_experts * hidden * 4
+ * bytes) must each stay under 2 GiB, else MOE_UNSUPPORTED. */
 typedef struct {
   int32_t hidden;        /* H, multiple of 64 */
   int32_t num_experts;   /* E routed experts, 1..512 */

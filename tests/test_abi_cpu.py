@@ -407,3 +407,67 @@ def test_workspace_layout_fits_the_reported_size_for_random_layers():
 
     run()
     assert {p for p, _ in seen} == {0, 1} and len(seen) >= 200, len(seen)
+
+
+def _header_accepts(d):
+    """The descriptor rules as include/moe.h states them (field comments, the
+    routing limits of moe_route, and the 2 GiB rule for one expert's weights)."""
+    H, E, K, I = d.hidden, d.num_experts, d.top_k, d.inter
+    wd, f32 = d.weight_dtype, d.act_dtype == B.DT_F32
+    rules = [
+        0 < H <= 8192 and H % 64 == 0, 1 <= E <= 512, 1 <= K <= min(E, 64), I > 0 and I % 64 == 0,
+        d.act in (0, 1), d.act_dtype in (B.DT_F32, B.DT_BF16),
+        wd == B.DT_F32 if f32 else wd in (B.DT_BF16, B.DT_FP8, B.DT_MXFP4),
+        d.router_mode in (0, 1), 0 <= d.n_shared <= 8,
+        not (wd in (B.DT_FP8, B.DT_MXFP4) and d.n_shared), K + d.n_shared <= 64,
+        d.inter_dense >= 0 and d.inter_dense % 64 == 0, not d.inter_dense or d.dense_act in (0, 1),
+        d.eps >= 0, d.scoring in (0, 1), 0 <= d.n_groups <= 64, d.act_quant in (0, 1),
+        not d.act_quant or (wd == B.DT_FP8 and not f32 and I <= 16384),
+        d.block_tail in (0, 1), d.combine in (0, 1), not (d.combine == 1 and f32),
+    ]
+    if d.n_groups > 1:
+        G, KG = d.n_groups, d.topk_groups
+        rules += [E % G == 0, 1 <= KG <= G, KG * (E // G) >= K if E % G == 0 else False]
+    wb = {B.DT_FP8: 1, B.DT_F32: 4}.get(wd, 2)
+    if all(rules):  # the 32-bit offset rule, only meaningful for otherwise valid sizes
+        rules += [2 * I * H * wb < 2 ** 31, 2 * d.inter_dense * H * 4 < 2 ** 31, E * H * 4 < 2 ** 31]
+    return all(rules)
+
+
+def test_descriptor_validation_follows_the_header():
+    """20000 random descriptors, each field drawn mostly from valid values and
+    sometimes from invalid ones: the library accepts exactly those the header's
+    rules accept (besides a layer whose row padding alone passes 2 GiB, which the
+    size query refuses by name), and every refusal carries a message."""
+    import numpy as np
+    lib = _lib()
+    rng = np.random.default_rng(3)
+
+    def pick(valid, invalid, p=0.08):
+        return int(rng.choice(invalid)) if rng.random() < p else int(rng.choice(valid))
+
+    accepted = 0
+    for _ in range(20000):
+        E = pick([1, 2, 8, 64, 128, 256, 512, int(rng.integers(1, 513))], [0, -1, 513, 1024])
+        d = _desc(hidden=pick([64, 128, 2816, 4096, 8192], [0, -64, 32, 100, 8256, 16384]),
+                  num_experts=E, top_k=pick([1, 2, 8, max(1, min(E, 64)), int(rng.integers(1, 65))], [0, -1, 65, 600]),
+                  inter=pick([64, 512, 704, 14336, 16384, 16448, 65536], [0, -64, 100, 32]),
+                  act=pick([0, 1], [2, -1]), act_dtype=pick([0, 1], [2, 3, -1]), weight_dtype=pick([0, 1, 2, 3], [4, -1]),
+                  renormalize=pick([0, 1, 5], [0]), router_mode=pick([0, 1], [2, -1]),
+                  n_shared=pick([0, 0, 1, 2, 8], [9, -1]), inter_dense=pick([0, 0, 64, 2112], [-64, 100]),
+                  dense_act=pick([0, 1], [2, -1]),
+                  eps=float(rng.choice([1e-6, 0.0])) if rng.random() > 0.05 else float(rng.choice([-1.0, np.nan])),
+                  scoring=pick([0, 1], [2, -1]), n_groups=pick([0, 1, 2, 4, 8, 16, 64], [-1, 3, 65, 128]),
+                  topk_groups=pick([0, 1, 2, 3, 4, 8], [-1, 65]), act_quant=pick([0, 1], [2, -1]),
+                  block_tail=pick([0, 1], [2, -1]), combine=pick([0, 1], [2, -1]))
+        st, _ = _ws(d, 16)
+        msg = lib.moe_last_error()
+        expect = _header_accepts(d)
+        if expect and st == B.MOE_UNSUPPORTED and b"padded rows" in msg:
+            Kp, Ep = d.top_k + d.n_shared, d.num_experts + d.n_shared
+            assert (16 * Kp + Ep * 255) * d.inter * 4 >= 2 ** 31, msg  # padding at the largest row block
+            continue
+        assert (st == B.MOE_OK) == expect, (st, msg, {f: getattr(d, f) for f, _ in B.LayerDesc._fields_})
+        assert st == B.MOE_OK or msg
+        accepted += st == B.MOE_OK
+    assert accepted >= 200, accepted
