@@ -471,3 +471,28 @@ def test_descriptor_validation_follows_the_header():
         assert st == B.MOE_OK or msg
         accepted += st == B.MOE_OK
     assert accepted >= 200, accepted
+
+
+def test_route_validation_follows_the_header():
+    """moe_route at T = 0 (nothing launches) over random options: accepted exactly
+    when the header's limits hold (1 <= K <= E <= 512, K <= 64, a known scoring,
+    no groups or 2..64 groups dividing E with 1..n_groups picked that hold at
+    least K experts), and every refusal carries a message."""
+    import numpy as np
+    lib = _lib()
+    rng = np.random.default_rng(4)
+    accepted = 0
+    for _ in range(20000):
+        E = int(rng.choice([-1, 0, 1, 2, 7, 8, 64, 128, 256, 512, 513, int(rng.integers(1, 600))]))
+        K = int(rng.choice([-1, 0, 1, 2, 5, 8, 64, 65, int(rng.integers(1, 80))]))
+        scoring = int(rng.choice([0, 1, 1, 2, -1]))
+        G = int(rng.choice([-1, 0, 1, 2, 3, 4, 8, 16, 64, 65, 128]))
+        KG = int(rng.choice([-1, 0, 1, 2, 3, 4, 8, 64, 65]))
+        ok = 1 <= K <= E <= 512 and K <= 64 and scoring in (0, 1) and 0 <= G <= 64
+        if ok and G > 1:
+            ok = E % G == 0 and 1 <= KG <= G and KG * (E // G) >= K
+        st = lib.moe_route(None, 0, E, K, 1, scoring, G, KG, None, None, None, None)
+        assert (st == B.MOE_OK) == ok, (E, K, scoring, G, KG, st, lib.moe_last_error())
+        assert st == B.MOE_OK or lib.moe_last_error()
+        accepted += ok
+    assert accepted >= 1000, accepted
