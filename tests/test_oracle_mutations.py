@@ -158,3 +158,72 @@ def test_mxfp4_scale_blocks_of_16_are_caught(monkeypatch):
         return O.decode_e2m1(codes) * sc
     monkeypatch.setattr(O, "decode_mxfp4", bad)
     _fails(P.test_mxfp4_layer_equals_layer_on_torch_decoded_weights)
+
+
+def test_unstable_permutation_is_caught(monkeypatch):
+    orig = O.permutation
+
+    def bad(ids, E):  # each expert's slots in descending flat order
+        counts, offsets, order = orig(ids, E)
+        order = np.concatenate([order[offsets[e]:offsets[e + 1]][::-1] for e in range(E)] or [order])
+        return counts, offsets, order.astype(np.int64)
+    monkeypatch.setattr(O, "permutation", bad)
+    _fails(P.test_permutation_matches_stable_argsort, 33, 8, 2)
+
+
+def test_gemma_router_without_the_hidden_size_factor_is_caught(monkeypatch):
+    orig = O.router_input
+
+    def bad(x, mode="plain", router_scale=None, eps=O.RMS_EPS):
+        r = orig(x, mode, router_scale, eps)
+        return r * np.sqrt(np.asarray(x).shape[-1]) if mode == "gemma" else r
+    monkeypatch.setattr(O, "router_input", bad)
+    _fails(P.test_router_input_has_unit_norm)
+    _fails(P.test_gemma_branch_matches_torch_composition)
+
+
+def test_scale_before_renormalisation_is_caught(monkeypatch):
+    orig = O.route
+
+    def bad(z, k, renormalize=True, per_expert_scale=None, *rest):
+        w, ids = orig(z, k, False, None, *rest)
+        if per_expert_scale is not None:
+            w = w * np.asarray(per_expert_scale, dtype=np.float64)[ids]
+        if renormalize:
+            w = w / w.sum(axis=-1, keepdims=True)  # the scale is renormalised away
+        return w, ids
+    monkeypatch.setattr(O, "route", bad)
+    _fails(P.test_scale_fold_identity)
+
+
+def test_shared_experts_not_at_unit_weight_are_caught(monkeypatch):
+    orig = O.moe_layer
+
+    def bad(x, layer, rows=None, logits=None, h_fp8=None):
+        sh = layer.get("shared")
+        if sh is not None:  # shared experts at weight 1/2: their down projections halved
+            sh = (sh[0], np.asarray(sh[1], dtype=np.float64) * 0.5)
+        return orig(x, dict(layer, shared=sh), rows, logits, h_fp8)
+    monkeypatch.setattr(O, "moe_layer", bad)
+    _fails(P.test_two_shared_experts_equal_one_of_double_width)
+
+
+def test_rmsnorm_eps_outside_the_root_is_caught(monkeypatch):
+    def bad(x, gamma=None, eps=O.RMS_EPS):
+        x = np.asarray(x, dtype=np.float64)
+        y = x / (np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) + eps)
+        return y if gamma is None else y * np.asarray(gamma, dtype=np.float64)
+    monkeypatch.setattr(O, "rmsnorm", bad)
+    _fails(P.test_gemma_branch_matches_torch_composition)
+
+
+def test_swapped_post_norm_weights_are_caught(monkeypatch):
+    orig = O.moe_layer
+
+    def bad(x, layer, rows=None, logits=None, h_fp8=None):
+        d = layer.get("dense")
+        if d is not None:
+            d = dict(d, gamma_post1=d.get("gamma_post2"), gamma_post2=d.get("gamma_post1"))
+        return orig(x, dict(layer, dense=d), rows, logits, h_fp8)
+    monkeypatch.setattr(O, "moe_layer", bad)
+    _fails(P.test_gemma_branch_matches_torch_composition)
