@@ -496,3 +496,24 @@ def test_route_validation_follows_the_header():
         assert st == B.MOE_OK or lib.moe_last_error()
         accepted += ok
     assert accepted >= 1000, accepted
+
+
+def test_permute_capacity_follows_the_header_formula():
+    """floor((T*K + E*(block_m-1)) / block_m) * block_m for valid arguments, -1 for
+    T < 0, K < 1, E < 1 or a block_m that is not a power of two in [16, 256]; the
+    capacity always holds every slot plus each expert's padding."""
+    import numpy as np
+    lib = _lib()
+    rng = np.random.default_rng(6)
+    for _ in range(20000):
+        T = int(rng.choice([-1, 0, 1, 16, 17, int(rng.integers(0, 1 << 20))]))
+        K = int(rng.choice([-1, 0, 1, 2, 8, 64, int(rng.integers(1, 65))]))
+        E = int(rng.choice([-1, 0, 1, 8, 128, 1024, int(rng.integers(1, 1025))]))
+        bm = int(rng.choice([-16, 0, 8, 16, 32, 48, 64, 128, 256, 512, int(rng.integers(1, 300))]))
+        got = lib.moe_permute_capacity(T, K, E, bm)
+        valid = T >= 0 and K >= 1 and E >= 1 and bm in (16, 32, 64, 128, 256)
+        if not valid:
+            assert got == -1, (T, K, E, bm, got)
+            continue
+        assert got == (T * K + E * (bm - 1)) // bm * bm, (T, K, E, bm, got)
+        assert got % bm == 0 and got >= T * K
